@@ -1,0 +1,43 @@
+"""CPU oracle for routed top-k sparse attention with a cross-layer shared index.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import or run anything here.
+The product path (the HIP library and its Python binding) never imports
+this package, and this package imports nothing from the product path; the
+two share only the seeded input generator in ``synth``.
+
+Everything here is the plain, slow definition of what the method computes:
+
+* indexer scores in exact integer arithmetic (int64),
+* top-k selection by a stable sort with the lowest position winning ties,
+* softmax attention in float64 with the row sum checked,
+* gist-chunk selection and unfolding (GSA/SSA) the same way,
+* the layer-group driver that computes one index set per group of layers.
+
+Sources (web pages on long-context sparse attention):
+
+* "You Only Index Once" (CLSA) explainer -- section 1.1 (attention formula),
+  sections 2.2-2.3 (indexer / selector / sharer workflow).
+* "长上下文：稀疏注意力 / DSA / IndexShare" tutorial -- DSA and IndexShare
+  section (lightning indexer, top-k, 4 layers share one index), KV-cache
+  volume section and the hands-on arithmetic section.
+* SSA article (arXiv 2604.20920) -- sections 2-3 (gist tokens, selective
+  unfolding, keep selected chunks' gists with their raw tokens), section 6
+  (key-order invariance, split decode with log-sum-exp merge).
+* IndexCache article (arXiv 2603.12201) -- section 2 (Full / Shared layers),
+  section 6 (one conditional plus one temporary index buffer).
+* GSA summary page (gist.science) -- section 2.2 (selective unfolding).
+
+Pins: every function is checked against values the pages print, closed
+forms, library routines for the special cases the method reduces to, and
+brute force on tiny inputs (``tests/test_oracle_pins.py``).  No function in
+this package is "parity unpinned".
+"""
+
+from .indexer import index_scores, index_scores_row  # noqa: F401
+from .topk import select_topk  # noqa: F401
+from .attention import softmax_attention, sparse_attention_gqa  # noqa: F401
+from .gsa import gist_scores, gsa_key_positions, gsa_attention, gsa_select  # noqa: F401
+from .driver import (decode_group, decode_layers, decode_step, gsa_step,  # noqa: F401
+                     prefill_attention_rows, prefill_index_rows)
+from .sizes import kv_cache_gib, kv_bytes_per_token, scored_pairs  # noqa: F401

@@ -1,0 +1,388 @@
+"""Pins for the CPU oracle: checks against facts that do not come from the oracle.
+
+Each ``pin_*`` function takes the oracle functions it checks as arguments
+and raises ``AssertionError`` on any mismatch, so the same pin can be run
+against the real oracle (must pass) and against a copy with a planted
+mistake (must fail, see ``test_oracle_mutants.py``).
+
+What the pins compare against:
+
+* closed forms and invariants of the indexer's bilinear score (one-hot
+  keys pick out coordinates, the best key for a query has a closed-form
+  score, additivity in the key),
+* a rank-counting characterisation of top-k, brute force over tiny rows,
+* ``torch.nn.functional.scaled_dot_product_attention`` (float64, CPU) for
+  the dense special cases (k >= number of valid keys; causal prefill rows
+  below k; GSA with every chunk chosen),
+* numbers printed on the pages (``tests/golden/pages_worked_values.json``).
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_worked_values.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _sdpa(q, k, v, scale, causal=False, gqa=False):
+    """Textbook attention via torch (float64, CPU). q[H, m, D], k/v[Hk, n, D]."""
+    q = torch.as_tensor(np.asarray(q, np.float64))
+    k = torch.as_tensor(np.asarray(k, np.float64))
+    v = torch.as_tensor(np.asarray(v, np.float64))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q[None], k[None], v[None], scale=scale, is_causal=causal, enable_gqa=gqa)
+    return o[0].numpy()
+
+
+# --------------------------------------------------------------------------
+# indexer
+# --------------------------------------------------------------------------
+
+def pin_index_scores(index_scores):
+    rng = np.random.default_rng(11)
+    B, Lq, H, d = 2, 3, 3, 5
+    HD = H * d
+    qi = rng.integers(-128, 128, size=(B, Lq, HD)).astype(np.int8)
+    # keys 0..HD-1 are one-hot (+1 at feature t), key HD.. are per-head blocks,
+    # then the best key per query row of batch 0, then random keys.
+    keys = []
+    for j in range(HD):
+        e = np.zeros(HD, np.int64)
+        e[j] = 1
+        keys.append(e)
+    for h in range(H):
+        e = np.zeros(HD, np.int64)
+        e[h * d:(h + 1) * d] = -3
+        keys.append(e)
+    n_fixed = len(keys)
+    rand = rng.integers(-128, 128, size=(6, HD))
+    L = n_fixed + Lq + rand.shape[0]
+    ki = np.zeros((B, L, HD), np.int8)
+    for b in range(B):
+        ki[b, :n_fixed] = np.stack(keys)
+        best = np.where(qi[b].astype(np.int64) >= 0, 127, -128)   # maximises every product
+        ki[b, n_fixed:n_fixed + Lq] = best
+        ki[b, n_fixed + Lq:] = rand
+    s = np.asarray(index_scores(qi, ki, H), dtype=np.int64)
+    assert s.shape == (B, Lq, L), s.shape
+    q64 = qi.astype(np.int64)
+    # one-hot keys pick out single query features
+    assert np.array_equal(s[:, :, :HD], q64), "one-hot key must return that query coordinate"
+    # a constant block on head h returns -3 x (sum of head h's query features)
+    for h in range(H):
+        exp = -3 * q64[:, :, h * d:(h + 1) * d].sum(-1)
+        assert np.array_equal(s[:, :, HD + h], exp), "per-head block key"
+    # the best key for row r scores sum_j max(127 q_j, -128 q_j)
+    for r in range(Lq):
+        exp = np.maximum(127 * q64[:, r], -128 * q64[:, r]).sum(-1)
+        assert np.array_equal(s[:, r, n_fixed + r], exp), "closed-form maximum score"
+        assert np.all(s[:, r, :] <= exp[:, None]), "no key may beat the maximising key"
+    # additivity in the key: s(q, a + b) = s(q, a) + s(q, b) for keys that stay in int8
+    a = rng.integers(-60, 60, size=(1, 4, HD)).astype(np.int8)
+    b2 = rng.integers(-60, 60, size=(1, 4, HD)).astype(np.int8)
+    ab = (a.astype(np.int64) + b2.astype(np.int64)).astype(np.int8)
+    q1 = qi[:1]
+    assert np.array_equal(index_scores(q1, ab, H),
+                          np.asarray(index_scores(q1, a, H)) + np.asarray(index_scores(q1, b2, H)))
+
+
+# --------------------------------------------------------------------------
+# top-k
+# --------------------------------------------------------------------------
+
+def _rank_select(row, k, nv):
+    """Brute force: position i is chosen iff fewer than k valid positions precede it.
+
+    j precedes i when s_j > s_i, or s_j == s_i and j < i.
+    """
+    chosen = []
+    for i in range(nv):
+        rank = 0
+        for j in range(nv):
+            if row[j] > row[i] or (row[j] == row[i] and j < i):
+                rank += 1
+        if rank < k:
+            chosen.append(i)
+    return chosen
+
+
+def pin_topk(select_topk):
+    rng = np.random.default_rng(5)
+    alphabets = [[0], [0, 1], [-1, 0, 1], list(range(-4, 5)), list(range(-1000, 1000))]
+    for alpha in alphabets:
+        for n in (1, 2, 5, 17, 40):
+            rows = rng.choice(alpha, size=(3, n)).astype(np.int64)
+            for k in sorted({1, 2, n // 2 + 1, n, n + 3}):
+                for nv in sorted({n, max(0, n - 3), 0, min(n, 1)}):
+                    got = np.asarray(select_topk(rows, k, nv))
+                    assert got.shape == (3, k)
+                    for r in range(3):
+                        exp = _rank_select(rows[r], k, nv)
+                        want = np.full(k, -1)
+                        want[:len(exp)] = exp
+                        assert np.array_equal(got[r], want), (alpha[:3], n, k, nv, got[r], want)
+    # per-row valid lengths
+    rows = rng.integers(-3, 3, size=(6, 12))
+    vl = np.array([0, 1, 5, 12, 7, 3])
+    got = np.asarray(select_topk(rows, 4, vl))
+    for r in range(6):
+        exp = _rank_select(rows[r], 4, vl[r])
+        assert list(got[r][got[r] >= 0]) == exp
+    # floats, including signed zeros (equal values) and exact ties
+    f = np.array([[0.0, -0.0, 1.5, 1.5, -2.0, 0.0, 3.25, -0.0]], dtype=np.float32)
+    got = np.asarray(select_topk(f, 5))
+    assert list(got[0]) == _rank_select(list(f[0]), 5, 8), got
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+def pin_attention(softmax_attention, sparse_attention_gqa):
+    rng = np.random.default_rng(7)
+    n, D, Hq, Hkv = 37, 16, 8, 2
+    q = rng.standard_normal((Hq, D))
+    k = rng.standard_normal((n, Hkv, D))
+    v = rng.standard_normal((n, Hkv, D))
+    scale = 1.0 / math.sqrt(D)
+    got = np.asarray(sparse_attention_gqa(q, k, v, scale))
+    # all keys selected: the textbook formula (torch SDPA, GQA convention)
+    ref = _sdpa(q[:, None, :], k.transpose(1, 0, 2), v.transpose(1, 0, 2), scale, gqa=True)[:, 0, :]
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), "k = n must equal dense attention"
+    # key order does not matter
+    perm = rng.permutation(n)
+    got_p = np.asarray(sparse_attention_gqa(q, k[perm], v[perm], scale))
+    assert np.allclose(got, got_p, rtol=1e-12, atol=1e-13), "permutation invariance"
+    # V == 1 gives O == 1 (softmax rows sum to 1)
+    ones = np.ones_like(v)
+    assert np.allclose(sparse_attention_gqa(q, k, ones, scale), 1.0, atol=1e-13)
+    # one-hot V columns return the attention probabilities themselves
+    qq = rng.standard_normal((3, D))
+    kk = rng.standard_normal((D, D))
+    eye = np.eye(D)
+    p = softmax_attention(qq, kk, eye, scale)
+    ref_p = torch.softmax(torch.as_tensor(qq @ kk.T * scale), dim=-1).numpy()
+    assert np.allclose(p, ref_p, rtol=1e-12, atol=1e-14)
+    # extreme logits (the GSA gist case) stay finite and match the textbook path
+    big = np.array([[700.0, -700.0, 699.0, 3.0]])
+    kx = np.eye(4)
+    vx = rng.standard_normal((4, 5))
+    got_x = softmax_attention(big, kx, vx, 1.0)
+    assert np.all(np.isfinite(got_x))
+    ref_x = _sdpa(big[None], kx[None], vx[None], 1.0)[0]
+    assert np.allclose(got_x, ref_x, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# driver: sharing, needles, dense equivalence end to end
+# --------------------------------------------------------------------------
+
+def small_decode_cfg(**kw):
+    from synth import configs as C
+    base = C.DecodeConfig("pin_decode", 77, B=2, Lq=3, L=300, n_layers=8, group=4, Hq=8,
+                          Hkv=2, D=32, H_idx=2, d_idx=16, topk=24)
+    return base.with_(**kw)
+
+
+def pin_driver_sharing(decode_step, oracle_module):
+    """One indexer call per group; every layer of a group sees the same set."""
+    import oracle.driver as drv
+    cfg = small_decode_cfg()
+    calls = []
+    real = drv.index_scores
+
+    def counting(*a, **k):
+        calls.append(1)
+        return real(*a, **k)
+
+    drv.index_scores = counting
+    try:
+        idx, outs = decode_step(cfg)
+    finally:
+        drv.index_scores = real
+    n_groups = cfg.n_layers // cfg.group
+    assert len(calls) == n_groups * cfg.B, (len(calls), n_groups, cfg.B)  # one call per (group, batch row)
+    removed = 1.0 - n_groups / cfg.n_layers
+    assert abs(removed - golden()["index_sharing"]["indexer_compute_removed_printed"]) < 1e-12
+    assert len(idx) == n_groups
+    assert not np.array_equal(idx[0], idx[1]), "different groups have different indexer inputs"
+    # each layer's output is attention over its group's set
+    for l, o in outs.items():
+        ref = oracle_module.decode_layers(cfg, l, idx[l // cfg.group])
+        assert np.allclose(o, ref, rtol=0, atol=0)
+
+
+def pin_dense_when_k_covers(decode_step):
+    """k >= L: sparse decode equals dense softmax(QK^T/sqrt(d))V over the whole cache."""
+    import synth
+    from synth import configs as C
+    cfg = small_decode_cfg(L=40, topk=64, n_layers=4)
+    idx, outs = decode_step(cfg, layers=[1, 2])
+    for g, ix in idx.items():
+        want = np.full(cfg.topk, -1)
+        want[:cfg.L] = np.arange(cfg.L)
+        assert np.all(ix == want), "k >= L must select every position"
+    for l in (1, 2):
+        q = synth.as_float(synth.BF16N, C.make(cfg, cfg.q_spec(l)))
+        k = synth.as_float(synth.BF16N, C.make(cfg, cfg.k_spec(l)))
+        v = synth.as_float(synth.BF16N, C.make(cfg, cfg.v_spec(l)))
+        for b in range(cfg.B):
+            ref = _sdpa(q[b].transpose(1, 0, 2), k[b].transpose(1, 0, 2), v[b].transpose(1, 0, 2),
+                        cfg.scale, gqa=True).transpose(1, 0, 2)
+            assert np.allclose(outs[l][b], ref, rtol=1e-12, atol=1e-12), "dense equivalence"
+
+
+def pin_needles(index_scores, select_topk):
+    """Keys planted with the closed-form maximum score are always chosen."""
+    rng = np.random.default_rng(3)
+    L, HD, k = 4096, 64, 32
+    qi = rng.integers(-8, 8, size=(1, 1, HD)).astype(np.int8)
+    ki = rng.integers(-8, 8, size=(1, L, HD)).astype(np.int8)
+    needles = np.sort(rng.choice(L, size=9, replace=False))
+    ki[0, needles] = np.where(qi[0, 0] >= 0, 7, -8).astype(np.int8)
+    s = index_scores(qi, ki, 1)
+    sel = np.asarray(select_topk(np.asarray(s)[0], k, L))[0]
+    assert set(needles.tolist()) <= set(sel.tolist()), (needles, sel)
+    best = int(np.maximum(7 * qi[0, 0].astype(np.int64), -8 * qi[0, 0].astype(np.int64)).sum())
+    assert np.all(np.asarray(s)[0, 0, needles] == best)
+
+
+def pin_prefill(prefill_index_rows, prefill_attention_rows):
+    """Causal prefill: rows below k see every earlier position (dense causal)."""
+    import synth
+    from synth import configs as C
+    cfg = C.DecodeConfig("pin_prefill", 91, B=1, Lq=96, L=96, n_layers=4, group=4, Hq=4, Hkv=2,
+                         D=16, H_idx=2, d_idx=8, topk=32, causal=True)
+    rows = list(range(0, 96, 5)) + [31, 32, 95]
+    idx = np.asarray(prefill_index_rows(cfg, 0, rows))
+    for j, r in enumerate(rows):
+        sel = idx[j][idx[j] >= 0]
+        assert sel.size == min(cfg.topk, r + 1)
+        assert np.all(sel <= r), "causal: no position after the query"
+        if r < cfg.topk:
+            assert np.array_equal(sel, np.arange(r + 1))
+    out = np.asarray(prefill_attention_rows(cfg, 2, rows, idx))
+    q = synth.as_float(synth.BF16N, C.make(cfg, cfg.q_spec(2)))[0]
+    k = synth.as_float(synth.BF16N, C.make(cfg, cfg.k_spec(2)))[0]
+    v = synth.as_float(synth.BF16N, C.make(cfg, cfg.v_spec(2)))[0]
+    ref = _sdpa(q.transpose(1, 0, 2), k.transpose(1, 0, 2), v.transpose(1, 0, 2), cfg.scale,
+                causal=True, gqa=True).transpose(1, 0, 2)
+    for j, r in enumerate(rows):
+        if r < cfg.topk:
+            assert np.allclose(out[j], ref[r], rtol=1e-12, atol=1e-12), r
+
+
+# --------------------------------------------------------------------------
+# GSA
+# --------------------------------------------------------------------------
+
+def small_gsa_cfg(**kw):
+    from synth import configs as C
+    base = C.GsaConfig("pin_gsa", 55, B=2, H=3, D=16, Nc=12, chunk=16, kc=4, tail_len=1)
+    return base.with_(**kw)
+
+
+def _gsa_inputs(cfg):
+    import synth
+    from synth import configs as C
+    f = synth.as_float
+    return (f(cfg.q_spec()[0], C.make(cfg, cfg.q_spec())), f(cfg.gk_spec()[0], C.make(cfg, cfg.gk_spec())),
+            f(synth.BF16N, C.make(cfg, cfg.gv_spec())), f(synth.BF16N, C.make(cfg, cfg.rk_spec())),
+            f(synth.BF16N, C.make(cfg, cfg.rv_spec())))
+
+
+def pin_gsa_dense(gsa_step):
+    """Every chunk chosen: attention over all raw tokens, all gists and the tail."""
+    for tail in (0, 1, 5, 15):
+        cfg = small_gsa_cfg(kc=12, tail_len=tail)
+        q, gk, gv, rk, rv = _gsa_inputs(cfg)
+        idx, out = gsa_step(cfg)
+        n_raw = cfg.Nc * cfg.chunk + tail
+        for i, (b, h) in enumerate([(b, h) for b in range(cfg.B) for h in range(cfg.H)]):
+            assert np.array_equal(idx[i], np.arange(cfg.Nc))
+            keys = np.concatenate([rk[b, h, :n_raw], gk[b, h]])
+            vals = np.concatenate([rv[b, h, :n_raw], gv[b, h]])
+            ref = _sdpa(q[b, h][None, None], keys[None], vals[None], cfg.scale)[0, 0]
+            assert np.allclose(out[i], ref, rtol=1e-12, atol=1e-12), (tail, b, h)
+
+
+def pin_gsa_sg_sr(gsa_step):
+    """One chunk chosen: its raw tokens + its own gist + the tail, nothing else.
+
+    Query and gist keys are overridden with small ternary values so that
+    every gist carries real attention weight (with the workload's [-8, 7]
+    integers the chosen gist's logit dwarfs all others and a wrong key set
+    would be invisible).  The planted gist equals the query, so its score
+    ||q||^2 is the unique maximum.  The expected key list is written out from
+    the pages' rule: selected gist and raw tokens kept, unselected gists
+    dropped, tail always kept.
+    """
+    import synth
+    cfg = small_gsa_cfg(kc=1, tail_len=3)
+    _, _, gv, rk, rv = _gsa_inputs(cfg)
+    rng = np.random.default_rng(8)
+    q2 = rng.choice([-1.0, 1.0], size=(cfg.B, cfg.H, cfg.D))
+    gk2 = rng.choice([-1.0, 0.0, 1.0], size=(cfg.B, cfg.H, cfg.Nc, cfg.D))
+    planted = 7
+    gk2[:, :, planted] = q2
+
+    import oracle.driver as drv
+    real_rows = drv.C.rows
+    override = {cfg.q_spec(): q2, cfg.gk_spec(): gk2}
+
+    def rows_patched(c, spec, lead):
+        if spec in override:
+            idxs = np.broadcast_arrays(*[np.asarray(a) for a in lead])
+            return synth.f32_to_bf16_bits(override[spec][tuple(idxs)].astype(np.float32))
+        return real_rows(c, spec, lead)
+
+    drv.C.rows = rows_patched
+    try:
+        idx, out = gsa_step(cfg)
+    finally:
+        drv.C.rows = real_rows
+    for i, (b, h) in enumerate([(b, h) for b in range(cfg.B) for h in range(cfg.H)]):
+        assert list(idx[i]) == [planted]
+        raw_pos = list(range(planted * 16, planted * 16 + 16)) + [cfg.Nc * 16 + t for t in range(3)]
+        keys = np.concatenate([rk[b, h, raw_pos], gk2[b, h, planted][None]])
+        vals = np.concatenate([rv[b, h, raw_pos], gv[b, h, planted][None]])
+        ref = _sdpa(q2[b, h][None, None], keys[None], vals[None], cfg.scale)[0, 0]
+        assert np.allclose(out[i], ref, rtol=1e-12, atol=1e-12), (b, h)
+
+
+# --------------------------------------------------------------------------
+# sizes
+# --------------------------------------------------------------------------
+
+def pin_sizes(kv_cache_gib, kv_bytes_per_token, scored_pairs):
+    g = golden()
+    kv = g["kv_cache_gib"]
+    for tok, printed in kv["printed_gib_1dp"].items():
+        v = kv_cache_gib(kv["n_layers"], kv["kv_heads"], kv["head_dim"], int(tok), kv["bytes_per"])
+        assert f"{v:.1f}" == printed, (tok, v, printed)
+    per_tok = kv_bytes_per_token(28, 4, 128, 2)
+    assert per_tok == 56 * 1024 and round(per_tok / 1024) == g["kv_per_token_kib"]["printed_kib_approx"]
+    # 2**20 tokens with this geometry is exactly 56 GiB
+    assert kv_cache_gib(28, 4, 128, 1 << 20) == 56.0
+    sp = g["scored_pairs_at_1M"]
+    n = sp["n_tok"]
+    full = scored_pairs(n)
+    assert full == sp["full_pairs_printed"]
+    for key in ("sliding_window", "topk"):
+        e = sp[key]
+        p = scored_pairs(n, e["per_query"])
+        assert abs(p - e["pairs_printed"]) / e["pairs_printed"] < 0.01, (key, p)
+        assert f"1/{round(full / p)}" == e["fraction_printed"], (key, full / p)
+    gc = g["gist_count_at_1M"]
+    n_gists = gc["n_tok"] // gc["chunk"]
+    assert gc["printed_lower_bound"] <= n_gists <= gc["printed_upper_bound"]

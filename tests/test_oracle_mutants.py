@@ -1,0 +1,204 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each test swaps one oracle function for a copy with a plausible slip (a
+dropped term, a wrong index, a reversed tie rule, ...) and checks that the
+pin covering it raises.  The real oracle passes the same pins in
+``test_oracle_pins.py``.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as A
+import oracle.driver as DRV
+import oracle.gsa as GSA
+import oracle.indexer as IDX
+import oracle.topk as TK
+from tests import oracle_pins as P
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+# ---- top-k ----
+
+def _topk_highest_index_wins(scores, k, valid_len=None):
+    s = np.asarray(scores)
+    flipped = s[..., ::-1]
+    n = s.shape[-1]
+    if valid_len is not None and np.any(np.asarray(valid_len) != n):
+        return TK.select_topk(scores, k, valid_len)
+    r = TK.select_topk(flipped, k)
+    out = np.where(r >= 0, n - 1 - r, -1)
+    out = np.sort(np.where(out < 0, 1 << 30, out), axis=-1)
+    return np.where(out == 1 << 30, -1, out)
+
+
+def _topk_unsorted_output(scores, k, valid_len=None):
+    s = np.asarray(scores)
+    r = TK.select_topk(scores, k, valid_len)
+    flat = r.reshape(-1, k).copy()
+    sf = s.reshape(-1, s.shape[-1])
+    for i in range(flat.shape[0]):
+        sel = flat[i][flat[i] >= 0]
+        order = np.argsort(-sf[i][sel].astype(np.float64), kind="stable")
+        flat[i, :sel.size] = sel[order]
+    return flat.reshape(r.shape)
+
+
+def _topk_valid_off_by_one(scores, k, valid_len=None):
+    n = np.asarray(scores).shape[-1]
+    vl = n if valid_len is None else valid_len
+    return TK.select_topk(scores, k, np.maximum(np.asarray(vl) - 1, 0))
+
+
+@pytest.mark.parametrize("mutant", [_topk_highest_index_wins, _topk_unsorted_output,
+                                    _topk_valid_off_by_one])
+def test_topk_mutants_caught(mutant):
+    _fails(P.pin_topk, mutant)
+
+
+# ---- indexer ----
+
+def _scores_first_head_only(qi, ki, n_heads):
+    d = qi.shape[-1] // n_heads
+    return IDX.index_scores(qi[..., :d], ki[..., :d], 1)
+
+
+def _scores_features_reversed(qi, ki, n_heads):
+    return IDX.index_scores(qi[..., ::-1].copy(), ki, n_heads)
+
+
+@pytest.mark.parametrize("mutant", [_scores_first_head_only, _scores_features_reversed])
+def test_indexer_mutants_caught(mutant):
+    _fails(P.pin_index_scores, mutant)
+
+
+# ---- attention ----
+
+def _attn_no_scale(q, k, v, scale):
+    return A.softmax_attention(q, k, v, 1.0)
+
+
+def _attn_softmax_wrong_axis(q, k, v, scale):
+    q = np.asarray(q, np.float64)
+    z = q @ np.asarray(k, np.float64).T * scale
+    e = np.exp(z - z.max(axis=0, keepdims=True))
+    p = e / e.sum(axis=0, keepdims=True)
+    return p @ np.asarray(v, np.float64)
+
+
+def _gqa_wrong_map(q, k_sel, v_sel, scale):
+    Hq, Hkv = q.shape[0], k_sel.shape[1]
+    out = np.zeros((Hq, v_sel.shape[2]))
+    for h in range(Hq):
+        kvh = h % Hkv
+        out[h] = A.softmax_attention(q[h:h + 1], k_sel[:, kvh], v_sel[:, kvh], scale)[0]
+    return out
+
+
+def test_attention_mutants_caught():
+    _fails(P.pin_attention, _attn_no_scale, lambda q, k, v, s: _gqa_scaled(q, k, v, s, _attn_no_scale))
+    _fails(P.pin_attention, _attn_softmax_wrong_axis,
+           lambda q, k, v, s: _gqa_scaled(q, k, v, s, _attn_softmax_wrong_axis))
+    _fails(P.pin_attention, A.softmax_attention, _gqa_wrong_map)
+
+
+def _gqa_scaled(q, k_sel, v_sel, scale, attn):
+    Hq, Hkv = q.shape[0], k_sel.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((Hq, v_sel.shape[2]))
+    for h in range(Hq):
+        out[h] = attn(q[h:h + 1], k_sel[:, h // G], v_sel[:, h // G], scale)[0]
+    return out
+
+
+# ---- driver ----
+
+def _step_no_sharing(cfg, batch=None, layers=None):
+    layers = list(range(cfg.n_layers)) if layers is None else list(layers)
+    idx, outs = {}, {}
+    for l in layers:
+        ix = DRV.decode_group(cfg, l // cfg.group, batch)   # indexer rerun for every layer
+        idx[l // cfg.group] = ix
+        outs[l] = DRV.decode_layers(cfg, l, ix, batch)
+    return idx, outs
+
+
+def test_driver_mutant_caught():
+    _fails(P.pin_driver_sharing, _step_no_sharing, oracle)
+
+
+def test_driver_group_mapping_mutant_caught(monkeypatch):
+    real = DRV.decode_layers
+
+    def wrong_group(cfg, layer, idx, batch=None, qrows=None):
+        return real(cfg, layer, idx, batch, qrows)
+
+    def step_wrong_group(cfg, batch=None, layers=None):
+        layers = list(range(cfg.n_layers)) if layers is None else list(layers)
+        groups = sorted({l // cfg.group for l in layers})
+        idx = {g: DRV.decode_group(cfg, g, batch) for g in groups}
+        outs = {l: real(cfg, l, idx[(l // cfg.group + 1) % len(groups)], batch) for l in layers}
+        return idx, outs
+
+    _fails(P.pin_driver_sharing, step_wrong_group, oracle)
+
+
+# ---- prefill ----
+
+def _prefill_excludes_self(cfg, g, rows):
+    rows = np.asarray(list(rows), dtype=np.int64)
+    from synth import configs as C
+    qi = C.rows(cfg, cfg.qi_spec(g), (np.zeros_like(rows), rows))
+    ki = C.rows(cfg, cfg.ki_spec(g), (np.array([0]),))[0]
+    s = IDX.index_scores(qi[None], ki[None], cfg.H_idx)[0]
+    return TK.select_topk(s, cfg.topk, rows)          # should be rows + 1
+
+
+def test_prefill_mutant_caught():
+    _fails(P.pin_prefill, _prefill_excludes_self, oracle.prefill_attention_rows)
+
+
+# ---- GSA ----
+
+def test_gsa_all_gists_mutant_caught(monkeypatch):
+    real = GSA.gsa_key_positions
+
+    def all_gists(chunk_idx, chunk, n_chunks, tail_len):
+        raw, _ = real(chunk_idx, chunk, n_chunks, tail_len)
+        return raw, np.arange(n_chunks, dtype=np.int64)
+
+    monkeypatch.setattr(GSA, "gsa_key_positions", all_gists)
+    _fails(P.pin_gsa_sg_sr, oracle.gsa_step)
+
+
+def test_gsa_tail_dropped_mutant_caught(monkeypatch):
+    real = GSA.gsa_key_positions
+
+    def no_tail(chunk_idx, chunk, n_chunks, tail_len):
+        return real(chunk_idx, chunk, n_chunks, 0)
+
+    monkeypatch.setattr(GSA, "gsa_key_positions", no_tail)
+    _fails(P.pin_gsa_dense, oracle.gsa_step)
+
+
+def test_gsa_gists_dropped_mutant_caught(monkeypatch):
+    real = GSA.gsa_key_positions
+
+    def raw_only(chunk_idx, chunk, n_chunks, tail_len):
+        raw, _ = real(chunk_idx, chunk, n_chunks, tail_len)
+        return raw, np.zeros(0, dtype=np.int64)
+
+    monkeypatch.setattr(GSA, "gsa_key_positions", raw_only)
+    _fails(P.pin_gsa_dense, oracle.gsa_step)
+
+
+# ---- sizes ----
+
+def test_sizes_mutant_caught():
+    _fails(P.pin_sizes, lambda L, H, D, n, b=2: L * H * D * b * n / 1024**3,   # K only, V dropped
+           oracle.kv_bytes_per_token, oracle.scored_pairs)
