@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed top-k sparse-attention hot path on one MI355X.
+
+Default workload: sparse decode at 128K context, batch 8, 28 layers (32 query
+heads, 4 KV heads, head dim 128, bf16 KV cache = 56 GiB resident in HBM),
+int8 indexer (4 heads x 64) with top-2048 and one index per group of 4
+layers (7 indexer calls per step).  One step = the whole hot path for one
+new token per sequence: 7 x (indexer scores + top-k select) + 28 x sparse
+attention, captured in a HIP graph and replayed.  value = tokens/s = B /
+step time.  Inputs are seeded synthetic tensors generated directly in HBM.
+
+Prints one JSON line.  Other workloads (``--config``) are for exploration:
+``decode_32k``, ``decode_1m``, ``gsa_128k`` and ``prefill_64k`` (indexer int8
+TOPS of the causal scorer).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, vendor figure
+MIB = 1 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ byte model ----
+
+def decode_step_bytes(cfg) -> dict:
+    """Algorithmic bytes of one decode step.
+
+    Indexer keys are read once per group (B x L x HD bytes); each layer reads
+    the selected K and V rows (B x Lq x k x Hkv x D x 2 bytes x 2).  Queries,
+    index sets, outputs and scratch are not counted.
+    """
+    idx_per_call = cfg.B * cfg.L * cfg.HD
+    kv_per_layer = cfg.B * cfg.Lq * min(cfg.topk, cfg.L) * cfg.Hkv * cfg.D * 2 * 2
+    total = cfg.n_groups * idx_per_call + cfg.n_layers * kv_per_layer
+    return {"indexer_per_call": idx_per_call, "kv_per_layer": kv_per_layer, "total": total}
+
+
+def gsa_step_bytes(cfg) -> dict:
+    """Gist keys once, then per (b, h): chosen chunks' raw K and V, gist V, tail K and V."""
+    BH = cfg.B * cfg.H
+    gk = BH * cfg.Nc * cfg.D * 2
+    sel = BH * cfg.kc * (cfg.chunk * 2 + 1) * cfg.D * 2 + BH * cfg.tail_len * 2 * cfg.D * 2
+    return {"gist_keys": gk, "selected": sel, "total": gk + sel}
+
+
+def causal_pairs(L: int) -> int:
+    return L * (L + 1) // 2
+
+
+# --------------------------------------------------------------- helpers ----
+
+def _timed_loop(fn, iters, stream):
+    import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(iters):
+        fn()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / iters  # ms
+
+
+def _flush(buf):
+    """Evict the 256 MiB Infinity Cache between small timed launches."""
+    buf.add_(1)
+
+
+def cpu_baseline_decode(cfg, budget_s=20.0):
+    """The oracle, as it stands, on one sequence of one group (1 token, 4 layers).
+
+    Scaled to tokens/s for a full step (all groups) of one sequence.  The
+    oracle is single-threaded numpy (its int64 products do not use BLAS;
+    BLAS is pinned to one thread for the attention part).
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from synth import configs as C
+
+    with threadpool_limits(limits=1):
+        b, g = 0, 0
+        qi = C.rows(cfg, cfg.qi_spec(g), (np.array([b]),))
+        ki = C.rows(cfg, cfg.ki_spec(g), (np.array([b]),))
+        t0 = time.perf_counter()
+        s = oracle.index_scores(qi, ki, cfg.H_idx)
+        idx = oracle.select_topk(s[0], cfg.topk, cfg.L)
+        t_sel = time.perf_counter() - t0
+        t_att = 0.0
+        import synth
+        for l in range(cfg.group):
+            sel = idx[0][idx[0] >= 0].astype(np.int64)
+            q = synth.as_float(synth.BF16N, C.rows(cfg, cfg.q_spec(l), (np.array(b), np.array(0))))
+            kk = synth.as_float(synth.BF16N, C.rows(cfg, cfg.k_spec(l), (np.zeros_like(sel), sel)))
+            vv = synth.as_float(synth.BF16N, C.rows(cfg, cfg.v_spec(l), (np.zeros_like(sel), sel)))
+            t0 = time.perf_counter()
+            oracle.sparse_attention_gqa(q, kk, vv, cfg.scale)
+            t_att += time.perf_counter() - t0
+    per_token = cfg.n_groups * (t_sel + t_att)
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"1 sequence (b=0), group 0: indexer scores over {cfg.L} positions + top-"
+                       f"{cfg.topk} select ({t_sel:.2f} s) and {cfg.group} layers of sparse attention "
+                       f"({t_att:.2f} s); scaled x{cfg.n_groups} groups to one token")}
+
+
+# ---------------------------------------------------------------- decode ----
+
+def bench_decode(cfg, steps, warmup, want_cpu):
+    import torch
+
+    import long_context_top_amd as lct
+    import synth.device as sd
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    ng = cfg.n_groups
+    qi = [sd.make(cfg, cfg.qi_spec(g), dev) for g in range(ng)]
+    ki = [sd.make(cfg, cfg.ki_spec(g), dev) for g in range(ng)]
+    q = [sd.make(cfg, cfg.q_spec(l), dev) for l in range(cfg.n_layers)]
+    k = [sd.make(cfg, cfg.k_spec(l), dev) for l in range(cfg.n_layers)]
+    v = [sd.make(cfg, cfg.v_spec(l), dev) for l in range(cfg.n_layers)]
+    out = [torch.empty((cfg.B, cfg.Lq, cfg.Hq, cfg.D), dtype=torch.float32, device=dev)
+           for _ in range(cfg.n_layers)]
+    idx_out = [torch.empty((cfg.B, cfg.Lq, cfg.topk), dtype=torch.int32, device=dev) for _ in range(ng)]
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
+    run = lct.GroupRun(qi, ki, q, k, v, out, cfg.topk, cfg.group, cfg.scale, idx_out=idx_out)
+    stream = torch.cuda.current_stream()
+    run()
+    torch.cuda.synchronize()
+
+    # one step as a HIP graph (42 kernels for 28 layers / 7 groups)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    log(f"warmup done ({warmup} steps)")
+    ms = _timed_loop(g.replay, steps, stream)
+    torch.cuda.synchronize()
+
+    # per-kernel timing of the dominant kernels, standalone launches on this stream
+    bytes_ = decode_step_bytes(cfg)
+    scores = torch.empty((cfg.B, cfg.Lq, cfg.L), dtype=torch.int32, device=dev)
+    n_k = max(10, steps)
+    ms_score = _timed_loop(lambda: lct.idx_score(qi[0], ki[0], out=scores), n_k, stream)
+    ws = lct.Workspace(dev)
+    ms_attn = _timed_loop(lambda: lct.sparse_attn_gather(q[0], k[0], v[0], idx_out[0], cfg.scale,
+                                                         out=out[0], ws=ws), n_k, stream)
+    torch.cuda.synchronize()
+    score_gbs = bytes_["indexer_per_call"] / (ms_score * 1e-3) / 1e9
+    attn_gbs = bytes_["kv_per_layer"] / (ms_attn * 1e-3) / 1e9
+    step_gbs = bytes_["total"] / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "sparse-decode tokens/s + HBM GB/s at 128K ctx; prefill indexer int8 TOPS",
+        "value": cfg.B * cfg.Lq / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 inputs generated in HBM; random-init, no trained weights)",
+        "config": {"workload": cfg.name, "global_batch": cfg.B, "seq_len": cfg.L,
+                   "layers": cfg.n_layers, "layers_per_index": cfg.group, "q_heads": cfg.Hq,
+                   "kv_heads": cfg.Hkv, "head_dim": cfg.D, "indexer": f"int8 {cfg.H_idx}x{cfg.d_idx}",
+                   "topk": cfg.topk, "parallelism": "single GPU"},
+        "hbm_gbs_step": step_gbs, "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": bytes_["total"],
+        "roofline": {"bound": "hbm", "kernel": "k_idx_score_stream (indexer scores, one group)",
+                     "achieved": score_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": score_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "us_per_launch": ms_score * 1e3, "bytes_per_launch": bytes_["indexer_per_call"]},
+        "attention_kernel": {"kernel": "k_sparse_attn (one layer)", "achieved": attn_gbs,
+                             "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
+                             "us_per_launch": ms_attn * 1e3, "bytes_per_launch": bytes_["kv_per_layer"]},
+    }
+    if want_cpu:
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline_decode(cfg)
+    return res
+
+
+# ------------------------------------------------------------------- GSA ----
+
+def bench_gsa(cfg, steps, warmup):
+    import torch
+
+    import long_context_top_amd as lct
+    import synth.device as sd
+
+    dev = torch.device("cuda", 0)
+    BH = cfg.B * cfg.H
+
+    def mk(spec):
+        t = sd.make(cfg, spec, dev)
+        return t.view((BH,) + tuple(t.shape[2:]))
+
+    qv, gk, gv, rk, rv = mk(cfg.q_spec()), mk(cfg.gk_spec()), mk(cfg.gv_spec()), mk(cfg.rk_spec()), mk(cfg.rv_spec())
+    out = torch.empty((BH, cfg.D), dtype=torch.float32, device=dev)
+    cidx = torch.empty((BH, cfg.kc), dtype=torch.int32, device=dev)
+    ws = lct.Workspace(dev)
+    step = lambda: lct.gsa_decode(qv, gk, gv, rk, rv, cfg.kc, cfg.tail_len, cfg.scale, idx_out=cidx, out=out, ws=ws)
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    stream = torch.cuda.current_stream()
+    ms = _timed_loop(g.replay, steps, stream)
+    b = gsa_step_bytes(cfg)
+    gs = torch.empty((BH, cfg.Nc), dtype=torch.float32, device=dev)
+    ms_gs = _timed_loop(lambda: lct.gist_score(qv, gk, out=gs), max(10, steps), stream)
+    gbs = b["total"] / (ms * 1e-3) / 1e9
+    return {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": BH // cfg.H * 1.0 / (ms * 1e-3),
+            "hbm_gbs_step": gbs, "hbm_frac_step": gbs / HBM_PEAK_GBS,
+            "gist_score_gbs": b["gist_keys"] / (ms_gs * 1e-3) / 1e9, "gist_score_us": ms_gs * 1e3}
+
+
+# --------------------------------------------------------------- prefill ----
+
+def bench_prefill_indexer(cfg, steps, warmup):
+    """Causal int8 MFMA scorer over one block of query rows (TOPS of the causal half)."""
+    import torch
+
+    import long_context_top_amd as lct
+    import synth.device as sd
+
+    dev = torch.device("cuda", 0)
+    qi = sd.make(cfg, cfg.qi_spec(0), dev)
+    ki = sd.make(cfg, cfg.ki_spec(0), dev)
+    rows = 2048
+    r0 = cfg.L - rows  # the last block: the most work per row
+    scores = torch.empty((1, rows, cfg.L), dtype=torch.int32, device=dev)
+    qb = qi[:, r0:r0 + rows].contiguous()
+    f = lambda: lct.idx_score(qb, ki, q_pos0=r0, out=scores)
+    for _ in range(warmup):
+        f()
+    ms = _timed_loop(f, steps, torch.cuda.current_stream())
+    pairs = sum(r0 + r + 1 for r in range(rows))
+    tops = 2 * cfg.HD * pairs / (ms * 1e-3) / 1e12
+    return {"workload": cfg.name + " indexer block (last 2048 rows)", "ms": ms, "int8_tops": tops,
+            "frac": tops / INT8_PEAK_TOPS}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode_128k",
+                    choices=["decode_128k", "decode_32k", "decode_1m", "gsa_128k", "prefill_64k", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every workload runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    from synth import configs as C
+    cfgs = {"decode_128k": C.DECODE_128K, "decode_32k": C.DECODE_32K, "decode_1m": C.DECODE_1M,
+            "gsa_128k": C.GSA_128K, "prefill_64k": C.PREFILL_64K, "tiny": C.TINY}
+    cfg = cfgs[args.config]
+    if args.config == "gsa_128k":
+        res = bench_gsa(cfg, args.steps, args.warmup)
+    elif args.config == "prefill_64k":
+        res = bench_prefill_indexer(cfg, args.steps, args.warmup)
+    else:
+        res = bench_decode(cfg, args.steps, args.warmup,
+                           want_cpu=not args.no_cpu_baseline and args.config == "decode_128k")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

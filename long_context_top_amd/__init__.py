@@ -1,0 +1,339 @@
+"""Python binding of liblct: routed top-k sparse attention with a shared index.
+
+Argument marshalling only: every step of the path runs in the gfx950 kernels
+of ``liblct.so`` (C-ABI declared in ``include/lct.h``).  PyTorch supplies
+device memory and the current HIP stream.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "LctError", "Workspace", "lib", "version", "idx_score", "gist_score", "topk_select",
+    "sparse_attn_gather", "gsa_attn", "gsa_decode", "group_run", "LCT_CONTROL_BYTES",
+]
+
+LCT_OK, LCT_EINVAL, LCT_EUNSUPPORTED, LCT_ENOWORKSPACE, LCT_ENODEV, LCT_EHIP = range(6)
+LCT_I32, LCT_F32 = 0, 1
+LCT_CONTROL_BYTES = 1 << 20
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblct.so")
+
+_c = ctypes
+_vp, _i32, _i64, _f32, _sz = _c.c_void_p, _c.c_int, _c.c_int64, _c.c_float, _c.c_size_t
+
+
+class LctError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"lct error {code}: {msg}")
+        self.code = code
+
+
+class GroupDesc(_c.Structure):
+    """Mirror of ``lct_group_desc``."""
+
+    _fields_ = [
+        ("B", _i32), ("Lq", _i32), ("L", _i64), ("HD", _i32), ("Hq", _i32), ("Hkv", _i32),
+        ("D", _i32), ("topk", _i32), ("n_layers", _i32), ("layers_per_group", _i32),
+        ("causal", _i32), ("scale", _f32), ("valid_len", _vp), ("qi", _c.POINTER(_vp)),
+        ("ki", _c.POINTER(_vp)), ("q", _c.POINTER(_vp)), ("k", _c.POINTER(_vp)),
+        ("v", _c.POINTER(_vp)), ("out", _c.POINTER(_vp)), ("idx_out", _c.POINTER(_vp)),
+        ("layer_idx_seen", _c.POINTER(_vp)),
+    ]
+
+
+_SIGS = {
+    "lct_version": ([], _c.c_char_p),
+    "lct_last_error": ([], _c.c_char_p),
+    "lct_workspace_init": ([_vp, _sz, _vp], _i32),
+    "lct_idx_score_i8": ([_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i64, _vp], _i32),
+    "lct_gist_score_bf16": ([_vp, _vp, _vp, _i32, _i64, _i32, _vp], _i32),
+    "lct_topk_select": ([_vp, _i32, _vp, _i32, _i64, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
+    "lct_topk_workspace_bytes": ([_i32, _i64, _i32, _c.POINTER(_sz)], _i32),
+    "lct_sparse_attn_gather": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i32,
+                                _f32, _vp, _sz, _vp], _i32),
+    "lct_sparse_attn_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _c.POINTER(_sz)], _i32),
+    "lct_gsa_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32,
+                      _f32, _vp, _sz, _vp], _i32),
+    "lct_gsa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32,
+                        _f32, _vp, _sz, _vp], _i32),
+    "lct_gsa_decode_workspace_bytes": ([_i32, _i32, _i64, _i32, _c.POINTER(_sz)], _i32),
+    "lct_gsa_attn_workspace_bytes": ([_i32, _i32, _i32, _i32, _c.POINTER(_sz)], _i32),
+    "lct_group_run": ([_c.POINTER(GroupDesc), _vp, _sz, _vp], _i32),
+    "lct_group_workspace_bytes": ([_c.POINTER(GroupDesc), _c.POINTER(_sz)], _i32),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded ``liblct.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        l = _c.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(l, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = l
+    return _lib
+
+
+def version() -> str:
+    return lib().lct_version().decode()
+
+
+def _check(rc: int):
+    if rc != LCT_OK:
+        raise LctError(rc, lib().lct_last_error().decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _stream():
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+class Workspace:
+    """Caller-owned scratch memory; grows on demand and keeps its control region zeroed."""
+
+    def __init__(self, device=None):
+        self.device = torch.device("cuda") if device is None else torch.device(device)
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        nbytes = max(int(nbytes), LCT_CONTROL_BYTES)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            _check(lib().lct_workspace_init(_p(self.buf), nbytes, _stream()))
+        return self.buf
+
+    @property
+    def nbytes(self) -> int:
+        return 0 if self.buf is None else self.buf.numel()
+
+
+_default_ws: dict = {}
+
+
+def _ws(ws: Optional[Workspace]) -> Workspace:
+    if ws is not None:
+        return ws
+    dev = torch.cuda.current_device()
+    if dev not in _default_ws:
+        _default_ws[dev] = Workspace(torch.device("cuda", dev))
+    return _default_ws[dev]
+
+
+# ----------------------------------------------------------------- calls ----
+
+def idx_score(q: torch.Tensor, k: torch.Tensor, q_pos0: int = -1,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int8 q [B, Lq, HD], k [B, L, HD] -> int32 scores [B, Lq, L]."""
+    _need(q, torch.int8, "q")
+    _need(k, torch.int8, "k")
+    B, Lq, HD = q.shape
+    L = k.shape[1]
+    if out is None:
+        out = torch.empty((B, Lq, L), dtype=torch.int32, device=q.device)
+    _need(out, torch.int32, "out")
+    _check(lib().lct_idx_score_i8(_p(q), _p(k), _p(out), B, Lq, L, HD, q_pos0, _stream()))
+    return out
+
+
+def gist_score(q: torch.Tensor, gk: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 q [BH, D], gk [BH, Nc, D] -> fp32 [BH, Nc] (unscaled dot products)."""
+    _need(q, torch.bfloat16, "q")
+    _need(gk, torch.bfloat16, "gk")
+    BH, Nc, D = gk.shape
+    if out is None:
+        out = torch.empty((BH, Nc), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    _check(lib().lct_gist_score_bf16(_p(q), _p(gk), _p(out), BH, Nc, D, _stream()))
+    return out
+
+
+def topk_select(scores: torch.Tensor, k: int, valid_len: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None) -> torch.Tensor:
+    """int32/fp32 scores [rows, n] -> int32 [rows, k] ascending positions, -1 padded."""
+    if scores.dtype not in (torch.int32, torch.float32):
+        raise TypeError("scores must be int32 or float32")
+    _need(scores, scores.dtype, "scores")
+    rows, n = scores.shape
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    _need(out, torch.int32, "out")
+    if valid_len is not None:
+        _need(valid_len, torch.int32, "valid_len")
+    nb = _sz()
+    _check(lib().lct_topk_workspace_bytes(rows, n, k, _c.byref(nb)))
+    buf = _ws(ws).get(nb.value)
+    dt = LCT_I32 if scores.dtype == torch.int32 else LCT_F32
+    _check(lib().lct_topk_select(_p(scores), dt, _p(out), rows, n, n, k, _p(valid_len), _p(buf),
+                                 buf.numel(), _stream()))
+    return out
+
+
+def sparse_attn_gather(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                       scale: float, out: Optional[torch.Tensor] = None,
+                       ws: Optional[Workspace] = None) -> torch.Tensor:
+    """bf16 q [B, Lq, Hq, D]; k, v [B, L, Hkv, D]; idx [B, Lq, kk] -> fp32 [B, Lq, Hq, D]."""
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    _need(v, torch.bfloat16, "v")
+    _need(idx, torch.int32, "idx")
+    B, Lq, Hq, D = q.shape
+    L, Hkv = k.shape[1], k.shape[2]
+    kk = idx.shape[-1]
+    if out is None:
+        out = torch.empty((B, Lq, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    nb = _sz()
+    _check(lib().lct_sparse_attn_workspace_bytes(B, Lq, Hq, Hkv, D, kk, _c.byref(nb)))
+    buf = _ws(ws).get(nb.value)
+    _check(lib().lct_sparse_attn_gather(_p(q), _p(k), _p(v), _p(idx), _p(out), B, Lq, Hq, Hkv, D, L,
+                                        kk, scale, _p(buf), buf.numel(), _stream()))
+    return out
+
+
+def gsa_attn(q, rk, rv, gv, gscores, chunk_idx, tail_len: int, scale: float, chunk: int = 16,
+             out=None, ws: Optional[Workspace] = None) -> torch.Tensor:
+    """One query per (batch x head) row: unfold the chosen chunks (raw + gist) and the tail."""
+    for t, n in ((q, "q"), (rk, "rk"), (rv, "rv"), (gv, "gv")):
+        _need(t, torch.bfloat16, n)
+    _need(gscores, torch.float32, "gscores")
+    _need(chunk_idx, torch.int32, "chunk_idx")
+    BH, D = q.shape
+    Nc = gv.shape[1]
+    raw_cap = rk.shape[1]
+    kc = chunk_idx.shape[-1]
+    if out is None:
+        out = torch.empty((BH, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    nb = _sz()
+    _check(lib().lct_gsa_attn_workspace_bytes(BH, D, kc, tail_len, _c.byref(nb)))
+    buf = _ws(ws).get(nb.value)
+    _check(lib().lct_gsa_attn(_p(q), _p(rk), _p(rv), _p(gv), _p(gscores), _p(chunk_idx), _p(out), BH,
+                              D, Nc, raw_cap, chunk, kc, tail_len, scale, _p(buf), buf.numel(),
+                              _stream()))
+    return out
+
+
+def gsa_decode(q, gk, gv, rk, rv, kc: int, tail_len: int, scale: float, chunk: int = 16,
+               idx_out=None, out=None, ws: Optional[Workspace] = None):
+    """Gist scores, top-kc chunks, unfold attention.  Returns (out, chunk_idx)."""
+    for t, n in ((q, "q"), (gk, "gk"), (gv, "gv"), (rk, "rk"), (rv, "rv")):
+        _need(t, torch.bfloat16, n)
+    BH, D = q.shape
+    Nc = gk.shape[1]
+    raw_cap = rk.shape[1]
+    if out is None:
+        out = torch.empty((BH, D), dtype=torch.float32, device=q.device)
+    if idx_out is None:
+        idx_out = torch.empty((BH, kc), dtype=torch.int32, device=q.device)
+    _need(out, torch.float32, "out")
+    _need(idx_out, torch.int32, "idx_out")
+    nb = _sz()
+    _check(lib().lct_gsa_decode_workspace_bytes(BH, D, Nc, kc, _c.byref(nb)))
+    buf = _ws(ws).get(nb.value)
+    _check(lib().lct_gsa_decode(_p(q), _p(gk), _p(gv), _p(rk), _p(rv), _p(idx_out), _p(out), BH, D,
+                                Nc, raw_cap, chunk, kc, tail_len, scale, _p(buf), buf.numel(),
+                                _stream()))
+    return out, idx_out
+
+
+class GroupRun:
+    """Prepared layer-group driver call (descriptor + workspace), reusable across steps.
+
+    Holding the descriptor lets a caller replay the same step cheaply (and
+    capture it in a HIP graph).  All tensors must stay alive while in use.
+    """
+
+    def __init__(self, qi: Sequence[torch.Tensor], ki: Sequence[torch.Tensor],
+                 q: Sequence[torch.Tensor], k: Sequence[torch.Tensor], v: Sequence[torch.Tensor],
+                 out: Sequence[torch.Tensor], topk: int, layers_per_group: int, scale: float,
+                 causal: bool = False, valid_len: Optional[torch.Tensor] = None,
+                 idx_out: Optional[Sequence[torch.Tensor]] = None, ws: Optional[Workspace] = None):
+        n_layers = len(q)
+        n_groups = n_layers // layers_per_group
+        if len(qi) != n_groups or len(ki) != n_groups:
+            raise ValueError("need one indexer query/key tensor per group")
+        for t in qi:
+            _need(t, torch.int8, "qi")
+        for t in ki:
+            _need(t, torch.int8, "ki")
+        for lst, n in ((q, "q"), (k, "k"), (v, "v")):
+            for t in lst:
+                _need(t, torch.bfloat16, n)
+        for t in out:
+            _need(t, torch.float32, "out")
+        if valid_len is not None:
+            _need(valid_len, torch.int32, "valid_len")
+        B, Lq, HD = qi[0].shape
+        L = ki[0].shape[1]
+        Hq, D = q[0].shape[2], q[0].shape[3]
+        Hkv = k[0].shape[2]
+        self._keep = [qi, ki, q, k, v, out, valid_len, idx_out]
+
+        def arr(ts):
+            a = (_vp * len(ts))()
+            for i, t in enumerate(ts):
+                a[i] = None if t is None else t.data_ptr()
+            return a
+
+        self._arrs = [arr(qi), arr(ki), arr(q), arr(k), arr(v), arr(out)]
+        self._idx_arr = arr(idx_out) if idx_out is not None else None
+        self._seen = (_vp * n_layers)()
+        d = GroupDesc()
+        d.B, d.Lq, d.L, d.HD, d.Hq, d.Hkv, d.D = B, Lq, L, HD, Hq, Hkv, D
+        d.topk, d.n_layers, d.layers_per_group = topk, n_layers, layers_per_group
+        d.causal, d.scale = int(causal), scale
+        d.valid_len = None if valid_len is None else valid_len.data_ptr()
+        d.qi, d.ki, d.q, d.k, d.v, d.out = [_c.cast(a, _c.POINTER(_vp)) for a in self._arrs]
+        d.idx_out = None if self._idx_arr is None else _c.cast(self._idx_arr, _c.POINTER(_vp))
+        d.layer_idx_seen = _c.cast(self._seen, _c.POINTER(_vp))
+        self.desc = d
+        nb = _sz()
+        _check(lib().lct_group_workspace_bytes(_c.byref(d), _c.byref(nb)))
+        self.ws_bytes = nb.value
+        self.ws = _ws(ws)
+        self.buf = self.ws.get(self.ws_bytes)
+
+    def __call__(self):
+        _check(lib().lct_group_run(_c.byref(self.desc), _p(self.buf), self.buf.numel(), _stream()))
+
+    def layer_index_addresses(self):
+        """Device address of the index set each layer read in the last call."""
+        return [self._seen[i] for i in range(len(self._seen))]
+
+
+def group_run(qi, ki, q, k, v, topk: int, layers_per_group: int, scale: float, causal=False,
+              valid_len=None, out=None, idx_out=None, ws: Optional[Workspace] = None):
+    """One decode step (or causal prefill) of a stack of layers; returns the outputs."""
+    if out is None:
+        out = [torch.empty(t.shape, dtype=torch.float32, device=t.device) for t in q]
+    run = GroupRun(qi, ki, q, k, v, out, topk, layers_per_group, scale, causal, valid_len,
+                   idx_out, ws)
+    run()
+    return out, run

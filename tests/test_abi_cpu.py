@@ -1,0 +1,149 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol and
+rejects bad arguments before touching a device (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import long_context_top_amd as lct
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lct.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lct.LIB_PATH),
+                                reason="liblct.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lct_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 15, names
+    so = ctypes.CDLL(lct.LIB_PATH)
+    for n in names:
+        assert hasattr(so, n), f"{n} declared in lct.h but not exported"
+    # and the binding knows the signature of each
+    assert set(names) <= set(lct._SIGS), set(names) - set(lct._SIGS)
+
+
+def test_version_and_error_strings():
+    assert "gfx950" in lct.version()
+    L = lct.lib()
+    rc = L.lct_idx_score_i8(None, None, None, 1, 1, 16, 64, -1, None)
+    assert rc == lct.LCT_EINVAL
+    assert b"null" in L.lct_last_error()
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned non-null address; never dereferenced by these calls
+
+
+def test_idx_score_validation():
+    L = lct.lib()
+    assert L.lct_idx_score_i8(FAKE, FAKE, FAKE, 0, 1, 16, 64, -1, None) == lct.LCT_EINVAL
+    assert L.lct_idx_score_i8(FAKE, FAKE, FAKE, 1, 1, 0, 64, -1, None) == lct.LCT_EINVAL
+    assert L.lct_idx_score_i8(FAKE, FAKE, FAKE, 1, 1, 16, 48, -1, None) == lct.LCT_EUNSUPPORTED
+    assert L.lct_idx_score_i8(FAKE, FAKE, FAKE, 1, 1, 16, 1024, -1, None) == lct.LCT_EUNSUPPORTED
+    assert L.lct_idx_score_i8(FAKE, FAKE, FAKE, 1, 64, 16, 32, 0, None) == lct.LCT_EUNSUPPORTED
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    assert L.lct_idx_score_i8(mis, FAKE, FAKE, 1, 1, 16, 64, -1, None) == lct.LCT_EINVAL
+    assert L.lct_idx_score_i8(FAKE, FAKE, FAKE, 1, 1, 1 << 31, 64, -1, None) == lct.LCT_EINVAL
+
+
+def test_topk_validation_and_workspace_sizes():
+    L = lct.lib()
+    nb = ctypes.c_size_t()
+    assert L.lct_topk_workspace_bytes(8, 131072, 2048, ctypes.byref(nb)) == 0
+    assert nb.value > lct.LCT_CONTROL_BYTES  # few long rows: multi-workgroup scratch
+    assert L.lct_topk_workspace_bytes(65536, 8192, 64, ctypes.byref(nb)) == 0
+    assert nb.value == lct.LCT_CONTROL_BYTES  # many rows: one workgroup per row, no scratch
+    assert L.lct_topk_select(FAKE, 7, FAKE, 1, 10, 10, 3, None, FAKE, 1 << 21, None) == lct.LCT_EINVAL
+    assert L.lct_topk_select(FAKE, 0, FAKE, 1, 10, 9, 3, None, FAKE, 1 << 21, None) == lct.LCT_EINVAL
+    assert L.lct_topk_select(FAKE, 0, FAKE, 1, 10, 10, 0, None, FAKE, 1 << 21, None) == lct.LCT_EINVAL
+    # multi-workgroup path with too small a workspace
+    assert L.lct_topk_select(FAKE, 0, FAKE, 2, 200000, 200000, 64, None, FAKE, 4096, None) \
+        == lct.LCT_ENOWORKSPACE
+
+
+def test_attention_validation():
+    L = lct.lib()
+    args = [FAKE] * 5
+    ws = FAKE
+    # D other than 128
+    assert L.lct_sparse_attn_gather(*args, 1, 1, 8, 2, 64, 100, 16, 0.1, ws, 1 << 22, None) \
+        == lct.LCT_EUNSUPPORTED
+    # Hq not a multiple of Hkv
+    assert L.lct_sparse_attn_gather(*args, 1, 1, 6, 4, 128, 100, 16, 0.1, ws, 1 << 22, None) \
+        == lct.LCT_EINVAL
+    # group of 32 query heads per KV head
+    assert L.lct_sparse_attn_gather(*args, 1, 1, 32, 1, 128, 100, 16, 0.1, ws, 1 << 22, None) \
+        == lct.LCT_EUNSUPPORTED
+    # non-finite scale
+    assert L.lct_sparse_attn_gather(*args, 1, 1, 8, 1, 128, 100, 16, float("inf"), ws, 1 << 22, None) \
+        == lct.LCT_EINVAL
+    # too small workspace
+    assert L.lct_sparse_attn_gather(*args, 1, 1, 8, 1, 128, 100, 16, 0.1, ws, 1024, None) \
+        == lct.LCT_ENOWORKSPACE
+
+
+def test_gsa_validation():
+    L = lct.lib()
+    p = [FAKE] * 7
+    # raw_cap too small for the tail
+    assert L.lct_gsa_attn(*p, 4, 128, 100, 1600, 16, 8, 1, 0.1, FAKE, 1 << 22, None) == lct.LCT_EINVAL
+    # chunk other than 16
+    assert L.lct_gsa_attn(*p, 4, 128, 100, 3300, 32, 8, 1, 0.1, FAKE, 1 << 22, None) == lct.LCT_EUNSUPPORTED
+    # tail longer than a chunk
+    assert L.lct_gsa_attn(*p, 4, 128, 100, 1700, 16, 8, 17, 0.1, FAKE, 1 << 22, None) == lct.LCT_EINVAL
+
+
+def _desc(**kw):
+    d = lct.GroupDesc()
+    d.B, d.Lq, d.L, d.HD, d.Hq, d.Hkv, d.D = 2, 1, 4096, 256, 8, 2, 128
+    d.topk, d.n_layers, d.layers_per_group, d.causal, d.scale = 64, 8, 4, 0, 0.088
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_group_validation_and_sizes():
+    L = lct.lib()
+    nb = ctypes.c_size_t()
+    d = _desc()
+    # pointer arrays missing
+    assert L.lct_group_workspace_bytes(ctypes.byref(d), ctypes.byref(nb)) == lct.LCT_EINVAL
+    arr_g = (ctypes.c_void_p * 2)(*([FAKE.value] * 2))
+    arr_l = (ctypes.c_void_p * 8)(*([FAKE.value] * 8))
+    P = ctypes.POINTER(ctypes.c_void_p)
+    d.qi = ctypes.cast(arr_g, P)
+    d.ki = ctypes.cast(arr_g, P)
+    d.q = d.k = d.v = d.out = ctypes.cast(arr_l, P)
+    assert L.lct_group_workspace_bytes(ctypes.byref(d), ctypes.byref(nb)) == 0
+    scores = 2 * 1 * 4096 * 4
+    assert nb.value >= lct.LCT_CONTROL_BYTES + scores
+    bad = _desc(n_layers=6)
+    bad.qi, bad.ki, bad.q, bad.k, bad.v, bad.out = d.qi, d.ki, d.q, d.k, d.v, d.out
+    assert L.lct_group_workspace_bytes(ctypes.byref(bad), ctypes.byref(nb)) == lct.LCT_EINVAL
+    causal_bad = _desc(causal=1)
+    causal_bad.qi, causal_bad.ki, causal_bad.q = d.qi, d.ki, d.q
+    causal_bad.k, causal_bad.v, causal_bad.out = d.k, d.v, d.out
+    assert L.lct_group_workspace_bytes(ctypes.byref(causal_bad), ctypes.byref(nb)) == lct.LCT_EINVAL
+    assert L.lct_group_run(ctypes.byref(d), FAKE, 1024, None) == lct.LCT_ENOWORKSPACE
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
+def test_no_device_reports_enodev():
+    L = lct.lib()
+    rc = L.lct_workspace_init(FAKE, lct.LCT_CONTROL_BYTES, None)
+    assert rc == lct.LCT_ENODEV, (rc, L.lct_last_error())
+
+
+def test_binding_refuses_host_tensors():
+    with pytest.raises((ValueError, TypeError)):
+        lct.idx_score(torch.zeros((1, 1, 64), dtype=torch.int8), torch.zeros((1, 8, 64), dtype=torch.int8))

@@ -1,0 +1,94 @@
+"""Layer-group driver parity (indexer once per group, shared index, sparse
+attention for every layer) against the CPU oracle on small workloads (MI355X)."""
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_top_amd as lct
+import oracle
+import synth.device as sd
+from synth import configs as C
+from tests.gpu_util import announce, dev_i32, host
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+
+
+def _inputs(cfg):
+    ng = cfg.n_groups
+    qi = [sd.make(cfg, cfg.qi_spec(g)) for g in range(ng)]
+    ki = [sd.make(cfg, cfg.ki_spec(g)) for g in range(ng)]
+    q = [sd.make(cfg, cfg.q_spec(l)) for l in range(cfg.n_layers)]
+    k = [sd.make(cfg, cfg.k_spec(l)) for l in range(cfg.n_layers)]
+    v = [sd.make(cfg, cfg.v_spec(l)) for l in range(cfg.n_layers)]
+    return qi, ki, q, k, v
+
+
+def _run(cfg, valid_len=None):
+    qi, ki, q, k, v = _inputs(cfg)
+    idx_out = [torch.full((cfg.B, cfg.Lq, cfg.topk), -7, dtype=torch.int32, device="cuda")
+               for _ in range(cfg.n_groups)]
+    vl = None if valid_len is None else dev_i32(np.asarray(valid_len))
+    out, run = lct.group_run(qi, ki, q, k, v, cfg.topk, cfg.group, cfg.scale, causal=cfg.causal,
+                             valid_len=vl, idx_out=idx_out)
+    torch.cuda.synchronize()
+    return [host(t) for t in idx_out], [host(t) for t in out], run
+
+
+def test_tiny_config_end_to_end():
+    cfg = C.TINY
+    announce(cfg.name)
+    idx, out, run = _run(cfg)
+    ref_idx, ref_out = oracle.decode_step(cfg)
+    assert np.array_equal(idx[0], ref_idx[0])
+    for l in range(cfg.n_layers):
+        assert np.abs(out[l] - ref_out[l]).max() < ATOL, l
+    seen = run.layer_index_addresses()
+    assert len(set(seen)) == 1  # one group: every layer read the same buffer
+
+
+def test_tiny_config_dense_when_k_is_context():
+    """k = L = 2048: every position is chosen, sparse attention is dense attention."""
+    cfg = C.TINY.with_(name="tiny_dense", topk=2048)
+    announce(cfg.name)
+    idx, out, _ = _run(cfg)
+    assert np.array_equal(idx[0][0, 0], np.arange(2048))
+    _, ref_out = oracle.decode_step(cfg)
+    for l in range(cfg.n_layers):
+        assert np.abs(out[l] - ref_out[l]).max() < ATOL
+
+
+@pytest.mark.parametrize("L,valid", [(5000, [5000, 100, 4000]), (40000, [40000, 2047, 33333])])
+def test_decode_ragged_valid_len(L, valid):
+    cfg = C.DecodeConfig("ragged", 4242, B=3, Lq=2, L=L, n_layers=8, group=4, Hq=16, Hkv=2, D=128,
+                         H_idx=4, d_idx=64, topk=512)
+    announce(f"{cfg.name} L={L}")
+    idx, out, run = _run(cfg, valid)
+    for g in range(cfg.n_groups):
+        for b in range(cfg.B):
+            from synth import configs as CC
+            qi = CC.rows(cfg, cfg.qi_spec(g), (np.array([b]),))
+            ki = CC.rows(cfg, cfg.ki_spec(g), (np.array([b]),))
+            s = oracle.index_scores(qi, ki, cfg.H_idx)[0]
+            want = oracle.select_topk(s, cfg.topk, valid[b])
+            assert np.array_equal(idx[g][b], want), (g, b)
+    for l in (0, 5):
+        ref = oracle.decode_layers(cfg, l, idx[l // cfg.group])
+        assert np.abs(out[l] - ref).max() < ATOL, l
+    seen = run.layer_index_addresses()
+    assert seen[0] == seen[3] and seen[4] == seen[7] and seen[0] != seen[4]
+
+
+def test_causal_prefill_small():
+    cfg = C.DecodeConfig("prefill_small", 5151, B=1, Lq=700, L=700, n_layers=4, group=4, Hq=8, Hkv=2,
+                         D=128, H_idx=4, d_idx=64, topk=64, causal=True)
+    announce(cfg.name)
+    idx, out, _ = _run(cfg)
+    rows = list(range(cfg.L))
+    want = oracle.prefill_index_rows(cfg, 0, rows)
+    assert np.array_equal(idx[0][0], want)
+    sample = [0, 1, 5, 63, 64, 65, 300, 699]
+    ref = oracle.prefill_attention_rows(cfg, 3, sample, want[sample])
+    assert np.abs(out[3][0, sample] - ref).max() < ATOL
