@@ -25,12 +25,14 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued asynchronously; buffers must stay alive until it completes.
  *     No call synchronises the device or allocates memory.
- *   - Scratch memory is caller-provided (`ws`, `ws_bytes`), sized by the
- *     matching *_workspace_bytes function.  Its first LCT_CONTROL_BYTES
- *     are a control region that must be all-zero before the first call
- *     that uses the workspace (lct_workspace_init does this); every call
- *     leaves that region all-zero again when its work completes.  Calls
- *     that share one workspace must not run concurrently.
+ *   - Scratch memory is caller-provided (`ws`, `ws_bytes`), 256-byte
+ *     aligned, sized by the matching *_workspace_bytes function (which may
+ *     be 0, in which case `ws` may be NULL).  Its contents need no
+ *     initialisation and are undefined afterwards.  Calls that share one
+ *     workspace must not run concurrently.
+ *   - No kernel of this library synchronises workgroups inside a kernel:
+ *     every hand-off between workgroups happens at a kernel boundary on
+ *     the caller's stream.
  *   - Every call validates its arguments on the host before enqueuing any
  *     work and returns LCT_OK or an error code; lct_last_error() returns a
  *     message for the last failing call on the calling thread.  No C++
@@ -59,14 +61,8 @@ extern "C" {
 #define LCT_I32 0
 #define LCT_F32 1
 
-/* size of the zero-invariant control region at the start of a workspace */
-#define LCT_CONTROL_BYTES ((size_t)1 << 20)
-
 const char* lct_version(void);
 const char* lct_last_error(void);
-
-/* Zero the control region of a workspace (ws_bytes >= LCT_CONTROL_BYTES). */
-int lct_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Indexer scores (step 1).  Source: tutorial page, section "DSA 与

@@ -16,12 +16,11 @@ import torch
 
 __all__ = [
     "LctError", "Workspace", "lib", "version", "idx_score", "gist_score", "topk_select",
-    "sparse_attn_gather", "gsa_attn", "gsa_decode", "group_run", "LCT_CONTROL_BYTES",
+    "sparse_attn_gather", "gsa_attn", "gsa_decode", "group_run", "GroupRun",
 ]
 
 LCT_OK, LCT_EINVAL, LCT_EUNSUPPORTED, LCT_ENOWORKSPACE, LCT_ENODEV, LCT_EHIP = range(6)
 LCT_I32, LCT_F32 = 0, 1
-LCT_CONTROL_BYTES = 1 << 20
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblct.so")
 
 _c = ctypes
@@ -50,7 +49,6 @@ class GroupDesc(_c.Structure):
 _SIGS = {
     "lct_version": ([], _c.c_char_p),
     "lct_last_error": ([], _c.c_char_p),
-    "lct_workspace_init": ([_vp, _sz, _vp], _i32),
     "lct_idx_score_i8": ([_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i64, _vp], _i32),
     "lct_gist_score_bf16": ([_vp, _vp, _vp, _i32, _i64, _i32, _vp], _i32),
     "lct_topk_select": ([_vp, _i32, _vp, _i32, _i64, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
@@ -116,17 +114,17 @@ def _need(t: torch.Tensor, dtype, name, device=None):
 
 
 class Workspace:
-    """Caller-owned scratch memory; grows on demand and keeps its control region zeroed."""
+    """Caller-owned scratch memory (a device byte buffer) that grows on demand."""
 
     def __init__(self, device=None):
         self.device = torch.device("cuda") if device is None else torch.device(device)
         self.buf: Optional[torch.Tensor] = None
 
     def get(self, nbytes: int) -> torch.Tensor:
-        nbytes = max(int(nbytes), LCT_CONTROL_BYTES)
+        nbytes = max(int(nbytes), 256)
         if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = None
             self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-            _check(lib().lct_workspace_init(_p(self.buf), nbytes, _stream()))
         return self.buf
 
     @property

@@ -9,7 +9,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/lct.h"
+#include "lct.h"
 #include "kernels.h"
 
 using namespace lct;
@@ -101,9 +101,9 @@ int run_topk(const void* scores, int dtype, int32_t* idx, int rows, int64_t n, i
       return fail(LCT_EUNSUPPORTED, "valid_len with grouped rows needs <= %d rows",
                   TOPK_MULTI_MAX_ROWS);
     LCT_HIP(launch_topk_minmax(sp, dtype, rc, n, ld, vl, vl_div, scratch, lay, st), "topk minmax");
-    LCT_HIP(launch_topk_hist(sp, dtype, rc, n, ld, k, vl, vl_div, scratch, lay, st), "topk hist");
-    LCT_HIP(launch_topk_emit(sp, dtype, idx + (size_t)r0 * k, rc, n, ld, k, scratch, lay, st),
-            "topk emit");
+    LCT_HIP(launch_topk_select_multi(sp, dtype, idx + (size_t)r0 * k, rc, n, ld, k, vl, vl_div,
+                                     scratch, lay, st),
+            "topk select");
   }
   return LCT_OK;
 }
@@ -121,18 +121,6 @@ const char* lct_version(void) { return "lct 0.1.0 (gfx950)"; }
 
 const char* lct_last_error(void) { return g_err.c_str(); }
 
-int lct_workspace_init(void* ws, size_t ws_bytes, void* stream) {
-  LCT_REQUIRE(ws != nullptr, "workspace is null");
-  LCT_REQUIRE(aligned(ws, 256), "workspace must be 256-byte aligned");
-  if (ws_bytes < LCT_CONTROL_BYTES)
-    return fail(LCT_ENOWORKSPACE, "workspace of %zu bytes is smaller than the %zu-byte control region",
-                ws_bytes, (size_t)LCT_CONTROL_BYTES);
-  int rc = check_device();
-  if (rc) return rc;
-  LCT_HIP(launch_zero(ws, LCT_CONTROL_BYTES, as_stream(stream)), "workspace init");
-  return LCT_OK;
-}
-
 int lct_idx_score_i8(const int8_t* q, const int8_t* k, int32_t* scores, int B, int Lq,
                      int64_t L, int HD, int64_t q_pos0, void* stream) {
   LCT_REQUIRE(q && k && scores, "null tensor pointer");
@@ -142,6 +130,8 @@ int lct_idx_score_i8(const int8_t* q, const int8_t* k, int32_t* scores, int B, i
   if (!pow2(HD) || HD < 16 || HD > 512)
     return fail(LCT_EUNSUPPORTED, "HD must be a power of two in [16, 512] (got %d)", HD);
   const bool mfma = Lq > 16;
+  if (!mfma && L * HD >= ((int64_t)1 << 31))
+    return fail(LCT_EUNSUPPORTED, "one batch entry's key cache must be < 2 GiB (L*HD = %lld)", (long long)(L * HD));
   if (mfma && HD < 64) return fail(LCT_EUNSUPPORTED, "the MFMA scorer needs HD >= 64");
   int rc = check_device();
   if (rc) return rc;
@@ -170,7 +160,7 @@ int lct_gist_score_bf16(const uint16_t* q, const uint16_t* gk, float* scores, in
 int lct_topk_workspace_bytes(int rows, int64_t n, int k, size_t* bytes) {
   LCT_REQUIRE(bytes, "bytes is null");
   LCT_REQUIRE(rows >= 1 && n >= 1 && n < ((int64_t)1 << 31) && k >= 1, "bad rows / n / k");
-  *bytes = LCT_CONTROL_BYTES + topk_scratch_bytes(rows, n);
+  *bytes = topk_scratch_bytes(rows, n);
   return LCT_OK;
 }
 
@@ -183,21 +173,21 @@ int lct_topk_select(const void* scores, int dtype, int32_t* idx, int rows, int64
   LCT_REQUIRE(rows >= 1 && n >= 1 && n < ((int64_t)1 << 31), "bad rows / n");
   LCT_REQUIRE(ld >= n, "ld must be >= n");
   LCT_REQUIRE(k >= 1, "k must be >= 1");
-  const size_t need = LCT_CONTROL_BYTES + topk_scratch_bytes(rows, n);
+  const size_t need = topk_scratch_bytes(rows, n);
   if (topk_use_multi(rows, n)) {
     LCT_REQUIRE(ws != nullptr && aligned(ws, 256), "workspace must be non-null and 256-byte aligned");
     if (ws_bytes < need) return fail(LCT_ENOWORKSPACE, "topk needs %zu workspace bytes, got %zu", need, ws_bytes);
   }
   int rc = check_device();
   if (rc) return rc;
-  return run_topk(scores, dtype, idx, rows, n, ld, k, valid_len, 1,
-                  reinterpret_cast<char*>(ws) + LCT_CONTROL_BYTES, as_stream(stream));
+  return run_topk(scores, dtype, idx, rows, n, ld, k, valid_len, 1, reinterpret_cast<char*>(ws),
+                  as_stream(stream));
 }
 
 int lct_sparse_attn_workspace_bytes(int B, int Lq, int Hq, int Hkv, int D, int kk, size_t* bytes) {
   LCT_REQUIRE(bytes, "bytes is null");
   LCT_REQUIRE(B >= 1 && Lq >= 1 && Hq >= 1 && Hkv >= 1 && D >= 1 && kk >= 1, "bad shape");
-  *bytes = LCT_CONTROL_BYTES + attn_scratch_bytes(B, Lq, Hkv, kk);
+  *bytes = attn_scratch_bytes(B, Lq, Hkv, kk);
   return LCT_OK;
 }
 
@@ -208,6 +198,8 @@ static int validate_attn_shape(int B, int Lq, int Hq, int Hkv, int D, int64_t L,
   LCT_REQUIRE(Hq % Hkv == 0, "Hq must be a multiple of Hkv");
   LCT_REQUIRE(std::isfinite(scale), "scale must be finite");
   if (D != 128) return fail(LCT_EUNSUPPORTED, "head dim %d (only 128 is built)", D);
+  if (L * Hkv * D * 2 >= ((int64_t)1 << 31))
+    return fail(LCT_EUNSUPPORTED, "one batch entry's K (or V) cache must be < 2 GiB");
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
     return fail(LCT_EUNSUPPORTED, "Hq/Hkv = %d (1, 2, 4, 8 or 16 supported)", G);
@@ -233,10 +225,10 @@ static int validate_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v
 
 static int run_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
                     float* out, int B, int Lq, int Hq, int Hkv, int64_t L, int kk, float scale,
-                    char* ws, char* partials, hipStream_t st) {
+                    char* partials, hipStream_t st) {
   const AttnPlan plan = attn_plan(B, Lq, Hkv, kk);
   LCT_HIP(launch_sparse_attn(q, k, v, idx, out, B, Lq, Hq, Hkv, L, kk, scale, plan,
-                             reinterpret_cast<uint32_t*>(ws), reinterpret_cast<float*>(partials), st),
+                             reinterpret_cast<float*>(partials), st),
           "sparse_attn_gather");
   return LCT_OK;
 }
@@ -247,13 +239,12 @@ int lct_sparse_attn_gather(const uint16_t* q, const uint16_t* k, const uint16_t*
                            void* stream) {
   int rc = validate_attn(q, k, v, idx, out, B, Lq, Hq, Hkv, D, L, kk, scale);
   if (rc) return rc;
-  LCT_REQUIRE(ws != nullptr && aligned(ws, 256), "workspace must be non-null and 256-byte aligned");
-  const size_t need = LCT_CONTROL_BYTES + attn_scratch_bytes(B, Lq, Hkv, kk);
+  const size_t need = attn_scratch_bytes(B, Lq, Hkv, kk);
+  LCT_REQUIRE(need == 0 || (ws != nullptr && aligned(ws, 256)), "workspace must be non-null and 256-byte aligned");
   if (ws_bytes < need) return fail(LCT_ENOWORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
   rc = check_device();
   if (rc) return rc;
-  char* w = reinterpret_cast<char*>(ws);
-  return run_attn(q, k, v, idx, out, B, Lq, Hq, Hkv, L, kk, scale, w, w + LCT_CONTROL_BYTES,
+  return run_attn(q, k, v, idx, out, B, Lq, Hq, Hkv, L, kk, scale, reinterpret_cast<char*>(ws),
                   as_stream(stream));
 }
 
@@ -276,7 +267,7 @@ static int validate_gsa(const uint16_t* q, const uint16_t* rk, const uint16_t* r
 int lct_gsa_attn_workspace_bytes(int BH, int D, int kc, int tail_len, size_t* bytes) {
   LCT_REQUIRE(bytes, "bytes is null");
   LCT_REQUIRE(BH >= 1 && D >= 1 && kc >= 1 && tail_len >= 0, "bad shape");
-  *bytes = LCT_CONTROL_BYTES + gsa_plan(BH, kc, tail_len).part_bytes;
+  *bytes = gsa_plan(BH, kc, tail_len).part_bytes;
   return LCT_OK;
 }
 
@@ -287,16 +278,15 @@ int lct_gsa_attn(const uint16_t* q, const uint16_t* rk, const uint16_t* rv, cons
   int rc = validate_gsa(q, rk, rv, gv, out, BH, D, Nc, raw_cap, chunk, kc, tail_len, scale);
   if (rc) return rc;
   LCT_REQUIRE(gscores && chunk_idx, "null gscores / chunk_idx");
-  LCT_REQUIRE(ws != nullptr && aligned(ws, 256), "workspace must be non-null and 256-byte aligned");
   const GsaPlan plan = gsa_plan(BH, kc, tail_len);
-  const size_t need = LCT_CONTROL_BYTES + plan.part_bytes;
+  const size_t need = plan.part_bytes;
+  LCT_REQUIRE(need == 0 || (ws != nullptr && aligned(ws, 256)), "workspace must be non-null and 256-byte aligned");
   if (ws_bytes < need) return fail(LCT_ENOWORKSPACE, "gsa_attn needs %zu workspace bytes, got %zu", need, ws_bytes);
   rc = check_device();
   if (rc) return rc;
   char* w = reinterpret_cast<char*>(ws);
   LCT_HIP(launch_gsa_attn(q, rk, rv, gv, gscores, chunk_idx, out, BH, Nc, raw_cap, kc, tail_len,
-                          scale, plan, reinterpret_cast<uint32_t*>(w),
-                          reinterpret_cast<float*>(w + LCT_CONTROL_BYTES), as_stream(stream)),
+                          scale, plan, reinterpret_cast<float*>(w), as_stream(stream)),
           "gsa_attn");
   return LCT_OK;
 }
@@ -307,7 +297,7 @@ struct GsaLayout {
 };
 GsaLayout gsa_layout(int BH, int64_t Nc, int kc, int tail_len) {
   GsaLayout l;
-  size_t off = LCT_CONTROL_BYTES;
+  size_t off = 0;
   l.scores = off;
   off += up256((size_t)BH * Nc * sizeof(float));
   l.cidx = off;
@@ -350,7 +340,7 @@ int lct_gsa_decode(const uint16_t* q, const uint16_t* gk, const uint16_t* gv,
   if (rc) return rc;
   const GsaPlan plan = gsa_plan(BH, kc, tail_len);
   LCT_HIP(launch_gsa_attn(q, rk, rv, gv, sc, cidx, out, BH, Nc, raw_cap, kc, tail_len, scale,
-                          plan, reinterpret_cast<uint32_t*>(w), reinterpret_cast<float*>(w + lay.part), st),
+                          plan, reinterpret_cast<float*>(w + lay.part), st),
           "gsa_decode: gsa_attn");
   return LCT_OK;
 }
@@ -368,7 +358,7 @@ struct GroupLayout {
 
 GroupLayout group_layout(const lct_group_desc* d) {
   GroupLayout l;
-  size_t off = LCT_CONTROL_BYTES;
+  size_t off = 0;
   const int64_t rows = (int64_t)d->B * d->Lq;
   if (!d->causal) {
     l.block_rows = rows;
@@ -426,6 +416,8 @@ int validate_group(const lct_group_desc* d) {
     if (d->L > TOPK_ROW_MAX_N) return fail(LCT_EUNSUPPORTED, "causal prefill supports L <= %lld", (long long)TOPK_ROW_MAX_N);
   } else {
     LCT_REQUIRE(d->Lq <= 64, "decode takes at most 64 query rows per batch entry");
+    if (d->L * d->HD >= ((int64_t)1 << 31))
+      return fail(LCT_EUNSUPPORTED, "one batch entry's indexer keys must be < 2 GiB");
     const GroupLayout lay = group_layout(d);
     if (!lay.multi && d->L > TOPK_ROW_MAX_N)
       return fail(LCT_EUNSUPPORTED, "too many rows for L = %lld", (long long)d->L);
@@ -468,10 +460,9 @@ int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stre
                                         reinterpret_cast<uint32_t*>(tw + tl.mm),
                                         reinterpret_cast<TopkRowState*>(tw + tl.state), d->valid_len, st),
                 "group: idx_score");
-        LCT_HIP(launch_topk_hist(scores, LCT_I32, rows, d->L, d->L, d->topk, d->valid_len, d->Lq, tw, tl, st),
-                "group: topk hist");
-        LCT_HIP(launch_topk_emit(scores, LCT_I32, ib, rows, d->L, d->L, d->topk, tw, tl, st),
-                "group: topk emit");
+        LCT_HIP(launch_topk_select_multi(scores, LCT_I32, ib, rows, d->L, d->L, d->topk,
+                                         d->valid_len, d->Lq, tw, tl, st),
+                "group: topk select");
       } else {
         LCT_HIP(launch_idx_score_stream(d->qi[g], d->ki[g], scores, d->B, d->Lq, d->L, d->HD, -1,
                                         nullptr, nullptr, nullptr, st),
@@ -495,7 +486,7 @@ int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stre
       const int l = g * d->layers_per_group + j;
       if (d->layer_idx_seen) d->layer_idx_seen[l] = ib;
       rc = run_attn(d->q[l], d->k[l], d->v[l], ib, d->out[l], d->B, d->Lq, d->Hq, d->Hkv, d->L,
-                    d->topk, d->scale, w, w + lay.attn, st);
+                    d->topk, d->scale, w + lay.attn, st);
       if (rc) return rc;
     }
   }

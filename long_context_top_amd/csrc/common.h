@@ -17,6 +17,17 @@ typedef uint32_t uintx4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 
+// Raw buffer resource over `bytes` bytes (bytes < 2^31).  Loads through it
+// take a 32-bit per-lane offset and a wave-uniform offset; reads at or past
+// `bytes` return zeros (hardware range check), so no clamping is needed.
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+constexpr int BUF_NT = 2;  // cache policy: non-temporal (streamed once)
+
+LCT_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           BUF_RSRC_WORD3);
+}
+
 LCT_DEV float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // Round-to-nearest-even fp32 -> bf16 bit pattern (finite values).

@@ -99,10 +99,9 @@ GsaPlan gsa_plan(int BH, int kc, int tail_len) {
   if (max_splits < 1) max_splits = 1;
   int splits = (512 + BH - 1) / BH;
   if (splits > max_splits) splits = max_splits;
+  if (splits > MERGE_MAX_SPLITS) splits = MERGE_MAX_SPLITS;
   if (splits < 1) splits = 1;
-  if (BH > LCT_CONTROL_COUNTERS) splits = 1;
   p.splits = splits;
-  p.counters = splits > 1 ? (size_t)BH : 0;
   p.part_bytes = splits > 1 ? (size_t)BH * splits * (GSA_D + 2) * sizeof(float) : 0;
   return p;
 }
@@ -112,11 +111,10 @@ __global__ __launch_bounds__(256) void k_gsa_attn(
     const uint16_t* __restrict__ rv, const uint16_t* __restrict__ gv,
     const float* __restrict__ gscores, const int32_t* __restrict__ cidx, float* __restrict__ out,
     int64_t Nc, int64_t raw_cap, int kc, int tail_len, float scale_log2, int splits,
-    uint32_t* __restrict__ counters, float* __restrict__ part) {
+    float* __restrict__ part) {
   constexpr int D = GSA_D;
   __shared__ float red_o[4][D];
   __shared__ float red_m[4], red_l[4];
-  __shared__ uint32_t s_last;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4, j = lane & 15;
   const int64_t bh = blockIdx.y;
@@ -243,39 +241,18 @@ __global__ __launch_bounds__(256) void k_gsa_attn(
     pp[D] = M;
     pp[D + 1] = Ls;
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&counters[bh], 1u) == (uint32_t)(splits - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (d < D) {
-    float Mx = -INFINITY;
-    for (int s2 = 0; s2 < splits; ++s2)
-      Mx = fmaxf(Mx, part[((size_t)bh * splits + s2) * (D + 2) + D]);
-    float L2 = 0.f, a2 = 0.f;
-    if (Mx != -INFINITY) {
-      for (int s2 = 0; s2 < splits; ++s2) {
-        const float* p2 = part + ((size_t)bh * splits + s2) * (D + 2);
-        const float sc = exp2f(p2[D] - Mx);
-        L2 += sc * p2[D + 1];
-        a2 += sc * p2[d];
-      }
-    }
-    out[bh * D + d] = L2 > 0.f ? a2 / L2 : 0.f;
-  }
-  if (d == 0) counters[bh] = 0u;
 }
 
 hipError_t launch_gsa_attn(const uint16_t* q, const uint16_t* rk, const uint16_t* rv,
                            const uint16_t* gv, const float* gscores, const int32_t* cidx,
                            float* out, int BH, int64_t Nc, int64_t raw_cap, int kc, int tail_len,
-                           float scale, const GsaPlan& plan, uint32_t* counters, float* partials,
-                           hipStream_t st) {
+                           float scale, const GsaPlan& plan, float* partials, hipStream_t st) {
   dim3 grid(plan.splits, BH);
   k_gsa_attn<<<grid, 256, 0, st>>>(q, rk, rv, gv, gscores, cidx, out, Nc, raw_cap, kc, tail_len,
-                                   scale * GSA_LOG2E, plan.splits, counters, partials);
-  return hipGetLastError();
+                                   scale * GSA_LOG2E, plan.splits, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.splits == 1) return e;
+  return launch_split_merge(partials, out, BH, plan.splits, 1, 1, GSA_D, st);
 }
 
 }  // namespace lct

@@ -53,9 +53,8 @@ __global__ __launch_bounds__(256) void k_idx_score_stream(
   intx4 qv[QC];
 #pragma unroll
   for (int i = 0; i < QC; ++i) {
-    int r = r0 + i;
-    qv[i] = r < Lq ? *reinterpret_cast<const intx4*>(q + ((size_t)b * Lq + r) * HD + j * 16)
-                   : intx4{0, 0, 0, 0};
+    const int r = r0 + i < Lq ? r0 + i : Lq - 1;  // rows past Lq are computed, never stored
+    qv[i] = *reinterpret_cast<const intx4*>(q + ((size_t)b * Lq + r) * HD + j * 16);
   }
   uint32_t nv = (uint32_t)L;
   if (valid_len) {
@@ -69,17 +68,24 @@ __global__ __launch_bounds__(256) void k_idx_score_stream(
     mx[i] = 0u;
   }
   const int8_t* kb = k + (size_t)b * L * HD;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, L * HD);
   for (int rd = 0; rd < SCORE_ROUNDS; ++rd) {
     const int64_t base = (int64_t)tile * SCORE_TILE + (int64_t)(rd * 4 + wid) * 64;
     if (base >= L) break;
+    // All P loads are issued before any arithmetic, as buffer loads: the key
+    // rows of this batch entry form one buffer resource, the wave's chunk is a
+    // uniform offset and rows past L read as zeros (never stored).
     intx4 kv[P];
+    {
+      const int sbase = __builtin_amdgcn_readfirstlane((int)(base * HD));
+      const int lane_off = g * HD + j * 16;
 #pragma unroll
-    for (int t = 0; t < P; ++t) {
-      int64_t pos = base + t * G + g;
-      kv[t] = pos < L ? __builtin_nontemporal_load(
-                            reinterpret_cast<const intx4*>(kb + pos * HD + j * 16))
-                      : intx4{0, 0, 0, 0};
+      for (int t = 0; t < P; ++t)
+        kv[t] = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, sbase + t * G * HD, BUF_NT);
     }
+    // keep the loads ahead of the arithmetic (the scheduler would otherwise
+    // trade memory-level parallelism for registers)
+    __builtin_amdgcn_sched_barrier(0);
     const int64_t pos = base + j * G + g;  // the position this lane ends up owning
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
@@ -133,11 +139,7 @@ __global__ __launch_bounds__(256) void k_idx_score_stream(
       const size_t row = (size_t)b * Lq + r0 + i;
       mm[(row * t1 + tile) * 2 + 0] = a;
       mm[(row * t1 + tile) * 2 + 1] = c;
-      if (tile == 0) {
-        st[row].cand_fill = 0;
-        st[row].done2 = 0;
-        st[row].done3 = 0;
-      }
+      if (tile == 0) st[row].cand_fill = 0;
     }
   }
 }

@@ -7,11 +7,6 @@
 
 namespace lct {
 
-// Zero-invariant control region at the start of every workspace: merge
-// counters of the split kernels (each op leaves them zero when it finishes).
-constexpr size_t CONTROL_BYTES = (size_t)1 << 20;
-constexpr int64_t LCT_CONTROL_COUNTERS = (int64_t)(CONTROL_BYTES / sizeof(uint32_t));
-
 // ---------------------------------------------------------------- top-k ----
 constexpr int TOPK_NB_LOG2 = 8;                 // bins of the multi-workgroup histogram
 constexpr int TOPK_NB = 1 << TOPK_NB_LOG2;
@@ -20,6 +15,7 @@ constexpr int TOPK_K2_TILE = 256 * 16;          // keys per histogram workgroup
 constexpr int TOPK_K3_THREADS = 512;
 constexpr int TOPK_K3_TILE = TOPK_K3_THREADS * 16;  // positions per emit workgroup
 constexpr int TOPK_MM_TILE = 256 * 16;          // keys per min/max workgroup
+constexpr int TOPK_K4_TILE = 1024 * 32;         // positions per finalize workgroup
 constexpr int TOPK_MULTI_MAX_ROWS = 64;
 constexpr uint32_t TOPK_ALL = 0xFFFFFFFFu;       // "every valid position is chosen"
 
@@ -28,32 +24,33 @@ constexpr int64_t TOPK_ROW_MAX_N = (int64_t)1 << 18;
 
 struct TopkRowState {
   uint32_t lo, shift, tb, need;
-  uint32_t cand_count, cand_fill, done2, done3;
-  uint32_t nvalid, kk, pad0, pad1;
-  uint32_t pad[4];
+  uint32_t cand_count, cand_fill, nvalid, kk;
+  uint32_t pad[8];
 };
 static_assert(sizeof(TopkRowState) == 64, "row state is one 64-byte line");
 
 // Workspace carve-up of the multi-workgroup select for `rows` rows of length n
 // whose min/max partials come from `t1` producer tiles per row.
 struct TopkMultiLayout {
-  size_t state, mm, hist, cands, bitmap, total;
-  int t1, t2, t3;
+  size_t state, mm, hist, cands, bitmap, tilecnt, total;
+  int t1, t2, t3, t4;
+  int64_t k2_tile;  // keys per histogram tile
   int64_t nwords;
 };
 TopkMultiLayout topk_multi_layout(int rows, int64_t n, int t1);
 
-// Producer-independent pieces.  `mm` holds (min, max) key pairs [rows][t1].
-// Row r's valid length is valid_len[r / vl_div] (null: n).
+// Producer of the multi-workgroup select for existing score rows: per-tile
+// (min, max) key partials [rows][t1] and a cleared candidate counter.  Row
+// r's valid length is valid_len[r / vl_div] (null: n).
 hipError_t launch_topk_minmax(const void* scores, int dtype, int rows, int64_t n, int64_t ld,
                               const int32_t* valid_len, int vl_div, char* ws,
                               const TopkMultiLayout& lay, hipStream_t s);
-hipError_t launch_topk_hist(const void* scores, int dtype, int rows, int64_t n, int64_t ld,
-                            int k, const int32_t* valid_len, int vl_div, char* ws,
-                            const TopkMultiLayout& lay, hipStream_t s);
-hipError_t launch_topk_emit(const void* scores, int dtype, int32_t* idx, int rows, int64_t n,
-                            int64_t ld, int k, char* ws, const TopkMultiLayout& lay,
-                            hipStream_t s);
+// The rest of the multi-workgroup select: histogram, emit, finalize (three
+// kernels; kernel boundaries carry the hand-offs).
+hipError_t launch_topk_select_multi(const void* scores, int dtype, int32_t* idx, int rows,
+                                    int64_t n, int64_t ld, int k, const int32_t* valid_len,
+                                    int vl_div, char* ws, const TopkMultiLayout& lay,
+                                    hipStream_t s);
 // One workgroup per row.  Row r's valid length is min(n, causal_pos0 + r + 1)
 // when causal_pos0 >= 0, else valid_len[r / vl_div] (or n when valid_len is null).
 hipError_t launch_topk_rows(const void* scores, int dtype, int32_t* idx, int rows, int64_t n,
@@ -63,7 +60,7 @@ hipError_t launch_topk_rows(const void* scores, int dtype, int32_t* idx, int row
 // ------------------------------------------------------------- indexer ----
 // Streaming decode scorer; optionally writes (min,max) partials + clears the
 // row states of a following multi-workgroup select (mm/state may be null).
-constexpr int SCORE_TILE = 1024;  // positions per workgroup (4 waves x 4 rounds x 64)
+constexpr int SCORE_TILE = 512;  // positions per workgroup (4 waves x 2 rounds x 64)
 hipError_t launch_idx_score_stream(const int8_t* q, const int8_t* k, int32_t* s, int B, int Lq,
                                    int64_t L, int HD, int64_t q_pos0, uint32_t* mm,
                                    TopkRowState* state, const int32_t* valid_len,
@@ -74,17 +71,25 @@ hipError_t launch_idx_score_mfma(const int8_t* q, const int8_t* k, int32_t* s, i
                                  int64_t L, int HD, int64_t q_pos0, hipStream_t st);
 
 // -------------------------------------------------------------- gather ----
+constexpr int MERGE_MAX_SPLITS = 32;  // split partials per unit the merge kernel combines
 struct AttnPlan {
   int splits;       // workgroups per (b, row, kv head)
   int per_split;    // entries per workgroup
+  int waves;        // waves per workgroup (1, 2 or 4)
+  int tok;          // positions per wave step (16 or 32)
   size_t part_bytes;
-  size_t counters;  // number of merge counters used in the control region
 };
 AttnPlan attn_plan(int B, int Lq, int Hkv, int kk);
+// With plan.splits > 1 the kernel writes (O, m, l) partials and a merge
+// kernel combines them (log-sum-exp merge).
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* idx, float* out, int B, int Lq, int Hq, int Hkv,
                               int64_t L, int kk, float scale, const AttnPlan& plan,
-                              uint32_t* counters, float* partials, hipStream_t st);
+                              float* partials, hipStream_t st);
+// Merge of split partials: part[unit][split][hs][D+2] (O[D], m, l) ->
+// out[(unit * G + h) * D + d] for h < G.
+hipError_t launch_split_merge(const float* part, float* out, int64_t units, int splits, int hs,
+                              int G, int D, hipStream_t st);
 
 // ----------------------------------------------------------------- GSA ----
 hipError_t launch_gist_score(const uint16_t* q, const uint16_t* gk, float* s, int BH, int64_t Nc,
@@ -92,14 +97,12 @@ hipError_t launch_gist_score(const uint16_t* q, const uint16_t* gk, float* s, in
 struct GsaPlan {
   int splits;
   size_t part_bytes;
-  size_t counters;
 };
 GsaPlan gsa_plan(int BH, int kc, int tail_len);
 hipError_t launch_gsa_attn(const uint16_t* q, const uint16_t* rk, const uint16_t* rv,
                            const uint16_t* gv, const float* gscores, const int32_t* cidx,
                            float* out, int BH, int64_t Nc, int64_t raw_cap, int kc, int tail_len,
-                           float scale, const GsaPlan& plan, uint32_t* counters, float* partials,
-                           hipStream_t st);
+                           float scale, const GsaPlan& plan, float* partials, hipStream_t st);
 
 // --------------------------------------------------------------- misc ----
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);

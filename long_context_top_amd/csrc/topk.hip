@@ -69,65 +69,6 @@ LCT_DEV uint32_t bin_of(uint32_t key, uint32_t lo, uint32_t shift, uint32_t nb) 
 
 LCT_DEV uint32_t next_pow2(uint32_t x) { return x <= 1 ? 1u : 1u << (32 - __clz(x - 1)); }
 
-// Resolve bin `tb` exactly by streaming the row (used when it holds more
-// candidates than fit in LDS): radix passes over the low `shift` bits, then
-// an ordered scan that takes the `need_eq` lowest positions among keys equal
-// to the exact threshold.  Sets the chosen bits in `bitmap`.
-template <int NT, int DT>
-LCT_DEV void resolve_bin_exact(const void* row, uint32_t nv, uint32_t lo, uint32_t shift,
-                               uint32_t nb, uint32_t tb, uint32_t need, uint32_t* bitmap,
-                               uint32_t* lds_hist, uint32_t* lds_scan) {
-  uint32_t prefix = 0, rb = shift, need_rem = need;
-  while (rb > 0) {
-    uint32_t w = rb < 8 ? rb : 8;
-    uint32_t ds = rb - w;
-    for (int i = threadIdx.x; i < 256; i += NT) lds_hist[i] = 0;
-    __syncthreads();
-    for (uint32_t p = threadIdx.x; p < nv; p += NT) {
-      const uint32_t key = load_key<DT>(row, p);
-      if (bin_of(key, lo, shift, nb) != tb) continue;
-      uint32_t sub = (key - lo) & ((1u << shift) - 1u);
-      if ((sub >> rb) != prefix) continue;
-      atomicAdd(&lds_hist[(sub >> ds) & ((1u << w) - 1u)], 1u);
-    }
-    __syncthreads();
-    // walk digits from the top (one thread: at most 256 bins)
-    if (threadIdx.x == 0) {
-      uint32_t cum = 0, dsel = 0;
-      for (int b = (1 << w) - 1; b >= 0; --b) {
-        uint32_t c = lds_hist[b];
-        if (cum + c >= need_rem) {
-          dsel = (uint32_t)b;
-          break;
-        }
-        cum += c;
-      }
-      lds_scan[0] = dsel;
-      lds_scan[1] = need_rem - cum;
-    }
-    __syncthreads();
-    prefix = (prefix << w) | lds_scan[0];
-    need_rem = lds_scan[1];
-    rb = ds;
-    __syncthreads();
-  }
-  const uint32_t T = lo + (tb << shift) + prefix;  // exact threshold key
-  uint32_t carry = 0;
-  for (uint32_t base = 0; base < nv; base += NT) {
-    uint32_t p = base + threadIdx.x;
-    uint32_t key = p < nv ? load_key<DT>(row, p) : 0u;
-    bool in = p < nv && bin_of(key, lo, shift, nb) == tb;
-    bool gt = in && key > T;
-    bool eq = in && key == T;
-    uint32_t tot;
-    uint32_t r = block_excl_scan<NT>(eq ? 1u : 0u, lds_scan, tot);
-    bool sel = gt || (eq && carry + r < need_rem);
-    if (sel) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
-    carry += tot;
-  }
-  __syncthreads();
-}
-
 // Ascending position list from a bitmap (all threads of the block).
 template <int NT>
 LCT_DEV void emit_bitmap(const uint32_t* bitmap, uint32_t nwords, int32_t* out, uint32_t k,
@@ -166,8 +107,12 @@ TopkMultiLayout topk_multi_layout(int rows, int64_t n, int t1) {
   TopkMultiLayout l;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   l.t1 = t1;
-  l.t2 = (int)((n + TOPK_K2_TILE - 1) / TOPK_K2_TILE);
+  int64_t per = 16;  // keys per thread of a histogram workgroup; at most 64 tiles per row
+  while ((n + 256 * per - 1) / (256 * per) > 64) per *= 2;
+  l.k2_tile = 256 * per;
+  l.t2 = (int)((n + l.k2_tile - 1) / l.k2_tile);
   l.t3 = (int)((n + TOPK_K3_TILE - 1) / TOPK_K3_TILE);
+  l.t4 = (int)((n + TOPK_K4_TILE - 1) / TOPK_K4_TILE);
   l.nwords = ((n + 63) / 64) * 2;
   size_t off = 0;
   l.state = off;
@@ -180,6 +125,8 @@ TopkMultiLayout topk_multi_layout(int rows, int64_t n, int t1) {
   off += up((size_t)rows * TOPK_CAP * sizeof(uint64_t));
   l.bitmap = off;
   off += up((size_t)rows * l.nwords * sizeof(uint32_t));
+  l.tilecnt = off;
+  off += up((size_t)rows * l.t3 * sizeof(uint32_t));
   l.total = off;
   return l;
 }
@@ -191,7 +138,9 @@ LCT_DEV uint32_t row_nvalid(const int32_t* valid_len, int row, int64_t n, int vl
   return (uint32_t)(v < n ? v : n);
 }
 
-// K1 (generic producer): per-tile (min,max) of the valid keys; clears state.
+// K1 (generic producer): per-tile (min,max) of the valid keys; clears the
+// row's candidate counter.  The indexer scorer does the same when it feeds
+// the select directly.
 template <int DT>
 __global__ __launch_bounds__(256) void k_topk_minmax(const void* __restrict__ scores, int64_t n,
                                                      int64_t ld, const int32_t* valid_len,
@@ -215,156 +164,365 @@ __global__ __launch_bounds__(256) void k_topk_minmax(const void* __restrict__ sc
   if (threadIdx.x == 0) {
     mm[((size_t)row * t1 + tile) * 2 + 0] = mn;
     mm[((size_t)row * t1 + tile) * 2 + 1] = mx;
-    if (tile == 0) {
-      st[row].cand_fill = 0;
-      st[row].done2 = 0;
-      st[row].done3 = 0;
-    }
+    if (tile == 0) st[row].cand_fill = 0;
   }
 }
 
-// K2: window from the (min,max) partials, 256-bin histogram per tile; the last
-// workgroup of a row sums the tile histograms and finds the threshold bin.
+// Window of a row from the producer's (min,max) partials.
+template <int NT>
+LCT_DEV void row_window(const uint32_t* mm_row, int t1, uint32_t nv, uint32_t& lo,
+                        uint32_t& shift, uint32_t* lds) {
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = threadIdx.x; i < t1; i += NT) {
+    mn = min(mn, mm_row[2 * i]);
+    mx = max(mx, mm_row[2 * i + 1]);
+  }
+  block_minmax<NT>(mn, mx, lds);
+  lo = mn;
+  shift = nv ? window_shift(mn, mx, TOPK_NB_LOG2) : 0u;
+}
+
+// K2: 256-bin histogram of one tile of a row (window from the partials).
 template <int DT>
 __global__ __launch_bounds__(256) void k_topk_hist(const void* __restrict__ scores, int64_t n,
                                                    int64_t ld, int k, const int32_t* valid_len,
-                                                   int vl_div, const uint32_t* __restrict__ mm, int t1,
-                                                   uint32_t* __restrict__ hist, int t2,
-                                                   TopkRowState* __restrict__ st) {
+                                                   int vl_div, const uint32_t* __restrict__ mm,
+                                                   int t1, uint32_t* __restrict__ hist, int t2,
+                                                   int64_t tile_len) {
   __shared__ uint32_t h[TOPK_NB];
   __shared__ uint32_t lds[16];
-  __shared__ uint32_t s_last;
   const int row = blockIdx.y, tile = blockIdx.x;
   const uint32_t nv = row_nvalid(valid_len, row, n, vl_div);
   const uint32_t kk = (uint32_t)k < nv ? (uint32_t)k : nv;
-  // reduce the producer's partials
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = threadIdx.x; i < t1; i += 256) {
-    mn = min(mn, mm[((size_t)row * t1 + i) * 2 + 0]);
-    mx = max(mx, mm[((size_t)row * t1 + i) * 2 + 1]);
+  const void* rp = reinterpret_cast<const char*>(scores) + (size_t)row * ld * 4;
+  const int64_t base = (int64_t)tile * tile_len;
+  const int64_t end = base + tile_len < (int64_t)nv ? base + tile_len : (int64_t)nv;
+  // the tile's keys are requested first; the window reduction overlaps them
+  constexpr int PF = 16;
+  uint32_t kbuf[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int64_t p = base + j * 256 + threadIdx.x;
+    kbuf[j] = load_key<DT>(rp, p < end ? p : (end > 0 ? end - 1 : 0));  // clamped, in bounds
   }
-  block_minmax<256>(mn, mx, lds);
-  const uint32_t lo = mn;
-  const uint32_t shift = nv ? window_shift(mn, mx, TOPK_NB_LOG2) : 0u;
+  uint32_t lo, shift;
+  row_window<256>(mm + (size_t)row * t1 * 2, t1, nv, lo, shift, lds);
   for (int i = threadIdx.x; i < TOPK_NB; i += 256) h[i] = 0;
   __syncthreads();
-  const void* rp = reinterpret_cast<const char*>(scores) + (size_t)row * ld * 4;
   if (kk < nv) {
-    const int64_t base = (int64_t)tile * TOPK_K2_TILE;
-    for (int j = 0; j < TOPK_K2_TILE / 256; ++j) {
-      int64_t p = base + j * 256 + threadIdx.x;
-      if (p < nv) atomicAdd(&h[bin_of(load_key<DT>(rp, p), lo, shift, TOPK_NB)], 1u);
-    }
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+      if (base + j * 256 + threadIdx.x < end) atomicAdd(&h[bin_of(kbuf[j], lo, shift, TOPK_NB)], 1u);
+    for (int64_t p = base + PF * 256 + threadIdx.x; p < end; p += 256)
+      atomicAdd(&h[bin_of(load_key<DT>(rp, p), lo, shift, TOPK_NB)], 1u);
   }
   __syncthreads();
   uint32_t* hp = hist + ((size_t)row * t2 + tile) * TOPK_NB;
   for (int i = threadIdx.x; i < TOPK_NB; i += 256) hp[i] = h[i];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&st[row].done2, 1u) == (uint32_t)(t2 - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // last workgroup of this row: total histogram, threshold bin from the top
-  for (int i = threadIdx.x; i < TOPK_NB; i += 256) {
-    uint32_t c = 0;
-    for (int t = 0; t < t2; ++t) c += hist[((size_t)row * t2 + t) * TOPK_NB + i];
-    h[i] = c;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    TopkRowState s = st[row];
-    s.lo = lo;
-    s.shift = shift;
-    s.nvalid = nv;
-    s.kk = kk;
-    if (kk >= nv) {
-      s.tb = TOPK_ALL;
-      s.need = 0;
-      s.cand_count = 0;
-    } else {
-      uint32_t cum = 0;
-      int b = TOPK_NB - 1;
-      for (; b > 0; --b) {
-        if (cum + h[b] >= kk) break;
-        cum += h[b];
-      }
-      s.tb = (uint32_t)b;
-      s.need = kk - cum;
-      s.cand_count = h[b];
-    }
-    s.done2 = 0;
-    st[row] = s;
-  }
 }
 
-// K3: bitmap of positions above the threshold bin + candidate list; the last
-// workgroup of a row selects among the candidates and writes the index row.
+struct RowSel {
+  uint32_t lo, shift, tb, need, ccount;
+};
+
+// Threshold bin of a row from the per-tile histograms (every caller derives
+// the same values).  NT >= TOPK_NB.
+template <int NT>
+LCT_DEV RowSel row_select_params(const uint32_t* mm_row, int t1, const uint32_t* hist_row,
+                                 int t2, uint32_t nv, uint32_t kk, uint32_t* lds_scan,
+                                 uint32_t* lds_small, uint32_t* lds_tot /* NT words */) {
+  static_assert(NT >= TOPK_NB, "one thread per bin");
+  RowSel r;
+  row_window<NT>(mm_row, t1, nv, r.lo, r.shift, lds_small);
+  if (kk >= nv) {
+    r.tb = TOPK_ALL;
+    r.need = 0;
+    r.ccount = 0;
+    return r;
+  }
+  // thread t < NB owns bin NB-1-t; an exclusive scan in thread order counts
+  // the keys in higher bins.  The per-tile partials are summed by all NT
+  // threads (NT/NB tile slices each, loads issued back to back).
+  constexpr int SL = NT / TOPK_NB;
+  const int b = TOPK_NB - 1 - (int)(threadIdx.x % TOPK_NB);
+  const int slice = threadIdx.x / TOPK_NB;
+  uint32_t part = 0;
+  {
+    const int t_begin = slice * ((t2 + SL - 1) / SL);
+    const int t_end = min(t2, t_begin + (t2 + SL - 1) / SL);
+    uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    int t = t_begin;
+    for (; t + 4 <= t_end; t += 4) {
+      a0 += hist_row[(size_t)(t + 0) * TOPK_NB + b];
+      a1 += hist_row[(size_t)(t + 1) * TOPK_NB + b];
+      a2 += hist_row[(size_t)(t + 2) * TOPK_NB + b];
+      a3 += hist_row[(size_t)(t + 3) * TOPK_NB + b];
+    }
+    for (; t < t_end; ++t) a0 += hist_row[(size_t)t * TOPK_NB + b];
+    part = a0 + a1 + a2 + a3;
+  }
+  if (SL > 1) {
+    lds_tot[threadIdx.x] = part;
+    __syncthreads();
+  }
+  uint32_t c = 0;
+  if ((int)threadIdx.x < TOPK_NB) {
+    c = part;
+    for (int j = 1; j < SL; ++j) c += lds_tot[j * TOPK_NB + threadIdx.x];
+  }
+  uint32_t tot;
+  const uint32_t higher = block_excl_scan<NT>(c, lds_scan, tot);
+  if ((int)threadIdx.x < TOPK_NB && higher < kk && higher + c >= kk) {
+    lds_small[0] = (uint32_t)b;
+    lds_small[1] = kk - higher;
+    lds_small[2] = c;
+  }
+  __syncthreads();
+  r.tb = lds_small[0];
+  r.need = lds_small[1];
+  r.ccount = lds_small[2];
+  __syncthreads();
+  return r;
+}
+
+// K3: bitmap words of positions above the threshold bin and the list of
+// candidates in it, for one tile of a row.
 template <int DT>
 __global__ __launch_bounds__(TOPK_K3_THREADS) void k_topk_emit(
-    const void* __restrict__ scores, int64_t n, int64_t ld, int k, int32_t* __restrict__ idx,
-    TopkRowState* __restrict__ st, uint64_t* __restrict__ cands, uint32_t* __restrict__ bitmap,
-    int64_t nwords, int t3) {
+    const void* __restrict__ scores, int64_t n, int64_t ld, int k, const int32_t* valid_len,
+    int vl_div, const uint32_t* __restrict__ mm, int t1, const uint32_t* __restrict__ hist,
+    int t2, TopkRowState* __restrict__ st, uint64_t* __restrict__ cands,
+    uint32_t* __restrict__ bitmap, int64_t nwords, uint32_t* __restrict__ tilecnt, int t3) {
   constexpr int NT = TOPK_K3_THREADS;
-  __shared__ uint64_t sc[TOPK_CAP];
   __shared__ uint32_t lds_scan[NT / 64 + 2];
-  __shared__ uint32_t lds_hist[256];
-  __shared__ uint32_t s_last;
+  __shared__ uint32_t lds_small[2 * (NT / 64) + 4];
+  __shared__ uint32_t lds_tot[NT];
+  __shared__ uint32_t wave_cnt[NT / 64];
   const int row = blockIdx.y, tile = blockIdx.x;
-  const TopkRowState s = st[row];
-  const uint32_t nv = s.nvalid;
+  const uint32_t nv = row_nvalid(valid_len, row, n, vl_div);
+  const uint32_t kk = (uint32_t)k < nv ? (uint32_t)k : nv;
   const void* rp = reinterpret_cast<const char*>(scores) + (size_t)row * ld * 4;
-  uint32_t* bm = bitmap + (size_t)row * nwords;
-  uint64_t* cd = cands + (size_t)row * TOPK_CAP;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t tbase = (int64_t)tile * TOPK_K3_TILE;
-  for (int c = wid; c < TOPK_K3_TILE / 64; c += NT / 64) {
-    int64_t cb = tbase + (int64_t)c * 64;
+  constexpr int CH = TOPK_K3_TILE / NT;  // 64-position chunks per wave
+  // the keys of this thread's chunks are requested first
+  uint32_t kbuf[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t p = tbase + (int64_t)(c * (NT / 64) + wid) * 64 + lane;
+    kbuf[c] = load_key<DT>(rp, p < nv ? p : (nv > 0 ? nv - 1 : 0));  // clamped, in bounds
+  }
+  const RowSel s = row_select_params<NT>(mm + (size_t)row * t1 * 2, t1,
+                                         hist + (size_t)row * t2 * TOPK_NB, t2, nv, kk, lds_scan,
+                                         lds_small, lds_tot);
+  if (tile == 0 && threadIdx.x == 0) {
+    TopkRowState w = st[row];
+    w.lo = s.lo;
+    w.shift = s.shift;
+    w.tb = s.tb;
+    w.need = s.need;
+    w.cand_count = s.ccount;
+    w.nvalid = nv;
+    w.kk = kk;
+    st[row] = w;
+  }
+  uint32_t* bm = bitmap + (size_t)row * nwords;
+  uint64_t* cd = cands + (size_t)row * TOPK_CAP;
+  uint32_t nabove = 0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t cb = tbase + (int64_t)(c * (NT / 64) + wid) * 64;
     if (cb >= n) break;
-    int64_t p = cb + lane;
-    bool valid = p < nv;
-    uint32_t key = valid ? load_key<DT>(rp, p) : 0u;
-    uint32_t bin = bin_of(key, s.lo, s.shift, TOPK_NB);
-    bool above = valid && (s.tb == TOPK_ALL || bin > s.tb);
-    bool cand = valid && s.tb != TOPK_ALL && bin == s.tb;
-    uint64_t am = __ballot(above);
+    const int64_t p = cb + lane;
+    const bool valid = p < nv;
+    const uint32_t key = kbuf[c];
+    const uint32_t bin = bin_of(key, s.lo, s.shift, TOPK_NB);
+    const bool above = valid && (s.tb == TOPK_ALL || bin > s.tb);
+    const bool cand = valid && s.tb != TOPK_ALL && bin == s.tb;
+    const uint64_t am = __ballot(above);
     if (lane == 0) *reinterpret_cast<uint64_t*>(bm + (cb >> 5)) = am;
-    uint64_t cm = __ballot(cand);
-    if (cm && s.cand_count <= TOPK_CAP) {
+    nabove += (uint32_t)__popcll(am);
+    const uint64_t cm = __ballot(cand);
+    if (cm && s.ccount <= TOPK_CAP) {
       uint32_t b0 = 0;
       if (lane == 0) b0 = atomicAdd(&st[row].cand_fill, (uint32_t)__popcll(cm));
       b0 = __shfl(b0, 0, 64);
       if (cand) {
-        uint32_t slot = b0 + lane_rank(cm);
+        const uint32_t slot = b0 + lane_rank(cm);
         if (slot < TOPK_CAP) cd[slot] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)p);
       }
     }
   }
-  __threadfence();
+  if (lane == 0) wave_cnt[wid] = nabove;
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&st[row].done3, 1u) == (uint32_t)(t3 - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < NT / 64; ++w) t += wave_cnt[w];
+    tilecnt[(size_t)row * t3 + tile] = t;
+  }
+}
+
+// Exact threshold inside bin tb by 8-bit radix passes over the row (used when
+// the bin holds more candidates than fit in LDS).  Returns the exact key T;
+// need_eq gets how many keys equal to T are taken (the lowest positions).
+template <int NT, int DT>
+LCT_DEV uint32_t exact_threshold(const void* row, uint32_t nv, uint32_t lo, uint32_t shift,
+                                 uint32_t nb, uint32_t tb, uint32_t need, uint32_t& need_eq,
+                                 uint32_t* lds_hist, uint32_t* lds_scan) {
+  uint32_t prefix = 0, rb = shift, need_rem = need;
+  while (rb > 0) {
+    const uint32_t w = rb < 8 ? rb : 8;
+    const uint32_t ds = rb - w;
+    for (int i = threadIdx.x; i < 256; i += NT) lds_hist[i] = 0;
+    __syncthreads();
+    for (uint32_t p = threadIdx.x; p < nv; p += NT) {
+      const uint32_t key = load_key<DT>(row, p);
+      if (bin_of(key, lo, shift, nb) != tb) continue;
+      const uint32_t sub = (key - lo) & ((1u << shift) - 1u);
+      if ((sub >> rb) != prefix) continue;
+      atomicAdd(&lds_hist[(sub >> ds) & ((1u << w) - 1u)], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t cum = 0, dsel = 0;
+      for (int b = (1 << w) - 1; b >= 0; --b) {
+        const uint32_t c = lds_hist[b];
+        if (cum + c >= need_rem) {
+          dsel = (uint32_t)b;
+          break;
+        }
+        cum += c;
+      }
+      lds_scan[0] = dsel;
+      lds_scan[1] = need_rem - cum;
+    }
+    __syncthreads();
+    prefix = (prefix << w) | lds_scan[0];
+    need_rem = lds_scan[1];
+    rb = ds;
+    __syncthreads();
+  }
+  need_eq = need_rem;
+  return lo + (tb << shift) + prefix;
+}
+
+// K4: the chosen candidates are decided (redundantly, by every workgroup of
+// the row: rank counting when there are few, a bitonic sort otherwise); each
+// workgroup then expands one tile of the bitmap into the ascending index row,
+// at the offset given by the per-tile counts of K3 plus the chosen
+// candidates below the tile.
+constexpr int FIN_NT = 1024;
+constexpr int TOPK_RANK_MAX = 512;  // rank counting up to this many candidates
+
+template <int DT>
+__global__ __launch_bounds__(FIN_NT) void k_topk_finalize(
+    const void* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx,
+    const TopkRowState* __restrict__ st, const uint64_t* __restrict__ cands,
+    const uint32_t* __restrict__ bitmap, int64_t nwords, const uint32_t* __restrict__ tilecnt,
+    int t3) {
+  constexpr int NT = FIN_NT;
+  static_assert(TOPK_K4_TILE == NT * 32, "one bitmap word per thread");
+  __shared__ uint64_t sc[TOPK_CAP];
+  __shared__ uint32_t tw[NT];
+  __shared__ uint32_t lds_scan[NT / 64 + 2];
+  __shared__ uint32_t lds_hist[256];
+  __shared__ uint32_t s_below;
+  const int row = blockIdx.y, tile = blockIdx.x;
+  const uint32_t* bm = bitmap + (size_t)row * nwords;
+  const uint32_t w0 = (uint32_t)tile * NT;             // first bitmap word of this tile
+  // independent loads first: this tile's bitmap word, candidates, tile counts
+  const uint32_t w = w0 + threadIdx.x;
+  const uint32_t word_raw = bm[w < (uint32_t)nwords ? w : (uint32_t)nwords - 1];
+  const uint64_t* cd = cands + (size_t)row * TOPK_CAP;
+  const uint64_t cand_raw = cd[threadIdx.x % TOPK_RANK_MAX];
+  uint32_t before = 0;
+  {
+    const int k3_per_k4 = TOPK_K4_TILE / TOPK_K3_TILE;
+    const int lim = tile * k3_per_k4 < t3 ? tile * k3_per_k4 : t3;
+    for (int t = threadIdx.x; t < lim; t += NT) before += tilecnt[(size_t)row * t3 + t];
+  }
+  const TopkRowState s = st[row];
+  const uint32_t nv = s.nvalid;
   int32_t* out = idx + (size_t)row * k;
+  const void* rp = reinterpret_cast<const char*>(scores) + (size_t)row * ld * 4;
+  const uint32_t nw = (nv + 31) / 32;
+
+  if (s.tb != TOPK_ALL && s.cand_count > TOPK_CAP) {
+    // too many candidates in the threshold bin: tile 0 resolves the bin exactly
+    // and writes the whole row with an ordered scan; the other tiles have nothing to do
+    if (tile != 0) return;
+    uint32_t need_eq;
+    const uint32_t T = exact_threshold<NT, DT>(rp, nv, s.lo, s.shift, TOPK_NB, s.tb, s.need,
+                                               need_eq, lds_hist, lds_scan);
+    uint32_t carry_eq = 0, carry = 0;
+    for (uint32_t base = 0; base < nv; base += NT) {
+      const uint32_t p = base + threadIdx.x;
+      const uint32_t key = p < nv ? load_key<DT>(rp, p) : 0u;
+      const uint32_t bin = bin_of(key, s.lo, s.shift, TOPK_NB);
+      const bool in = p < nv && bin == s.tb;
+      const bool eq = in && key == T;
+      uint32_t teq;
+      const uint32_t req = block_excl_scan<NT>(eq ? 1u : 0u, lds_scan, teq);
+      const bool sel = (p < nv && bin > s.tb) || (in && key > T) || (eq && carry_eq + req < need_eq);
+      uint32_t tsel;
+      const uint32_t rs = block_excl_scan<NT>(sel ? 1u : 0u, lds_scan, tsel);
+      if (sel && carry + rs < (uint32_t)k) out[carry + rs] = (int32_t)p;
+      carry_eq += teq;
+      carry += tsel;
+    }
+    for (uint32_t j = carry + threadIdx.x; j < (uint32_t)k; j += NT) out[j] = -1;
+    return;
+  }
+
+  tw[threadIdx.x] = w < nw ? word_raw : 0u;
+  if (threadIdx.x == 0) s_below = 0;
+  __syncthreads();
+  uint32_t chosen_below = 0;
   if (s.tb != TOPK_ALL) {
-    if (s.cand_count <= TOPK_CAP) {
-      uint32_t m = next_pow2(s.cand_count);
-      for (uint32_t i = threadIdx.x; i < m; i += NT) sc[i] = i < s.cand_count ? cd[i] : 0ull;
+    const uint32_t c = s.cand_count;
+    if (c <= TOPK_RANK_MAX) {
+      if (threadIdx.x < c) sc[threadIdx.x] = cand_raw;
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < c; i += NT) {
+        const uint64_t me = sc[i];
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < c; ++j) rank += sc[j] > me ? 1u : 0u;
+        if (rank < s.need) {
+          const uint32_t p = ~(uint32_t)(me & 0xFFFFFFFFull);
+          const uint32_t pw = p >> 5;
+          if (pw < w0) ++chosen_below;
+          else if (pw < w0 + NT) atomicOr(&tw[pw - w0], 1u << (p & 31));
+        }
+      }
+    } else {
+      const uint32_t m = next_pow2(c);
+      for (uint32_t i = threadIdx.x; i < m; i += NT) sc[i] = i < c ? cd[i] : 0ull;
       __syncthreads();
       bitonic_sort_desc<NT>(sc, (int)m);
       for (uint32_t i = threadIdx.x; i < s.need; i += NT) {
-        uint32_t p = ~(uint32_t)(sc[i] & 0xFFFFFFFFull);
-        atomicOr(&bm[p >> 5], 1u << (p & 31));
+        const uint32_t p = ~(uint32_t)(sc[i] & 0xFFFFFFFFull);
+        const uint32_t pw = p >> 5;
+        if (pw < w0) ++chosen_below;
+        else if (pw < w0 + NT) atomicOr(&tw[pw - w0], 1u << (p & 31));
       }
-    } else {
-      resolve_bin_exact<NT, DT>(rp, nv, s.lo, s.shift, TOPK_NB, s.tb, s.need, bm, lds_hist, lds_scan);
     }
-    __threadfence();
-    __syncthreads();
   }
-  emit_bitmap<NT>(bm, (uint32_t)((nv + 31) / 32), out, (uint32_t)k, lds_scan);
-  if (threadIdx.x == 0) st[row].done3 = 0;
+  uint32_t tot;
+  const uint32_t off0 = block_excl_scan<NT>(before + chosen_below, lds_scan, tot);
+  (void)off0;
+  const uint32_t offset = tot;  // everything before this tile
+  const uint32_t word = tw[threadIdx.x];
+  uint32_t tot2;
+  uint32_t off = offset + block_excl_scan<NT>(__popc(word), lds_scan, tot2);
+  uint32_t wv = word;
+  while (wv) {
+    const uint32_t bit = __ffs(wv) - 1;
+    wv &= wv - 1;
+    if (off < (uint32_t)k) out[off] = (int32_t)(w * 32 + bit);
+    ++off;
+  }
+  if (tile == 0)
+    for (uint32_t j = s.kk + threadIdx.x; j < (uint32_t)k; j += NT) out[j] = -1;
 }
 
 hipError_t launch_topk_minmax(const void* scores, int dtype, int rows, int64_t n, int64_t ld,
@@ -380,33 +538,26 @@ hipError_t launch_topk_minmax(const void* scores, int dtype, int rows, int64_t n
   return hipGetLastError();
 }
 
-hipError_t launch_topk_hist(const void* scores, int dtype, int rows, int64_t n, int64_t ld,
-                            int k, const int32_t* valid_len, int vl_div, char* ws,
-                            const TopkMultiLayout& lay, hipStream_t s) {
-  dim3 grid(lay.t2, rows);
+hipError_t launch_topk_select_multi(const void* scores, int dtype, int32_t* idx, int rows,
+                                    int64_t n, int64_t ld, int k, const int32_t* valid_len,
+                                    int vl_div, char* ws, const TopkMultiLayout& lay,
+                                    hipStream_t s) {
   auto st = reinterpret_cast<TopkRowState*>(ws + lay.state);
   auto mm = reinterpret_cast<const uint32_t*>(ws + lay.mm);
   auto hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
-  if (dtype == 0)
-    k_topk_hist<0><<<grid, 256, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, st);
-  else
-    k_topk_hist<1><<<grid, 256, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, st);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_emit(const void* scores, int dtype, int32_t* idx, int rows, int64_t n,
-                            int64_t ld, int k, char* ws, const TopkMultiLayout& lay,
-                            hipStream_t s) {
-  dim3 grid(lay.t3, rows);
-  auto st = reinterpret_cast<TopkRowState*>(ws + lay.state);
   auto cands = reinterpret_cast<uint64_t*>(ws + lay.cands);
   auto bm = reinterpret_cast<uint32_t*>(ws + lay.bitmap);
-  if (dtype == 0)
-    k_topk_emit<0><<<grid, TOPK_K3_THREADS, 0, s>>>(scores, n, ld, k, idx, st, cands, bm,
-                                                    lay.nwords, lay.t3);
-  else
-    k_topk_emit<1><<<grid, TOPK_K3_THREADS, 0, s>>>(scores, n, ld, k, idx, st, cands, bm,
-                                                    lay.nwords, lay.t3);
+  auto tc = reinterpret_cast<uint32_t*>(ws + lay.tilecnt);
+  const dim3 g2(lay.t2, rows), g3(lay.t3, rows), g4(lay.t4, rows);
+  if (dtype == 0) {
+    k_topk_hist<0><<<g2, 256, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, lay.k2_tile);
+    k_topk_emit<0><<<g3, TOPK_K3_THREADS, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, st, cands, bm, lay.nwords, tc, lay.t3);
+    k_topk_finalize<0><<<g4, FIN_NT, 0, s>>>(scores, ld, k, idx, st, cands, bm, lay.nwords, tc, lay.t3);
+  } else {
+    k_topk_hist<1><<<g2, 256, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, lay.k2_tile);
+    k_topk_emit<1><<<g3, TOPK_K3_THREADS, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, st, cands, bm, lay.nwords, tc, lay.t3);
+    k_topk_finalize<1><<<g4, FIN_NT, 0, s>>>(scores, ld, k, idx, st, cands, bm, lay.nwords, tc, lay.t3);
+  }
   return hipGetLastError();
 }
 
@@ -521,7 +672,20 @@ __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ s
       atomicOr(&bm[p >> 5], 1u << (p & 31));
     }
   } else {
-    resolve_bin_exact<NT, DT>(rp, nv, lo, shift, ROW_NB, tb, need, bm, h, lds_scan);
+    uint32_t need_eq;
+    const uint32_t T = exact_threshold<NT, DT>(rp, nv, lo, shift, ROW_NB, tb, need, need_eq, h, lds_scan);
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < nv; base += NT) {
+      const uint32_t p = base + threadIdx.x;
+      const uint32_t key = p < nv ? load_key<DT>(rp, p) : 0u;
+      const bool in = p < nv && bin_of(key, lo, shift, ROW_NB) == tb;
+      const bool gt = in && key > T;
+      const bool eq = in && key == T;
+      uint32_t tot2;
+      const uint32_t r = block_excl_scan<NT>(eq ? 1u : 0u, lds_scan, tot2);
+      if (gt || (eq && carry + r < need_eq)) atomicOr(&bm[p >> 5], 1u << (p & 31));
+      carry += tot2;
+    }
   }
   __syncthreads();
   emit_bitmap<NT>(bm, nwords, out, (uint32_t)k, lds_scan);

@@ -1,0 +1,157 @@
+"""Parity at the full workload sizes (MI355X), in the launch configuration the
+benchmark times, on outputs the oracle computes one sampled row at a time.
+
+Every index set is also checked for properties that hold at any size
+(ascending, unique, in range, exactly min(k, valid) entries, one buffer per
+group).  Inputs are generated in HBM by the device filler; the oracle
+regenerates only the rows it reads.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_top_amd as lct
+import oracle
+import synth
+import synth.device as sd
+from synth import configs as C
+from tests.gpu_util import announce, host
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _check_index_rows(idx, L, k, valid):
+    """Properties of an index row that hold at any size."""
+    n = min(k, valid)
+    assert np.all(idx[:n] >= 0) and np.all(idx[n:] == -1)
+    assert np.all(np.diff(idx[:n]) > 0), "ascending and unique"
+    assert idx[n - 1] < valid
+
+
+def _oracle_scores_row(cfg, g, b, qrow=0, chunk=1 << 16):
+    """Exact int64 indexer scores of one query row over all L positions, chunked."""
+    qi = C.rows(cfg, cfg.qi_spec(g), (np.array([b]), np.array([qrow])))[0].astype(np.int64)
+    out = np.empty(cfg.L, dtype=np.int64)
+    for t0 in range(0, cfg.L, chunk):
+        t = np.arange(t0, min(cfg.L, t0 + chunk))
+        ki = C.rows(cfg, cfg.ki_spec(g), (np.full_like(t, b), t)).astype(np.int64)
+        out[t0:t0 + t.size] = oracle.index_scores_row(qi, ki)
+    return out
+
+
+def _decode_full(cfg, sample_groups, sample_rows, sample_layers):
+    announce(cfg.name)
+    ng = cfg.n_groups
+    qi = [sd.make(cfg, cfg.qi_spec(g)) for g in range(ng)]
+    ki = [sd.make(cfg, cfg.ki_spec(g)) for g in range(ng)]
+    q = [sd.make(cfg, cfg.q_spec(l)) for l in range(cfg.n_layers)]
+    k = [sd.make(cfg, cfg.k_spec(l)) for l in range(cfg.n_layers)]
+    v = [sd.make(cfg, cfg.v_spec(l)) for l in range(cfg.n_layers)]
+    out = [torch.empty((cfg.B, cfg.Lq, cfg.Hq, cfg.D), dtype=torch.float32, device="cuda")
+           for _ in range(cfg.n_layers)]
+    idx_out = [torch.empty((cfg.B, cfg.Lq, cfg.topk), dtype=torch.int32, device="cuda") for _ in range(ng)]
+    run = lct.GroupRun(qi, ki, q, k, v, out, cfg.topk, cfg.group, cfg.scale, idx_out=idx_out)
+    run()
+    torch.cuda.synchronize()
+    seen = run.layer_index_addresses()
+    for l in range(cfg.n_layers):
+        assert seen[l] == idx_out[l // cfg.group].data_ptr(), "a layer read another group's buffer"
+    idx = [host(t) for t in idx_out]
+    for g in range(ng):
+        for b in range(cfg.B):
+            _check_index_rows(idx[g][b, 0], cfg.L, cfg.topk, cfg.L)
+    for g in sample_groups:
+        for b in sample_rows:
+            s = _oracle_scores_row(cfg, g, b)
+            want = oracle.select_topk(s, cfg.topk, cfg.L)
+            assert np.array_equal(idx[g][b, 0], want), (g, b)
+    for l in sample_layers:
+        g = l // cfg.group
+        ref = oracle.decode_layers(cfg, l, idx[g][sample_rows], batch=sample_rows)
+        got = host(out[l])[sample_rows]
+        err = np.abs(got - ref).max()
+        assert err < ATOL, (l, err)
+    del qi, ki, q, k, v, out, idx_out, run
+    _free()
+
+
+def test_decode_128k_b8_full_size():
+    _decode_full(C.DECODE_128K, sample_groups=[0, 6], sample_rows=[0, 7], sample_layers=[0, 3, 27])
+
+
+def test_decode_32k_b8_full_size():
+    _decode_full(C.DECODE_32K, sample_groups=[2], sample_rows=[3, 5], sample_layers=[9, 10])
+
+
+def test_decode_1m_b1_full_size():
+    _decode_full(C.DECODE_1M, sample_groups=[0, 5], sample_rows=[0], sample_layers=[1, 22])
+
+
+def test_gsa_128k_b16_full_size():
+    cfg = C.GSA_128K
+    announce(cfg.name)
+    BH = cfg.B * cfg.H
+
+    def mk(spec):
+        t = sd.make(cfg, spec)
+        return t.view((BH,) + tuple(t.shape[2:]))
+
+    qv, gk, gv, rk, rv = (mk(cfg.q_spec()), mk(cfg.gk_spec()), mk(cfg.gv_spec()),
+                          mk(cfg.rk_spec()), mk(cfg.rv_spec()))
+    out, cidx = lct.gsa_decode(qv, gk, gv, rk, rv, cfg.kc, cfg.tail_len, cfg.scale)
+    torch.cuda.synchronize()
+    got_idx, got = host(cidx), host(out)
+    for i in range(BH):
+        _check_index_rows(got_idx[i], cfg.Nc, cfg.kc, cfg.Nc)
+    pairs = [(0, 0), (3, 7), (9, 15), (15, 2)]
+    ref_idx, ref_out = oracle.driver.gsa_step(cfg, pairs)
+    for j, (b, h) in enumerate(pairs):
+        i = b * cfg.H + h
+        assert np.array_equal(got_idx[i], ref_idx[j]), (b, h)
+        assert np.abs(got[i] - ref_out[j]).max() < ATOL, (b, h)
+    del qv, gk, gv, rk, rv, out, cidx
+    _free()
+
+
+def test_causal_prefill_64k_full_size():
+    """One group (4 layers) of the 64K causal prefill; index sets checked on
+    every row for the structural properties and against the oracle on rows
+    below k (all of them) and a spread of longer rows."""
+    cfg = C.PREFILL_64K.with_(n_layers=4)
+    announce(cfg.name)
+    qi = [sd.make(cfg, cfg.qi_spec(0))]
+    ki = [sd.make(cfg, cfg.ki_spec(0))]
+    q = [sd.make(cfg, cfg.q_spec(l)) for l in range(4)]
+    k = [sd.make(cfg, cfg.k_spec(l)) for l in range(4)]
+    v = [sd.make(cfg, cfg.v_spec(l)) for l in range(4)]
+    out = [torch.empty((1, cfg.L, cfg.Hq, cfg.D), dtype=torch.float32, device="cuda") for _ in range(4)]
+    idx_out = [torch.empty((1, cfg.L, cfg.topk), dtype=torch.int32, device="cuda")]
+    run = lct.GroupRun(qi, ki, q, k, v, out, cfg.topk, cfg.group, cfg.scale, causal=True,
+                       idx_out=idx_out)
+    run()
+    torch.cuda.synchronize()
+    idx = host(idx_out[0])[0]
+    for r in range(0, cfg.L, 97):
+        _check_index_rows(idx[r], cfg.L, cfg.topk, r + 1)
+    below = np.arange(cfg.topk)  # rows whose set is every earlier position
+    for r in below[::37]:
+        assert np.array_equal(idx[r][: r + 1], np.arange(r + 1))
+    rows = [2047, 2048, 2049, 4095, 10000, 33333, 50001, 65535]
+    want = oracle.prefill_index_rows(cfg, 0, rows)
+    for j, r in enumerate(rows):
+        assert np.array_equal(idx[r], want[j]), r
+    sample = [0, 5, 2047, 2048, 33333, 65535]
+    ref = oracle.prefill_attention_rows(cfg, 2, sample, idx[sample])
+    assert np.abs(host(out[2])[0, sample] - ref).max() < ATOL
+    del qi, ki, q, k, v, out, idx_out, run
+    _free()
