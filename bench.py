@@ -66,6 +66,7 @@ def causal_pairs(L: int) -> int:
 # --------------------------------------------------------------- helpers ----
 
 def _timed_loop(fn, iters, stream):
+    """Average ms per call of ``fn``: events around back-to-back calls on ``stream``."""
     import torch
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
@@ -77,9 +78,55 @@ def _timed_loop(fn, iters, stream):
     return s.elapsed_time(e) / iters  # ms
 
 
+def _timed_graph(fn, iters, stream):
+    """Average ms per call of ``fn`` with ``iters`` calls captured in one HIP
+    graph (no host launch overhead); events on the capturing stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(iters):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    return _timed_loop(g.replay, 1, stream) / iters
+
+
 def _flush(buf):
     """Evict the 256 MiB Infinity Cache between small timed launches."""
     buf.add_(1)
+
+
+SCORER_SOURCES = ["long_context_top_amd/csrc/idx_score.hip", "long_context_top_amd/csrc/common.h",
+                  "long_context_top_amd/csrc/kernels.h"]
+PROFILE_128K = os.path.join(ROOT, "profiles", "decode_128k_b8_kernels.txt")
+
+
+def scorer_traffic():
+    """HBM bytes per launch of the indexer scorer from the committed counter
+    profile (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
+    scorer's sources changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(PROFILE_128K):
+        return None
+    h = hashlib.sha256()
+    for f in SCORER_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    vals, sha = {}, None
+    for line in open(PROFILE_128K):
+        parts = line.split()
+        if len(parts) == 4 and parts[0] == "traffic" and parts[1] == "k_idx_score_stream":
+            vals[parts[2]] = parts[3]
+        if len(parts) == 3 and parts[0] == "source_sha256" and parts[1] == "k_idx_score_stream":
+            sha = parts[2]
+    if sha != h.hexdigest():
+        return None
+    try:
+        return int(vals["fetch_bytes_per_launch"]) + int(vals["write_bytes_per_launch"])
+    except KeyError:
+        return None
 
 
 def cpu_baseline_decode(cfg, budget_s=20.0):
@@ -163,10 +210,10 @@ def bench_decode(cfg, steps, warmup, want_cpu):
     bytes_ = decode_step_bytes(cfg)
     scores = torch.empty((cfg.B, cfg.Lq, cfg.L), dtype=torch.int32, device=dev)
     n_k = max(10, steps)
-    ms_score = _timed_loop(lambda: lct.idx_score(qi[0], ki[0], out=scores), n_k, stream)
+    ms_score = _timed_graph(lambda: lct.idx_score(qi[0], ki[0], out=scores), n_k, stream)
     ws = lct.Workspace(dev)
-    ms_attn = _timed_loop(lambda: lct.sparse_attn_gather(q[0], k[0], v[0], idx_out[0], cfg.scale,
-                                                         out=out[0], ws=ws), n_k, stream)
+    ms_attn = _timed_graph(lambda: lct.sparse_attn_gather(q[0], k[0], v[0], idx_out[0], cfg.scale,
+                                                          out=out[0], ws=ws), n_k, stream)
     torch.cuda.synchronize()
     score_gbs = bytes_["indexer_per_call"] / (ms_score * 1e-3) / 1e9
     attn_gbs = bytes_["kv_per_layer"] / (ms_attn * 1e-3) / 1e9
@@ -186,9 +233,10 @@ def bench_decode(cfg, steps, warmup, want_cpu):
         "algorithmic_bytes_per_step": bytes_["total"],
         "roofline": {"bound": "hbm", "kernel": "k_idx_score_stream (indexer scores, one group)",
                      "achieved": score_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": score_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": score_gbs / HBM_PEAK_GBS, "traffic": scorer_traffic(),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "us_per_launch": ms_score * 1e3, "bytes_per_launch": bytes_["indexer_per_call"]},
-        "attention_kernel": {"kernel": "k_sparse_attn (one layer)", "achieved": attn_gbs,
+        "attention_kernel": {"kernel": "k_sparse_attn + k_split_merge (one layer)", "achieved": attn_gbs,
                              "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
                              "us_per_launch": ms_attn * 1e3, "bytes_per_launch": bytes_["kv_per_layer"]},
     }
@@ -229,7 +277,7 @@ def bench_gsa(cfg, steps, warmup):
     ms = _timed_loop(g.replay, steps, stream)
     b = gsa_step_bytes(cfg)
     gs = torch.empty((BH, cfg.Nc), dtype=torch.float32, device=dev)
-    ms_gs = _timed_loop(lambda: lct.gist_score(qv, gk, out=gs), max(10, steps), stream)
+    ms_gs = _timed_graph(lambda: lct.gist_score(qv, gk, out=gs), max(10, steps), stream)
     gbs = b["total"] / (ms * 1e-3) / 1e9
     return {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": BH // cfg.H * 1.0 / (ms * 1e-3),
             "hbm_gbs_step": gbs, "hbm_frac_step": gbs / HBM_PEAK_GBS,
@@ -255,11 +303,63 @@ def bench_prefill_indexer(cfg, steps, warmup):
     f = lambda: lct.idx_score(qb, ki, q_pos0=r0, out=scores)
     for _ in range(warmup):
         f()
-    ms = _timed_loop(f, steps, torch.cuda.current_stream())
+    ms = _timed_graph(f, steps, torch.cuda.current_stream())
     pairs = sum(r0 + r + 1 for r in range(rows))
     tops = 2 * cfg.HD * pairs / (ms * 1e-3) / 1e12
     return {"workload": cfg.name + " indexer block (last 2048 rows)", "ms": ms, "int8_tops": tops,
             "frac": tops / INT8_PEAK_TOPS}
+
+
+def copy_calibration(steps):
+    """A plain device copy of known size (1 GiB read + 1 GiB written per launch),
+    used to scale the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"mode": "copy_calibration", "bytes_read_per_launch": src.numel() * 4,
+            "bytes_written_per_launch": dst.numel() * 4, "launches": steps}
+
+
+def summarize_profile(stats_csv, pmc_csvs, calib_csvs):
+    """Text summary of rocprofv3 output: per-kernel average duration, and the
+    average counter value per dispatch for each kernel, scaled by the copy
+    calibration (counter units per byte of a known plain copy)."""
+    import csv
+    lines = []
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines.append(f"{'kernel':30s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share':>7s}")
+    for r in rows:
+        lines.append(f"{r['Name'][:30]:30s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:9.2f} "
+                     f"{float(r['MinNs'])/1e3:9.2f} {float(r['MaxNs'])/1e3:9.2f} {float(r['Percentage']):6.2f}%")
+
+    def per_kernel(path):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            acc.setdefault(key, {})
+            d = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            acc[key][d] = acc[key].get(d, 0.0) + float(r["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+
+    scale = {}
+    for c in calib_csvs:
+        for (kname, cname), val in per_kernel(c).items():
+            if "elementwise" in kname or "copy" in kname.lower():
+                want = 1 << 30  # bytes read (FETCH) or written (WRITE) per copy launch
+                scale[cname] = want / (val * 1024.0)
+    if pmc_csvs:
+        lines.append("")
+        lines.append("counters per dispatch (KiB as read) -> bytes after copy calibration")
+        for c in pmc_csvs:
+            for (kname, cname), val in sorted(per_kernel(c).items()):
+                if kname.startswith("k_fill") or "elementwise" in kname:
+                    continue
+                sc = scale.get(cname, 1.0)
+                lines.append(f"{kname[:30]:30s} {cname:12s} {val:14.1f} KiB  x{sc:.4f} = {val*1024*sc/2**20:10.2f} MiB")
+    return "\n".join(lines)
 
 
 def main():
@@ -270,7 +370,22 @@ def main():
     ap.add_argument("--config", default="decode_128k",
                     choices=["decode_128k", "decode_32k", "decode_1m", "gsa_128k", "prefill_64k", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
+                    help="copy: a plain 1 GiB device copy used to calibrate HBM byte counters")
+    ap.add_argument("--summarize", nargs="+", metavar="CSV",
+                    help="print a summary of rocprofv3 CSVs: STATS [PMC ...] [--calib CSV ...]")
+    args, rest = ap.parse_known_args()
+    if args.summarize:
+        files = args.summarize + rest
+        calib = files[files.index("--calib") + 1:] if "--calib" in files else []
+        main_files = files[:files.index("--calib")] if "--calib" in files else files
+        print(summarize_profile(main_files[0], main_files[1:], calib))
+        return
+    if rest:
+        ap.error(f"unknown arguments {rest}")
+    if args.mode == "copy":
+        print(json.dumps(copy_calibration(args.steps)))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(every workload runs on a single MI355X).", file=sys.stderr)
