@@ -137,7 +137,7 @@ int lct_idx_score_i8(const int8_t* q, const int8_t* k, int32_t* scores, int B, i
   if (rc) return rc;
   if (!mfma)
     LCT_HIP(launch_idx_score_stream(q, k, scores, B, Lq, L, HD, q_pos0, nullptr, nullptr, nullptr,
-                                    as_stream(stream)),
+                                    nullptr, as_stream(stream)),
             "idx_score (stream)");
   else
     LCT_HIP(launch_idx_score_mfma(q, k, scores, B, Lq, L, HD, q_pos0, as_stream(stream)),
@@ -458,14 +458,15 @@ int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stre
         char* tw = w + lay.topk;
         LCT_HIP(launch_idx_score_stream(d->qi[g], d->ki[g], scores, d->B, d->Lq, d->L, d->HD, -1,
                                         reinterpret_cast<uint32_t*>(tw + tl.mm),
-                                        reinterpret_cast<TopkRowState*>(tw + tl.state), d->valid_len, st),
+                                        reinterpret_cast<TopkRowState*>(tw + tl.state),
+                                        reinterpret_cast<uint32_t*>(tw + tl.hist), d->valid_len, st),
                 "group: idx_score");
         LCT_HIP(launch_topk_select_multi(scores, LCT_I32, ib, rows, d->L, d->L, d->topk,
                                          d->valid_len, d->Lq, tw, tl, st),
                 "group: topk select");
       } else {
         LCT_HIP(launch_idx_score_stream(d->qi[g], d->ki[g], scores, d->B, d->Lq, d->L, d->HD, -1,
-                                        nullptr, nullptr, nullptr, st),
+                                        nullptr, nullptr, nullptr, nullptr, st),
                 "group: idx_score");
         LCT_HIP(launch_topk_rows(scores, LCT_I32, ib, rows, d->L, d->L, d->topk, d->valid_len, d->Lq, -1, st),
                 "group: topk rows");

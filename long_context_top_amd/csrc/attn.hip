@@ -285,35 +285,34 @@ __global__ __launch_bounds__(NW * 64) void k_sparse_attn(
 __global__ __launch_bounds__(256) void k_split_merge(const float* __restrict__ part,
                                                      float* __restrict__ out, int splits, int hs,
                                                      int G, int D) {
+  __shared__ float wts[MERGE_MAX_SPLITS];
+  __shared__ float s_inv;
   const int64_t unit = blockIdx.x;
   const int h = blockIdx.y;
   const int d = threadIdx.x < D ? threadIdx.x : D - 1;
   const size_t stride = (size_t)hs * (D + 2);
   const float* base = part + ((size_t)unit * splits * hs + h) * (D + 2);
-  // every load is issued up front and unconditionally (split indices past
-  // `splits` re-read the last split and get weight 0): the feature of each
-  // split for this thread, and each split's (m, l), which are uniform
-  float o[MERGE_MAX_SPLITS], mm[MERGE_MAX_SPLITS], ll[MERGE_MAX_SPLITS];
+  // all loads are issued together: this thread's feature of every split
+  // (unconditional; split indices past `splits` re-read the last split and get
+  // weight 0) and, in the first wave, one split's (m, l) per lane
+  float o[MERGE_MAX_SPLITS];
 #pragma unroll
-  for (int s = 0; s < MERGE_MAX_SPLITS; ++s) {
-    const size_t so = (size_t)(s < splits ? s : splits - 1) * stride;
-    o[s] = base[so + d];
-    mm[s] = base[so + D];
-    ll[s] = base[so + D + 1];
+  for (int s = 0; s < MERGE_MAX_SPLITS; ++s) o[s] = base[(size_t)(s < splits ? s : splits - 1) * stride + d];
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x < splits ? threadIdx.x : splits - 1;
+    const float m = base[(size_t)s * stride + D];
+    const float l = base[(size_t)s * stride + D + 1];
+    const float M = wave_max(m);
+    const float w = (M == -INFINITY || (int)threadIdx.x >= splits) ? 0.f : exp2f(m - M);
+    const float L = wave_sum(w * l);
+    if (threadIdx.x < MERGE_MAX_SPLITS) wts[threadIdx.x] = w;
+    if (threadIdx.x == 0) s_inv = L > 0.f ? 1.f / L : 0.f;
   }
-  float M = -INFINITY;
+  __syncthreads();
+  float acc = 0.f;
 #pragma unroll
-  for (int s = 0; s < MERGE_MAX_SPLITS; ++s) M = fmaxf(M, mm[s]);
-  float L = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int s = 0; s < MERGE_MAX_SPLITS; ++s) {
-      const float w = s < splits ? exp2f(mm[s] - M) : 0.f;
-      L += w * ll[s];
-      acc += w * o[s];
-    }
-  }
-  if (threadIdx.x < D) out[((size_t)unit * G + h) * D + d] = L > 0.f ? acc / L : 0.f;
+  for (int s = 0; s < MERGE_MAX_SPLITS; ++s) acc += wts[s] * o[s];
+  if (threadIdx.x < D) out[((size_t)unit * G + h) * D + d] = acc * s_inv;
 }
 
 hipError_t launch_split_merge(const float* part, float* out, int64_t units, int splits, int hs,

@@ -40,7 +40,8 @@ template <int P, int QC>
 __global__ __launch_bounds__(256) void k_idx_score_stream(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, int32_t* __restrict__ s, int Lq,
     int64_t L, int64_t q_pos0, int n_qchunks, uint32_t* __restrict__ mm, int t1,
-    TopkRowState* __restrict__ st, const int32_t* __restrict__ valid_len) {
+    TopkRowState* __restrict__ st, uint32_t* __restrict__ hist,
+    const int32_t* __restrict__ valid_len) {
   constexpr int HD = P * 16;
   constexpr int G = 64 / P;  // consecutive rows read per step
   __shared__ uint32_t lds[2 * QC * 4];
@@ -141,40 +142,45 @@ __global__ __launch_bounds__(256) void k_idx_score_stream(
       mm[(row * t1 + tile) * 2 + 1] = c;
       if (tile == 0) st[row].cand_fill = 0;
     }
+    if (tile == 0) {
+      // clear the rows' select histograms (accumulated by the next kernel)
+      for (int i = 0; i < QC; ++i)
+        if (r0 + i < Lq) hist[((size_t)b * Lq + r0 + i) * TOPK_NB + threadIdx.x % TOPK_NB] = 0u;
+    }
   }
 }
 
 template <int P>
 static hipError_t stream_dispatch_qc(int qc, dim3 grid, const int8_t* q, const int8_t* k,
                                      int32_t* s, int Lq, int64_t L, int64_t q_pos0, int nqc,
-                                     uint32_t* mm, int t1, TopkRowState* st, const int32_t* vl,
-                                     hipStream_t stream) {
+                                     uint32_t* mm, int t1, TopkRowState* st, uint32_t* hist,
+                                     const int32_t* vl, hipStream_t stream) {
   switch (qc) {
-    case 1: k_idx_score_stream<P, 1><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, vl); break;
-    case 2: k_idx_score_stream<P, 2><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, vl); break;
-    case 4: k_idx_score_stream<P, 4><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, vl); break;
-    case 8: k_idx_score_stream<P, 8><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, vl); break;
-    default: k_idx_score_stream<P, 16><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, vl); break;
+    case 1: k_idx_score_stream<P, 1><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
+    case 2: k_idx_score_stream<P, 2><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
+    case 4: k_idx_score_stream<P, 4><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
+    case 8: k_idx_score_stream<P, 8><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
+    default: k_idx_score_stream<P, 16><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_idx_score_stream(const int8_t* q, const int8_t* k, int32_t* s, int B, int Lq,
                                    int64_t L, int HD, int64_t q_pos0, uint32_t* mm,
-                                   TopkRowState* state, const int32_t* valid_len,
-                                   hipStream_t stream) {
+                                   TopkRowState* state, uint32_t* hist,
+                                   const int32_t* valid_len, hipStream_t stream) {
   int qc = Lq <= 1 ? 1 : Lq <= 2 ? 2 : Lq <= 4 ? 4 : Lq <= 8 ? 8 : 16;
   if (HD >= 512 && qc > 4) qc = 4;  // register budget
   const int nqc = (Lq + qc - 1) / qc;
   const int t1 = idx_score_stream_tiles(L);
   dim3 grid(t1, B * nqc);
   switch (HD) {
-    case 16: return stream_dispatch_qc<1>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, valid_len, stream);
-    case 32: return stream_dispatch_qc<2>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, valid_len, stream);
-    case 64: return stream_dispatch_qc<4>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, valid_len, stream);
-    case 128: return stream_dispatch_qc<8>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, valid_len, stream);
-    case 256: return stream_dispatch_qc<16>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, valid_len, stream);
-    case 512: return stream_dispatch_qc<32>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, valid_len, stream);
+    case 16: return stream_dispatch_qc<1>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
+    case 32: return stream_dispatch_qc<2>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
+    case 64: return stream_dispatch_qc<4>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
+    case 128: return stream_dispatch_qc<8>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
+    case 256: return stream_dispatch_qc<16>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
+    case 512: return stream_dispatch_qc<32>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -10,10 +10,10 @@ namespace lct {
 // ---------------------------------------------------------------- top-k ----
 constexpr int TOPK_NB_LOG2 = 8;                 // bins of the multi-workgroup histogram
 constexpr int TOPK_NB = 1 << TOPK_NB_LOG2;
-constexpr int TOPK_CAP = 4096;                  // candidates sorted in LDS by the last block
+constexpr int TOPK_CAP = 4096;                  // threshold-bin candidates resolved in LDS
 constexpr int TOPK_K2_TILE = 256 * 16;          // keys per histogram workgroup
 constexpr int TOPK_K3_THREADS = 512;
-constexpr int TOPK_K3_TILE = TOPK_K3_THREADS * 16;  // positions per emit workgroup
+constexpr int TOPK_K3_TILE = TOPK_K3_THREADS * 8;   // positions per emit workgroup
 constexpr int TOPK_MM_TILE = 256 * 16;          // keys per min/max workgroup
 constexpr int TOPK_K4_TILE = 1024 * 32;         // positions per finalize workgroup
 constexpr int TOPK_MULTI_MAX_ROWS = 64;
@@ -63,8 +63,8 @@ hipError_t launch_topk_rows(const void* scores, int dtype, int32_t* idx, int row
 constexpr int SCORE_TILE = 512;  // positions per workgroup (4 waves x 2 rounds x 64)
 hipError_t launch_idx_score_stream(const int8_t* q, const int8_t* k, int32_t* s, int B, int Lq,
                                    int64_t L, int HD, int64_t q_pos0, uint32_t* mm,
-                                   TopkRowState* state, const int32_t* valid_len,
-                                   hipStream_t st);
+                                   TopkRowState* state, uint32_t* hist,
+                                   const int32_t* valid_len, hipStream_t st);
 int idx_score_stream_tiles(int64_t L);
 // Causal/prefill scorer on int8 MFMA: rows [r0, r0+R) of q against all L keys.
 hipError_t launch_idx_score_mfma(const int8_t* q, const int8_t* k, int32_t* s, int B, int Lq,

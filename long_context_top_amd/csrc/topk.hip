@@ -17,12 +17,13 @@
 //      block-wide prefix sum of popcounts.
 // The bitmap yields ascending order without any sort of the k outputs.
 //
-// Multi-workgroup variant (few long rows): K1 (a producer: the indexer
-// scorer or k_topk_minmax) writes per-tile (min,max) and clears the row
-// state; K2 builds per-tile 256-bin histograms and its last workgroup per
-// row finds tb; K3 writes the bitmap and candidates and its last workgroup
-// per row finishes the row.  Cross-workgroup hand-off uses device-scope
-// fences and an atomic ticket; no workgroup ever waits on another.
+// Multi-workgroup variant (few long rows), four kernels whose boundaries are
+// the only hand-offs between workgroups: K1 (a producer: the indexer scorer
+// or k_topk_minmax) writes per-tile (min,max) and clears the row's candidate
+// counter and 256-bin histogram; K2 adds each tile's histogram into the row
+// histogram with atomics; K3 finds tb from it, writes the bitmap words, the
+// candidates and per-tile chosen counts; K4 resolves the candidates and
+// expands the bitmap into the ascending list.
 
 #include "common.h"
 #include "kernels.h"
@@ -107,9 +108,7 @@ TopkMultiLayout topk_multi_layout(int rows, int64_t n, int t1) {
   TopkMultiLayout l;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   l.t1 = t1;
-  int64_t per = 16;  // keys per thread of a histogram workgroup; at most 64 tiles per row
-  while ((n + 256 * per - 1) / (256 * per) > 64) per *= 2;
-  l.k2_tile = 256 * per;
+  l.k2_tile = TOPK_K2_TILE;
   l.t2 = (int)((n + l.k2_tile - 1) / l.k2_tile);
   l.t3 = (int)((n + TOPK_K3_TILE - 1) / TOPK_K3_TILE);
   l.t4 = (int)((n + TOPK_K4_TILE - 1) / TOPK_K4_TILE);
@@ -120,7 +119,7 @@ TopkMultiLayout topk_multi_layout(int rows, int64_t n, int t1) {
   l.mm = off;
   off += up((size_t)rows * t1 * 2 * sizeof(uint32_t));
   l.hist = off;
-  off += up((size_t)rows * l.t2 * TOPK_NB * sizeof(uint32_t));
+  off += up((size_t)rows * TOPK_NB * sizeof(uint32_t));
   l.cands = off;
   off += up((size_t)rows * TOPK_CAP * sizeof(uint64_t));
   l.bitmap = off;
@@ -145,7 +144,8 @@ template <int DT>
 __global__ __launch_bounds__(256) void k_topk_minmax(const void* __restrict__ scores, int64_t n,
                                                      int64_t ld, const int32_t* valid_len,
                                                      int vl_div, uint32_t* __restrict__ mm, int t1,
-                                                     TopkRowState* __restrict__ st) {
+                                                     TopkRowState* __restrict__ st,
+                                                     uint32_t* __restrict__ hist) {
   __shared__ uint32_t lds[16];
   const int row = blockIdx.y, tile = blockIdx.x;
   const uint32_t nv = row_nvalid(valid_len, row, n, vl_div);
@@ -166,6 +166,7 @@ __global__ __launch_bounds__(256) void k_topk_minmax(const void* __restrict__ sc
     mm[((size_t)row * t1 + tile) * 2 + 1] = mx;
     if (tile == 0) st[row].cand_fill = 0;
   }
+  if (tile == 0) hist[(size_t)row * TOPK_NB + threadIdx.x % TOPK_NB] = 0u;
 }
 
 // Window of a row from the producer's (min,max) partials.
@@ -187,7 +188,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void k_topk_hist(const void* __restrict__ scores, int64_t n,
                                                    int64_t ld, int k, const int32_t* valid_len,
                                                    int vl_div, const uint32_t* __restrict__ mm,
-                                                   int t1, uint32_t* __restrict__ hist, int t2,
+                                                   int t1, uint32_t* __restrict__ hist,
                                                    int64_t tile_len) {
   __shared__ uint32_t h[TOPK_NB];
   __shared__ uint32_t lds[16];
@@ -217,20 +218,22 @@ __global__ __launch_bounds__(256) void k_topk_hist(const void* __restrict__ scor
       atomicAdd(&h[bin_of(load_key<DT>(rp, p), lo, shift, TOPK_NB)], 1u);
   }
   __syncthreads();
-  uint32_t* hp = hist + ((size_t)row * t2 + tile) * TOPK_NB;
-  for (int i = threadIdx.x; i < TOPK_NB; i += 256) hp[i] = h[i];
+  // accumulate into the row histogram (cleared by the producer kernel)
+  uint32_t* hp = hist + (size_t)row * TOPK_NB;
+  for (int i = threadIdx.x; i < TOPK_NB; i += 256)
+    if (h[i]) atomicAdd(&hp[i], h[i]);
 }
 
 struct RowSel {
   uint32_t lo, shift, tb, need, ccount;
 };
 
-// Threshold bin of a row from the per-tile histograms (every caller derives
-// the same values).  NT >= TOPK_NB.
+// Threshold bin of a row from its histogram (every caller derives the same
+// values).  NT >= TOPK_NB.
 template <int NT>
 LCT_DEV RowSel row_select_params(const uint32_t* mm_row, int t1, const uint32_t* hist_row,
-                                 int t2, uint32_t nv, uint32_t kk, uint32_t* lds_scan,
-                                 uint32_t* lds_small, uint32_t* lds_tot /* NT words */) {
+                                 uint32_t nv, uint32_t kk, uint32_t* lds_scan,
+                                 uint32_t* lds_small) {
   static_assert(NT >= TOPK_NB, "one thread per bin");
   RowSel r;
   row_window<NT>(mm_row, t1, nv, r.lo, r.shift, lds_small);
@@ -241,39 +244,12 @@ LCT_DEV RowSel row_select_params(const uint32_t* mm_row, int t1, const uint32_t*
     return r;
   }
   // thread t < NB owns bin NB-1-t; an exclusive scan in thread order counts
-  // the keys in higher bins.  The per-tile partials are summed by all NT
-  // threads (NT/NB tile slices each, loads issued back to back).
-  constexpr int SL = NT / TOPK_NB;
-  const int b = TOPK_NB - 1 - (int)(threadIdx.x % TOPK_NB);
-  const int slice = threadIdx.x / TOPK_NB;
-  uint32_t part = 0;
-  {
-    const int t_begin = slice * ((t2 + SL - 1) / SL);
-    const int t_end = min(t2, t_begin + (t2 + SL - 1) / SL);
-    uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-    int t = t_begin;
-    for (; t + 4 <= t_end; t += 4) {
-      a0 += hist_row[(size_t)(t + 0) * TOPK_NB + b];
-      a1 += hist_row[(size_t)(t + 1) * TOPK_NB + b];
-      a2 += hist_row[(size_t)(t + 2) * TOPK_NB + b];
-      a3 += hist_row[(size_t)(t + 3) * TOPK_NB + b];
-    }
-    for (; t < t_end; ++t) a0 += hist_row[(size_t)t * TOPK_NB + b];
-    part = a0 + a1 + a2 + a3;
-  }
-  if (SL > 1) {
-    lds_tot[threadIdx.x] = part;
-    __syncthreads();
-  }
-  uint32_t c = 0;
-  if ((int)threadIdx.x < TOPK_NB) {
-    c = part;
-    for (int j = 1; j < SL; ++j) c += lds_tot[j * TOPK_NB + threadIdx.x];
-  }
+  // the keys in higher bins
+  const uint32_t c = (int)threadIdx.x < TOPK_NB ? hist_row[TOPK_NB - 1 - threadIdx.x] : 0u;
   uint32_t tot;
   const uint32_t higher = block_excl_scan<NT>(c, lds_scan, tot);
   if ((int)threadIdx.x < TOPK_NB && higher < kk && higher + c >= kk) {
-    lds_small[0] = (uint32_t)b;
+    lds_small[0] = (uint32_t)(TOPK_NB - 1 - threadIdx.x);
     lds_small[1] = kk - higher;
     lds_small[2] = c;
   }
@@ -291,13 +267,13 @@ template <int DT>
 __global__ __launch_bounds__(TOPK_K3_THREADS) void k_topk_emit(
     const void* __restrict__ scores, int64_t n, int64_t ld, int k, const int32_t* valid_len,
     int vl_div, const uint32_t* __restrict__ mm, int t1, const uint32_t* __restrict__ hist,
-    int t2, TopkRowState* __restrict__ st, uint64_t* __restrict__ cands,
+    TopkRowState* __restrict__ st, uint64_t* __restrict__ cands,
     uint32_t* __restrict__ bitmap, int64_t nwords, uint32_t* __restrict__ tilecnt, int t3) {
   constexpr int NT = TOPK_K3_THREADS;
   __shared__ uint32_t lds_scan[NT / 64 + 2];
   __shared__ uint32_t lds_small[2 * (NT / 64) + 4];
-  __shared__ uint32_t lds_tot[NT];
   __shared__ uint32_t wave_cnt[NT / 64];
+  __shared__ uint32_t wave_cand[NT / 64 + 2];
   const int row = blockIdx.y, tile = blockIdx.x;
   const uint32_t nv = row_nvalid(valid_len, row, n, vl_div);
   const uint32_t kk = (uint32_t)k < nv ? (uint32_t)k : nv;
@@ -313,8 +289,8 @@ __global__ __launch_bounds__(TOPK_K3_THREADS) void k_topk_emit(
     kbuf[c] = load_key<DT>(rp, p < nv ? p : (nv > 0 ? nv - 1 : 0));  // clamped, in bounds
   }
   const RowSel s = row_select_params<NT>(mm + (size_t)row * t1 * 2, t1,
-                                         hist + (size_t)row * t2 * TOPK_NB, t2, nv, kk, lds_scan,
-                                         lds_small, lds_tot);
+                                         hist + (size_t)row * TOPK_NB, nv, kk, lds_scan,
+                                         lds_small);
   if (tile == 0 && threadIdx.x == 0) {
     TopkRowState w = st[row];
     w.lo = s.lo;
@@ -328,37 +304,54 @@ __global__ __launch_bounds__(TOPK_K3_THREADS) void k_topk_emit(
   }
   uint32_t* bm = bitmap + (size_t)row * nwords;
   uint64_t* cd = cands + (size_t)row * TOPK_CAP;
-  uint32_t nabove = 0;
+  // pass 1: bitmap words and this wave's counts (chosen keys, candidates)
+  uint32_t nabove = 0, ncand = 0;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t cb = tbase + (int64_t)(c * (NT / 64) + wid) * 64;
     if (cb >= n) break;
     const int64_t p = cb + lane;
     const bool valid = p < nv;
-    const uint32_t key = kbuf[c];
-    const uint32_t bin = bin_of(key, s.lo, s.shift, TOPK_NB);
-    const bool above = valid && (s.tb == TOPK_ALL || bin > s.tb);
-    const bool cand = valid && s.tb != TOPK_ALL && bin == s.tb;
-    const uint64_t am = __ballot(above);
+    const uint32_t bin = bin_of(kbuf[c], s.lo, s.shift, TOPK_NB);
+    const uint64_t am = __ballot(valid && (s.tb == TOPK_ALL || bin > s.tb));
     if (lane == 0) *reinterpret_cast<uint64_t*>(bm + (cb >> 5)) = am;
     nabove += (uint32_t)__popcll(am);
-    const uint64_t cm = __ballot(cand);
-    if (cm && s.ccount <= TOPK_CAP) {
-      uint32_t b0 = 0;
-      if (lane == 0) b0 = atomicAdd(&st[row].cand_fill, (uint32_t)__popcll(cm));
-      b0 = __shfl(b0, 0, 64);
-      if (cand) {
-        const uint32_t slot = b0 + lane_rank(cm);
-        if (slot < TOPK_CAP) cd[slot] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)p);
-      }
-    }
+    ncand += (uint32_t)__popcll(__ballot(valid && s.tb != TOPK_ALL && bin == s.tb));
   }
-  if (lane == 0) wave_cnt[wid] = nabove;
+  if (lane == 0) {
+    wave_cnt[wid] = nabove;
+    wave_cand[wid] = ncand;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t t = 0;
-    for (int w = 0; w < NT / 64; ++w) t += wave_cnt[w];
+    uint32_t t = 0, cs = 0;
+    for (int w = 0; w < NT / 64; ++w) {
+      t += wave_cnt[w];
+      const uint32_t x = wave_cand[w];
+      wave_cand[w] = cs;
+      cs += x;
+    }
     tilecnt[(size_t)row * t3 + tile] = t;
+    // one slot reservation per workgroup
+    wave_cand[NT / 64] = (cs && s.ccount <= TOPK_CAP) ? atomicAdd(&st[row].cand_fill, cs) : 0u;
+    wave_cand[NT / 64 + 1] = cs;
+  }
+  __syncthreads();
+  if (wave_cand[NT / 64 + 1] == 0 || s.ccount > TOPK_CAP) return;  // uniform over the block
+  // pass 2: candidates (key, ~position) into the reserved slots
+  uint32_t slot = wave_cand[NT / 64] + wave_cand[wid];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t cb = tbase + (int64_t)(c * (NT / 64) + wid) * 64;
+    if (cb >= n) break;
+    const int64_t p = cb + lane;
+    const bool cand = p < nv && bin_of(kbuf[c], s.lo, s.shift, TOPK_NB) == s.tb;
+    const uint64_t cm = __ballot(cand);
+    if (cand) {
+      const uint32_t at = slot + lane_rank(cm);
+      if (at < TOPK_CAP) cd[at] = ((uint64_t)kbuf[c] << 32) | (uint32_t)(~(uint32_t)p);
+    }
+    slot += (uint32_t)__popcll(cm);
   }
 }
 
@@ -531,10 +524,11 @@ hipError_t launch_topk_minmax(const void* scores, int dtype, int rows, int64_t n
   dim3 grid(lay.t1, rows);
   auto st = reinterpret_cast<TopkRowState*>(ws + lay.state);
   auto mm = reinterpret_cast<uint32_t*>(ws + lay.mm);
+  auto hist = reinterpret_cast<uint32_t*>(ws + lay.hist);
   if (dtype == 0)
-    k_topk_minmax<0><<<grid, 256, 0, s>>>(scores, n, ld, valid_len, vl_div, mm, lay.t1, st);
+    k_topk_minmax<0><<<grid, 256, 0, s>>>(scores, n, ld, valid_len, vl_div, mm, lay.t1, st, hist);
   else
-    k_topk_minmax<1><<<grid, 256, 0, s>>>(scores, n, ld, valid_len, vl_div, mm, lay.t1, st);
+    k_topk_minmax<1><<<grid, 256, 0, s>>>(scores, n, ld, valid_len, vl_div, mm, lay.t1, st, hist);
   return hipGetLastError();
 }
 
@@ -550,12 +544,12 @@ hipError_t launch_topk_select_multi(const void* scores, int dtype, int32_t* idx,
   auto tc = reinterpret_cast<uint32_t*>(ws + lay.tilecnt);
   const dim3 g2(lay.t2, rows), g3(lay.t3, rows), g4(lay.t4, rows);
   if (dtype == 0) {
-    k_topk_hist<0><<<g2, 256, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, lay.k2_tile);
-    k_topk_emit<0><<<g3, TOPK_K3_THREADS, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, st, cands, bm, lay.nwords, tc, lay.t3);
+    k_topk_hist<0><<<g2, 256, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.k2_tile);
+    k_topk_emit<0><<<g3, TOPK_K3_THREADS, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, st, cands, bm, lay.nwords, tc, lay.t3);
     k_topk_finalize<0><<<g4, FIN_NT, 0, s>>>(scores, ld, k, idx, st, cands, bm, lay.nwords, tc, lay.t3);
   } else {
-    k_topk_hist<1><<<g2, 256, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, lay.k2_tile);
-    k_topk_emit<1><<<g3, TOPK_K3_THREADS, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.t2, st, cands, bm, lay.nwords, tc, lay.t3);
+    k_topk_hist<1><<<g2, 256, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, lay.k2_tile);
+    k_topk_emit<1><<<g3, TOPK_K3_THREADS, 0, s>>>(scores, n, ld, k, valid_len, vl_div, mm, lay.t1, hist, st, cands, bm, lay.nwords, tc, lay.t3);
     k_topk_finalize<1><<<g4, FIN_NT, 0, s>>>(scores, ld, k, idx, st, cands, bm, lay.nwords, tc, lay.t3);
   }
   return hipGetLastError();
