@@ -375,7 +375,7 @@ GroupLayout group_layout(const lct_group_desc* d) {
   off += up256((size_t)rows * d->topk * sizeof(int32_t));
   l.topk = off;
   if (l.multi) {
-    const int t1 = idx_score_stream_tiles(d->L);
+    const int t1 = score_plan(d->B, d->Lq, d->L, d->HD).tiles;
     off += up256(topk_multi_layout((int)rows, d->L, t1).total);
   }
   l.attn = off;
@@ -453,7 +453,7 @@ int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stre
     int32_t* ib = (d->idx_out && d->idx_out[g]) ? d->idx_out[g] : reinterpret_cast<int32_t*>(w + lay.idx);
     if (!d->causal) {
       if (lay.multi) {
-        const int t1 = idx_score_stream_tiles(d->L);
+        const int t1 = score_plan(d->B, d->Lq, d->L, d->HD).tiles;
         const TopkMultiLayout tl = topk_multi_layout(rows, d->L, t1);
         char* tw = w + lay.topk;
         LCT_HIP(launch_idx_score_stream(d->qi[g], d->ki[g], scores, d->B, d->Lq, d->L, d->HD, -1,

@@ -17,6 +17,11 @@ typedef uint32_t uintx4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 
+// Index of the calling wave in its workgroup, as a scalar: the compiler then
+// knows it is uniform across the wave (loop bounds and branches derived from
+// it stay scalar instead of becoming per-lane masked loops).
+LCT_DEV int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // Raw buffer resource over `bytes` bytes (bytes < 2^31).  Loads through it
 // take a 32-bit per-lane offset and a wave-uniform offset; reads at or past
 // `bytes` return zeros (hardware range check), so no clamping is needed.
@@ -86,7 +91,7 @@ LCT_DEV uint32_t wave_incl_scan(uint32_t x) {
 template <int NT>
 LCT_DEV uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t& total) {
   constexpr int NW = NT / WAVE;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   uint32_t x = wave_incl_scan(v);
   if (lane == WAVE - 1) lds[wid] = x;
   __syncthreads();
@@ -107,7 +112,7 @@ LCT_DEV uint32_t block_excl_scan(uint32_t v, uint32_t* lds, uint32_t& total) {
 template <int NT>
 LCT_DEV void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* lds /* 2*NT/64 */) {
   constexpr int NW = NT / WAVE;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   mn = wave_min(mn);
   mx = wave_max(mx);
   if (lane == 0) {

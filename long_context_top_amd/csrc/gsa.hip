@@ -23,6 +23,7 @@ namespace lct {
 
 constexpr int GS_TILE = 1024;   // gists per workgroup
 constexpr int GSA_D = 128;
+constexpr int GSA_MAX_SPLITS = 32;  // slices of one (b, head) row merged by k_split_merge
 constexpr float GSA_LOG2E = 1.4426950408889634f;
 
 template <int P>
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void k_gist_score(const uint16_t* __restrict__
                                                    const uint16_t* __restrict__ gk,
                                                    float* __restrict__ s, int64_t Nc) {
   constexpr int D = P * 8, G = 64 / P;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int64_t bh = blockIdx.y;
   const int g = lane / P, j = lane % P;
   float qv[8];
@@ -99,7 +100,7 @@ GsaPlan gsa_plan(int BH, int kc, int tail_len) {
   if (max_splits < 1) max_splits = 1;
   int splits = (512 + BH - 1) / BH;
   if (splits > max_splits) splits = max_splits;
-  if (splits > MERGE_MAX_SPLITS) splits = MERGE_MAX_SPLITS;
+  if (splits > GSA_MAX_SPLITS) splits = GSA_MAX_SPLITS;
   if (splits < 1) splits = 1;
   p.splits = splits;
   p.part_bytes = splits > 1 ? (size_t)BH * splits * (GSA_D + 2) * sizeof(float) : 0;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void k_gsa_attn(
   constexpr int D = GSA_D;
   __shared__ float red_o[4][D];
   __shared__ float red_m[4], red_l[4];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int g = lane >> 4, j = lane & 15;
   const int64_t bh = blockIdx.y;
   const int split = blockIdx.x;
@@ -252,7 +253,7 @@ hipError_t launch_gsa_attn(const uint16_t* q, const uint16_t* rk, const uint16_t
                                    scale * GSA_LOG2E, plan.splits, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  return launch_split_merge(partials, out, BH, plan.splits, 1, 1, GSA_D, st);
+  return launch_split_merge(partials, out, BH, plan.splits, 1, 1, GSA_D, GSA_D + 2, st);
 }
 
 }  // namespace lct

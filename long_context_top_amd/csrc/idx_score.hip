@@ -11,8 +11,10 @@
 // with v_dot4_i32_i8 against the query bytes the lane holds, and keeps one
 // partial per step.  A butterfly reduce-scatter over the P lanes (P-1
 // shuffles) then leaves every lane with the full score of one position, so
-// each wave ends a round with 64 scores to store.  The same pass records the
-// per-tile (min, max) of the keys a following top-k select needs.
+// each wave ends a round of 64 positions with 64 scores to store.
+// One workgroup per tile of SCORE_TILE positions of one row (4 waves, each
+// taking every 4th round of the tile).  The same pass records the per-tile
+// (min, max) of the keys a following top-k select needs.
 //
 // Prefill (many query rows): S = Qi * Ki^T is a dense int8 contraction, run
 // on v_mfma_i32_16x16x64_i8 with 128x128 output tiles per workgroup; tiles
@@ -23,9 +25,14 @@
 
 namespace lct {
 
-constexpr int SCORE_ROUNDS = SCORE_TILE / (4 * 64);
-
-int idx_score_stream_tiles(int64_t L) { return (int)((L + SCORE_TILE - 1) / SCORE_TILE); }
+ScorePlan score_plan(int B, int Lq, int64_t L, int HD) {
+  ScorePlan p;
+  p.qc = Lq <= 1 ? 1 : Lq <= 2 ? 2 : Lq <= 4 ? 4 : Lq <= 8 ? 8 : 16;
+  if (HD >= 512 && p.qc > 4) p.qc = 4;  // register budget
+  p.nqc = (Lq + p.qc - 1) / p.qc;
+  p.tiles = (int)((L + SCORE_TILE - 1) / SCORE_TILE);
+  return p;
+}
 
 LCT_DEV int dot16(intx4 a, intx4 b) {
   int acc = 0;
@@ -44,8 +51,9 @@ __global__ __launch_bounds__(256) void k_idx_score_stream(
     const int32_t* __restrict__ valid_len) {
   constexpr int HD = P * 16;
   constexpr int G = 64 / P;  // consecutive rows read per step
+  constexpr int ROUNDS = SCORE_TILE / (4 * 64);
   __shared__ uint32_t lds[2 * QC * 4];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int tile = blockIdx.x;
   const int b = blockIdx.y / n_qchunks;
   const int r0 = (blockIdx.y % n_qchunks) * QC;
@@ -68,22 +76,20 @@ __global__ __launch_bounds__(256) void k_idx_score_stream(
     mn[i] = 0xFFFFFFFFu;
     mx[i] = 0u;
   }
-  const int8_t* kb = k + (size_t)b * L * HD;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, L * HD);
-  for (int rd = 0; rd < SCORE_ROUNDS; ++rd) {
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (size_t)b * L * HD, L * HD);
+  const uint32_t lane_off = (uint32_t)(g * HD + j * 16);
+  for (int rd = 0; rd < ROUNDS; ++rd) {
     const int64_t base = (int64_t)tile * SCORE_TILE + (int64_t)(rd * 4 + wid) * 64;
     if (base >= L) break;
-    // All P loads are issued before any arithmetic, as buffer loads: the key
-    // rows of this batch entry form one buffer resource, the wave's chunk is a
-    // uniform offset and rows past L read as zeros (never stored).
+    // All P loads are issued before any arithmetic, as buffer loads over the
+    // key rows of this batch entry.  The whole byte offset is in the per-lane
+    // operand, so the buffer range check covers it: rows past L read zeros
+    // (their scores are never stored).
     intx4 kv[P];
-    {
-      const int sbase = __builtin_amdgcn_readfirstlane((int)(base * HD));
-      const int lane_off = g * HD + j * 16;
+    const uint32_t off = (uint32_t)(base * HD) + lane_off;
 #pragma unroll
-      for (int t = 0; t < P; ++t)
-        kv[t] = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, sbase + t * G * HD, BUF_NT);
-    }
+    for (int t = 0; t < P; ++t)
+      kv[t] = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(off + (uint32_t)(t * G * HD)), 0, BUF_NT);
     // keep the loads ahead of the arithmetic (the scheduler would otherwise
     // trade memory-level parallelism for registers)
     __builtin_amdgcn_sched_barrier(0);
@@ -151,17 +157,22 @@ __global__ __launch_bounds__(256) void k_idx_score_stream(
 }
 
 template <int P>
-static hipError_t stream_dispatch_qc(int qc, dim3 grid, const int8_t* q, const int8_t* k,
-                                     int32_t* s, int Lq, int64_t L, int64_t q_pos0, int nqc,
-                                     uint32_t* mm, int t1, TopkRowState* st, uint32_t* hist,
-                                     const int32_t* vl, hipStream_t stream) {
-  switch (qc) {
-    case 1: k_idx_score_stream<P, 1><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
-    case 2: k_idx_score_stream<P, 2><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
-    case 4: k_idx_score_stream<P, 4><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
-    case 8: k_idx_score_stream<P, 8><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
-    default: k_idx_score_stream<P, 16><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, nqc, mm, t1, st, hist, vl); break;
+static hipError_t stream_dispatch_qc(const ScorePlan& pl, int B, const int8_t* q, const int8_t* k,
+                                     int32_t* s, int Lq, int64_t L, int64_t q_pos0, uint32_t* mm,
+                                     TopkRowState* st, uint32_t* hist, const int32_t* vl,
+                                     hipStream_t stream) {
+  const dim3 grid(pl.tiles, B * pl.nqc);
+#define LCT_SC(QC)                                                                             \
+  k_idx_score_stream<P, QC><<<grid, 256, 0, stream>>>(q, k, s, Lq, L, q_pos0, pl.nqc, mm,      \
+                                                      pl.tiles, st, hist, vl)
+  switch (pl.qc) {
+    case 1: LCT_SC(1); break;
+    case 2: LCT_SC(2); break;
+    case 4: LCT_SC(4); break;
+    case 8: LCT_SC(8); break;
+    default: LCT_SC(16); break;
   }
+#undef LCT_SC
   return hipGetLastError();
 }
 
@@ -169,18 +180,14 @@ hipError_t launch_idx_score_stream(const int8_t* q, const int8_t* k, int32_t* s,
                                    int64_t L, int HD, int64_t q_pos0, uint32_t* mm,
                                    TopkRowState* state, uint32_t* hist,
                                    const int32_t* valid_len, hipStream_t stream) {
-  int qc = Lq <= 1 ? 1 : Lq <= 2 ? 2 : Lq <= 4 ? 4 : Lq <= 8 ? 8 : 16;
-  if (HD >= 512 && qc > 4) qc = 4;  // register budget
-  const int nqc = (Lq + qc - 1) / qc;
-  const int t1 = idx_score_stream_tiles(L);
-  dim3 grid(t1, B * nqc);
+  const ScorePlan pl = score_plan(B, Lq, L, HD);
   switch (HD) {
-    case 16: return stream_dispatch_qc<1>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
-    case 32: return stream_dispatch_qc<2>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
-    case 64: return stream_dispatch_qc<4>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
-    case 128: return stream_dispatch_qc<8>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
-    case 256: return stream_dispatch_qc<16>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
-    case 512: return stream_dispatch_qc<32>(qc, grid, q, k, s, Lq, L, q_pos0, nqc, mm, t1, state, hist, valid_len, stream);
+    case 16: return stream_dispatch_qc<1>(pl, B, q, k, s, Lq, L, q_pos0, mm, state, hist, valid_len, stream);
+    case 32: return stream_dispatch_qc<2>(pl, B, q, k, s, Lq, L, q_pos0, mm, state, hist, valid_len, stream);
+    case 64: return stream_dispatch_qc<4>(pl, B, q, k, s, Lq, L, q_pos0, mm, state, hist, valid_len, stream);
+    case 128: return stream_dispatch_qc<8>(pl, B, q, k, s, Lq, L, q_pos0, mm, state, hist, valid_len, stream);
+    case 256: return stream_dispatch_qc<16>(pl, B, q, k, s, Lq, L, q_pos0, mm, state, hist, valid_len, stream);
+    case 512: return stream_dispatch_qc<32>(pl, B, q, k, s, Lq, L, q_pos0, mm, state, hist, valid_len, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(256) void k_idx_score_mfma(const int8_t* __restrict
                                                         const int8_t* __restrict__ k,
                                                         int32_t* __restrict__ s, int Lq,
                                                         int64_t L, int HD, int64_t q_pos0) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int b = blockIdx.z;
   const int64_t row0 = (int64_t)blockIdx.y * MF_TILE + (wid >> 1) * 64;
   const int64_t col0 = (int64_t)blockIdx.x * MF_TILE + (wid & 1) * 64;

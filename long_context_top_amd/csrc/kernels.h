@@ -60,23 +60,27 @@ hipError_t launch_topk_rows(const void* scores, int dtype, int32_t* idx, int row
 // ------------------------------------------------------------- indexer ----
 // Streaming decode scorer; optionally writes (min,max) partials + clears the
 // row states of a following multi-workgroup select (mm/state may be null).
+// One workgroup per tile of SCORE_TILE positions of a (batch, query chunk)
+// row; the select reads `tiles` (min, max) partials per row.
 constexpr int SCORE_TILE = 512;  // positions per workgroup (4 waves x 2 rounds x 64)
+struct ScorePlan {
+  int qc, nqc;  // query rows per workgroup, query chunks per batch entry
+  int tiles;    // tiles (and partials) per row
+};
+ScorePlan score_plan(int B, int Lq, int64_t L, int HD);
 hipError_t launch_idx_score_stream(const int8_t* q, const int8_t* k, int32_t* s, int B, int Lq,
                                    int64_t L, int HD, int64_t q_pos0, uint32_t* mm,
                                    TopkRowState* state, uint32_t* hist,
                                    const int32_t* valid_len, hipStream_t st);
-int idx_score_stream_tiles(int64_t L);
 // Causal/prefill scorer on int8 MFMA: rows [r0, r0+R) of q against all L keys.
 hipError_t launch_idx_score_mfma(const int8_t* q, const int8_t* k, int32_t* s, int B, int Lq,
                                  int64_t L, int HD, int64_t q_pos0, hipStream_t st);
 
 // -------------------------------------------------------------- gather ----
-constexpr int MERGE_MAX_SPLITS = 32;  // split partials per unit the merge kernel combines
+constexpr int MERGE_MAX_SPLITS = 64;  // split partials per unit the merge kernel combines
 struct AttnPlan {
-  int splits;       // workgroups per (b, row, kv head)
-  int per_split;    // entries per workgroup
-  int waves;        // waves per workgroup (1, 2 or 4)
-  int tok;          // positions per wave step (16 or 32)
+  int splits;       // waves per (b, row, kv head)
+  int per_split;    // index entries per wave (a multiple of 32)
   size_t part_bytes;
 };
 AttnPlan attn_plan(int B, int Lq, int Hkv, int kk);
@@ -86,10 +90,10 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               const int32_t* idx, float* out, int B, int Lq, int Hq, int Hkv,
                               int64_t L, int kk, float scale, const AttnPlan& plan,
                               float* partials, hipStream_t st);
-// Merge of split partials: part[unit][split][hs][D+2] (O[D], m, l) ->
+// Merge of split partials: part[unit][split][hs][rs] (O[D], m, l, pad) ->
 // out[(unit * G + h) * D + d] for h < G.
 hipError_t launch_split_merge(const float* part, float* out, int64_t units, int splits, int hs,
-                              int G, int D, hipStream_t st);
+                              int G, int D, int rs, hipStream_t st);
 
 // ----------------------------------------------------------------- GSA ----
 hipError_t launch_gist_score(const uint16_t* q, const uint16_t* gk, float* s, int BH, int64_t Nc,

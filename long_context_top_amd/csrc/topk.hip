@@ -278,7 +278,7 @@ __global__ __launch_bounds__(TOPK_K3_THREADS) void k_topk_emit(
   const uint32_t nv = row_nvalid(valid_len, row, n, vl_div);
   const uint32_t kk = (uint32_t)k < nv ? (uint32_t)k : nv;
   const void* rp = reinterpret_cast<const char*>(scores) + (size_t)row * ld * 4;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int64_t tbase = (int64_t)tile * TOPK_K3_TILE;
   constexpr int CH = TOPK_K3_TILE / NT;  // 64-position chunks per wave
   // the keys of this thread's chunks are requested first
@@ -415,10 +415,12 @@ __global__ __launch_bounds__(FIN_NT) void k_topk_finalize(
     int t3) {
   constexpr int NT = FIN_NT;
   static_assert(TOPK_K4_TILE == NT * 32, "one bitmap word per thread");
+  static_assert(TOPK_RANK_MAX <= NT && TOPK_RANK_MAX / 64 <= NT / 64 / 2, "rank counting layout");
   __shared__ uint64_t sc[TOPK_CAP];
   __shared__ uint32_t tw[NT];
   __shared__ uint32_t lds_scan[NT / 64 + 2];
   __shared__ uint32_t lds_hist[256];
+  __shared__ uint32_t rank[TOPK_RANK_MAX];
   __shared__ uint32_t s_below;
   const int row = blockIdx.y, tile = blockIdx.x;
   const uint32_t* bm = bitmap + (size_t)row * nwords;
@@ -475,17 +477,34 @@ __global__ __launch_bounds__(FIN_NT) void k_topk_finalize(
     const uint32_t c = s.cand_count;
     if (c <= TOPK_RANK_MAX) {
       if (threadIdx.x < c) sc[threadIdx.x] = cand_raw;
+      if (threadIdx.x < TOPK_RANK_MAX) rank[threadIdx.x] = 0u;
       __syncthreads();
-      for (uint32_t i = threadIdx.x; i < c; i += NT) {
-        const uint64_t me = sc[i];
-        uint32_t rank = 0;
-        for (uint32_t j = 0; j < c; ++j) rank += sc[j] > me ? 1u : 0u;
-        if (rank < s.need) {
-          const uint32_t p = ~(uint32_t)(me & 0xFFFFFFFFull);
-          const uint32_t pw = p >> 5;
-          if (pw < w0) ++chosen_below;
-          else if (pw < w0 + NT) atomicOr(&tw[pw - w0], 1u << (p & 31));
+      // rank of a candidate = how many candidates order before it.  The c*c
+      // comparisons are spread over all waves: wave w compares candidate
+      // group w / S (64 candidates, one per lane) with slice w % S of the list.
+      // (wave_id() is a scalar, so the loop below has uniform bounds and is
+      // unrolled with its LDS reads pipelined)
+      const int lane = threadIdx.x & 63, wv = wave_id();
+      const int ng = (int)(c + 63) / 64;  // <= TOPK_RANK_MAX / 64
+      const int S = (NT / 64) / ng;
+      if (wv < ng * S) {
+        const int g = wv / S, sl = wv % S;
+        const uint32_t i = (uint32_t)(g * 64 + lane);
+        const uint32_t j0 = c * sl / S, j1 = c * (sl + 1) / S;
+        if (i < c) {
+          const uint64_t me = sc[i];
+          uint32_t r = 0;
+#pragma unroll 8
+          for (uint32_t j = j0; j < j1; ++j) r += sc[j] > me ? 1u : 0u;
+          if (r) atomicAdd(&rank[i], r);
         }
+      }
+      __syncthreads();
+      if (threadIdx.x < c && rank[threadIdx.x] < s.need) {
+        const uint32_t p = ~(uint32_t)(sc[threadIdx.x] & 0xFFFFFFFFull);
+        const uint32_t pw = p >> 5;
+        if (pw < w0) ++chosen_below;
+        else if (pw < w0 + NT) atomicOr(&tw[pw - w0], 1u << (p & 31));
       }
     } else {
       const uint32_t m = next_pow2(c);
@@ -587,7 +606,7 @@ __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ s
   const void* rp = reinterpret_cast<const char*>(scores) + (size_t)row * ld * 4;
   int32_t* out = idx + (size_t)row * k;
   const uint32_t nwords = (nv + 31) / 32;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   if (kk == nv) {  // every valid position is chosen
     for (uint32_t j = threadIdx.x; j < (uint32_t)k; j += NT) out[j] = j < nv ? (int32_t)j : -1;
     return;
