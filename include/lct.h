@@ -78,7 +78,8 @@ const char* lct_last_error(void);
  *          entries t > q_pos0 + r are undefined (not candidates).
  * Lq <= 16 runs a coalesced HBM streaming kernel; larger Lq (prefill) runs
  * an int8 MFMA kernel.  HD must be a power of two in [16, 512]
- * (LCT_EUNSUPPORTED otherwise; the MFMA kernel needs HD >= 64).
+ * (LCT_EUNSUPPORTED otherwise; the MFMA kernel needs HD >= 64 and
+ * L < 2^22, the streaming kernel L * HD < 2^31).
  */
 int lct_idx_score_i8(const int8_t* q, const int8_t* k, int32_t* scores, int B, int Lq,
                      int64_t L, int HD, int64_t q_pos0, void* stream);

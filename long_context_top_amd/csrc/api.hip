@@ -133,6 +133,8 @@ int lct_idx_score_i8(const int8_t* q, const int8_t* k, int32_t* scores, int B, i
   if (!mfma && L * HD >= ((int64_t)1 << 31))
     return fail(LCT_EUNSUPPORTED, "one batch entry's key cache must be < 2 GiB (L*HD = %lld)", (long long)(L * HD));
   if (mfma && HD < 64) return fail(LCT_EUNSUPPORTED, "the MFMA scorer needs HD >= 64");
+  if (mfma && L >= ((int64_t)1 << 22))
+    return fail(LCT_EUNSUPPORTED, "the MFMA scorer needs L < 2^22 (128 score rows < 2 GiB)");
   int rc = check_device();
   if (rc) return rc;
   if (!mfma)

@@ -193,71 +193,197 @@ hipError_t launch_idx_score_stream(const int8_t* q, const int8_t* k, int32_t* s,
 }
 
 // ------------------------------------------------------------- prefill ----
-// 128x128 output tile per workgroup, four waves of 64x64, each a 4x4 grid of
-// 16x16 int8 MFMA blocks.  Operands are read straight from global memory in
-// the MFMA lane layout (lane: row lane%16, 16 contiguous bytes at
-// k = 16*(lane/16)); the 128-row panels are shared through L2.
-constexpr int MF_TILE = 128;
+// Dense scores S = Qi Ki^T on v_mfma_i32_16x16x64_i8, computed as S^T tiles
+// (keys are the MFMA rows, queries the columns) so that every lane ends with
+// 4 consecutive keys of one query row: 16-byte stores along the score rows.
+// Workgroup: MF_Q queries x MF_KT key tiles of 128.  The query fragments stay
+// in registers for the whole loop; each 128-key tile is brought into LDS by
+// LDS DMA (global_load_lds_dwordx4, one 1 KiB MFMA fragment per instruction)
+// while the previous tile is multiplied.  2*MF_NWR waves of 64 queries x 64
+// keys; a key tile serves all MF_Q queries (fewer re-reads of the keys).
+// Tiles strictly above the causal diagonal are skipped, entries above it in
+// the diagonal tiles are written as INT32_MIN.  Scores go out as buffer
+// stores over the workgroup's rows: out-of-range elements (rows past Lq,
+// keys past L) get an offset past the buffer and are dropped, so every wave
+// issues the same number of stores per tile and the wait for the next tile's
+// DMA can count them.  With 16-byte stores, each 16-query slice of a wave's
+// tile is first turned around in a 4 KiB LDS buffer (chunk index XOR row,
+// conflict-free both ways) so that each store instruction writes 4 whole
+// 256-byte row pieces instead of 16 pieces of 64 bytes.
+constexpr int MF_NWR = 2;   // waves along the query dimension (x2 along keys)
+constexpr int MF_Q = 64 * MF_NWR;  // queries per workgroup
+constexpr int MF_K = 128;   // keys per tile
+constexpr int MF_KT = 4;    // key tiles per workgroup (more, smaller workgroups write faster)
 
-__global__ __launch_bounds__(256) void k_idx_score_mfma(const int8_t* __restrict__ q,
+typedef __attribute__((address_space(3))) void mf_lds_void;
+typedef const __attribute__((address_space(1))) void mf_global_cvoid;
+
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left at their maxima (n < 64)
+#define MF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
+// KS = HD / 64 k-steps; VEC: 16-byte stores (L % 4 == 0), else 4-byte ones
+template <int KS, bool VEC>
+__global__ __launch_bounds__(128 * MF_NWR) void k_idx_score_mfma(const int8_t* __restrict__ q,
                                                         const int8_t* __restrict__ k,
                                                         int32_t* __restrict__ s, int Lq,
-                                                        int64_t L, int HD, int64_t q_pos0) {
+                                                        int64_t L, int64_t q_pos0) {
+  constexpr int HD = KS * 64;
+  constexpr int CHUNKS = 8 * KS;          // 1 KiB fragments per key tile
+  constexpr int NWV = 2 * MF_NWR;         // waves
+  constexpr int CPW = CHUNKS / NWV;       // per wave
+  static_assert(CHUNKS % NWV == 0, "chunks per wave");
+  // the two key-tile buffers are separate objects so that the compiler can
+  // tell the DMA into one from the reads of the other (otherwise it drains
+  // vmcnt before every LDS read, serialising DMA and compute)
+  __shared__ __attribute__((aligned(16))) char kt_a[CHUNKS][1024];
+  __shared__ __attribute__((aligned(16))) char kt_b[CHUNKS][1024];
+  __shared__ __attribute__((aligned(16))) intx4 st_lds[NWV][16][16];  // [wave][row][16-byte chunk]
   const int lane = threadIdx.x & 63, wid = wave_id();
+  const int wr = wid >> 1, wc = wid & 1;
   const int b = blockIdx.z;
-  const int64_t row0 = (int64_t)blockIdx.y * MF_TILE + (wid >> 1) * 64;
-  const int64_t col0 = (int64_t)blockIdx.x * MF_TILE + (wid & 1) * 64;
+  const int64_t q0 = (int64_t)blockIdx.y * MF_Q;           // first query of the workgroup
+  const int64_t kt_first = (int64_t)blockIdx.x * MF_KT;     // first key tile
+  int64_t n_kt = (L + MF_K - 1) / MF_K - kt_first;
+  if (n_kt > MF_KT) n_kt = MF_KT;
   if (q_pos0 >= 0) {
-    // whole workgroup tile above the diagonal: nothing to compute
-    const int64_t last_row_pos = q_pos0 + (int64_t)blockIdx.y * MF_TILE + MF_TILE - 1;
-    if ((int64_t)blockIdx.x * MF_TILE > last_row_pos) return;
+    // key tiles beyond the last query's diagonal are not needed
+    const int64_t last_q = q0 + MF_Q - 1 < Lq ? q0 + MF_Q - 1 : Lq - 1;
+    const int64_t lim = (q_pos0 + last_q) / MF_K + 1 - kt_first;  // tiles that hold a key <= it
+    if (lim < n_kt) n_kt = lim;
   }
+  if (n_kt <= 0) return;  // uniform over the workgroup
   const int8_t* qb = q + (size_t)b * Lq * HD;
   const int8_t* kb = k + (size_t)b * L * HD;
-  const int rl = lane & 15, kq = lane >> 4;
-  intx4 acc[4][4];
+  const int n = lane & 15, g = lane >> 4;
+
+  // DMA of key tile t into a buffer: chunk c = (key block c / KS, k-step
+  // c % KS); lane (n, g) brings key 16*block + n, bytes 64*ks + 16*g .. +15.
+  // Keys past L read key L-1 (in bounds; their scores are never stored).
+  auto issue_tile = [&](auto& buf, int64_t t) {
+    const int64_t key0 = (kt_first + t) * MF_K;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[i][c] = intx4{0, 0, 0, 0};
-  for (int kk = 0; kk < HD; kk += 64) {
-    intx4 a[4], bb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int64_t r = row0 + i * 16 + rl;
-      a[i] = r < Lq ? *reinterpret_cast<const intx4*>(qb + r * HD + kk + kq * 16)
-                    : intx4{0, 0, 0, 0};
-      int64_t c = col0 + i * 16 + rl;
-      bb[i] = c < L ? *reinterpret_cast<const intx4*>(kb + c * HD + kk + kq * 16)
-                    : intx4{0, 0, 0, 0};
+    for (int i = 0; i < CPW; ++i) {
+      const int c = wid * CPW + i;
+      int64_t key = key0 + (c / KS) * 16 + n;
+      if (key >= L) key = L - 1;
+      __builtin_amdgcn_global_load_lds((mf_global_cvoid*)(kb + key * HD + (c % KS) * 64 + g * 16),
+                                       (mf_lds_void*)&buf[c][0], 16, 0, 0);
     }
+  };
+  issue_tile(kt_a, 0);
+
+  // query fragments (B operand): block qb, k-step ks: lane (n, g) holds query
+  // q0 + 64 wr + 16 qb + n, bytes 64 ks + 16 g .. +15
+  intx4 qf[4][KS];
+#pragma unroll
+  for (int qb4 = 0; qb4 < 4; ++qb4) {
+    const int64_t row = q0 + wr * 64 + qb4 * 16 + n;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[qb4][ks] = row < Lq ? *reinterpret_cast<const intx4*>(qb + row * HD + ks * 64 + g * 16)
+                             : intx4{0, 0, 0, 0};
+  }
+
+  // the workgroup's score rows as one buffer (MF_Q * L * 4 < 2^31 bytes)
+  const int64_t nrows = Lq - q0 < MF_Q ? Lq - q0 : MF_Q;
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(s + ((size_t)b * Lq + q0) * L, (short)0,
+                                        (int)(nrows * L * 4), BUF_RSRC_WORD3);
+  constexpr uint32_t DROP = 0x80000000u;  // an offset past the buffer
+
+  auto step = [&](auto& cur, auto& nxt, int64_t t) {
+    // this wave's DMA of tile t has landed once at most the score stores of
+    // tile t-1 (issued after it) are outstanding; the barrier then makes
+    // every wave's chunks visible and retires all reads of tile t-1
+    if (t == 0 || !VEC) MF_WAIT_VM(0); else MF_WAIT_VM(16);
+    // a plain barrier: __syncthreads() would also wait for the score stores
+    __builtin_amdgcn_s_barrier();
+    if (t + 1 < n_kt) issue_tile(nxt, t + 1);
+    __asm__ __volatile__("" ::: "memory");
+    intx4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[i][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bb[c], acc[i][c], 0, 0, 0);
-  }
-  // C layout: lane holds rows 4*(lane/16)+e, column lane%16 of each block
+      for (int j = 0; j < 4; ++j) acc[i][j] = intx4{0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = (wc * 4 + kb4) * KS + ks;
+        const intx4 a = *reinterpret_cast<const intx4*>(&cur[c][lane * 16]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int64_t r = row0 + i * 16 + kq * 4 + e;
-        int64_t col = col0 + c * 16 + rl;
-        if (r < Lq && col < L) {
-          int32_t v = acc[i][c][e];
-          if (q_pos0 >= 0 && col > q_pos0 + r) v = INT32_MIN;
-          s[((size_t)b * Lq + r) * L + col] = v;
+        for (int qb4 = 0; qb4 < 4; ++qb4)
+          acc[qb4][kb4] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qf[qb4][ks], acc[qb4][kb4], 0, 0, 0);
+      }
+    }
+    // acc[qb][kb][e] = S[query q0 + 64wr + 16qb + n][key key0 + 16kb + 4g + e]
+    const int64_t key0 = (kt_first + t) * MF_K + wc * 64;
+#pragma unroll
+    for (int qb4 = 0; qb4 < 4; ++qb4) {
+      const int64_t rl = wr * 64 + qb4 * 16 + n;  // row within the workgroup
+      const int64_t diag = q_pos0 >= 0 ? q_pos0 + q0 + rl : INT64_MAX;  // last unmasked key
+      intx4 v[4];
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        const int64_t col = key0 + kb4 * 16 + g * 4;
+        v[kb4] = acc[qb4][kb4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e > diag) v[kb4][e] = INT32_MIN;
+      }
+      if (VEC) {
+        // turn the 16 x 64 slice around in LDS: chunk (row n, 4kb + g) ...
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4) st_lds[wid][n][(kb4 * 4 + g) ^ n] = v[kb4];
+        __asm__ __volatile__("" ::: "memory");
+        // ... and read 4 rows x 16 chunks per instruction: lane -> row 4i + lane/16, chunk lane%16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = i * 4 + (lane >> 4), c = lane & 15;
+          const intx4 w = st_lds[wid][r][c ^ r];
+          const int64_t rr = wr * 64 + qb4 * 16 + r;
+          const int64_t col = key0 + c * 4;
+          const uint32_t off = (uint32_t)((rr * L + col) * 4);
+          __builtin_amdgcn_raw_buffer_store_b128(w, srs, rr < nrows && col < L ? (int)off : (int)DROP, 0, 0);
+        }
+        __asm__ __volatile__("" ::: "memory");
+      } else {
+        const bool row_ok = rl < nrows;
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+          const int64_t col = key0 + kb4 * 16 + g * 4;
+          const uint32_t off = (uint32_t)((rl * L + col) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(v[kb4][e], srs, row_ok && col + e < L ? (int)(off + 4 * e) : (int)DROP, 0, 0);
         }
       }
+    }
+  };
+  for (int64_t t = 0; t < n_kt; t += 2) {
+    step(kt_a, kt_b, t);
+    if (t + 1 < n_kt) step(kt_b, kt_a, t + 1);
+  }
 }
 
 hipError_t launch_idx_score_mfma(const int8_t* q, const int8_t* k, int32_t* s, int B, int Lq,
                                  int64_t L, int HD, int64_t q_pos0, hipStream_t st) {
-  dim3 grid((unsigned)((L + MF_TILE - 1) / MF_TILE), (unsigned)((Lq + MF_TILE - 1) / MF_TILE), B);
-  k_idx_score_mfma<<<grid, 256, 0, st>>>(q, k, s, Lq, L, HD, q_pos0);
+  if ((int64_t)MF_Q * L * 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int64_t kts = (L + MF_K - 1) / MF_K;
+  dim3 grid((unsigned)((kts + MF_KT - 1) / MF_KT), (unsigned)((Lq + MF_Q - 1) / MF_Q), B);
+  // 16-byte stores need 16-byte aligned score rows
+  const bool vec = L % 4 == 0 && ((uintptr_t)s % 16) == 0;
+#define LCT_MF(KS)                                                                             \
+  if (vec) k_idx_score_mfma<KS, true><<<grid, 128 * MF_NWR, 0, st>>>(q, k, s, Lq, L, q_pos0);   \
+  else k_idx_score_mfma<KS, false><<<grid, 128 * MF_NWR, 0, st>>>(q, k, s, Lq, L, q_pos0)
+  switch (HD) {
+    case 64: LCT_MF(1); break;
+    case 128: LCT_MF(2); break;
+    case 256: LCT_MF(4); break;
+    case 512: LCT_MF(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef LCT_MF
   return hipGetLastError();
 }
 

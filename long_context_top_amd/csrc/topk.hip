@@ -169,12 +169,19 @@ __global__ __launch_bounds__(256) void k_topk_minmax(const void* __restrict__ sc
   if (tile == 0) hist[(size_t)row * TOPK_NB + threadIdx.x % TOPK_NB] = 0u;
 }
 
-// Window of a row from the producer's (min,max) partials.
+// Window of a row from the producer's (min,max) partials.  The caller loads
+// this thread's first partial (index threadIdx.x) before anything else, so
+// that waiting for it does not also wait for loads issued later (vmcnt
+// counts in issue order); further partials (t1 > NT) are read here.
+LCT_DEV uint2 first_partial(const uint32_t* mm_row, int t1) {
+  return (int)threadIdx.x < t1 ? reinterpret_cast<const uint2*>(mm_row)[threadIdx.x]
+                               : uint2{0xFFFFFFFFu, 0u};
+}
 template <int NT>
-LCT_DEV void row_window(const uint32_t* mm_row, int t1, uint32_t nv, uint32_t& lo,
+LCT_DEV void row_window(const uint32_t* mm_row, int t1, uint2 first, uint32_t nv, uint32_t& lo,
                         uint32_t& shift, uint32_t* lds) {
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = threadIdx.x; i < t1; i += NT) {
+  uint32_t mn = first.x, mx = first.y;
+  for (int i = threadIdx.x + NT; i < t1; i += NT) {
     mn = min(mn, mm_row[2 * i]);
     mx = max(mx, mm_row[2 * i + 1]);
   }
@@ -198,7 +205,9 @@ __global__ __launch_bounds__(256) void k_topk_hist(const void* __restrict__ scor
   const void* rp = reinterpret_cast<const char*>(scores) + (size_t)row * ld * 4;
   const int64_t base = (int64_t)tile * tile_len;
   const int64_t end = base + tile_len < (int64_t)nv ? base + tile_len : (int64_t)nv;
-  // the tile's keys are requested first; the window reduction overlaps them
+  const uint32_t* mm_row = mm + (size_t)row * t1 * 2;
+  const uint2 first = first_partial(mm_row, t1);
+  // then the tile's keys; the window reduction overlaps them
   constexpr int PF = 16;
   uint32_t kbuf[PF];
 #pragma unroll
@@ -207,7 +216,7 @@ __global__ __launch_bounds__(256) void k_topk_hist(const void* __restrict__ scor
     kbuf[j] = load_key<DT>(rp, p < end ? p : (end > 0 ? end - 1 : 0));  // clamped, in bounds
   }
   uint32_t lo, shift;
-  row_window<256>(mm + (size_t)row * t1 * 2, t1, nv, lo, shift, lds);
+  row_window<256>(mm_row, t1, first, nv, lo, shift, lds);
   for (int i = threadIdx.x; i < TOPK_NB; i += 256) h[i] = 0;
   __syncthreads();
   if (kk < nv) {
@@ -229,23 +238,26 @@ struct RowSel {
 };
 
 // Threshold bin of a row from its histogram (every caller derives the same
-// values).  NT >= TOPK_NB.
+// values).  NT >= TOPK_NB.  `first` and `c` are loaded by the caller ahead of
+// its other loads: first_partial(mm_row, t1) and hist_entry(hist_row).
+LCT_DEV uint32_t hist_entry(const uint32_t* hist_row) {
+  // thread t < NB owns bin NB-1-t
+  return (int)threadIdx.x < TOPK_NB ? hist_row[TOPK_NB - 1 - threadIdx.x] : 0u;
+}
 template <int NT>
-LCT_DEV RowSel row_select_params(const uint32_t* mm_row, int t1, const uint32_t* hist_row,
+LCT_DEV RowSel row_select_params(const uint32_t* mm_row, int t1, uint2 first, uint32_t c,
                                  uint32_t nv, uint32_t kk, uint32_t* lds_scan,
                                  uint32_t* lds_small) {
   static_assert(NT >= TOPK_NB, "one thread per bin");
   RowSel r;
-  row_window<NT>(mm_row, t1, nv, r.lo, r.shift, lds_small);
+  row_window<NT>(mm_row, t1, first, nv, r.lo, r.shift, lds_small);
   if (kk >= nv) {
     r.tb = TOPK_ALL;
     r.need = 0;
     r.ccount = 0;
     return r;
   }
-  // thread t < NB owns bin NB-1-t; an exclusive scan in thread order counts
-  // the keys in higher bins
-  const uint32_t c = (int)threadIdx.x < TOPK_NB ? hist_row[TOPK_NB - 1 - threadIdx.x] : 0u;
+  // an exclusive scan in thread order counts the keys in higher bins
   uint32_t tot;
   const uint32_t higher = block_excl_scan<NT>(c, lds_scan, tot);
   if ((int)threadIdx.x < TOPK_NB && higher < kk && higher + c >= kk) {
@@ -281,16 +293,18 @@ __global__ __launch_bounds__(TOPK_K3_THREADS) void k_topk_emit(
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int64_t tbase = (int64_t)tile * TOPK_K3_TILE;
   constexpr int CH = TOPK_K3_TILE / NT;  // 64-position chunks per wave
-  // the keys of this thread's chunks are requested first
+  // the row's window partial and histogram entry first, then the keys of
+  // this thread's chunks
+  const uint32_t* mm_row = mm + (size_t)row * t1 * 2;
+  const uint2 first = first_partial(mm_row, t1);
+  const uint32_t hc = hist_entry(hist + (size_t)row * TOPK_NB);
   uint32_t kbuf[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t p = tbase + (int64_t)(c * (NT / 64) + wid) * 64 + lane;
     kbuf[c] = load_key<DT>(rp, p < nv ? p : (nv > 0 ? nv - 1 : 0));  // clamped, in bounds
   }
-  const RowSel s = row_select_params<NT>(mm + (size_t)row * t1 * 2, t1,
-                                         hist + (size_t)row * TOPK_NB, nv, kk, lds_scan,
-                                         lds_small);
+  const RowSel s = row_select_params<NT>(mm_row, t1, first, hc, nv, kk, lds_scan, lds_small);
   if (tile == 0 && threadIdx.x == 0) {
     TopkRowState w = st[row];
     w.lo = s.lo;
