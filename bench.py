@@ -306,8 +306,15 @@ def bench_prefill_indexer(cfg, steps, warmup):
     ms = _timed_graph(f, steps, torch.cuda.current_stream())
     pairs = sum(r0 + r + 1 for r in range(rows))
     tops = 2 * cfg.HD * pairs / (ms * 1e-3) / 1e12
+    # the scores are materialised: 4 bytes stored per 2*HD int8 ops, so the
+    # kernel's bound is HBM (stores of the causal entries + the key/query reads)
+    nbytes = 4 * pairs + cfg.L * cfg.HD + rows * cfg.HD
+    gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": cfg.name + " indexer block (last 2048 rows)", "ms": ms, "int8_tops": tops,
-            "frac": tops / INT8_PEAK_TOPS}
+            "frac": tops / INT8_PEAK_TOPS,
+            "roofline": {"bound": "hbm", "kernel": "k_idx_score_mfma", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "bytes_per_launch": nbytes, "us_per_launch": ms * 1e3}}
 
 
 def copy_calibration(steps):
@@ -323,7 +330,7 @@ def copy_calibration(steps):
             "bytes_written_per_launch": dst.numel() * 4, "launches": steps}
 
 
-def summarize_profile(stats_csv, pmc_csvs, calib_csvs):
+def summarize_profile(stats_csv, pmc_csvs, calib_csvs, trace_csv=None):
     """Text summary of rocprofv3 output: per-kernel average duration, and the
     average counter value per dispatch for each kernel, scaled by the copy
     calibration (counter units per byte of a known plain copy)."""
@@ -350,6 +357,7 @@ def summarize_profile(stats_csv, pmc_csvs, calib_csvs):
             if "elementwise" in kname or "copy" in kname.lower():
                 want = 1 << 30  # bytes read (FETCH) or written (WRITE) per copy launch
                 scale[cname] = want / (val * 1024.0)
+    traffic = {}
     if pmc_csvs:
         lines.append("")
         lines.append("counters per dispatch (KiB as read) -> bytes after copy calibration")
@@ -359,7 +367,60 @@ def summarize_profile(stats_csv, pmc_csvs, calib_csvs):
                     continue
                 sc = scale.get(cname, 1.0)
                 lines.append(f"{kname[:30]:30s} {cname:12s} {val:14.1f} KiB  x{sc:.4f} = {val*1024*sc/2**20:10.2f} MiB")
+                short = kname.split("(")[0].split("<")[0].replace("void ", "").replace("lct::", "")
+                traffic[(short, cname)] = val * 1024 * sc
+    if trace_csv:
+        lines.append("")
+        lines.extend(step_breakdown(trace_csv))
+    if ("k_idx_score_stream", "FETCH_SIZE") in traffic and ("k_idx_score_stream", "WRITE_SIZE") in traffic:
+        import hashlib
+        h = hashlib.sha256()
+        for f in SCORER_SOURCES:
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        lines.append("")
+        lines.append(f"traffic k_idx_score_stream fetch_bytes_per_launch {int(traffic[('k_idx_score_stream', 'FETCH_SIZE')])}")
+        lines.append(f"traffic k_idx_score_stream write_bytes_per_launch {int(traffic[('k_idx_score_stream', 'WRITE_SIZE')])}")
+        lines.append(f"source_sha256 k_idx_score_stream {h.hexdigest()}")
     return "\n".join(lines)
+
+
+def step_breakdown(trace_csv, n_steps=5):
+    """Per-kernel durations inside graph-replayed decode steps (the last
+    n_steps complete steps of the trace): a step starts at a scorer launch
+    that is followed by the select's first kernel."""
+    import csv
+    rows = list(csv.DictReader(open(trace_csv)))
+    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                  r["Kernel_Name"].split("(")[0].replace("void ", "").replace("lct::", "").split("<")[0])
+                 for r in rows)
+    names = [x[2] for x in seq]
+    starts = [i for i in range(len(seq) - 1)
+              if names[i] == "k_idx_score_stream" and names[i + 1] == "k_topk_hist"]
+    if len(starts) < 2:
+        return ["(no graph-replayed steps found in the trace)"]
+    groups = 7
+    per_step = groups
+    sel = starts[-per_step * n_steps:]
+    first, last = sel[0], sel[-1]
+    end = last + 1
+    while end < len(seq) and names[end] != "k_idx_score_stream":
+        end += 1
+    agg = {}
+    for i in range(first, end):
+        s0, e0, n = seq[i]
+        agg.setdefault(n, []).append((e0 - s0) / 1e3)
+    span = (seq[end - 1][1] - seq[first][0]) / 1e3
+    out = [f"steady-state decode steps (last {n_steps} graph-replayed steps of the trace)",
+           f"{'kernel':24s} {'launches/step':>13s} {'mean_us':>9s} {'us/step':>9s}"]
+    total = 0.0
+    for n, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        ps = sum(v) / n_steps
+        total += ps
+        out.append(f"{n:24s} {len(v) / n_steps:13.1f} {sum(v) / len(v):9.2f} {ps:9.1f}")
+    out.append(f"{'sum of kernel time':24s} {'':13s} {'':9s} {total:9.1f}")
+    out.append(f"{'step span (first start to last end)':38s} {span / n_steps:9.1f} us/step")
+    return out
 
 
 def main():
@@ -373,13 +434,15 @@ def main():
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy used to calibrate HBM byte counters")
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
-                    help="print a summary of rocprofv3 CSVs: STATS [PMC ...] [--calib CSV ...]")
+                    help="print a summary of rocprofv3 CSVs: STATS [TRACE] [PMC ...] [--calib CSV ...]")
     args, rest = ap.parse_known_args()
     if args.summarize:
         files = args.summarize + rest
         calib = files[files.index("--calib") + 1:] if "--calib" in files else []
         main_files = files[:files.index("--calib")] if "--calib" in files else files
-        print(summarize_profile(main_files[0], main_files[1:], calib))
+        trace = [f for f in main_files[1:] if f.endswith("kernel_trace.csv")]
+        pmc = [f for f in main_files[1:] if not f.endswith("kernel_trace.csv")]
+        print(summarize_profile(main_files[0], pmc, calib, trace[0] if trace else None))
         return
     if rest:
         ap.error(f"unknown arguments {rest}")
