@@ -85,6 +85,33 @@ int lct_idx_score_i8(const int8_t* q, const int8_t* k, int32_t* scores, int B, i
                      int64_t L, int HD, int64_t q_pos0, void* stream);
 
 /*
+ * Causal prefill index of one layer group (steps 1 and 2 together).
+ * Source: tutorial page, sections "DSA 与 IndexShare" and "两个阶段各付一笔"
+ * (in prefill every query scores all earlier positions and keeps its top k);
+ * CLSA explainer section 2.3 (the index set is a small integer array).
+ *   q    int8  [L, HD]     indexer queries; row i sits at position i
+ *   k    int8  [L, HD]     indexer keys
+ *   idx  int32 [L, topk]   out: row i holds the min(topk, i + 1) positions
+ *                          t <= i with the largest q[i].k[t] (sum over HD of
+ *                          int8 products, int32), equal scores to the lower
+ *                          position, ascending, padded with -1.
+ * HD = 256, L <= 65536, topk <= 2048: the scores are never stored; they are
+ * filtered to per-row candidate lists on the fly and an exact select runs
+ * on those; rows the lists cannot settle go through the plain path.  This
+ * synchronizes `stream` once (the number of such rows sizes the plain work)
+ * and writes it to *n_fallback (host pointer, may be NULL).  Other shapes
+ * (HD a power of two in [64, 512], L <= 2^18) score blocks of rows into the
+ * workspace and select per row; *n_fallback is then 0.
+ * ws: at least lct_prefill_index_workspace_bytes(L, HD, topk) bytes, 256-byte
+ * aligned, device memory owned by the caller.  q, k 16-byte aligned.
+ * Errors: LCT_EINVAL (null / misaligned / bad sizes), LCT_EUNSUPPORTED
+ * (shape), LCT_ENOWORKSPACE, LCT_EHIP.
+ */
+int lct_prefill_index_i8(const int8_t* q, const int8_t* k, int32_t* idx, int64_t L, int HD,
+                         int topk, void* ws, size_t ws_bytes, int* n_fallback, void* stream);
+int lct_prefill_index_workspace_bytes(int64_t L, int HD, int topk, size_t* bytes);
+
+/*
  * Gist scores (GSA step 1).  Source: SSA article section 3 / GSA summary
  * section 2.2 (the query is compared with every gist by a dot product).
  *   q      bf16 [BH, D], gk bf16 [BH, Nc, D], scores fp32 [BH, Nc] (unscaled).

@@ -50,6 +50,9 @@ _SIGS = {
     "lct_version": ([], _c.c_char_p),
     "lct_last_error": ([], _c.c_char_p),
     "lct_idx_score_i8": ([_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i64, _vp], _i32),
+    "lct_prefill_index_i8": ([_vp, _vp, _vp, _i64, _i32, _i32, _vp, _sz, _c.POINTER(_i32), _vp],
+                             _i32),
+    "lct_prefill_index_workspace_bytes": ([_i64, _i32, _i32, _c.POINTER(_sz)], _i32),
     "lct_gist_score_bf16": ([_vp, _vp, _vp, _i32, _i64, _i32, _vp], _i32),
     "lct_topk_select": ([_vp, _i32, _vp, _i32, _i64, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
     "lct_topk_workspace_bytes": ([_i32, _i64, _i32, _c.POINTER(_sz)], _i32),
@@ -157,6 +160,34 @@ def idx_score(q: torch.Tensor, k: torch.Tensor, q_pos0: int = -1,
         out = torch.empty((B, Lq, L), dtype=torch.int32, device=q.device)
     _need(out, torch.int32, "out")
     _check(lib().lct_idx_score_i8(_p(q), _p(k), _p(out), B, Lq, L, HD, q_pos0, _stream()))
+    return out
+
+
+def prefill_index(q: torch.Tensor, k: torch.Tensor, topk: int, out: Optional[torch.Tensor] = None,
+                  ws: Optional[Workspace] = None, stats: Optional[dict] = None) -> torch.Tensor:
+    """Causal index of one group: int8 q, k [L, HD] -> int32 [L, topk].
+
+    Row i lists the min(topk, i + 1) positions t <= i with the largest
+    q[i].k[t] (ties to the lower position), ascending, -1 padded.  With
+    ``stats`` given, ``stats["n_fallback"]`` receives the number of rows the
+    fused filter left to the plain path.
+    """
+    _need(q, torch.int8, "q")
+    _need(k, torch.int8, "k")
+    L, HD = q.shape
+    if tuple(k.shape) != (L, HD):
+        raise ValueError("q and k must both be [L, HD]")
+    if out is None:
+        out = torch.empty((L, topk), dtype=torch.int32, device=q.device)
+    _need(out, torch.int32, "out")
+    nb = _sz()
+    _check(lib().lct_prefill_index_workspace_bytes(L, HD, topk, _c.byref(nb)))
+    buf = _ws(ws).get(nb.value)
+    nf = _i32(0)
+    _check(lib().lct_prefill_index_i8(_p(q), _p(k), _p(out), L, HD, topk, _p(buf), buf.numel(),
+                                      _c.byref(nf), _stream()))
+    if stats is not None:
+        stats["n_fallback"] = int(nf.value)
     return out
 
 

@@ -113,6 +113,58 @@ size_t attn_scratch_bytes(int B, int Lq, int Hkv, int kk) {
   return attn_plan(B, Lq, Hkv, kk).part_bytes;
 }
 
+constexpr int64_t PREFILL_BLOCK_BYTES = (int64_t)512 << 20;  // score block of the causal path
+
+// Causal prefill index of one group: the fused filter + select when the
+// shape fits it, else blocks of plain scores + a row select.
+struct PrefillPlan {
+  bool fused;
+  int64_t block_rows;  // plain path: query rows scored per block
+  size_t bytes;        // workspace
+};
+
+PrefillPlan prefill_plan(int64_t L, int HD, int kk) {
+  PrefillPlan p;
+  p.fused = HD == 256 && L <= PF_MAX_L && kk <= PF_MAX_K;
+  if (p.fused) {
+    p.block_rows = 0;
+    p.bytes = pf_workspace_layout(L, HD, kk, nullptr);
+  } else {
+    int64_t br = PREFILL_BLOCK_BYTES / (L * 4);
+    br = br < 128 ? 128 : (br / 128) * 128;
+    p.block_rows = br < L ? br : L;
+    p.bytes = up256((size_t)p.block_rows * L * sizeof(int32_t));
+  }
+  return p;
+}
+
+int validate_prefill(int64_t L, int HD, int kk) {
+  LCT_REQUIRE(L >= 1 && kk >= 1, "L and topk must be >= 1");
+  if (!pow2(HD) || HD < 64 || HD > 512)
+    return fail(LCT_EUNSUPPORTED, "causal prefill needs HD a power of two in [64, 512] (got %d)", HD);
+  if (L > TOPK_ROW_MAX_N) return fail(LCT_EUNSUPPORTED, "causal prefill supports L <= %lld", (long long)TOPK_ROW_MAX_N);
+  return LCT_OK;
+}
+
+int run_prefill(const int8_t* q, const int8_t* k, int32_t* idx, int64_t L, int HD, int kk,
+                char* ws, int* n_fallback, hipStream_t st) {
+  const PrefillPlan p = prefill_plan(L, HD, kk);
+  if (n_fallback) *n_fallback = 0;
+  if (p.fused) {
+    LCT_HIP(launch_pf_fused(q, k, L, HD, kk, idx, ws, st, n_fallback), "prefill index (fused)");
+    return LCT_OK;
+  }
+  int32_t* scores = reinterpret_cast<int32_t*>(ws);
+  for (int64_t r0 = 0; r0 < L; r0 += p.block_rows) {
+    const int64_t nr = L - r0 < p.block_rows ? L - r0 : p.block_rows;
+    LCT_HIP(launch_idx_score_mfma(q + r0 * HD, k, scores, 1, (int)nr, L, HD, r0, st),
+            "prefill index: idx_score");
+    LCT_HIP(launch_topk_rows(scores, LCT_I32, idx + r0 * kk, (int)nr, L, L, kk, nullptr, 1, r0, st),
+            "prefill index: topk rows");
+  }
+  return LCT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,6 +197,28 @@ int lct_idx_score_i8(const int8_t* q, const int8_t* k, int32_t* scores, int B, i
     LCT_HIP(launch_idx_score_mfma(q, k, scores, B, Lq, L, HD, q_pos0, as_stream(stream)),
             "idx_score (mfma)");
   return LCT_OK;
+}
+
+int lct_prefill_index_workspace_bytes(int64_t L, int HD, int topk, size_t* bytes) {
+  LCT_REQUIRE(bytes, "bytes is null");
+  int rc = validate_prefill(L, HD, topk);
+  if (rc) return rc;
+  *bytes = prefill_plan(L, HD, topk).bytes;
+  return LCT_OK;
+}
+
+int lct_prefill_index_i8(const int8_t* q, const int8_t* k, int32_t* idx, int64_t L, int HD,
+                         int topk, void* ws, size_t ws_bytes, int* n_fallback, void* stream) {
+  LCT_REQUIRE(q && k && idx, "null tensor pointer");
+  LCT_REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(idx, 4), "misaligned tensor");
+  int rc = validate_prefill(L, HD, topk);
+  if (rc) return rc;
+  const size_t need = prefill_plan(L, HD, topk).bytes;
+  LCT_REQUIRE(ws != nullptr && aligned(ws, 256), "workspace must be non-null and 256-byte aligned");
+  if (ws_bytes < need) return fail(LCT_ENOWORKSPACE, "prefill index needs %zu workspace bytes, got %zu", need, ws_bytes);
+  rc = check_device();
+  if (rc) return rc;
+  return run_prefill(q, k, idx, L, HD, topk, reinterpret_cast<char*>(ws), n_fallback, as_stream(stream));
 }
 
 int lct_gist_score_bf16(const uint16_t* q, const uint16_t* gk, float* scores, int BH, int64_t Nc,
@@ -350,8 +424,6 @@ int lct_gsa_decode(const uint16_t* q, const uint16_t* gk, const uint16_t* gv,
 // ------------------------------------------------------------- driver ----
 namespace {
 
-constexpr int64_t PREFILL_BLOCK_BYTES = (int64_t)512 << 20;  // score block of the causal path
-
 struct GroupLayout {
   size_t scores, idx, topk, attn, total;
   int64_t block_rows;  // causal: query rows scored per block
@@ -366,13 +438,12 @@ GroupLayout group_layout(const lct_group_desc* d) {
     l.block_rows = rows;
     l.multi = topk_use_multi((int)rows, d->L);
   } else {
-    int64_t br = PREFILL_BLOCK_BYTES / (d->L * 4);
-    br = br < 128 ? 128 : (br / 128) * 128;
-    l.block_rows = br < d->Lq ? br : d->Lq;
+    l.block_rows = 0;
     l.multi = false;
   }
   l.scores = off;
-  off += up256((size_t)l.block_rows * d->L * sizeof(int32_t));
+  if (!d->causal) off += up256((size_t)l.block_rows * d->L * sizeof(int32_t));
+  else off += prefill_plan(d->L, d->HD, d->topk).bytes;
   l.idx = off;
   off += up256((size_t)rows * d->topk * sizeof(int32_t));
   l.topk = off;
@@ -414,8 +485,8 @@ int validate_group(const lct_group_desc* d) {
   if (d->causal) {
     LCT_REQUIRE(d->B == 1 && d->Lq == d->L, "causal prefill needs B == 1 and Lq == L");
     LCT_REQUIRE(d->valid_len == nullptr, "valid_len is not used by the causal path");
-    if (d->HD < 64) return fail(LCT_EUNSUPPORTED, "causal prefill needs HD >= 64 (MFMA scorer)");
-    if (d->L > TOPK_ROW_MAX_N) return fail(LCT_EUNSUPPORTED, "causal prefill supports L <= %lld", (long long)TOPK_ROW_MAX_N);
+    int rc = validate_prefill(d->L, d->HD, d->topk);
+    if (rc) return rc;
   } else {
     LCT_REQUIRE(d->Lq <= 64, "decode takes at most 64 query rows per batch entry");
     if (d->L * d->HD >= ((int64_t)1 << 31))
@@ -474,15 +545,8 @@ int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stre
                 "group: topk rows");
       }
     } else {
-      for (int64_t r0 = 0; r0 < d->Lq; r0 += lay.block_rows) {
-        const int64_t nr = d->Lq - r0 < lay.block_rows ? d->Lq - r0 : lay.block_rows;
-        LCT_HIP(launch_idx_score_mfma(d->qi[g] + r0 * d->HD, d->ki[g], scores, 1, (int)nr, d->L,
-                                      d->HD, r0, st),
-                "group: idx_score (prefill)");
-        LCT_HIP(launch_topk_rows(scores, LCT_I32, ib + r0 * d->topk, (int)nr, d->L, d->L, d->topk,
-                                 nullptr, 1, r0, st),
-                "group: topk rows (prefill)");
-      }
+      rc = run_prefill(d->qi[g], d->ki[g], ib, d->L, d->HD, d->topk, w + lay.scores, nullptr, st);
+      if (rc) return rc;
     }
     // Shared layers (and the Full layer itself) read the same buffer
     for (int j = 0; j < d->layers_per_group; ++j) {

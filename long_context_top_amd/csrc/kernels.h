@@ -108,6 +108,26 @@ hipError_t launch_gsa_attn(const uint16_t* q, const uint16_t* rk, const uint16_t
                            float* out, int BH, int64_t Nc, int64_t raw_cap, int kc, int tail_len,
                            float scale, const GsaPlan& plan, float* partials, hipStream_t st);
 
+// ------------------------------------------------------------ prefill ----
+// Fused causal prefill score + select (B = 1, Lq = L, HD = 256, L <= 2^16,
+// k <= 2048): scores are filtered to per-row candidate lists (PF_NSUB
+// sub-lists, PF_CROW entries in all) with a bin histogram, an exact select
+// runs on those, and rows they cannot settle go through the plain path in
+// batches of PF_FAIL_CAP.  Synchronizes `st` once (the count of such rows
+// sizes the plain work); *n_failed (if not null) receives that count.
+constexpr int PF_CROW = 5120;
+constexpr int PF_NSUB = 16;
+constexpr int PF_META = 32;  // words per row: sub-list counts, bin base, bin shift
+constexpr int PF_FAIL_CAP = 256;
+constexpr int64_t PF_MAX_L = (int64_t)1 << 16;
+constexpr int PF_MAX_K = 2048;
+struct PfLayout {
+  size_t strict, hist, meta, fails, qc, vlen, fscores, fidx, total;
+};
+size_t pf_workspace_layout(int64_t L, int HD, int kk, PfLayout* lay);
+hipError_t launch_pf_fused(const int8_t* q, const int8_t* k, int64_t L, int HD, int kk,
+                           int32_t* idx, char* ws, hipStream_t st, int* n_failed);
+
 // --------------------------------------------------------------- misc ----
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -30,7 +30,8 @@ def test_every_declared_symbol_is_exported():
         "lct_topk_select", "lct_topk_workspace_bytes", "lct_sparse_attn_gather",
         "lct_sparse_attn_workspace_bytes", "lct_gsa_attn", "lct_gsa_attn_workspace_bytes",
         "lct_gsa_decode", "lct_gsa_decode_workspace_bytes", "lct_group_run",
-        "lct_group_workspace_bytes"]), names
+        "lct_group_workspace_bytes", "lct_prefill_index_i8",
+        "lct_prefill_index_workspace_bytes"]), names
     so = ctypes.CDLL(lct.LIB_PATH)
     for n in names:
         assert hasattr(so, n), f"{n} declared in lct.h but not exported"
@@ -153,3 +154,20 @@ def test_no_device_reports_enodev():
 def test_binding_refuses_host_tensors():
     with pytest.raises((ValueError, TypeError)):
         lct.idx_score(torch.zeros((1, 1, 64), dtype=torch.int8), torch.zeros((1, 8, 64), dtype=torch.int8))
+
+
+def test_prefill_index_validation_and_sizing():
+    L = lct.lib()
+    nb = ctypes.c_size_t(0)
+    # fused shape: the candidate lists (5120 per row) dominate
+    assert L.lct_prefill_index_workspace_bytes(65536, 256, 2048, ctypes.byref(nb)) == lct.LCT_OK
+    assert nb.value >= 65536 * 5120 * 4
+    # other HD: one block of int32 score rows
+    assert L.lct_prefill_index_workspace_bytes(4096, 128, 64, ctypes.byref(nb)) == lct.LCT_OK
+    assert nb.value >= 128 * 4096 * 4
+    assert L.lct_prefill_index_workspace_bytes(4096, 32, 64, ctypes.byref(nb)) == lct.LCT_EUNSUPPORTED
+    assert L.lct_prefill_index_workspace_bytes(0, 256, 64, ctypes.byref(nb)) == lct.LCT_EINVAL
+    assert L.lct_prefill_index_workspace_bytes((1 << 18) + 1, 256, 64, ctypes.byref(nb)) == lct.LCT_EUNSUPPORTED
+    rc = L.lct_prefill_index_i8(None, None, None, 4096, 256, 64, None, 0, None, None)
+    assert rc == lct.LCT_EINVAL
+    assert "null" in lct.lib().lct_last_error().decode()
