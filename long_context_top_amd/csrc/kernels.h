@@ -110,19 +110,18 @@ hipError_t launch_gsa_attn(const uint16_t* q, const uint16_t* rk, const uint16_t
 
 // ------------------------------------------------------------ prefill ----
 // Fused causal prefill score + select (B = 1, Lq = L, HD = 256, L <= 2^16,
-// k <= 2048): scores are filtered to per-row candidate lists (PF_NSUB
-// sub-lists, PF_CROW entries in all) with a bin histogram, an exact select
-// runs on those, and rows they cannot settle go through the plain path in
-// batches of PF_FAIL_CAP.  Synchronizes `st` once (the count of such rows
-// sizes the plain work); *n_failed (if not null) receives that count.
+// k <= 2048): scores are filtered to per-row candidate lists (PF_CROW
+// entries), an exact select runs on those, rows with few earlier positions
+// take one plain block, and rows the lists cannot settle go through the
+// plain path in batches of PF_FAIL_CAP.  Synchronizes `st` once (the count
+// of such rows sizes the plain work); *n_failed (if not null) receives it.
 constexpr int PF_CROW = 5120;
-constexpr int PF_NSUB = 16;
-constexpr int PF_META = 32;  // words per row: sub-list counts, bin base, bin shift
+constexpr int PF_META = 4;  // words per row: candidates, overflow flag, threshold
 constexpr int PF_FAIL_CAP = 256;
 constexpr int64_t PF_MAX_L = (int64_t)1 << 16;
 constexpr int PF_MAX_K = 2048;
 struct PfLayout {
-  size_t strict, hist, meta, fails, qc, vlen, fscores, fidx, total;
+  size_t list, meta, fails, short_scores, qc, vlen, fscores, fidx, total;
 };
 size_t pf_workspace_layout(int64_t L, int HD, int kk, PfLayout* lay);
 hipError_t launch_pf_fused(const int8_t* q, const int8_t* k, int64_t L, int HD, int kk,

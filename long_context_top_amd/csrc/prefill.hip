@@ -17,26 +17,27 @@
 //   S1/S2  two sweeps over every 16th key: per-row min/max of the sampled
 //          scores, then a 128-bin histogram of them -> a threshold t_r with
 //          m_s samples at or above it, m_s = k/16 + 6 sqrt(k/16) + 4 (about
-//          1.56 k keys expected above it at k = 2048); rows with fewer
-//          samples keep every key;
+//          1.56 k keys expected above it at k = 2048);
 //   M      one sweep over all keys <= the row: every score >= t_r is a
-//          candidate, stored as (position << 8 | bin), bin a monotone 7-bit
-//          quantisation of the score, and counted in a per-row LDS histogram
-//          of bins.  Each lane appends to its own sub-list of the row (16 per
-//          row), so no slot is ever negotiated between lanes.
-// k_pf_select (one wave per row): the bin histogram names the bin holding
-// the k-th largest candidate; higher bins are all in; the exact scores of
-// that bin's entries (recomputed, int32) settle the rest by (score desc,
-// position asc).  Output through a position bitmap, ascending.
-// Rows the lists cannot settle (a full sub-list, a crowded bin, fewer than
-// k candidates) are listed and recomputed by the plain score + row select.
+//          candidate (position << 16 | min(score - t_r, 65535)).  Candidates
+//          go to a per-row ring in LDS; a flush wave copies whole 128-byte
+//          lines of it to the row's list in memory, so that memory sees full
+//          lines, few store instructions and no partially written lines.
+// Rows with fewer than 32 m_s earlier positions (a dense candidate stream)
+// are left to the plain path: one block of scores and a row select.
+// k_pf_select (one wave per row): the entries sit in registers; a histogram
+// of score - t_r names the bin holding the k-th largest; higher bins are all
+// in; that bin is settled exactly (an exact-score histogram, then the ties
+// by position).  Output through a position bitmap, ascending.
+// Rows the lists cannot settle (a ring or list overflow, a crowded bin,
+// fewer than k candidates) are listed and recomputed by the plain path.
 //
-// k_pf_filter: waves 0..7 compute (rows 64*(w&1).., keys 32*(w>>1).. of each
-// 128-key tile); wave 8 only brings key tiles into LDS by LDS DMA.  The
-// compute waves never wait on a global memory operation inside a sweep, so
-// their candidate stores are fire-and-forget; the helper's waits count only
-// its own DMA.  Scores start from -base_r in the MFMA accumulator, so the
-// threshold test and the bin come straight from the accumulated value.
+// k_pf_filter waves: 0..7 compute (rows 64*(w&1).., keys 16*(w>>1).. of
+// each 64-key tile); wave 8 keeps three key tiles in flight by LDS DMA;
+// wave 9 flushes the candidate rings.  The compute waves issue no global
+// memory operation inside a sweep.  Scores start from -t_r in the MFMA
+// accumulator, so the threshold test and the entry come straight from the
+// accumulated value.
 
 #include <math.h>
 #include <stddef.h>
@@ -52,17 +53,20 @@ namespace lct {
 constexpr int PF_HD = 256;                 // indexer features per row (int8)
 constexpr int PF_KS = PF_HD / 64;          // 64-byte MFMA k-steps per row
 constexpr int PF_RB = 128;                 // query rows per block
-constexpr int PF_TK = 128;                 // keys per tile
+constexpr int PF_TK = 64;                  // keys per tile
+constexpr int PF_KL = PF_TK / 64;          // 16-key blocks per compute wave and tile
+constexpr int PF_NBUF = 4;                 // key-tile buffers: 3 tiles in flight
 constexpr int PF_SS = 16;                  // sample stride (positions)
-constexpr int PF_NBIN = 128;               // histogram bins (sample and candidate)
-constexpr int PF_BIN_FILL = 96;            // the sampled range spans < 96 candidate bins
+constexpr int PF_NBIN = 128;               // histogram bins
 constexpr int PF_CW = 8;                   // compute waves
-constexpr int PF_NT = (PF_CW + 1) * 64;    // + one DMA wave
-constexpr int PF_CHUNKS = 8 * PF_KS;       // 1 KiB fragments per key tile
-constexpr int PF_SUB = PF_CROW / PF_NSUB;  // entries per sub-list; the last 8 are dump slots
+constexpr int PF_DMA_W = PF_CW;            // the DMA wave
+constexpr int PF_FL_W = PF_CW + 1;         // the flush wave
+constexpr int PF_NT = (PF_CW + 2) * 64;
+constexpr int PF_CHUNKS = (PF_TK / 16) * PF_KS;  // 1 KiB fragments per key tile
+constexpr int PF_RING = 128;               // candidate ring entries per row (LDS)
 constexpr int PF_LCAP = 512;               // select: entries of the k-th bin a wave can hold
 constexpr int PF_SEL_W = 4;                // select: waves (rows) per workgroup
-static_assert(PF_CROW % PF_NSUB == 0, "sub-lists tile the row list");
+static_assert(PF_RB * PF_RING <= PF_RB * PF_NBIN, "the rings reuse the sample histogram");
 
 typedef __attribute__((address_space(3))) void pf_lds_void;
 
@@ -78,80 +82,99 @@ LCT_DEV void pf_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-// The two key-tile buffers are objects of their own, apart from the rest:
-// the compiler then sees that the LDS DMA writes only them and does not
-// drain the (store-laden) vector memory counter before other LDS accesses.
+// The key-tile buffers are objects of their own, apart from the rest and
+// from each other: the compiler then sees that a DMA into one buffer does not
+// touch the LDS data being read, and inserts no wait on the vector memory
+// counter (which for the compute waves also counts their candidate stores).
 struct PfShared {
-  char (&kt_a)[PF_CHUNKS][1024];
-  char (&kt_b)[PF_CHUNKS][1024];
-  uint32_t (&hist)[PF_RB][PF_NBIN];  // sample histogram, then candidate bins
+  char (&kt0)[PF_CHUNKS][1024];
+  char (&kt1)[PF_CHUNKS][1024];
+  char (&kt2)[PF_CHUNKS][1024];
+  char (&kt3)[PF_CHUNKS][1024];
+  uint32_t (&hist)[PF_RB][PF_NBIN];  // sample histogram, then the candidate rings
   int32_t (&smax)[PF_RB];
   int32_t (&smin)[PF_RB];
   int32_t (&base)[PF_RB];
   int32_t (&thd)[PF_RB];
-  int32_t (&shf)[PF_RB];
+  uint32_t (&scnt)[3][PF_RB];  // candidates per row and step (steps mod 3)
 };
 
 // One sweep over key tiles [0, n_tiles) of keys at positions stride * j
-// (j = tile * 128 + ..).  The helper wave DMAs tile t+1 while the compute
-// waves run `body(tile, buf)` on tile t.  Every wave calls this.  Key rows
-// past the cache read as zeros (range-checked buffer loads; the whole offset
-// is in the per-lane register).
-template <typename Body>
-LCT_DEV void pf_sweep(PfShared& sh, __amdgpu_buffer_rsrc_t krs, int n_tiles, int stride, int wid,
-                      int lane, Body body) {
+// (j = tile * PF_TK + ..), in ascending or (desc) descending tile order.
+// The helper wave keeps PF_NBUF - 1 tiles in flight by LDS DMA while the
+// compute waves run `body(tile, buf)` on the current one.  Every wave calls
+// this; the flush wave runs `aux(step)` once per tile.  Key rows past the cache
+// read as zeros (range-checked buffer loads; the whole offset is in the
+// per-lane register).
+#define PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n)&15) | (((n) >> 4) << 14)) | 0x0F70)
+template <typename Body, typename Aux>
+LCT_DEV void pf_sweep(PfShared& sh, __amdgpu_buffer_rsrc_t krs, int n_tiles, int stride, bool desc,
+                      int wid, int lane, Body body, Aux aux) {
   const int n = lane & 15, g = lane >> 4;
-  // LDS addresses as 32-bit local pointers
   typedef __attribute__((address_space(3))) char lds_char;
-  lds_char* const kta = (lds_char*)&sh.kt_a[0][0];
-  lds_char* const ktb = (lds_char*)&sh.kt_b[0][0];
-  auto issue = [&](int b, int t) {
-    // opaque to the compiler, so that the 32 per-chunk offsets are formed
-    // per tile instead of being hoisted out of the sweep (and spilled)
+  typedef char Buf[PF_CHUNKS][1024];
+  auto issue = [&](Buf& buf, int ts) {
+    const int t = desc ? n_tiles - 1 - ts : ts;
+    // opaque to the compiler, so that the per-chunk offsets are formed per
+    // tile instead of being hoisted out of the sweep (and spilled)
     uint32_t vb = (uint32_t)((t * PF_TK + n) * stride) * PF_HD + g * 16;
     __asm__ volatile("" : "+v"(vb));
+    lds_char* const dst = (lds_char*)&buf[0][0];
     // (the instruction's immediate offset would move the LDS destination
     // too, so every offset goes into the per-lane register)
-    auto go = [&](lds_char* dst) {
 #pragma unroll
-      for (int c = 0; c < PF_CHUNKS; ++c) {
-        const uint32_t voff = vb + (uint32_t)((c / PF_KS) * 16 * stride * PF_HD + (c % PF_KS) * 64);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (pf_lds_void*)(dst + c * 1024), 16, voff, 0, 0, 0);
-      }
-    };
-    if (b) go(ktb);
-    else go(kta);
-  };
-  if (wid == PF_CW && n_tiles > 0) issue(0, 0);
-  auto step = [&](char (&cur)[PF_CHUNKS][1024], int nb, int t) {
-    if (wid == PF_CW) PF_WAIT_VM0();  // tile t has landed (the helper issues nothing else)
-    pf_barrier();
-    if (wid == PF_CW) {
-      if (t + 1 < n_tiles) issue(nb, t + 1);
-    } else {
-      body(t, cur);
+    for (int c = 0; c < PF_CHUNKS; ++c) {
+      const uint32_t voff = vb + (uint32_t)((c / PF_KS) * 16 * stride * PF_HD + (c % PF_KS) * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (pf_lds_void*)(dst + c * 1024), 16, voff, 0, 0, 0);
     }
   };
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(sh.kt_a, 1, t);
-    if (t + 1 < n_tiles) step(sh.kt_b, 0, t + 1);
+  static_assert(PF_NBUF == 4 && PF_CHUNKS == 16, "the waits below count 16 loads per tile, 2 tiles ahead");
+  if (wid == PF_DMA_W) {
+    if (n_tiles > 0) issue(sh.kt0, 0);
+    if (n_tiles > 1) issue(sh.kt1, 1);
+    if (n_tiles > 2) issue(sh.kt2, 2);
+  }
+  // step ts computes on `cur` (buffer ts % 4) while tile ts + 3 goes to
+  // `ahead3` (buffer (ts + 3) % 4, last read in step ts - 1)
+  auto step = [&](Buf& cur, Buf& ahead3, int ts) {
+    if (wid == PF_DMA_W) {
+      // tile ts has landed once at most the tiles issued after it are in flight
+      const int ahead = n_tiles - 1 - ts;
+      if (ahead >= 2) PF_WAIT_VM(32);
+      else if (ahead == 1) PF_WAIT_VM(16);
+      else PF_WAIT_VM(0);
+    }
+    pf_barrier();
+    if (wid == PF_DMA_W) {
+      if (ts + 3 < n_tiles) issue(ahead3, ts + 3);
+    } else if (wid == PF_FL_W) {
+      aux(ts);
+    } else {
+      body(desc ? n_tiles - 1 - ts : ts, ts, cur);
+    }
+  };
+  for (int ts = 0; ts < n_tiles; ts += 4) {
+    step(sh.kt0, sh.kt3, ts);
+    if (ts + 1 < n_tiles) step(sh.kt1, sh.kt0, ts + 1);
+    if (ts + 2 < n_tiles) step(sh.kt2, sh.kt1, ts + 2);
+    if (ts + 3 < n_tiles) step(sh.kt3, sh.kt2, ts + 3);
   }
   pf_barrier();  // every read of the last tile is done
 }
 
 // acc[qb][kl] = ini[qb] + scores of query rows 16qb + n (of the wave's 64)
-// against keys 32wk + 16kl + 4g + e of the tile, e = vector element.
+// against keys PF_KL*16 wk + 16kl + 4g + e of the tile, e = vector element.
 LCT_DEV void pf_tile_mfma(const char (&buf)[PF_CHUNKS][1024], const intx4 (&qf)[4][PF_KS], int wk,
-                          int lane, const int32_t (&ini)[4], intx4 (&acc)[4][2]) {
+                          int lane, const int32_t (&ini)[4], intx4 (&acc)[4][PF_KL]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = intx4{ini[i], ini[i], ini[i], ini[i]};
+    for (int j = 0; j < PF_KL; ++j) acc[i][j] = intx4{ini[i], ini[i], ini[i], ini[i]};
 #pragma unroll
-  for (int kl = 0; kl < 2; ++kl) {
+  for (int kl = 0; kl < PF_KL; ++kl) {
 #pragma unroll
     for (int ks = 0; ks < PF_KS; ++ks) {
-      const intx4 a = *reinterpret_cast<const intx4*>(&buf[(wk * 2 + kl) * PF_KS + ks][lane * 16]);
+      const intx4 a = *reinterpret_cast<const intx4*>(&buf[(wk * PF_KL + kl) * PF_KS + ks][lane * 16]);
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb)
         acc[qb][kl] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qf[qb][ks], acc[qb][kl], 0, 0, 0);
@@ -159,14 +182,35 @@ LCT_DEV void pf_tile_mfma(const char (&buf)[PF_CHUNKS][1024], const intx4 (&qf)[
   }
 }
 
-// LDS counter increment written as inline assembly: the compiler would
-// otherwise drain the vector memory counter before every LDS atomic (it
-// cannot tell it from the key DMA), which for the compute waves means
-// waiting for all of their candidate stores.  Only the counter updates go
-// this way; reads of the counters follow an explicit LDS wait and barrier.
-template <int OFF>
-LCT_DEV void pf_lds_inc(uint32_t lds_addr) {
-  __asm__ volatile("ds_add_u32 %0, %1 offset:%2" ::"v"(lds_addr), "v"(1u), "i"(OFF) : "memory");
+// LDS accesses of the flush wave, written as inline assembly with the wait
+// inside: the compiler would otherwise drain the vector memory counter before
+// every LDS access (it cannot tell them from the key DMA), which for the flush
+// wave means waiting for all of its earlier stores.
+LCT_DEV uint32_t pf_lds_ld(uint32_t a) {
+  uint32_t v;
+  __asm__ volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+LCT_DEV uintx4 pf_lds_ld4(uint32_t a) {
+  uintx4 v;
+  __asm__ volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+LCT_DEV void pf_lds_st(uint32_t a, uint32_t v) {
+  __asm__ volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+LCT_DEV void pf_lds_st4(uint32_t a, uintx4 v) {
+  __asm__ volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+// two 16-byte and two 4-byte LDS loads, one wait
+LCT_DEV void pf_lds_ld_state(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, uintx4& s0,
+                             uintx4& s1, uint32_t& c0, uint32_t& c1) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b32 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(s0), "=&v"(s1), "=&v"(c0), "=&v"(c1)
+      : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
+      : "memory");
 }
 
 // Sample-histogram bin of d = score - min over a span of `span` values:
@@ -179,29 +223,39 @@ LCT_DEV uint32_t pf_sample_bin(uint32_t d, uint32_t M) {
 
 __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ q,
                                                      const int8_t* __restrict__ k, int L, int kk,
-                                                     uint32_t* __restrict__ strict_buf,
-                                                     uint32_t* __restrict__ hist_out,
+                                                     int r_all, uint32_t* __restrict__ list,
                                                      uint32_t* __restrict__ meta, int m_s) {
-  __shared__ __attribute__((aligned(16))) char kt_a[PF_CHUNKS][1024];
-  __shared__ __attribute__((aligned(16))) char kt_b[PF_CHUNKS][1024];
+  __shared__ __attribute__((aligned(16))) char kt0[PF_CHUNKS][1024];
+  __shared__ __attribute__((aligned(16))) char kt1[PF_CHUNKS][1024];
+  __shared__ __attribute__((aligned(16))) char kt2[PF_CHUNKS][1024];
+  __shared__ __attribute__((aligned(16))) char kt3[PF_CHUNKS][1024];
   __shared__ __attribute__((aligned(16))) uint32_t hist[PF_RB][PF_NBIN];
-  __shared__ int32_t smax[PF_RB], smin[PF_RB], basev[PF_RB], thdv[PF_RB], shfv[PF_RB];
-  PfShared sh{kt_a, kt_b, hist, smax, smin, basev, thdv, shfv};
+  __shared__ int32_t smax[PF_RB], smin[PF_RB], basev[PF_RB], thdv[PF_RB];
+  __shared__ uint32_t scnt[3][PF_RB];
+  __shared__ uint32_t wl[PF_RB * PF_RING / 32];  // flush work list: lines of all rows
+  __shared__ __attribute__((aligned(16))) uint32_t fst[PF_RB][4];  // flush state per row
+  PfShared sh{kt0, kt1, kt2, kt3, hist, smax, smin, basev, thdv, scnt};
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int n = lane & 15, g = lane >> 4;
   const int wq = wid & 1, wk = wid >> 1;  // compute waves: row half, key quarter
-  const int sub = wk * 4 + g;             // the lane's sub-list in each of its rows
   const int NB = (L + PF_RB - 1) / PF_RB;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k, (int64_t)L * PF_HD);
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(strict_buf, (int64_t)L * PF_CROW * 4);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(list, (int64_t)L * PF_CROW * 4);
   const int32_t zero[4] = {0, 0, 0, 0};
+  auto no_aux = [](int) {};
 
+  // The long block first, its sweeps ascending; then the short one, its
+  // sweeps descending.  At any time the workgroups in their first block all
+  // read tile t and those in their second block all read tile NB - t, so the
+  // key tiles in flight are shared through L2 instead of being fetched once
+  // per workgroup.
   for (int half = 0; half < 2; ++half) {
-    const int rb = half == 0 ? (int)blockIdx.x : NB - 1 - (int)blockIdx.x;
-    if (half == 1 && rb <= (int)blockIdx.x) break;  // the middle block has no partner
+    const int rb = half == 0 ? NB - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    if (half == 1 && rb >= NB - 1 - (int)blockIdx.x) break;  // the middle block has no partner
+    const bool desc = half == 1;
     const int r0 = rb * PF_RB;
     const int r_last = (r0 + PF_RB < L ? r0 + PF_RB : L) - 1;
-    if (r_last < kk) continue;  // rows < k take every earlier position: nothing to score
+    if (r_last < r_all) continue;  // shorter rows: every earlier position, or the plain path
 
     // ---- query fragments (compute waves): rows r0 + 64wq + 16qb + n
     intx4 qf[4][PF_KS];
@@ -219,6 +273,7 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
     for (int i = threadIdx.x; i < PF_RB; i += PF_NT) {
       sh.smax[i] = INT32_MIN;
       sh.smin[i] = INT32_MAX;
+      sh.scnt[0][i] = sh.scnt[1][i] = sh.scnt[2][i] = 0u;
     }
     for (int i = threadIdx.x; i < PF_RB * PF_NBIN; i += PF_NT) (&sh.hist[0][0])[i] = 0u;
     __syncthreads();
@@ -234,25 +289,25 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
         mx[i] = INT32_MIN;
         mn[i] = INT32_MAX;
       }
-      pf_sweep(sh, krs, st_tiles, PF_SS, wid, lane, [&](int t, auto& buf) {
-        intx4 acc[4][2];
+      pf_sweep(sh, krs, st_tiles, PF_SS, desc, wid, lane, [&](int t, int, auto& buf) {
+        intx4 acc[4][PF_KL];
         pf_tile_mfma(buf, qf, wk, lane, zero, acc);
         const bool diag = (t * PF_TK + PF_TK - 1) * PF_SS > r0;  // a sample past some row
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
           const int row = r0 + wq * 64 + qb * 16 + n;
 #pragma unroll
-          for (int kl = 0; kl < 2; ++kl)
+          for (int kl = 0; kl < PF_KL; ++kl)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int pos = (t * PF_TK + wk * 32 + kl * 16 + g * 4 + e) * PF_SS;
+              const int pos = (t * PF_TK + wk * PF_KL * 16 + kl * 16 + g * 4 + e) * PF_SS;
               if (!diag || pos <= row) {
                 mx[qb] = max(mx[qb], acc[qb][kl][e]);
                 mn[qb] = min(mn[qb], acc[qb][kl][e]);
               }
             }
         }
-      });
+      }, no_aux);
       if (wid < PF_CW) {
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
@@ -281,8 +336,8 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
         const uint32_t span = (uint32_t)(sh.smax[rl] - lo[qb]) + 1u;
         M[qb] = span == 0u ? 1u : ((1u << 23) - 1u) / span;
       }
-      pf_sweep(sh, krs, st_tiles, PF_SS, wid, lane, [&](int t, auto& buf) {
-        intx4 acc[4][2];
+      pf_sweep(sh, krs, st_tiles, PF_SS, desc, wid, lane, [&](int t, int, auto& buf) {
+        intx4 acc[4][PF_KL];
         pf_tile_mfma(buf, qf, wk, lane, zero, acc);
         const bool diag = (t * PF_TK + PF_TK - 1) * PF_SS > r0;
 #pragma unroll
@@ -290,134 +345,205 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
           const int rl = wq * 64 + qb * 16 + n;
           const int row = r0 + rl;
 #pragma unroll
-          for (int kl = 0; kl < 2; ++kl)
+          for (int kl = 0; kl < PF_KL; ++kl)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int pos = (t * PF_TK + wk * 32 + kl * 16 + g * 4 + e) * PF_SS;
+              const int pos = (t * PF_TK + wk * PF_KL * 16 + kl * 16 + g * 4 + e) * PF_SS;
               if (!diag || pos <= row)
                 atomicAdd(&sh.hist[rl][pf_sample_bin((uint32_t)(acc[qb][kl][e] - lo[qb]), M[qb])], 1u);
             }
         }
-      });
+      }, no_aux);
     }
-    // ---- threshold, bin base and bin shift per row
+    // ---- threshold per row: the smallest score whose sample bin holds the
+    // m_s-th largest sample; rows below r_all take no candidates here
     if (threadIdx.x < PF_RB) {
       const int rl = threadIdx.x;
       const int row = r0 + rl;
-      int32_t thd = INT32_MAX, bs = 0, sf = 0;  // rows without candidates
-      if (row <= r_last && row >= kk) {
-        const int32_t lo = sh.smin[rl], hi = sh.smax[rl];
-        const uint32_t span = (uint32_t)(hi - lo) + 1u;
-        if (row / PF_SS + 1 >= m_s) {
-          const uint32_t M = ((1u << 23) - 1u) / span;
-          uint32_t acc = 0;
-          int b = PF_NBIN - 1;
-          for (; b > 0; --b) {
-            acc += sh.hist[rl][b];
-            if (acc >= (uint32_t)m_s) break;
-          }
-          // the smallest score whose sample bin is >= b: every score at or
-          // above it is a candidate
-          bs = lo + (int32_t)(((uint32_t)b * 65536u + M - 1u) / M);
-          thd = -1;  // candidate: score - bs >= 0
-        } else {
-          bs = lo - (int32_t)(span >> 2) - 1;  // every key is a candidate
-          thd = INT32_MIN;
+      int32_t thd = INT32_MAX, bs = 0;
+      if (row <= r_last && row >= r_all) {
+        const int32_t lo = sh.smin[rl];
+        const uint32_t span = (uint32_t)(sh.smax[rl] - lo) + 1u;
+        const uint32_t M = ((1u << 23) - 1u) / span;
+        uint32_t acc = 0;
+        int b = PF_NBIN - 1;
+        for (; b > 0; --b) {
+          acc += sh.hist[rl][b];
+          if (acc >= (uint32_t)m_s) break;
         }
-        while ((((int64_t)hi - bs) >> sf) >= PF_BIN_FILL) ++sf;
+        bs = lo + (int32_t)(((uint32_t)b * 65536u + M - 1u) / M);
+        thd = -1;  // candidate: score - bs >= 0
+        // the select bins score - bs by this shift: the sampled range spans
+        // fewer than 96 of its 128 bins
+        int sf = 0;
+        while ((((int64_t)sh.smax[rl] - bs) >> sf) >= 96) ++sf;
+        meta[(size_t)row * PF_META + 3] = (uint32_t)sf;
       }
       sh.base[rl] = bs;
       sh.thd[rl] = thd;
-      sh.shf[rl] = sf;
-      if (row <= r_last) {
-        meta[(size_t)row * PF_META + PF_NSUB] = (uint32_t)bs;
-        meta[(size_t)row * PF_META + PF_NSUB + 1] = (uint32_t)sf;
-      }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < PF_RB * PF_NBIN; i += PF_NT) (&sh.hist[0][0])[i] = 0u;
-    __syncthreads();
 
-    // ---- M: all keys <= the block's last row; candidates to the sub-lists
+    // ---- M: all keys <= the block's last row; candidates to the rings
+    uint32_t* const ring = &sh.hist[0][0];  // [PF_RB][PF_RING]
+    // flush-wave state per row, kept in LDS (not in registers across the
+    // sweep): candidates of the steps before the current one (all written),
+    // entries flushed, flushed count when the previous step began, overflow
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)ring;
+    const uint32_t scnt_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&sh.scnt[0][0];
+    const uint32_t wl_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&wl[0];
+    const uint32_t fst_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&fst[0][0];
+    if (wid == PF_FL_W) {
+      pf_lds_st4(fst_lds + 16 * lane, uintx4{0u, 0u, 0u, 0u});
+      pf_lds_st4(fst_lds + 16 * (lane + 64), uintx4{0u, 0u, 0u, 0u});
+    }
+    // whole lines [ff, lim) of both rows: listed as (row << 16 | line), then
+    // copied eight lanes (16 bytes each) per line; ff advances
+    auto flush_lines = [&](uintx4 (&st)[2], const uint32_t (&lim)[2]) {
+      uint32_t nl[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) nl[h] = lim[h] > st[h].y + 31u ? (lim[h] - st[h].y) >> 5 : 0u;
+      const uint32_t mine = nl[0] + nl[1];
+      const uint32_t incl = wave_incl_scan(mine);
+      const uint32_t total = __shfl(incl, 63, 64);
+      uint32_t at = incl - mine;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        for (uint32_t j = 0; j < nl[h]; ++j, ++at)
+          pf_lds_st(wl_lds + 4 * at, ((uint32_t)(lane + 64 * h) << 16) | ((st[h].y >> 5) + j));
+        st[h].y += 32u * nl[h];
+      }
+      for (uint32_t b0 = 0; b0 < total; b0 += 8) {
+        const uint32_t item = b0 + (lane >> 3), part = lane & 7;
+        if (item < total) {
+          const uint32_t w = pf_lds_ld(wl_lds + 4 * item);
+          const uint32_t rl = w >> 16, line = w & 0xFFFFu;
+          const uintx4 v = pf_lds_ld4(ring_lds + 4 * (rl * PF_RING + ((line * 32u) & (PF_RING - 1)) + part * 4));
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, lrs, (int)((((uint32_t)r0 + rl) * PF_CROW + line * 32u + part * 4) * 4u), 0, 0);
+        }
+      }
+    };
+    // state and the last finished step's counts of rows lane, lane + 64
+    auto load_state = [&](int step, uintx4 (&st)[2], uint32_t (&c)[2]) {
+      pf_lds_ld_state(fst_lds + 16 * lane, fst_lds + 16 * (lane + 64),
+                      scnt_lds + 4 * ((step % 3) * PF_RB + lane),
+                      scnt_lds + 4 * ((step % 3) * PF_RB + lane + 64), st[0], st[1], c[0], c[1]);
+    };
+    // step ts: the counts of step ts - 1 are final; the counters of step
+    // ts + 1 (last read in step ts - 1) are cleared for it
+    auto flush_step = [&](int ts) {
+      uintx4 st[2];
+      uint32_t c[2], lim[2] = {0u, 0u};
+      load_state(ts > 0 ? ts - 1 : 0, st, c);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rl = lane + 64 * h;
+        const int row = r0 + rl;
+        pf_lds_st(scnt_lds + 4 * (((ts + 1) % 3) * PF_RB + rl), 0u);
+        if (row > r_last || row < r_all) continue;
+        if (ts > 0) st[h].x += c[h];
+        // a slot written in the previous step may have wrapped onto a line
+        // that step's flush was still reading
+        if (st[h].x - st[h].z > (uint32_t)PF_RING) st[h].w = 1u;
+        st[h].z = st[h].y;
+        lim[h] = min(st[h].x, (uint32_t)PF_CROW);
+      }
+      flush_lines(st, lim);
+      pf_lds_st4(fst_lds + 16 * lane, st[0]);
+      pf_lds_st4(fst_lds + 16 * (lane + 64), st[1]);
+    };
+    int m_tiles;
     {
-      int32_t ini[4], thd[4], sf[4];
-      uint32_t off[4];
-      // byte offset of sub-list `sub` of row r0 + 64 wq + n; row 16 qb
-      // further on starts 16 qb PF_CROW entries later
-      const uint32_t off0 = ((uint32_t)(r0 + wq * 64 + n) * PF_CROW + sub * PF_SUB) * 4u;
+      int32_t ini[4], thd[4];
+      uint32_t base[4];  // candidates of the row before the current step
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
         const int rl = wq * 64 + qb * 16 + n;
         ini[qb] = -sh.base[rl];
         thd[qb] = sh.thd[rl];
-        sf[qb] = sh.shf[rl];
-        off[qb] = off0 + (uint32_t)(qb * 16 * PF_CROW * 4);
+        base[qb] = 0u;
       }
-      const uint32_t g8 = (uint32_t)(g * 4) << 8;
-      // LDS byte address of hist[64 wq + n][0]; row 16 qb further on is the
-      // instruction's immediate offset
-      const uint32_t hrow = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&hist[0][0] +
-                            (uint32_t)((wq * 64 + n) * PF_NBIN * 4);
-      auto emit = [&](auto diag_c, int t, const intx4 (&acc)[4][2]) {
+      auto emit = [&](auto diag_c, int t, int ts, const intx4 (&acc)[4][PF_KL]) {
         constexpr bool DIAG = decltype(diag_c)::value;
-        // entry = position << 8 | bin; the position's tile / wave / element
-        // part is uniform across the wave (one scalar per element)
-        uint32_t pu[2][4];
-#pragma unroll
-        for (int kl = 0; kl < 2; ++kl)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pu[kl][e] = __builtin_amdgcn_readfirstlane((uint32_t)(t * PF_TK + wk * 32 + kl * 16 + e) << 8);
-        auto per_qb = [&](auto qb_c) {
-          constexpr int qb = decltype(qb_c)::value;
-          const int rl = wq * 64 + qb * 16 + n;
-#pragma unroll
-          for (int kl = 0; kl < 2; ++kl)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int32_t d = acc[qb][kl][e];
-              bool c = d > thd[qb];
-              if (DIAG) c = c && t * PF_TK + wk * 32 + kl * 16 + g * 4 + e <= r0 + rl;
-              if (c) {
-                const int32_t bq = d >> sf[qb];
-                const uint32_t bin = (uint32_t)(bq < 0 ? 0 : bq > PF_NBIN - 1 ? PF_NBIN - 1 : bq);
-                pf_lds_inc<qb * 16 * PF_NBIN * 4>(hrow + bin * 4);
-                __builtin_amdgcn_raw_buffer_store_b32(pu[kl][e] + g8 + bin, srs, (int)off[qb], 0, 0);
-                off[qb] += 4u;
-              }
-            }
-          // a lane adds at most 8 entries per row and tile: past the usable
-          // slots, the next 8 writes land in the dump slots
-          off[qb] = min(off[qb], off0 + (uint32_t)((qb * 16 * PF_CROW + PF_SUB - 8) * 4));
-        };
-        per_qb(std::integral_constant<int, 0>{});
-        per_qb(std::integral_constant<int, 1>{});
-        per_qb(std::integral_constant<int, 2>{});
-        per_qb(std::integral_constant<int, 3>{});
-      };
-      const int m_tiles = (r_last + 1 + PF_TK - 1) / PF_TK;
-      pf_sweep(sh, krs, m_tiles, 1, wid, lane, [&](int t, auto& buf) {
-        intx4 acc[4][2];
-        pf_tile_mfma(buf, qf, wk, lane, ini, acc);
-        if (t * PF_TK + PF_TK - 1 > r0) emit(std::true_type{}, t, acc);
-        else emit(std::false_type{}, t, acc);
-      });
-      // candidate counts per (row, sub-list); a count of PF_SUB - 8 means
-      // the sub-list may have overflowed into its dump slots
-      if (wid < PF_CW) {
+        const int cs = ts % 3;
+        // candidates of this lane per row: a bit per element, then one slot
+        // reservation per row for all of them (the four reservations are
+        // unconditional, so their LDS round trips overlap), then the writes
+        uint32_t bits[4], first[4];
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
-          const int row = r0 + wq * 64 + qb * 16 + n;
-          if (row <= r_last && row >= kk)
-            meta[(size_t)row * PF_META + sub] = (off[qb] - off0 - (uint32_t)(qb * 16 * PF_CROW * 4)) >> 2;
+          const int rl = wq * 64 + qb * 16 + n;
+          uint32_t b = 0;
+#pragma unroll
+          for (int kl = 0; kl < PF_KL; ++kl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              bool c = acc[qb][kl][e] > thd[qb];
+              if (DIAG) c = c && t * PF_TK + wk * PF_KL * 16 + kl * 16 + g * 4 + e <= r0 + rl;
+              b |= c ? 1u << (kl * 4 + e) : 0u;
+            }
+          bits[qb] = b;
         }
-      }
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+          first[qb] = base[qb] + atomicAdd(&sh.scnt[cs][wq * 64 + qb * 16 + n], (uint32_t)__popc(bits[qb]));
+        const uint32_t pos0 = (uint32_t)(t * PF_TK + wk * PF_KL * 16 + g * 4);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          const int rl = wq * 64 + qb * 16 + n;
+          uint32_t slot = first[qb];
+#pragma unroll
+          for (int kl = 0; kl < PF_KL; ++kl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (bits[qb] & (1u << (kl * 4 + e))) {
+                const uint32_t d = min((uint32_t)acc[qb][kl][e], 65535u);
+                ring[rl * PF_RING + (slot & (PF_RING - 1))] = ((pos0 + kl * 16 + e) << 16) | d;
+                ++slot;
+              }
+        }
+      };
+      m_tiles = (r_last + 1 + PF_TK - 1) / PF_TK;
+      pf_sweep(sh, krs, m_tiles, 1, desc, wid, lane, [&](int t, int ts, auto& buf) {
+        intx4 acc[4][PF_KL];
+        if (ts > 0) {
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb) base[qb] += sh.scnt[(ts - 1) % 3][wq * 64 + qb * 16 + n];
+        }
+        pf_tile_mfma(buf, qf, wk, lane, ini, acc);
+        if (t * PF_TK + PF_TK - 1 > r0) emit(std::true_type{}, t, ts, acc);
+        else emit(std::false_type{}, t, ts, acc);
+      }, flush_step);
+
     }
-    __syncthreads();
-    // ---- per-row bin histogram for the select
-    for (int i = threadIdx.x; i < PF_RB * PF_NBIN; i += PF_NT) {
-      const int rl = i / PF_NBIN;
-      if (r0 + rl <= r_last) hist_out[(size_t)r0 * PF_NBIN + i] = (&sh.hist[0][0])[i];
+    // ---- the rest of every ring, the counts and the flags
+    if (wid == PF_FL_W) {
+      uintx4 st[2];
+      uint32_t c[2], lim[2] = {0u, 0u};
+      load_state(m_tiles - 1, st, c);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rl = lane + 64 * h;
+        const int row = r0 + rl;
+        if (row > r_last || row < r_all) continue;
+        st[h].x += c[h];
+        if (st[h].x - st[h].z > (uint32_t)PF_RING || st[h].x > (uint32_t)PF_CROW) st[h].w = 1u;
+        lim[h] = min(st[h].x, (uint32_t)PF_CROW);
+      }
+      flush_lines(st, lim);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rl = lane + 64 * h;
+        const int row = r0 + rl;
+        if (row > r_last || row < r_all) continue;
+        for (uint32_t i = st[h].y; i < lim[h]; ++i)
+          __builtin_amdgcn_raw_buffer_store_b32(pf_lds_ld(ring_lds + 4 * (rl * PF_RING + (i & (PF_RING - 1)))),
+                                                lrs, (int)(((uint32_t)row * PF_CROW + i) * 4u), 0, 0);
+        meta[(size_t)row * PF_META + 0] = st[h].x;
+        meta[(size_t)row * PF_META + 1] = st[h].w;
+        meta[(size_t)row * PF_META + 2] = (uint32_t)sh.base[rl];
+      }
     }
     __syncthreads();  // LDS reuse by the next block
   }
@@ -429,6 +555,7 @@ struct PfSelShared {
   uint32_t bm[PF_SEL_W][2048];  // position bitmap (65536 positions)
   uint32_t lpos[PF_SEL_W][PF_LCAP];
   int32_t lsc[PF_SEL_W][PF_LCAP];
+  uint32_t hist[PF_SEL_W][PF_NBIN];
   uint32_t sub[PF_SEL_W][256];  // exact-score histogram of the k-th bin, then its ties
   uint32_t qrow[PF_SEL_W][PF_HD / 4];
 };
@@ -472,9 +599,9 @@ LCT_DEV bool pf_find_bin(uint32_t c_hi, uint32_t c_lo, int top, uint32_t need, i
 }
 
 __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
-    const int8_t* __restrict__ q, const int8_t* __restrict__ k, int L, int kk,
-    const uint32_t* __restrict__ strict_buf, const uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ meta, int32_t* __restrict__ idx, int32_t* __restrict__ fails) {
+    const int8_t* __restrict__ q, const int8_t* __restrict__ k, int L, int kk, int r_all,
+    const uint32_t* __restrict__ list, const uint32_t* __restrict__ meta,
+    int32_t* __restrict__ idx, int32_t* __restrict__ fails) {
   __shared__ __attribute__((aligned(16))) PfSelShared sh;
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int row = blockIdx.x * PF_SEL_W + wid;
@@ -484,24 +611,43 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
     for (int j = lane; j < kk; j += 64) out[j] = j <= row ? j : -1;
     return;
   }
-  // counts of the 16 sub-lists, the bin base and shift
-  const uint32_t mw = lane < PF_NSUB + 2 ? meta[(size_t)row * PF_META + lane] : 0u;
-  const uint32_t cnt_l = lane < PF_NSUB ? mw : 0u;
-  const uint32_t total = wave_sum(cnt_l);
-  const bool full = __ballot(lane < PF_NSUB && mw >= (uint32_t)(PF_SUB - 8)) != 0;
-  const int32_t base = (int32_t)__shfl(mw, PF_NSUB, 64);
-  const int sf = (int)__shfl(mw, PF_NSUB + 1, 64);
-  bool fail = full || total < (uint32_t)kk;
-  uint32_t bsel = 0, above = 0, nsel = 0;
-  if (!fail) {
-    const uint2 hw = reinterpret_cast<const uint2*>(hist + (size_t)row * PF_NBIN)[63 - lane];
-    // hw.y = bin 127 - 2 lane, hw.x = bin 126 - 2 lane
-    if (!pf_find_bin(hw.y, hw.x, PF_NBIN - 1, (uint32_t)kk, lane, bsel, above, nsel)) fail = true;
-    if (nsel > (uint32_t)PF_LCAP) fail = true;
-  }
-  if (fail) {
+  if (row < r_all) return;  // the plain path writes these rows
+  const uint4 m = *reinterpret_cast<const uint4*>(meta + (size_t)row * PF_META);
+  const uint32_t c = m.x;
+  const int32_t base = (int32_t)m.z;
+  const int sf = (int)m.w;
+  if (m.y != 0u || c < (uint32_t)kk || c > (uint32_t)PF_CROW) {
     if (lane == 0) fails[1 + atomicAdd(&fails[0], 1)] = row;
     return;
+  }
+  // entry = position << 16 | min(score - base, 65535); bin = min(value >> sf, 127)
+  const uint32_t* lp = list + (size_t)row * PF_CROW;
+  auto bin_of = [&](uint32_t e) { return min((e & 0xFFFFu) >> sf, (uint32_t)(PF_NBIN - 1)); };
+  uint32_t* hh = sh.hist[wid];
+  for (int i = lane; i < PF_NBIN; i += 64) hh[i] = 0u;
+  pf_wave_sync();
+  // pass 1: the bin histogram (eight loads in flight per lane)
+  for (uint32_t i0 = 0; i0 < c; i0 += 512) {
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t i = i0 + j * 64 + lane;
+      e[j] = i < c ? lp[i] : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (e[j] != 0xFFFFFFFFu) atomicAdd(&hh[bin_of(e[j])], 1u);
+  }
+  pf_wave_sync();
+  uint32_t bsel, above, nsel;
+  {
+    const uint2 hw = reinterpret_cast<const uint2*>(hh)[63 - lane];
+    // hw.y = bin 127 - 2 lane, hw.x = bin 126 - 2 lane
+    const bool ok = pf_find_bin(hw.y, hw.x, PF_NBIN - 1, (uint32_t)kk, lane, bsel, above, nsel);
+    if (!ok || nsel > (uint32_t)PF_LCAP) {
+      if (lane == 0) fails[1 + atomicAdd(&fails[0], 1)] = row;
+      return;
+    }
   }
   const uint32_t need1 = (uint32_t)kk - above;  // taken from the k-th bin, 1..nsel
   uint32_t* bm = sh.bm[wid];
@@ -510,64 +656,65 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
   const uint32_t nwords = (uint32_t)((row + 1 + 31) / 32);
   for (uint32_t w = lane; w < nwords; w += 64) bm[w] = 0u;
   pf_wave_sync();
-  // bins above bsel are in; bin bsel goes to the list (two sub-lists, ten
-  // loads in flight per lane)
+  // pass 2: bins above bsel are in; bin bsel goes to the list with its value
+  bool clamped = false;
   {
-    const uint32_t* sp = strict_buf + (size_t)row * PF_CROW;
     uint32_t lcount = 0;
-    for (int s0 = 0; s0 < PF_NSUB; s0 += 2) {
-      uint32_t e[2][5];
+    for (uint32_t i0 = 0; i0 < c; i0 += 512) {
+      uint32_t e[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t c = __shfl(cnt_l, s0 + h, 64);
-#pragma unroll
-        for (int m = 0; m < 5; ++m) {
-          const uint32_t i = m * 64 + lane;
-          e[h][m] = i < c ? sp[(s0 + h) * PF_SUB + i] : 0xFFFFFFFFu;
-        }
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = i0 + j * 64 + lane;
+        e[j] = i < c ? lp[i] : 0xFFFFFFFFu;
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int m = 0; m < 5; ++m) {
-          const uint32_t b = e[h][m] & 255u, p = e[h][m] >> 8;
-          const bool valid = e[h][m] != 0xFFFFFFFFu;
-          if (valid && b > bsel) atomicOr(&bm[p >> 5], 1u << (p & 31));
-          const bool inl = valid && b == bsel;
-          const uint64_t bl = __ballot(inl);
-          if (inl) {
-            const uint32_t slot = lcount + pf_mbcnt(bl);
-            if (slot < (uint32_t)PF_LCAP) lpos[slot] = p;  // the bin holds exactly nsel entries
+      for (int j = 0; j < 8; ++j) {
+        const bool valid = e[j] != 0xFFFFFFFFu;
+        const uint32_t d = e[j] & 0xFFFFu, p = e[j] >> 16, b = bin_of(e[j]);
+        if (valid && b > bsel) atomicOr(&bm[p >> 5], 1u << (p & 31));
+        const bool inl = valid && b == bsel;
+        const uint64_t bl = __ballot(inl);
+        if (inl) {
+          const uint32_t slot = lcount + pf_mbcnt(bl);
+          if (slot < (uint32_t)PF_LCAP) {  // the bin holds exactly nsel entries
+            lpos[slot] = p;
+            lsc[slot] = (int32_t)d;
           }
-          lcount += (uint32_t)__popcll(bl);
+          clamped = clamped || d == 0xFFFFu;
         }
+        lcount += (uint32_t)__popcll(bl);
+      }
     }
   }
-  // exact scores of the bin's entries
-  sh.qrow[wid][lane] = reinterpret_cast<const uint32_t*>(q + (size_t)row * PF_HD)[lane];
+  clamped = __ballot(clamped) != 0;
   pf_wave_sync();
-  for (uint32_t j = lane; j < nsel; j += 64) {
-    const int8_t* kp = k + (size_t)lpos[j] * PF_HD;
-    int32_t s = 0;
+  if (clamped) {
+    // values clamped at 65535 are not exact: recompute the bin's scores
+    sh.qrow[wid][lane] = reinterpret_cast<const uint32_t*>(q + (size_t)row * PF_HD)[lane];
+    pf_wave_sync();
+    for (uint32_t j = lane; j < nsel; j += 64) {
+      const int8_t* kp = k + (size_t)lpos[j] * PF_HD;
+      int32_t s = 0;
 #pragma unroll
-    for (int w = 0; w < PF_HD / 16; ++w) {
-      const uintx4 kv = *reinterpret_cast<const uintx4*>(kp + w * 16);
-      const uintx4 qv = *reinterpret_cast<const uintx4*>(&sh.qrow[wid][w * 4]);
-      s = __builtin_amdgcn_sdot4((int)qv.x, (int)kv.x, s, false);
-      s = __builtin_amdgcn_sdot4((int)qv.y, (int)kv.y, s, false);
-      s = __builtin_amdgcn_sdot4((int)qv.z, (int)kv.z, s, false);
-      s = __builtin_amdgcn_sdot4((int)qv.w, (int)kv.w, s, false);
+      for (int w = 0; w < PF_HD / 16; ++w) {
+        const uintx4 kv = *reinterpret_cast<const uintx4*>(kp + w * 16);
+        const uintx4 qv = *reinterpret_cast<const uintx4*>(&sh.qrow[wid][w * 4]);
+        s = __builtin_amdgcn_sdot4((int)qv.x, (int)kv.x, s, false);
+        s = __builtin_amdgcn_sdot4((int)qv.y, (int)kv.y, s, false);
+        s = __builtin_amdgcn_sdot4((int)qv.z, (int)kv.z, s, false);
+        s = __builtin_amdgcn_sdot4((int)qv.w, (int)kv.w, s, false);
+      }
+      lsc[j] = s - base;
     }
-    lsc[j] = s;
+    pf_wave_sync();
   }
-  pf_wave_sync();
-  // the need1 best of the bin by (score desc, position asc).  Inner bins
-  // span 2^sf consecutive scores from lo_b: with sf <= 7 a 128-counter
-  // exact-score histogram finds the cut score T, and only the ties at T are
-  // ranked.
-  const int32_t lo_b = base + (int32_t)(bsel << sf);
+  // the need1 best of the bin by (score desc, position asc).  Below the
+  // top bin and with sf <= 7 the bin spans 2^sf consecutive exact values
+  // from bsel << sf: a 128-counter histogram finds the cut value T, and only
+  // the ties at T are ranked by position.
   bool ranked = false;
-  if (bsel > 0 && bsel < (uint32_t)(PF_NBIN - 1) && sf <= 7) {
+  if (!clamped && sf <= 7 && bsel < (uint32_t)(PF_NBIN - 1)) {
+    const int32_t lo_b = (int32_t)(bsel << sf);
     uint32_t* sh_sub = sh.sub[wid];
     for (int i = lane; i < 128; i += 64) sh_sub[i] = 0u;
     pf_wave_sync();
@@ -585,18 +732,18 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
       for (uint32_t j0 = 0; j0 < nsel; j0 += 64) {
         const uint32_t j = j0 + lane;
         const bool in = j < nsel;
-        const int32_t s = in ? lsc[j] : INT32_MIN;
+        const int32_t sv = in ? lsc[j] : INT32_MIN;
         const uint32_t p = in ? lpos[j] : 0u;
-        if (in && s > T) atomicOr(&bm[p >> 5], 1u << (p & 31));
-        const uint64_t bl = __ballot(in && s == T);
-        if (in && s == T) sh_sub[tcount + pf_mbcnt(bl)] = p;
+        if (in && sv > T) atomicOr(&bm[p >> 5], 1u << (p & 31));
+        const uint64_t bl = __ballot(in && sv == T);
+        if (in && sv == T) sh_sub[tcount + pf_mbcnt(bl)] = p;
         tcount += (uint32_t)__popcll(bl);
       }
       pf_wave_sync();
       for (uint32_t j = lane; j < n_eq; j += 64) {
         const uint32_t p = sh_sub[j];
         uint32_t r = 0;
-        for (uint32_t m = 0; m < n_eq; ++m) r += sh_sub[m] < p ? 1u : 0u;
+        for (uint32_t mm = 0; mm < n_eq; ++mm) r += sh_sub[mm] < p ? 1u : 0u;
         if (r < need_eq) atomicOr(&bm[p >> 5], 1u << (p & 31));
       }
       ranked = true;
@@ -605,13 +752,13 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
   if (!ranked) {
     // any bin: rank every entry of the bin against all the others
     for (uint32_t j = lane; j < nsel; j += 64) {
-      const int32_t s = lsc[j];
+      const int32_t sv = lsc[j];
       const uint32_t p = lpos[j];
       uint32_t r = 0;
-      for (uint32_t m = 0; m < nsel; ++m) {
-        const int32_t sm = lsc[m];
-        const uint32_t pm = lpos[m];
-        r += (sm > s || (sm == s && pm < p)) ? 1u : 0u;
+      for (uint32_t mm = 0; mm < nsel; ++mm) {
+        const int32_t sm = lsc[mm];
+        const uint32_t pm = lpos[mm];
+        r += (sm > sv || (sm == sv && pm < p)) ? 1u : 0u;
       }
       if (r < need1) atomicOr(&bm[p >> 5], 1u << (p & 31));
     }
@@ -664,19 +811,33 @@ __global__ void k_pf_zero_fails(int32_t* fails) {
   if (threadIdx.x == 0) fails[0] = 0;
 }
 
+// Rows with fewer than 32 m_s earlier positions are left to the plain path.
+static void pf_params(int64_t L, int kk, int* m_s, int* r_all) {
+  // sampled keys (every 16th) wanted at or above the threshold: k/16 plus
+  // six times the spread of that count, so that fewer than k candidates is rare
+  const double ks = kk / (double)PF_SS;
+  *m_s = (int)std::ceil(ks + 6.0 * std::sqrt(ks)) + 4;
+  int64_t ra = 2 * PF_SS * (int64_t)*m_s;
+  if (ra < kk) ra = kk;
+  if (ra > L) ra = L;
+  *r_all = (int)ra;
+}
+
 size_t pf_workspace_layout(int64_t L, int HD, int kk, PfLayout* lay) {
   (void)HD;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  int m_s, r_all;
+  pf_params(L, kk, &m_s, &r_all);
   PfLayout l;
   size_t off = 0;
-  l.strict = off;
+  l.list = off;
   off += up((size_t)L * PF_CROW * 4);
-  l.hist = off;
-  off += up((size_t)L * PF_NBIN * 4);
   l.meta = off;
   off += up((size_t)L * PF_META * 4);
   l.fails = off;
   off += up((size_t)(1 + L) * 4);
+  l.short_scores = off;
+  off += up((size_t)(r_all - kk > 0 ? r_all - kk : 0) * r_all * 4);
   l.qc = off;
   off += up((size_t)PF_FAIL_CAP * PF_HD);
   l.vlen = off;
@@ -695,23 +856,28 @@ hipError_t launch_pf_fused(const int8_t* q, const int8_t* k, int64_t L, int HD, 
   if (HD != PF_HD || L < 1 || L > PF_MAX_L || kk < 1 || kk > PF_MAX_K) return hipErrorInvalidValue;
   PfLayout l;
   pf_workspace_layout(L, HD, kk, &l);
-  auto strict = reinterpret_cast<uint32_t*>(ws + l.strict);
-  auto hist = reinterpret_cast<uint32_t*>(ws + l.hist);
+  int m_s, r_all;
+  pf_params(L, kk, &m_s, &r_all);
+  auto list = reinterpret_cast<uint32_t*>(ws + l.list);
   auto meta = reinterpret_cast<uint32_t*>(ws + l.meta);
   auto fails = reinterpret_cast<int32_t*>(ws + l.fails);
   hipError_t e;
   k_pf_zero_fails<<<1, 64, 0, st>>>(fails);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // rows [k, r_all): one block of plain scores against keys [0, r_all)
+  if (r_all > kk) {
+    auto ss = reinterpret_cast<int32_t*>(ws + l.short_scores);
+    if ((e = launch_idx_score_mfma(q + (size_t)kk * PF_HD, k, ss, 1, r_all - kk, r_all, PF_HD, kk, st)) != hipSuccess)
+      return e;
+    if ((e = launch_topk_rows(ss, 0, idx + (size_t)kk * kk, r_all - kk, r_all, r_all, kk, nullptr, 1, kk, st)) !=
+        hipSuccess)
+      return e;
+  }
   const int64_t NB = (L + PF_RB - 1) / PF_RB;
-  // sampled keys (every 16th) wanted at or above the threshold: k/16 plus
-  // six times the spread of that count, so that fewer than k candidates is rare
-  const double ks = kk / (double)PF_SS;
-  const int m_s = (int)std::ceil(ks + 6.0 * std::sqrt(ks)) + 4;
-  k_pf_filter<<<dim3((unsigned)((NB + 1) / 2)), PF_NT, 0, st>>>(q, k, (int)L, kk, strict, hist,
-                                                                meta, m_s);
+  k_pf_filter<<<dim3((unsigned)((NB + 1) / 2)), PF_NT, 0, st>>>(q, k, (int)L, kk, r_all, list, meta, m_s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   k_pf_select<<<dim3((unsigned)((L + PF_SEL_W - 1) / PF_SEL_W)), PF_SEL_W * 64, 0, st>>>(
-      q, k, (int)L, kk, strict, hist, meta, idx, fails);
+      q, k, (int)L, kk, r_all, list, meta, idx, fails);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // rows the lists could not settle: the count decides how much plain work follows
   int32_t nf = 0;
