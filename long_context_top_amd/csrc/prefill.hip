@@ -191,16 +191,21 @@ LCT_DEV uint32_t pf_lds_ld(uint32_t a) {
   __asm__ volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
   return v;
 }
-LCT_DEV uintx4 pf_lds_ld4(uint32_t a) {
-  uintx4 v;
-  __asm__ volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-  return v;
-}
 LCT_DEV void pf_lds_st(uint32_t a, uint32_t v) {
   __asm__ volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
 LCT_DEV void pf_lds_st4(uint32_t a, uintx4 v) {
   __asm__ volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+// one 128-byte line of a ring (eight 16-byte LDS loads, one wait)
+LCT_DEV void pf_lds_ld_line(uint32_t a, uintx4 (&v)[8]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\tds_read_b128 %2, %8 offset:32\n\t"
+      "ds_read_b128 %3, %8 offset:48\n\tds_read_b128 %4, %8 offset:64\n\tds_read_b128 %5, %8 offset:80\n\t"
+      "ds_read_b128 %6, %8 offset:96\n\tds_read_b128 %7, %8 offset:112\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a)
+      : "memory");
 }
 // two 16-byte and two 4-byte LDS loads, one wait
 LCT_DEV void pf_lds_ld_state(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, uintx4& s0,
@@ -232,7 +237,6 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
   __shared__ __attribute__((aligned(16))) uint32_t hist[PF_RB][PF_NBIN];
   __shared__ int32_t smax[PF_RB], smin[PF_RB], basev[PF_RB], thdv[PF_RB];
   __shared__ uint32_t scnt[3][PF_RB];
-  __shared__ uint32_t wl[PF_RB * PF_RING / 32];  // flush work list: lines of all rows
   __shared__ __attribute__((aligned(16))) uint32_t fst[PF_RB][4];  // flush state per row
   PfShared sh{kt0, kt1, kt2, kt3, hist, smax, smin, basev, thdv, scnt};
   const int lane = threadIdx.x & 63, wid = wave_id();
@@ -391,36 +395,24 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
     // entries flushed, flushed count when the previous step began, overflow
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)ring;
     const uint32_t scnt_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&sh.scnt[0][0];
-    const uint32_t wl_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&wl[0];
     const uint32_t fst_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&fst[0][0];
     if (wid == PF_FL_W) {
       pf_lds_st4(fst_lds + 16 * lane, uintx4{0u, 0u, 0u, 0u});
       pf_lds_st4(fst_lds + 16 * (lane + 64), uintx4{0u, 0u, 0u, 0u});
     }
-    // whole lines [ff, lim) of both rows: listed as (row << 16 | line), then
-    // copied eight lanes (16 bytes each) per line; ff advances
+    // whole lines [ff, lim) of both rows: each lane copies its own rows'
+    // lines, 128 bytes per line (one LDS round trip, eight 16-byte stores)
     auto flush_lines = [&](uintx4 (&st)[2], const uint32_t (&lim)[2]) {
-      uint32_t nl[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) nl[h] = lim[h] > st[h].y + 31u ? (lim[h] - st[h].y) >> 5 : 0u;
-      const uint32_t mine = nl[0] + nl[1];
-      const uint32_t incl = wave_incl_scan(mine);
-      const uint32_t total = __shfl(incl, 63, 64);
-      uint32_t at = incl - mine;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        for (uint32_t j = 0; j < nl[h]; ++j, ++at)
-          pf_lds_st(wl_lds + 4 * at, ((uint32_t)(lane + 64 * h) << 16) | ((st[h].y >> 5) + j));
-        st[h].y += 32u * nl[h];
-      }
-      for (uint32_t b0 = 0; b0 < total; b0 += 8) {
-        const uint32_t item = b0 + (lane >> 3), part = lane & 7;
-        if (item < total) {
-          const uint32_t w = pf_lds_ld(wl_lds + 4 * item);
-          const uint32_t rl = w >> 16, line = w & 0xFFFFu;
-          const uintx4 v = pf_lds_ld4(ring_lds + 4 * (rl * PF_RING + ((line * 32u) & (PF_RING - 1)) + part * 4));
-          __builtin_amdgcn_raw_buffer_store_b128(
-              v, lrs, (int)((((uint32_t)r0 + rl) * PF_CROW + line * 32u + part * 4) * 4u), 0, 0);
+        const uint32_t rl = (uint32_t)(lane + 64 * h);
+        while (st[h].y + 32u <= lim[h]) {
+          uintx4 v[8];
+          pf_lds_ld_line(ring_lds + 4 * (rl * PF_RING + (st[h].y & (PF_RING - 1))), v);
+          const uint32_t dst = (((uint32_t)r0 + rl) * PF_CROW + st[h].y) * 4u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) __builtin_amdgcn_raw_buffer_store_b128(v[j], lrs, (int)(dst + 16 * j), 0, 0);
+          st[h].y += 32u;
         }
       }
     };
