@@ -543,13 +543,22 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
 
 // ---- exact select per row from the candidate lists ----------------------
 
+struct PfSelWave {
+  uint32_t bm[2048];  // position bitmap (65536 positions)
+  union {
+    struct {
+      uint32_t lpos[PF_LCAP];  // the k-th bin's entries
+      int32_t lsc[PF_LCAP];
+    } l;
+    uint16_t stage[PF_MAX_K];  // then the output row, before a coalesced copy
+  } u;
+  uint32_t hist[PF_NBIN];
+  uint32_t sub[256];  // exact-score histogram of the k-th bin, then its ties
+  uint32_t qrow[PF_HD / 4];
+};
+static_assert(sizeof(uint16_t) * PF_MAX_K <= 2 * sizeof(uint32_t) * PF_LCAP, "output staging fits");
 struct PfSelShared {
-  uint32_t bm[PF_SEL_W][2048];  // position bitmap (65536 positions)
-  uint32_t lpos[PF_SEL_W][PF_LCAP];
-  int32_t lsc[PF_SEL_W][PF_LCAP];
-  uint32_t hist[PF_SEL_W][PF_NBIN];
-  uint32_t sub[PF_SEL_W][256];  // exact-score histogram of the k-th bin, then its ties
-  uint32_t qrow[PF_SEL_W][PF_HD / 4];
+  PfSelWave w[PF_SEL_W];
 };
 
 LCT_DEV void pf_wave_sync() {
@@ -557,6 +566,10 @@ LCT_DEV void pf_wave_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// LDS slot of bitmap word w: lane l reads words 32 l + j together, so the
+// low five bits are XORed with l to spread those reads over the banks
+LCT_DEV uint32_t pf_bw(uint32_t w) { return w ^ ((w >> 5) & 31u); }
 
 LCT_DEV uint32_t pf_mbcnt(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -615,20 +628,31 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
   // entry = position << 16 | min(score - base, 65535); bin = min(value >> sf, 127)
   const uint32_t* lp = list + (size_t)row * PF_CROW;
   auto bin_of = [&](uint32_t e) { return min((e & 0xFFFFu) >> sf, (uint32_t)(PF_NBIN - 1)); };
-  uint32_t* hh = sh.hist[wid];
+  PfSelWave& sw = sh.w[wid];
+  uint32_t* hh = sw.hist;
   for (int i = lane; i < PF_NBIN; i += 64) hh[i] = 0u;
   pf_wave_sync();
-  // pass 1: the bin histogram (eight loads in flight per lane)
-  for (uint32_t i0 = 0; i0 < c; i0 += 512) {
-    uint32_t e[8];
+  // 2048 entries per round: eight 16-byte loads in flight per lane; a lane
+  // holds entries i0 + 256 m + 4 lane + u
+  auto load_round = [&](uint32_t i0, uintx4 (&e)[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t i = i0 + j * 64 + lane;
-      e[j] = i < c ? lp[i] : 0xFFFFFFFFu;
+    for (int m8 = 0; m8 < 8; ++m8) {
+      const uint32_t i = i0 + 256u * m8 + 4u * lane;
+      e[m8] = i < c ? *reinterpret_cast<const uintx4*>(lp + i) : uintx4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i + u >= c) e[m8][u] = 0xFFFFFFFFu;
     }
+  };
+  // pass 1: the bin histogram
+  for (uint32_t i0 = 0; i0 < c; i0 += 2048) {
+    uintx4 e[8];
+    load_round(i0, e);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (e[j] != 0xFFFFFFFFu) atomicAdd(&hh[bin_of(e[j])], 1u);
+    for (int m8 = 0; m8 < 8; ++m8)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e[m8][u] != 0xFFFFFFFFu) atomicAdd(&hh[bin_of(e[m8][u])], 1u);
   }
   pf_wave_sync();
   uint32_t bsel, above, nsel;
@@ -642,47 +666,46 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
     }
   }
   const uint32_t need1 = (uint32_t)kk - above;  // taken from the k-th bin, 1..nsel
-  uint32_t* bm = sh.bm[wid];
-  uint32_t* lpos = sh.lpos[wid];
-  int32_t* lsc = sh.lsc[wid];
+  uint32_t* bm = sw.bm;
+  uint32_t* lpos = sw.u.l.lpos;
+  int32_t* lsc = sw.u.l.lsc;
   const uint32_t nwords = (uint32_t)((row + 1 + 31) / 32);
-  for (uint32_t w = lane; w < nwords; w += 64) bm[w] = 0u;
+  for (uint32_t w = lane; w < nwords; w += 64) bm[pf_bw(w)] = 0u;
   pf_wave_sync();
   // pass 2: bins above bsel are in; bin bsel goes to the list with its value
   bool clamped = false;
   {
     uint32_t lcount = 0;
-    for (uint32_t i0 = 0; i0 < c; i0 += 512) {
-      uint32_t e[8];
+    for (uint32_t i0 = 0; i0 < c; i0 += 2048) {
+      uintx4 e[8];
+      load_round(i0, e);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t i = i0 + j * 64 + lane;
-        e[j] = i < c ? lp[i] : 0xFFFFFFFFu;
-      }
+      for (int m8 = 0; m8 < 8; ++m8)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool valid = e[j] != 0xFFFFFFFFu;
-        const uint32_t d = e[j] & 0xFFFFu, p = e[j] >> 16, b = bin_of(e[j]);
-        if (valid && b > bsel) atomicOr(&bm[p >> 5], 1u << (p & 31));
-        const bool inl = valid && b == bsel;
-        const uint64_t bl = __ballot(inl);
-        if (inl) {
-          const uint32_t slot = lcount + pf_mbcnt(bl);
-          if (slot < (uint32_t)PF_LCAP) {  // the bin holds exactly nsel entries
-            lpos[slot] = p;
-            lsc[slot] = (int32_t)d;
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t x = e[m8][u];
+          const bool valid = x != 0xFFFFFFFFu;
+          const uint32_t d = x & 0xFFFFu, p = x >> 16, b = bin_of(x);
+          if (valid && b > bsel) atomicOr(&bm[pf_bw(p >> 5)], 1u << (p & 31));
+          const bool inl = valid && b == bsel;
+          const uint64_t bl = __ballot(inl);
+          if (inl) {
+            const uint32_t slot = lcount + pf_mbcnt(bl);
+            if (slot < (uint32_t)PF_LCAP) {  // the bin holds exactly nsel entries
+              lpos[slot] = p;
+              lsc[slot] = (int32_t)d;
+            }
+            clamped = clamped || d == 0xFFFFu;
           }
-          clamped = clamped || d == 0xFFFFu;
+          lcount += (uint32_t)__popcll(bl);
         }
-        lcount += (uint32_t)__popcll(bl);
-      }
     }
   }
   clamped = __ballot(clamped) != 0;
   pf_wave_sync();
   if (clamped) {
     // values clamped at 65535 are not exact: recompute the bin's scores
-    sh.qrow[wid][lane] = reinterpret_cast<const uint32_t*>(q + (size_t)row * PF_HD)[lane];
+    sw.qrow[lane] = reinterpret_cast<const uint32_t*>(q + (size_t)row * PF_HD)[lane];
     pf_wave_sync();
     for (uint32_t j = lane; j < nsel; j += 64) {
       const int8_t* kp = k + (size_t)lpos[j] * PF_HD;
@@ -690,7 +713,7 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
 #pragma unroll
       for (int w = 0; w < PF_HD / 16; ++w) {
         const uintx4 kv = *reinterpret_cast<const uintx4*>(kp + w * 16);
-        const uintx4 qv = *reinterpret_cast<const uintx4*>(&sh.qrow[wid][w * 4]);
+        const uintx4 qv = *reinterpret_cast<const uintx4*>(&sw.qrow[w * 4]);
         s = __builtin_amdgcn_sdot4((int)qv.x, (int)kv.x, s, false);
         s = __builtin_amdgcn_sdot4((int)qv.y, (int)kv.y, s, false);
         s = __builtin_amdgcn_sdot4((int)qv.z, (int)kv.z, s, false);
@@ -707,7 +730,7 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
   bool ranked = false;
   if (!clamped && sf <= 7 && bsel < (uint32_t)(PF_NBIN - 1)) {
     const int32_t lo_b = (int32_t)(bsel << sf);
-    uint32_t* sh_sub = sh.sub[wid];
+    uint32_t* sh_sub = sw.sub;
     for (int i = lane; i < 128; i += 64) sh_sub[i] = 0u;
     pf_wave_sync();
     for (uint32_t j = lane; j < nsel; j += 64) atomicAdd(&sh_sub[lsc[j] - lo_b], 1u);
@@ -726,7 +749,7 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
         const bool in = j < nsel;
         const int32_t sv = in ? lsc[j] : INT32_MIN;
         const uint32_t p = in ? lpos[j] : 0u;
-        if (in && sv > T) atomicOr(&bm[p >> 5], 1u << (p & 31));
+        if (in && sv > T) atomicOr(&bm[pf_bw(p >> 5)], 1u << (p & 31));
         const uint64_t bl = __ballot(in && sv == T);
         if (in && sv == T) sh_sub[tcount + pf_mbcnt(bl)] = p;
         tcount += (uint32_t)__popcll(bl);
@@ -736,7 +759,7 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
         const uint32_t p = sh_sub[j];
         uint32_t r = 0;
         for (uint32_t mm = 0; mm < n_eq; ++mm) r += sh_sub[mm] < p ? 1u : 0u;
-        if (r < need_eq) atomicOr(&bm[p >> 5], 1u << (p & 31));
+        if (r < need_eq) atomicOr(&bm[pf_bw(p >> 5)], 1u << (p & 31));
       }
       ranked = true;
     }
@@ -752,30 +775,34 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
         const uint32_t pm = lpos[mm];
         r += (sm > sv || (sm == sv && pm < p)) ? 1u : 0u;
       }
-      if (r < need1) atomicOr(&bm[p >> 5], 1u << (p & 31));
+      if (r < need1) atomicOr(&bm[pf_bw(p >> 5)], 1u << (p & 31));
     }
   }
   pf_wave_sync();
-  // emit ascending: lane l expands words [32l, 32l + 32)
+  // ascending: lane l expands words [32l, 32l + 32) into the LDS stage (the
+  // k-th bin's list is dead now), then the row goes out in coalesced stores
   uint32_t cnt = 0;
   for (int j = 0; j < 32; ++j) {
     const uint32_t w = lane * 32 + j;
-    cnt += w < nwords ? __popc(bm[w]) : 0u;
+    cnt += w < nwords ? __popc(bm[pf_bw(w)]) : 0u;
   }
   const uint32_t incl = wave_incl_scan(cnt);
   uint32_t off = incl - cnt;
+  uint16_t* stage = sw.u.stage;
+  pf_wave_sync();
   for (int j = 0; j < 32; ++j) {
     const uint32_t w = lane * 32 + j;
-    uint32_t v = w < nwords ? bm[w] : 0u;
+    uint32_t v = w < nwords ? bm[pf_bw(w)] : 0u;
     while (v) {
       const uint32_t b = __ffs(v) - 1;
       v &= v - 1;
-      if (off < (uint32_t)kk) out[off] = (int32_t)(w * 32 + b);
+      if (off < (uint32_t)kk) stage[off] = (uint16_t)(w * 32 + b);
       ++off;
     }
   }
   const uint32_t tot = __shfl(incl, 63, 64);
-  for (uint32_t j = tot + lane; j < (uint32_t)kk; j += 64) out[j] = -1;
+  pf_wave_sync();
+  for (uint32_t j = lane; j < (uint32_t)kk; j += 64) out[j] = j < tot ? (int32_t)stage[j] : -1;
 }
 
 // ---- plain path for the rows the lists could not settle -----------------
