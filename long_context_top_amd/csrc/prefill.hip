@@ -781,18 +781,23 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
   pf_wave_sync();
   // ascending: lane l expands words [32l, 32l + 32) into the LDS stage (the
   // k-th bin's list is dead now), then the row goes out in coalesced stores
-  uint32_t cnt = 0;
+  // (the lane's 32 words are read once, all loads in flight together)
+  uint32_t wv[32], cnt = 0;
+#pragma unroll
   for (int j = 0; j < 32; ++j) {
     const uint32_t w = lane * 32 + j;
-    cnt += w < nwords ? __popc(bm[pf_bw(w)]) : 0u;
+    wv[j] = w < nwords ? bm[pf_bw(w)] : 0u;
   }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) cnt += __popc(wv[j]);
   const uint32_t incl = wave_incl_scan(cnt);
   uint32_t off = incl - cnt;
   uint16_t* stage = sw.u.stage;
   pf_wave_sync();
+#pragma unroll
   for (int j = 0; j < 32; ++j) {
     const uint32_t w = lane * 32 + j;
-    uint32_t v = w < nwords ? bm[pf_bw(w)] : 0u;
+    uint32_t v = wv[j];
     while (v) {
       const uint32_t b = __ffs(v) - 1;
       v &= v - 1;
