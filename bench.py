@@ -287,34 +287,43 @@ def bench_gsa(cfg, steps, warmup):
 # --------------------------------------------------------------- prefill ----
 
 def bench_prefill_indexer(cfg, steps, warmup):
-    """Causal int8 MFMA scorer over one block of query rows (TOPS of the causal half)."""
+    """Causal index of one group at full length: int8 MFMA scores of every
+    earlier position, filtered on the fly, exact top-k per row
+    (lct_prefill_index_i8).  Throughput over the causal pairs' int8 ops."""
     import torch
 
     import long_context_top_amd as lct
     import synth.device as sd
 
     dev = torch.device("cuda", 0)
-    qi = sd.make(cfg, cfg.qi_spec(0), dev)
-    ki = sd.make(cfg, cfg.ki_spec(0), dev)
-    rows = 2048
-    r0 = cfg.L - rows  # the last block: the most work per row
-    scores = torch.empty((1, rows, cfg.L), dtype=torch.int32, device=dev)
-    qb = qi[:, r0:r0 + rows].contiguous()
-    f = lambda: lct.idx_score(qb, ki, q_pos0=r0, out=scores)
-    for _ in range(warmup):
+    qi = sd.make(cfg, cfg.qi_spec(0), dev)[0]
+    ki = sd.make(cfg, cfg.ki_spec(0), dev)[0]
+    out = torch.empty((cfg.L, cfg.topk), dtype=torch.int32, device=dev)
+    ws = lct.Workspace(dev)
+    stats = {}
+    f = lambda: lct.prefill_index(qi, ki, cfg.topk, out=out, ws=ws, stats=stats)
+    for _ in range(max(warmup, 1)):
         f()
-    ms = _timed_graph(f, steps, torch.cuda.current_stream())
-    pairs = sum(r0 + r + 1 for r in range(rows))
-    tops = 2 * cfg.HD * pairs / (ms * 1e-3) / 1e12
-    # the scores are materialised: 4 bytes stored per 2*HD int8 ops, so the
-    # kernel's bound is HBM (stores of the causal entries + the key/query reads)
-    nbytes = 4 * pairs + cfg.L * cfg.HD + rows * cfg.HD
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": cfg.name + " indexer block (last 2048 rows)", "ms": ms, "int8_tops": tops,
-            "frac": tops / INT8_PEAK_TOPS,
-            "roofline": {"bound": "hbm", "kernel": "k_idx_score_mfma", "achieved": gbs,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "bytes_per_launch": nbytes, "us_per_launch": ms * 1e3}}
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        f()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    pairs = cfg.L * (cfg.L + 1) // 2
+    ops = 2 * cfg.HD * pairs
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"workload": cfg.name + " indexer (one group, fused score filter + exact top-k)",
+            "ms_per_group": ms, "int8_tops": tops, "rows_on_plain_path": stats.get("n_fallback"),
+            "roofline": {"bound": "mfma", "kernel": "k_pf_filter + k_pf_select (+ short-row block)",
+                         "achieved": tops, "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                         "frac": tops / INT8_PEAK_TOPS, "ops_per_launch": ops,
+                         "us_per_launch": ms * 1e3}}
 
 
 def copy_calibration(steps):
