@@ -13,7 +13,8 @@ Sources:
 
 Reading: group ``g`` is layers ``[g*G, (g+1)*G)``; its first layer is the
 Full layer and owns the group's indexer inputs ``Qi_g``/``Ki_g``; the others
-are Shared.  All inputs come from the seeded generator in ``synth`` and
+are Shared.  With a free Full/Shared pattern (IndexCache article, section 3)
+group ``g`` runs from the ``g``-th Full layer up to the next one.  All inputs come from the seeded generator in ``synth`` and
 only the rows a computation reads are regenerated.
 """
 
@@ -79,6 +80,41 @@ def decode_step(cfg: C.DecodeConfig, batch=None, layers=None):
     groups = sorted({l // cfg.group for l in layers})
     idx = {g: decode_group(cfg, g, batch) for g in groups}
     outs = {l: decode_layers(cfg, l, idx[l // cfg.group], batch) for l in layers}
+    return idx, outs
+
+
+def layer_owner(layer_full) -> list:
+    """Ordinal of the Full layer whose index set each layer reads.
+
+    IndexCache article, section 2: a Shared layer inherits the index of the
+    most recent Full layer.  Section 3: the training-free greedy search drops
+    indexers one at a time by their effect on quality, so the Full layers it
+    keeps need not be evenly spaced.  Layer 0 has no earlier index to inherit
+    and must be Full.
+    """
+    owner, g = [], -1
+    for f in layer_full:
+        if f:
+            g += 1
+        elif g < 0:
+            raise ValueError("the first layer must be a Full layer")
+        owner.append(g)
+    return owner
+
+
+def decode_step_pattern(cfg: C.DecodeConfig, layer_full, batch=None, layers=None):
+    """Decode step with the Full layers placed by ``layer_full``.
+
+    Returns ``({g: idx}, {layer: out})`` where ``g`` counts the Full layers
+    in order; the ``g``-th Full layer owns the indexer inputs ``Qi_g``/``Ki_g``
+    and every layer attends over the set of its owner (:func:`layer_owner`).
+    """
+    assert len(layer_full) == cfg.n_layers
+    owner = layer_owner(layer_full)
+    layers = list(range(cfg.n_layers)) if layers is None else list(layers)
+    groups = sorted({owner[l] for l in layers})
+    idx = {g: decode_group(cfg, g, batch) for g in groups}
+    outs = {l: decode_layers(cfg, l, idx[owner[l]], batch) for l in layers}
     return idx, outs
 
 

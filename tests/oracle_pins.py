@@ -222,6 +222,57 @@ def pin_driver_sharing(decode_step, oracle_module):
         assert np.allclose(o, ref, rtol=0, atol=0)
 
 
+def pin_layer_pattern(layer_owner, decode_step_pattern, decode_step):
+    """Free Full/Shared placement: each layer reads the set of the last Full
+    layer at or before it (brute force over random patterns); every layer
+    Full is per-layer routing; the evenly spaced pattern is the group driver;
+    one indexer call per Full layer and batch row."""
+    import oracle.driver as drv
+    assert layer_owner([1, 0, 0, 0, 1, 0, 0, 0]) == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert layer_owner([1] * 6) == list(range(6))
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        n = int(rng.integers(1, 20))
+        full = [1] + [int(x) for x in rng.integers(0, 2, n - 1)]
+        got = layer_owner(full)
+        for l in range(n):
+            last = max(j for j in range(l + 1) if full[j])
+            assert got[l] == sum(full[:last]), (full, l)
+    try:
+        layer_owner([0, 1, 0])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a leading Shared layer has no index to read")
+    cfg = small_decode_cfg()
+    idx_u, out_u = decode_step(cfg)
+    idx_p, out_p = decode_step_pattern(cfg, [1, 0, 0, 0, 1, 0, 0, 0])
+    assert sorted(idx_p) == sorted(idx_u)
+    for g in idx_u:
+        assert np.array_equal(idx_p[g], idx_u[g])
+    for l in out_u:
+        assert np.array_equal(out_p[l], out_u[l])
+    pattern = [1, 1, 0, 0, 0, 1, 0, 1]
+    calls = []
+    real = drv.index_scores
+
+    def counting(*a, **k):
+        calls.append(1)
+        return real(*a, **k)
+
+    drv.index_scores = counting
+    try:
+        idx, outs = decode_step_pattern(cfg, pattern)
+    finally:
+        drv.index_scores = real
+    assert len(calls) == sum(pattern) * cfg.B
+    assert len(idx) == sum(pattern)
+    # layers 1-4 read Full layer 1's set, layer 5-6 Full layer 2's, layer 7 its own
+    for l, g in ((1, 1), (4, 1), (5, 2), (6, 2), (7, 3)):
+        assert np.array_equal(outs[l], drv.decode_layers(cfg, l, drv.decode_group(cfg, g)))
+    assert not np.array_equal(idx[1], idx[2])
+
+
 def pin_dense_when_k_covers(decode_step):
     """k >= L: sparse decode equals dense softmax(QK^T/sqrt(d))V over the whole cache."""
     import synth

@@ -148,6 +148,38 @@ def test_driver_group_mapping_mutant_caught(monkeypatch):
     _fails(P.pin_driver_sharing, step_wrong_group, oracle)
 
 
+def _owner_next_full(layer_full):
+    """Shared layers read the upcoming Full layer's set instead of the last one."""
+    full = list(layer_full)
+    owner, g = [], sum(1 for f in full if f) - 1
+    for l in range(len(full) - 1, -1, -1):
+        owner.append(g)
+        if full[l]:
+            g -= 1
+    owner = owner[::-1]
+    n_full = sum(1 for f in full if f)
+    return [min(o + (0 if full[l] else 1), n_full - 1) for l, o in enumerate(owner)]
+
+
+def _owner_counts_from_one(layer_full):
+    """Off by one: the first Full layer is numbered 1."""
+    return [o + 1 for o in DRV.layer_owner(layer_full)]
+
+
+def _step_pattern_ignored(cfg, layer_full, batch=None, layers=None):
+    """Uses the evenly spaced groups whatever the pattern says."""
+    return DRV.decode_step(cfg, batch, layers)
+
+
+@pytest.mark.parametrize("owner", [_owner_next_full, _owner_counts_from_one])
+def test_layer_owner_mutants_caught(owner):
+    _fails(P.pin_layer_pattern, owner, DRV.decode_step_pattern, DRV.decode_step)
+
+
+def test_pattern_ignored_mutant_caught():
+    _fails(P.pin_layer_pattern, DRV.layer_owner, _step_pattern_ignored, DRV.decode_step)
+
+
 # ---- prefill ----
 
 def _prefill_excludes_self(cfg, g, rows):

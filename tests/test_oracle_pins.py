@@ -20,6 +20,10 @@ def test_driver_shares_one_index_per_group():
     P.pin_driver_sharing(oracle.decode_step, oracle)
 
 
+def test_free_full_shared_pattern():
+    P.pin_layer_pattern(oracle.layer_owner, oracle.decode_step_pattern, oracle.decode_step)
+
+
 def test_decode_dense_when_k_covers_cache():
     P.pin_dense_when_k_covers(oracle.decode_step)
 
