@@ -204,12 +204,14 @@ int lct_gsa_decode_workspace_bytes(int BH, int D, int64_t Nc, int kc, size_t* by
  * temporary index buffer, Shared layers read it, the next Full layer
  * overwrites it).
  *
- * Group g = layers [g*layers_per_group, (g+1)*layers_per_group).  For each
- * group: idx_g = topk(idx_score(qi[g], ki[g])), then every layer of the
- * group runs sparse attention with that same buffer.  With `causal` set the
- * step is a causal prefill: Lq == L, query row r sits at position r, may
- * choose among positions 0..r and keeps min(topk, r+1) of them; scores are
- * produced in blocks of rows so the L x L matrix is never materialised.
+ * Group g = layers [g*layers_per_group, (g+1)*layers_per_group), or, with
+ * a layer_full pattern (IndexCache article section 3: the kept indexers
+ * need not be evenly spaced), the run of layers from the g-th Full layer to
+ * the next.  For each group: idx_g = topk(idx_score(qi[g], ki[g])), then
+ * every layer of the group runs sparse attention with that same buffer.
+ * With `causal` set the step is a causal prefill: Lq == L, query row r sits
+ * at position r, may choose among positions 0..r and keeps min(topk, r+1) of
+ * them; the L x L score matrix is never materialised.
  */
 typedef struct lct_group_desc {
   int B;                 /* batch                                          */
@@ -218,7 +220,7 @@ typedef struct lct_group_desc {
   int HD;                /* indexer features per row (H_idx * d_idx)       */
   int Hq, Hkv, D;        /* attention heads and head dim                   */
   int topk;              /* k                                              */
-  int n_layers;          /* multiple of layers_per_group                   */
+  int n_layers;          /* multiple of layers_per_group without layer_full */
   int layers_per_group;  /* layers sharing one index set (4 in IndexShare) */
   int causal;            /* 0: decode, 1: causal prefill (B == 1)          */
   float scale;           /* softmax scale, usually 1/sqrt(D)               */
@@ -235,6 +237,13 @@ typedef struct lct_group_desc {
                                      buffer is reused by every group                 */
   const int32_t** layer_idx_seen; /* NULL, or host array [n_layers]: filled with the
                                      device address of the index set each layer read */
+  const uint8_t* layer_full;      /* NULL (uniform: every layers_per_group-th layer is
+                                     Full), or host array [n_layers]: non-zero marks a
+                                     Full layer, which runs the indexer; every other
+                                     (Shared) layer reuses the index of the most recent
+                                     Full layer.  layer_full[0] must be non-zero; the
+                                     groups (qi, ki, idx_out entries) are then the Full
+                                     layers in order and layers_per_group is ignored  */
 } lct_group_desc;
 
 int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stream);

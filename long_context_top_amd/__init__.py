@@ -42,7 +42,7 @@ class GroupDesc(_c.Structure):
         ("causal", _i32), ("scale", _f32), ("valid_len", _vp), ("qi", _c.POINTER(_vp)),
         ("ki", _c.POINTER(_vp)), ("q", _c.POINTER(_vp)), ("k", _c.POINTER(_vp)),
         ("v", _c.POINTER(_vp)), ("out", _c.POINTER(_vp)), ("idx_out", _c.POINTER(_vp)),
-        ("layer_idx_seen", _c.POINTER(_vp)),
+        ("layer_idx_seen", _c.POINTER(_vp)), ("layer_full", _c.POINTER(_c.c_uint8)),
     ]
 
 
@@ -303,9 +303,15 @@ class GroupRun:
                  q: Sequence[torch.Tensor], k: Sequence[torch.Tensor], v: Sequence[torch.Tensor],
                  out: Sequence[torch.Tensor], topk: int, layers_per_group: int, scale: float,
                  causal: bool = False, valid_len: Optional[torch.Tensor] = None,
-                 idx_out: Optional[Sequence[torch.Tensor]] = None, ws: Optional[Workspace] = None):
+                 idx_out: Optional[Sequence[torch.Tensor]] = None, ws: Optional[Workspace] = None,
+                 layer_full: Optional[Sequence[int]] = None):
         n_layers = len(q)
-        n_groups = n_layers // layers_per_group
+        if layer_full is not None:
+            if len(layer_full) != n_layers:
+                raise ValueError("layer_full needs one flag per layer")
+            n_groups = sum(1 for f in layer_full if f)
+        else:
+            n_groups = n_layers // layers_per_group
         if len(qi) != n_groups or len(ki) != n_groups:
             raise ValueError("need one indexer query/key tensor per group")
         for t in qi:
@@ -342,6 +348,10 @@ class GroupRun:
         d.qi, d.ki, d.q, d.k, d.v, d.out = [_c.cast(a, _c.POINTER(_vp)) for a in self._arrs]
         d.idx_out = None if self._idx_arr is None else _c.cast(self._idx_arr, _c.POINTER(_vp))
         d.layer_idx_seen = _c.cast(self._seen, _c.POINTER(_vp))
+        self._full = None
+        if layer_full is not None:
+            self._full = (_c.c_uint8 * n_layers)(*[1 if f else 0 for f in layer_full])
+            d.layer_full = _c.cast(self._full, _c.POINTER(_c.c_uint8))
         self.desc = d
         nb = _sz()
         _check(lib().lct_group_workspace_bytes(_c.byref(d), _c.byref(nb)))
@@ -358,11 +368,15 @@ class GroupRun:
 
 
 def group_run(qi, ki, q, k, v, topk: int, layers_per_group: int, scale: float, causal=False,
-              valid_len=None, out=None, idx_out=None, ws: Optional[Workspace] = None):
-    """One decode step (or causal prefill) of a stack of layers; returns the outputs."""
+              valid_len=None, out=None, idx_out=None, ws: Optional[Workspace] = None,
+              layer_full=None):
+    """One decode step (or causal prefill) of a stack of layers; returns the outputs.
+
+    ``layer_full`` (one flag per layer, first one set) places the Full layers
+    freely; without it every ``layers_per_group``-th layer is Full."""
     if out is None:
         out = [torch.empty(t.shape, dtype=torch.float32, device=t.device) for t in q]
     run = GroupRun(qi, ki, q, k, v, out, topk, layers_per_group, scale, causal, valid_len,
-                   idx_out, ws)
+                   idx_out, ws, layer_full)
     run()
     return out, run

@@ -457,15 +457,30 @@ GroupLayout group_layout(const lct_group_desc* d) {
   return l;
 }
 
+// Full layer test and the number of groups (Full layers)
+bool layer_is_full(const lct_group_desc* d, int l) {
+  return d->layer_full ? d->layer_full[l] != 0 : l % d->layers_per_group == 0;
+}
+
+int group_count(const lct_group_desc* d) {
+  int ng = 0;
+  for (int l = 0; l < d->n_layers; ++l) ng += layer_is_full(d, l) ? 1 : 0;
+  return ng;
+}
+
 int validate_group(const lct_group_desc* d) {
   LCT_REQUIRE(d != nullptr, "descriptor is null");
   LCT_REQUIRE(d->B >= 1 && d->Lq >= 1 && d->L >= 1 && d->topk >= 1, "bad B / Lq / L / topk");
   LCT_REQUIRE(d->L < ((int64_t)1 << 31), "L must be < 2^31");
-  LCT_REQUIRE(d->layers_per_group >= 1 && d->n_layers >= 1 &&
-                  d->n_layers % d->layers_per_group == 0,
-              "n_layers must be a positive multiple of layers_per_group");
+  LCT_REQUIRE(d->n_layers >= 1, "n_layers must be >= 1");
+  if (d->layer_full) {
+    LCT_REQUIRE(d->layer_full[0] != 0, "layer_full[0] must mark a Full layer (no index to reuse yet)");
+  } else {
+    LCT_REQUIRE(d->layers_per_group >= 1 && d->n_layers % d->layers_per_group == 0,
+                "n_layers must be a positive multiple of layers_per_group");
+  }
   LCT_REQUIRE(d->qi && d->ki && d->q && d->k && d->v && d->out, "null pointer array");
-  const int ng = d->n_layers / d->layers_per_group;
+  const int ng = group_count(d);
   for (int g = 0; g < ng; ++g) {
     LCT_REQUIRE(d->qi[g] && d->ki[g], "null indexer tensor for group %d", g);
     LCT_REQUIRE(aligned(d->qi[g], 16) && aligned(d->ki[g], 16), "misaligned indexer tensor (group %d)", g);
@@ -519,43 +534,43 @@ int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stre
   hipStream_t st = as_stream(stream);
   char* w = reinterpret_cast<char*>(ws);
   int32_t* scores = reinterpret_cast<int32_t*>(w + lay.scores);
-  const int ng = d->n_layers / d->layers_per_group;
   const int rows = d->B * d->Lq;
-  for (int g = 0; g < ng; ++g) {
-    // Full layer of the group: indexer + select into the group's index buffer
-    int32_t* ib = (d->idx_out && d->idx_out[g]) ? d->idx_out[g] : reinterpret_cast<int32_t*>(w + lay.idx);
-    if (!d->causal) {
-      if (lay.multi) {
-        const int t1 = score_plan(d->B, d->Lq, d->L, d->HD).tiles;
-        const TopkMultiLayout tl = topk_multi_layout(rows, d->L, t1);
-        char* tw = w + lay.topk;
-        LCT_HIP(launch_idx_score_stream(d->qi[g], d->ki[g], scores, d->B, d->Lq, d->L, d->HD, -1,
-                                        reinterpret_cast<uint32_t*>(tw + tl.mm),
-                                        reinterpret_cast<TopkRowState*>(tw + tl.state),
-                                        reinterpret_cast<uint32_t*>(tw + tl.hist), d->valid_len, st),
-                "group: idx_score");
-        LCT_HIP(launch_topk_select_multi(scores, LCT_I32, ib, rows, d->L, d->L, d->topk,
-                                         d->valid_len, d->Lq, tw, tl, st),
-                "group: topk select");
+  int32_t* ib = nullptr;
+  for (int l = 0, g = -1; l < d->n_layers; ++l) {
+    if (layer_is_full(d, l)) {
+      // a Full layer: indexer + select into its group's index buffer
+      ++g;
+      ib = (d->idx_out && d->idx_out[g]) ? d->idx_out[g] : reinterpret_cast<int32_t*>(w + lay.idx);
+      if (!d->causal) {
+        if (lay.multi) {
+          const int t1 = score_plan(d->B, d->Lq, d->L, d->HD).tiles;
+          const TopkMultiLayout tl = topk_multi_layout(rows, d->L, t1);
+          char* tw = w + lay.topk;
+          LCT_HIP(launch_idx_score_stream(d->qi[g], d->ki[g], scores, d->B, d->Lq, d->L, d->HD, -1,
+                                          reinterpret_cast<uint32_t*>(tw + tl.mm),
+                                          reinterpret_cast<TopkRowState*>(tw + tl.state),
+                                          reinterpret_cast<uint32_t*>(tw + tl.hist), d->valid_len, st),
+                  "group: idx_score");
+          LCT_HIP(launch_topk_select_multi(scores, LCT_I32, ib, rows, d->L, d->L, d->topk,
+                                           d->valid_len, d->Lq, tw, tl, st),
+                  "group: topk select");
+        } else {
+          LCT_HIP(launch_idx_score_stream(d->qi[g], d->ki[g], scores, d->B, d->Lq, d->L, d->HD, -1,
+                                          nullptr, nullptr, nullptr, nullptr, st),
+                  "group: idx_score");
+          LCT_HIP(launch_topk_rows(scores, LCT_I32, ib, rows, d->L, d->L, d->topk, d->valid_len, d->Lq, -1, st),
+                  "group: topk rows");
+        }
       } else {
-        LCT_HIP(launch_idx_score_stream(d->qi[g], d->ki[g], scores, d->B, d->Lq, d->L, d->HD, -1,
-                                        nullptr, nullptr, nullptr, nullptr, st),
-                "group: idx_score");
-        LCT_HIP(launch_topk_rows(scores, LCT_I32, ib, rows, d->L, d->L, d->topk, d->valid_len, d->Lq, -1, st),
-                "group: topk rows");
+        rc = run_prefill(d->qi[g], d->ki[g], ib, d->L, d->HD, d->topk, w + lay.scores, nullptr, st);
+        if (rc) return rc;
       }
-    } else {
-      rc = run_prefill(d->qi[g], d->ki[g], ib, d->L, d->HD, d->topk, w + lay.scores, nullptr, st);
-      if (rc) return rc;
     }
-    // Shared layers (and the Full layer itself) read the same buffer
-    for (int j = 0; j < d->layers_per_group; ++j) {
-      const int l = g * d->layers_per_group + j;
-      if (d->layer_idx_seen) d->layer_idx_seen[l] = ib;
-      rc = run_attn(d->q[l], d->k[l], d->v[l], ib, d->out[l], d->B, d->Lq, d->Hq, d->Hkv, d->L,
-                    d->topk, d->scale, w + lay.attn, st);
-      if (rc) return rc;
-    }
+    // the Full layer and the Shared layers after it read the same buffer
+    if (d->layer_idx_seen) d->layer_idx_seen[l] = ib;
+    rc = run_attn(d->q[l], d->k[l], d->v[l], ib, d->out[l], d->B, d->Lq, d->Hq, d->Hkv, d->L,
+                  d->topk, d->scale, w + lay.attn, st);
+    if (rc) return rc;
   }
   return LCT_OK;
 }

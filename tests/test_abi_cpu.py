@@ -141,6 +141,17 @@ def test_group_validation_and_sizes():
     causal_bad.k, causal_bad.v, causal_bad.out = d.k, d.v, d.out
     assert L.lct_group_workspace_bytes(ctypes.byref(causal_bad), ctypes.byref(nb)) == lct.LCT_EINVAL
     assert L.lct_group_run(ctypes.byref(d), FAKE, 1024, None) == lct.LCT_ENOWORKSPACE
+    # a Full/Shared pattern lifts the multiple-of-group rule; its first layer must be Full
+    U8 = ctypes.POINTER(ctypes.c_uint8)
+    pat = (ctypes.c_uint8 * 6)(1, 0, 1, 1, 0, 0)
+    free = _desc(n_layers=6, layers_per_group=0)
+    arr_3 = (ctypes.c_void_p * 3)(*([FAKE.value] * 3))  # one indexer tensor per Full layer
+    free.qi = free.ki = ctypes.cast(arr_3, P)
+    free.q, free.k, free.v, free.out = d.q, d.k, d.v, d.out
+    free.layer_full = ctypes.cast(pat, U8)
+    assert L.lct_group_workspace_bytes(ctypes.byref(free), ctypes.byref(nb)) == 0
+    pat[0] = 0
+    assert L.lct_group_workspace_bytes(ctypes.byref(free), ctypes.byref(nb)) == lct.LCT_EINVAL
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")

@@ -92,3 +92,49 @@ def test_causal_prefill_small():
     sample = [0, 1, 5, 63, 64, 65, 300, 699]
     ref = oracle.prefill_attention_rows(cfg, 3, sample, want[sample])
     assert np.abs(out[3][0, sample] - ref).max() < ATOL
+
+
+def _run_pattern(cfg, layer_full):
+    n_full = sum(layer_full)
+    qi = [sd.make(cfg, cfg.qi_spec(g)) for g in range(n_full)]
+    ki = [sd.make(cfg, cfg.ki_spec(g)) for g in range(n_full)]
+    _, _, q, k, v = _inputs(cfg)
+    idx_out = [torch.full((cfg.B, cfg.Lq, cfg.topk), -7, dtype=torch.int32, device="cuda")
+               for _ in range(n_full)]
+    out, run = lct.group_run(qi, ki, q, k, v, cfg.topk, cfg.group, cfg.scale, causal=cfg.causal,
+                             idx_out=idx_out, layer_full=layer_full)
+    torch.cuda.synchronize()
+    return idx_out, [host(t) for t in idx_out], [host(t) for t in out], run
+
+
+def test_decode_free_full_shared_pattern():
+    """Full layers at uneven places (IndexCache greedy-search patterns): each
+    layer attends over the set of the last Full layer at or before it."""
+    pattern = [1, 0, 0, 1, 0, 1, 1, 0, 0, 0]
+    cfg = C.DecodeConfig("pattern", 6060, B=2, Lq=2, L=5000, n_layers=len(pattern), group=1,
+                         Hq=8, Hkv=2, D=128, H_idx=4, d_idx=64, topk=256)
+    announce(f"{cfg.name} {pattern}")
+    bufs, idx, out, run = _run_pattern(cfg, pattern)
+    owner = oracle.layer_owner(pattern)
+    for g in range(sum(pattern)):
+        assert np.array_equal(idx[g], oracle.decode_group(cfg, g)), g
+    for l in range(cfg.n_layers):
+        ref = oracle.decode_layers(cfg, l, idx[owner[l]])
+        assert np.abs(out[l] - ref).max() < ATOL, l
+    seen = run.layer_index_addresses()
+    assert seen == [bufs[owner[l]].data_ptr() for l in range(cfg.n_layers)]
+
+
+def test_causal_prefill_free_pattern():
+    pattern = [1, 1, 0]
+    cfg = C.DecodeConfig("prefill_pattern", 7171, B=1, Lq=600, L=600, n_layers=3, group=1, Hq=8,
+                         Hkv=2, D=128, H_idx=4, d_idx=64, topk=64, causal=True)
+    announce(f"{cfg.name} {pattern}")
+    _, idx, out, _ = _run_pattern(cfg, pattern)
+    rows = list(range(cfg.L))
+    for g in range(2):
+        assert np.array_equal(idx[g][0], oracle.prefill_index_rows(cfg, g, rows)), g
+    sample = [0, 1, 63, 64, 65, 599]
+    for l, g in ((1, 1), (2, 1)):
+        ref = oracle.prefill_attention_rows(cfg, l, sample, idx[g][0][sample])
+        assert np.abs(out[l][0, sample] - ref).max() < ATOL, l
