@@ -158,7 +158,7 @@ int lct_sparse_attn_gather(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* idx, float* out, int B, int Lq, int Hq, int Hkv,
                            int D, int64_t L, int kk, float scale, void* ws, size_t ws_bytes,
                            void* stream);
-int lct_sparse_attn_workspace_bytes(int B, int Lq, int Hq, int Hkv, int D, int kk,
+int lct_sparse_attn_workspace_bytes(int B, int Lq, int Hq, int Hkv, int D, int64_t L, int kk,
                                     size_t* bytes);
 
 /*

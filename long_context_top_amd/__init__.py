@@ -58,7 +58,8 @@ _SIGS = {
     "lct_topk_workspace_bytes": ([_i32, _i64, _i32, _c.POINTER(_sz)], _i32),
     "lct_sparse_attn_gather": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i32,
                                 _f32, _vp, _sz, _vp], _i32),
-    "lct_sparse_attn_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _c.POINTER(_sz)], _i32),
+    "lct_sparse_attn_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i64, _i32, _c.POINTER(_sz)],
+                                        _i32),
     "lct_gsa_attn": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32,
                       _f32, _vp, _sz, _vp], _i32),
     "lct_gsa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32,
@@ -239,7 +240,7 @@ def sparse_attn_gather(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: t
         out = torch.empty((B, Lq, Hq, D), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
     nb = _sz()
-    _check(lib().lct_sparse_attn_workspace_bytes(B, Lq, Hq, Hkv, D, kk, _c.byref(nb)))
+    _check(lib().lct_sparse_attn_workspace_bytes(B, Lq, Hq, Hkv, D, L, kk, _c.byref(nb)))
     buf = _ws(ws).get(nb.value)
     _check(lib().lct_sparse_attn_gather(_p(q), _p(k), _p(v), _p(idx), _p(out), B, Lq, Hq, Hkv, D, L,
                                         kk, scale, _p(buf), buf.numel(), _stream()))

@@ -109,8 +109,8 @@ int run_topk(const void* scores, int dtype, int32_t* idx, int rows, int64_t n, i
 }
 
 // --------------------------------------------------------- attention plan ----
-size_t attn_scratch_bytes(int B, int Lq, int Hkv, int kk) {
-  return attn_plan(B, Lq, Hkv, kk).part_bytes;
+size_t attn_scratch_bytes(int B, int Lq, int Hq, int Hkv, int kk, int64_t L) {
+  return attn_ws_bytes(attn_plan(B, Lq, Hq, Hkv, kk, L));
 }
 
 constexpr int64_t PREFILL_BLOCK_BYTES = (int64_t)512 << 20;  // score block of the causal path
@@ -260,10 +260,12 @@ int lct_topk_select(const void* scores, int dtype, int32_t* idx, int rows, int64
                   as_stream(stream));
 }
 
-int lct_sparse_attn_workspace_bytes(int B, int Lq, int Hq, int Hkv, int D, int kk, size_t* bytes) {
+int lct_sparse_attn_workspace_bytes(int B, int Lq, int Hq, int Hkv, int D, int64_t L, int kk,
+                                    size_t* bytes) {
   LCT_REQUIRE(bytes, "bytes is null");
-  LCT_REQUIRE(B >= 1 && Lq >= 1 && Hq >= 1 && Hkv >= 1 && D >= 1 && kk >= 1, "bad shape");
-  *bytes = attn_scratch_bytes(B, Lq, Hkv, kk);
+  LCT_REQUIRE(B >= 1 && Lq >= 1 && Hq >= 1 && Hkv >= 1 && D >= 1 && kk >= 1 && L >= 1, "bad shape");
+  LCT_REQUIRE(Hq % Hkv == 0, "Hq must be a multiple of Hkv");
+  *bytes = attn_scratch_bytes(B, Lq, Hq, Hkv, kk, L);
   return LCT_OK;
 }
 
@@ -302,7 +304,7 @@ static int validate_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v
 static int run_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
                     float* out, int B, int Lq, int Hq, int Hkv, int64_t L, int kk, float scale,
                     char* partials, hipStream_t st) {
-  const AttnPlan plan = attn_plan(B, Lq, Hkv, kk);
+  const AttnPlan plan = attn_plan(B, Lq, Hq, Hkv, kk, L);
   LCT_HIP(launch_sparse_attn(q, k, v, idx, out, B, Lq, Hq, Hkv, L, kk, scale, plan,
                              reinterpret_cast<float*>(partials), st),
           "sparse_attn_gather");
@@ -315,7 +317,7 @@ int lct_sparse_attn_gather(const uint16_t* q, const uint16_t* k, const uint16_t*
                            void* stream) {
   int rc = validate_attn(q, k, v, idx, out, B, Lq, Hq, Hkv, D, L, kk, scale);
   if (rc) return rc;
-  const size_t need = attn_scratch_bytes(B, Lq, Hkv, kk);
+  const size_t need = attn_scratch_bytes(B, Lq, Hq, Hkv, kk, L);
   LCT_REQUIRE(need == 0 || (ws != nullptr && aligned(ws, 256)), "workspace must be non-null and 256-byte aligned");
   if (ws_bytes < need) return fail(LCT_ENOWORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
   rc = check_device();
@@ -452,7 +454,7 @@ GroupLayout group_layout(const lct_group_desc* d) {
     off += up256(topk_multi_layout((int)rows, d->L, t1).total);
   }
   l.attn = off;
-  off += up256(attn_scratch_bytes(d->B, d->Lq, d->Hkv, d->topk));
+  off += up256(attn_scratch_bytes(d->B, d->Lq, d->Hq, d->Hkv, d->topk, d->L));
   l.total = off;
   return l;
 }

@@ -5,22 +5,28 @@
 // split decode with a log-sum-exp merge of partial results and one KV-tile
 // load serving every query head of its KV group (SSA article, section 6).
 //
-// Work unit: one (batch, query row, KV head).  Each wave owns one unit and a
-// contiguous slice of its index row, and works through it 64 selected
-// positions at a time; the waves of a workgroup are independent (no
-// workgroup barrier, each wave has its own LDS region):
-//   * the 16-byte pieces of the gathered K rows go straight into the A
-//     operand of v_mfma_f32_16x16x32_bf16 (lane = row lane%16, 8 features at
+// Work unit: one (batch, query row, KV head) and a run of its index entries.
+// Each wave owns one unit and works through the run 64 selected positions at
+// a time; the waves of a workgroup are independent (no workgroup barrier,
+// each wave has its own LDS region):
+//   * gathers read 16 tokens x 64 contiguous bytes per instruction (a quad
+//     of lanes per token piece, the rate the address unit takes);
+//   * the K pieces are moved by ds_bpermute into the A operand of
+//     v_mfma_f32_16x16x32_bf16 (lane = row lane%16, 8 features at
 //     8*(lane/16)); the G query heads of the KV group form the B operand, so
 //     S^T[token][head] comes out in C layout (4 tokens x 1 head per lane);
 //   * fp32 online softmax per head (running max and sum, exp2 domain);
 //   * O^T += V^T P^T on the same MFMA: P^T from the C fragments is already in
 //     B-operand layout (the k order inside the MFMA is a fixed permutation of
-//     32 tokens); the gathered V pieces go from global memory straight into
-//     LDS (global_load_lds_dwordx4, no registers) and are read back
-//     transposed with ds_read_b64_tr_b16 (4 tokens x 4 features per lane).
-// A wave that owns a whole index row writes the normalised output; otherwise
-// it writes an (O, m, l) partial and k_split_merge combines the slices.
+//     32 tokens); the V pieces go from memory straight into LDS (buffer loads
+//     to LDS, no registers) and are read back transposed with
+//     ds_read_b64_tr_b16 (4 tokens x 4 features per lane);
+//   * software pipelined: the next 64 positions' gathers are in flight while
+//     this iteration's MFMA and softmax run.
+// Few rows (decode): the index row is split over several waves, each writes
+// an (O, m, l) partial and k_split_merge combines them.  Many rows over a
+// long cache (prefill): the positions are cut into segments and the units
+// ordered segment-major so the gathers hit L2 (k_sparse_attn_seg below).
 
 #include "common.h"
 #include "kernels.h"
@@ -33,6 +39,11 @@ constexpr int ATT_NW = 4;                // independent waves per workgroup
 constexpr int ATT_PS = ATT_D + 4;        // partial row: O[D], m, l, 2 pad (16-byte rows)
 constexpr int ATT_TARGET_WAVES = 1024;   // split short index rows until this many waves
 constexpr float LOG2E = 1.4426950408889634f;
+#ifndef ATT_SEG_SHIFT
+#define ATT_SEG_SHIFT 14                 // log2 positions per segment (segmented path)
+#endif
+constexpr int ATT_SEG_MAX = 64;          // segments per row at most (the segment grows)
+constexpr int64_t ATT_SEG_MIN_UNITS = 16384;  // (row, KV head) pairs that take the segmented path
 
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -41,10 +52,33 @@ typedef const __attribute__((address_space(1))) void global_cvoid;
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima): the LDS DMA
 // writes are counted by vmcnt and the compiler does not track them
 constexpr int WAITCNT_VM0 = 0x0F70;
+// s_waitcnt vmcnt(n): vmcnt is 6 bits, low 4 in [3:0], high 2 in [15:14]
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int WAITCNT_VM8 = waitcnt_vm(8);
+constexpr int WAITCNT_VM24 = waitcnt_vm(24);
+// s_waitcnt lgkmcnt(0) (vmcnt, expcnt at their maxima)
+constexpr int WAITCNT_LGKM0 = 0xC07F;
 
-AttnPlan attn_plan(int B, int Lq, int Hkv, int kk) {
+AttnPlan attn_plan(int B, int Lq, int Hq, int Hkv, int kk, int64_t L) {
   AttnPlan p;
-  const int64_t units = (int64_t)B * Lq * Hkv;
+  const int G = Hq / Hkv;
+  const int64_t rows = (int64_t)B * Lq;
+  const int64_t units = rows * Hkv;
+  p.nseg = 0;
+  p.seg_shift = 0;
+  p.bnd_bytes = 0;
+  // many rows over a long cache: position segments (see k_sparse_attn_seg)
+  if (units >= ATT_SEG_MIN_UNITS && L > ((int64_t)2 << ATT_SEG_SHIFT)) {
+    int shift = ATT_SEG_SHIFT;
+    while (((L - 1) >> shift) + 1 > ATT_SEG_MAX) ++shift;
+    p.seg_shift = shift;
+    p.nseg = (int)(((L - 1) >> shift) + 1);
+    p.splits = 1;
+    p.per_split = kk;
+    p.part_bytes = (size_t)units * p.nseg * G * ATT_PS * sizeof(float);
+    p.bnd_bytes = (size_t)rows * (p.nseg + 1) * sizeof(int32_t);
+    return p;
+  }
   const int64_t pieces = (kk + 31) / 32;  // 32-position pieces of an index row
   int64_t splits = (ATT_TARGET_WAVES + units - 1) / units;
   if (splits > MERGE_MAX_SPLITS) splits = MERGE_MAX_SPLITS;
@@ -62,6 +96,281 @@ AttnPlan attn_plan(int B, int Lq, int Hkv, int kk) {
 
 LCT_DEV void compiler_fence() { __asm__ __volatile__("" ::: "memory"); }
 
+// Index entries [e0, e0 + 64) gate the gathers of one iteration: lane l
+// holds entry e0 + 16j + l/4 for j < 4, the token whose row its gathers
+// read (clamped into the slice, so in bounds; entries past the slice are
+// masked by the caller).
+LCT_DEV void attn_entries(const int32_t* ix, int e0, int e_end, int tk, int (&pos)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + 16 * j + tk;
+    pos[j] = ix[e < e_end ? e : e_end - 1];
+  }
+}
+
+LCT_DEV bf16x8 lane_permute(bf16x8 x, int src_byte) {
+  const int4 w = __builtin_bit_cast(int4, x);
+  int4 r;
+  r.x = __builtin_amdgcn_ds_bpermute(src_byte, w.x);
+  r.y = __builtin_amdgcn_ds_bpermute(src_byte, w.y);
+  r.z = __builtin_amdgcn_ds_bpermute(src_byte, w.z);
+  r.w = __builtin_amdgcn_ds_bpermute(src_byte, w.w);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Query fragment (B operand): the G query heads of KV head kvh of query row
+// br; lanes of head slots >= G load head G-1 and are zeroed.
+template <int G>
+LCT_DEV void attn_query(const uint16_t* q, int64_t br, int Hq, int kvh, int hl, int kg,
+                        bf16x8 (&qf)[4]) {
+  constexpr int D = ATT_D;
+  const int hq = hl < G ? hl : G - 1;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    qf[st] = *reinterpret_cast<const bf16x8*>(q + ((br * Hq) + kvh * G + hq) * D + st * 32 + kg * 8);
+    if (hl >= G) qf[st] = bf16x8{};
+  }
+}
+
+// Gather roles.  Each load instruction reads 16 tokens x 64 bytes (a
+// 32-feature slice st of each row), lane l taking 16-byte chunk ck = l%4 of
+// token tk = l/4: the four lanes of a quad read one contiguous 64-byte
+// piece, so the address unit takes a quad per cycle (one row per lane, as
+// the MFMA operand layout would have it, costs a cycle per lane).  K chunks
+// land in registers and are moved to the A-operand layout (lane (hl, kg):
+// token hl, chunk kg) with ds_bpermute; V chunks go to LDS by DMA, lane l's
+// 16 bytes at 16*l, the chunk order inside a quad swizzled (chunk
+// ck ^ 2*(tk/4 % 2)) so the transposed reads of lanes 0-31 fall on distinct
+// banks.
+
+// Positions of one iteration's tokens: -1 where the entry is past the slice,
+// -1 or outside [0, L); msk[j] bit 4t set <=> token t of block j is valid.
+LCT_DEV bool attn_mask(int e0, int e_end, int64_t L, int tk, const int (&pos)[4], int (&pp)[4],
+                       uint64_t (&msk)[4]) {
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + 16 * j + tk;
+    int p = pos[j];
+    if (e >= e_end || p < 0 || (int64_t)p >= L) p = -1;
+    pp[j] = p;
+    msk[j] = __ballot(p >= 0);
+    any = any || msk[j] != 0;
+  }
+  return any;  // uniform over the wave
+}
+
+// K chunks of one iteration into registers; masked tokens read row 0 (in
+// bounds) and are masked in the softmax.
+LCT_DEV void attn_gather_k(__amdgpu_buffer_rsrc_t krs, int row_bytes, int ck, const int (&pp)[4],
+                           bf16x8 (&kr)[4][4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int roff = (pp[j] >= 0 ? pp[j] : 0) * row_bytes + ck * 16;  // < 2 GiB
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      kr[j][st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, roff + st * 64, 0, 0));
+  }
+}
+
+// V chunks of blocks 2h, 2h+1 of one iteration into half h of the wave's
+// LDS tile by DMA (no registers).  The halves are separate LDS objects, so
+// the compiler can tell that reads of one do not wait for DMA into the other.
+// (Buffer loads rather than global ones: the compiler counts a global load
+// that writes LDS as touching both memories and then waits for every
+// outstanding load whenever any register load result is needed.)
+LCT_DEV void attn_gather_v_half(__amdgpu_buffer_rsrc_t vrs, int row_bytes, int cv,
+                                const int (&pp)[4], int h, char (*vh)[4][1024]) {
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int j = 2 * h + jj;
+    // byte offset of the chunk inside the batch entry's V (< 2 GiB)
+    const int roff = (pp[j] >= 0 ? pp[j] : 0) * row_bytes + cv * 16;  // < 2 GiB
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vh[jj][st][0], 16, roff + st * 64, 0, 0, 0);
+  }
+}
+
+// Per-lane constants of the gather and transposed-read layouts.
+struct AttnLanes {
+  int hl, kg;  // MFMA layout: row / column lane%16, k-group lane/16
+  int tk, ck;  // gather layout: token lane/4, chunk lane%4
+  int cv;      // swizzled V chunk
+  int bsrc;    // ds_bpermute byte address of the lane holding (token hl, chunk kg)
+  int tr0, tr1;  // transposed-read byte offsets for even / odd feature tiles
+};
+
+LCT_DEV AttnLanes attn_lanes(int lane) {
+  AttnLanes a;
+  a.hl = lane & 15;
+  a.kg = lane >> 4;
+  a.tk = lane >> 2;
+  // K chunk order inside a quad: tokens 8-15 take their chunks rotated by
+  // two, so the 32 source lanes of each half of a ds_bpermute below are
+  // distinct modulo 32
+  a.ck = (lane & 3) ^ ((a.tk >> 3) << 1);
+  a.cv = (lane & 3) ^ (((a.tk >> 2) & 1) << 1);
+  a.bsrc = (4 * a.hl + (a.kg ^ ((a.hl >> 3) << 1))) * 4;
+  // transposed read of 16-feature tile dt of block j: this lane supplies
+  // token T = 4*kg + hl/4, features 16*dt + 4*(hl%4) .. +3: chunk
+  // c = 2*(dt%2) + (hl%4)/2 of slice dt/2, stored at lane 4T + (c ^ 2*(kg%2)),
+  // byte 8*(hl%2) of it
+  const int trb = 64 * (4 * a.kg + (a.hl >> 2)) + 16 * ((a.hl & 3) >> 1) + 8 * (a.hl & 1);
+  a.tr0 = trb + 32 * (a.kg & 1);
+  a.tr1 = trb + 32 * ((a.kg & 1) ^ 1);
+  return a;
+}
+
+// One iteration (64 index entries) of the online softmax.  On entry kr
+// holds this iteration's K chunks (gather layout), the V tile is in flight
+// or landed, pp/msk describe its tokens and pos holds the next iteration's
+// entries.  With NEXT the next iteration's K gathers are issued once this
+// iteration's K has gone through the MFMAs, its V gathers (two halves) once
+// the matching half of this iteration's V tile has been read, so both
+// overlap this iteration's MFMA and softmax work; on exit kr, pp, msk and
+// pos describe the next iteration.
+template <int G, bool NEXT>
+LCT_DEV void attn_iter(const int32_t* ix, int e0, int e_end, int64_t L, const AttnLanes& a,
+                       int (&pos)[4], int (&pp)[4], uint64_t (&msk)[4], bf16x8 (&kr)[4][4],
+                       const bf16x8 (&qf)[4], __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                       int row_bytes, float scale_log2, char (*vta)[4][1024],
+                       char (*vtb)[4][1024], float& m, float& lsum, floatx4 (&o)[ATT_D / 16]) {
+  constexpr int D = ATT_D;
+  // S^T = K Q^T per 16-token block; sacc[j][e] = S^T[token 16j + 4kg + e][head hl]
+  floatx4 sacc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lane_permute(kr[j][st], a.bsrc), qf[st], sacc[j],
+                                                         0, 0, 0);
+  }
+  uint64_t mskc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mskc[j] = msk[j];
+  int ppn[4];
+  if (NEXT) {
+    attn_mask(e0 + ATT_STEP, e_end, L, a.tk, pos, ppn, msk);
+    attn_gather_k(krs, row_bytes, a.ck, ppn, kr);
+    attn_entries(ix, e0 + 2 * ATT_STEP, e_end, a.tk, pos);
+  }
+  float z[4][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      z[j][e] = ((mskc[j] >> (16 * a.kg + 4 * e)) & 1) ? sacc[j][e] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, z[j][e]);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  const float mnew = fmaxf(m, tmax);
+  // no valid token yet (a run of skipped entries): any finite reference
+  // keeps alpha and the weights at 0 instead of NaN
+  const float mref = mnew == -INFINITY ? 0.f : mnew;
+  const float alpha = __builtin_amdgcn_exp2f(m - mref);
+  // the weights enter the PV product as bf16; the denominator sums the same
+  // rounded weights so that the normalisation is consistent
+  __bf16 pw[4][4];
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pw[j][e] = (__bf16)__builtin_amdgcn_exp2f(z[j][e] - mref);
+      psum += (float)pw[j][e];
+    }
+  lsum = lsum * alpha + psum;
+  m = mnew;
+  // the running maximum moves ever more rarely: rescale only when it did
+  if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
+  }
+  // O^T += V^T P^T, 32 tokens (blocks 2h, 2h+1: half h of the tile) per
+  // MFMA: the MFMA's k = 8kg + jj is token 4kg + jj of block 2h (jj < 4) or
+  // 4kg + jj - 4 of block 2h+1, in both operands
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    char(*vh)[4][1024] = h == 0 ? vta : vtb;
+    // half h of this iteration's V tile has landed once at most 24 memory
+    // operations issued after its DMA are outstanding: after half 0 come
+    // half 1 (8) and, with NEXT, the next K gathers (16); after half 1 come,
+    // with NEXT, the next K gathers and the next half 0 (24)
+    if (NEXT) __builtin_amdgcn_s_waitcnt(WAITCNT_VM24);
+    else if (h == 0) __builtin_amdgcn_s_waitcnt(WAITCNT_VM8);
+    else __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+    compiler_fence();
+    bf16x8 va[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int tro = (dt & 1) ? a.tr1 : a.tr0;
+      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)&vh[0][dt >> 1][tro]);
+      const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)&vh[1][dt >> 1][tro]);
+      // whole-vector reinterpretation (element-wise bf16 casts of the read
+      // results are mis-assembled by the compiler)
+      va[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    if (NEXT) {
+      // half h is free once its reads have returned: the next iteration's
+      // blocks 2h, 2h+1 go there
+      __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+      compiler_fence();
+      attn_gather_v_half(vrs, row_bytes, a.cv, ppn, h, vh);
+    }
+    bf16x8 pf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pf[e] = pw[2 * h][e];
+      pf[4 + e] = pw[2 * h + 1][e];
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pf, o[dt], 0, 0, 0);
+  }
+  compiler_fence();
+  if (NEXT) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pp[j] = ppn[j];
+  }
+}
+
+// Online softmax attention of one query row's G heads over the index
+// entries [e_begin, e_end) of its row `ix`, 64 entries per iteration, into
+// the running (m, lsum, O^T).  `pos` holds the first iteration's entries
+// (attn_entries).  Entries that are -1 or outside [0, L) are skipped.
+template <int G>
+LCT_DEV void attn_span(const int32_t* ix, int e_begin, int e_end, int (&pos)[4],
+                       const bf16x8 (&qf)[4], const uint16_t* kbase, const uint16_t* vbase,
+                       size_t row_stride, int64_t L, float scale_log2, char (*vta)[4][1024],
+                       char (*vtb)[4][1024], int lane, float& m, float& lsum,
+                       floatx4 (&o)[ATT_D / 16]) {
+  if (e_begin >= e_end) return;
+  const AttnLanes a = attn_lanes(lane);
+  int pp[4];
+  uint64_t msk[4];
+  attn_mask(e_begin, e_end, L, a.tk, pos, pp, msk);
+  // K and V rows of this KV head (a batch entry's cache is < 2 GiB, so
+  // 32-bit offsets; the range check only guards, every access is in bounds)
+  const int row_bytes = (int)(row_stride * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, L * (int64_t)row_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, L * (int64_t)row_bytes);
+  bf16x8 kr[4][4];
+  attn_gather_k(krs, row_bytes, a.ck, pp, kr);
+  attn_entries(ix, e_begin + ATT_STEP, e_end, a.tk, pos);  // the next iteration's entries
+  attn_gather_v_half(vrs, row_bytes, a.cv, pp, 0, vta);
+  attn_gather_v_half(vrs, row_bytes, a.cv, pp, 1, vtb);
+  int e0 = e_begin;
+  for (; e0 + ATT_STEP < e_end; e0 += ATT_STEP)
+    attn_iter<G, true>(ix, e0, e_end, L, a, pos, pp, msk, kr, qf, krs, vrs, row_bytes, scale_log2, vta,
+                       vtb, m, lsum, o);
+  attn_iter<G, false>(ix, e0, e_end, L, a, pos, pp, msk, kr, qf, krs, vrs, row_bytes, scale_log2, vta,
+                      vtb, m, lsum, o);
+}
+
 template <int G>
 __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -70,8 +379,10 @@ __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn(
     int per_split, float* __restrict__ part) {
   constexpr int D = ATT_D;
   // per wave, per (16-token block j, 32-feature slice st): the 1 KiB that one
-  // LDS DMA instruction writes, lane l's 16 bytes at 16*l
-  __shared__ __attribute__((aligned(16))) char vt[ATT_NW][4][4][1024];
+  // LDS DMA instruction writes, lane l's 16 bytes at 16*l; blocks 0-1 and
+  // 2-3 in separate objects
+  __shared__ __attribute__((aligned(16))) char vta[ATT_NW][2][4][1024];
+  __shared__ __attribute__((aligned(16))) char vtb[ATT_NW][2][4][1024];
   const int lane = threadIdx.x & 63, wid = wave_id();
   // wave order: KV head fastest, then split, then (b, r): the waves of a
   // workgroup read the same selected positions of neighbouring KV heads, so
@@ -88,143 +399,20 @@ __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn(
   const int e_begin = split * per_split;
   const int e_end = min(kk, e_begin + per_split);
   const int32_t* ix = idx + br * kk;
-  char(*vw)[4][1024] = vt[wid];
 
   // index entries of the first iteration (they gate the gathers), then q
   int pos[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = e_begin + 16 * j + hl;
-    pos[j] = ix[e < e_end ? e : e_end - 1];
-  }
-  // query fragment (B operand): lanes of head slots >= G load head G-1, zeroed
+  attn_entries(ix, e_begin, e_end, lane >> 2, pos);
   bf16x8 qf[4];
-  {
-    const int hq = hl < G ? hl : G - 1;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      qf[st] = *reinterpret_cast<const bf16x8*>(q + ((br * Hq) + kvh * G + hq) * D + st * 32 + kg * 8);
-      if (hl >= G) qf[st] = bf16x8{};
-    }
-  }
+  attn_query<G>(q, br, Hq, kvh, hl, kg, qf);
   float m = -INFINITY, lsum = 0.f;
   floatx4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
   const size_t row_stride = (size_t)Hkv * D;  // elements between positions
-  const uint16_t* kbase = k + ((size_t)b * L * Hkv + kvh) * D;
-  const uint16_t* vbase = v + ((size_t)b * L * Hkv + kvh) * D;
-  // transposed read of 16-feature tile dt of block j: this lane supplies
-  // token 4*kg + hl/4, features 16*dt + 4*(hl%4) .. +3, which the DMA put in
-  // slice dt/2, lane (4*kg + hl/4) + 16*(2*(dt%2) + (hl%4)/2), byte 8*(hl%2)
-  const int tr_off = 16 * ((4 * kg + (hl >> 2)) + 16 * ((hl & 3) >> 1)) + 8 * (hl & 1);
-
-  for (int e0 = e_begin; e0 < e_end; e0 += ATT_STEP) {
-    int pp[4];
-    uint64_t msk[4];
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + 16 * j + hl;
-      int p = pos[j];
-      if (e >= e_end || p < 0 || (int64_t)p >= L) p = -1;  // padding / out of range: skipped
-      pp[j] = p;
-      msk[j] = __ballot(p >= 0);
-      any = any || msk[j] != 0;
-    }
-    // next iteration's index entries (clamped, so always in bounds)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + ATT_STEP + 16 * j + hl;
-      pos[j] = ix[e < e_end ? e : e_end - 1];
-    }
-    if (!any) continue;  // uniform over the wave
-    // gathers; masked positions read row 0 (in bounds) and are masked below.
-    // K pieces into registers (MFMA A operand), V pieces into LDS by DMA.
-    bf16x8 kf[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const size_t roff = (size_t)(pp[j] >= 0 ? pp[j] : 0) * row_stride + kg * 8;
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        kf[j][st] = *reinterpret_cast<const bf16x8*>(kbase + roff + st * 32);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const size_t roff = (size_t)(pp[j] >= 0 ? pp[j] : 0) * row_stride + kg * 8;
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        __builtin_amdgcn_global_load_lds((global_cvoid*)(vbase + roff + st * 32),
-                                         (lds_void*)&vw[j][st][0], 16, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any MFMA
-    // S^T = K Q^T per 16-token block
-    floatx4 sacc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][st], qf[st], sacc[j], 0, 0, 0);
-    }
-    // sacc[j][e] = S^T[token 16j + 4kg + e][head hl]
-    float z[4][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        z[j][e] = ((msk[j] >> (kg * 4 + e)) & 1) ? sacc[j][e] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, z[j][e]);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(m, tmax);  // finite: the iteration has a valid position
-    const float alpha = exp2f(m - mnew);
-    // the weights enter the PV product as bf16; the denominator sums the same
-    // rounded weights so that the normalisation is consistent
-    __bf16 pw[4][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pw[j][e] = (__bf16)exp2f(z[j][e] - mnew);
-        psum += (float)pw[j][e];
-      }
-    lsum = lsum * alpha + psum;
-    m = mnew;
-    // the V pieces have landed in LDS once vmcnt drains
-    __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
-    compiler_fence();
-    // O^T += V^T P^T, 32 tokens (blocks 2h, 2h+1) per MFMA: the MFMA's
-    // k = 8kg + jj is token 4kg + jj of block 2h (jj < 4) or 4kg + jj - 4 of
-    // block 2h+1, in both operands
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = pw[2 * h][e];
-        pf[4 + e] = pw[2 * h + 1][e];
-      }
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4v*)&vw[2 * h][dt >> 1][512 * (dt & 1) + tr_off]);
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4v*)&vw[2 * h + 1][dt >> 1][512 * (dt & 1) + tr_off]);
-        // whole-vector reinterpretation (element-wise bf16 casts of the
-        // read results are mis-assembled by the compiler)
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[dt], 0, 0, 0);
-      }
-    }
-    compiler_fence();
-  }
+  attn_span<G>(ix, e_begin, e_end, pos, qf, k + ((size_t)b * L * Hkv + kvh) * D,
+               v + ((size_t)b * L * Hkv + kvh) * D, row_stride, L, scale_log2, vta[wid], vtb[wid], lane, m,
+               lsum, o);
 
   // o[dt][e] = O^T[d = 16dt + 4kg + e][head hl]; lsum: this lane's share
   lsum += __shfl_xor(lsum, 16, 64);
@@ -289,15 +477,213 @@ hipError_t launch_split_merge(const float* part, float* out, int64_t units, int 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Segmented path for many query rows over a long cache (causal prefill).
+//
+// Every (row, position) pair of the index sets reads that position's K and V
+// pieces; with many rows the same K/V rows are read again and again, and the
+// rate is set by where they come from.  A layer's K/V (128 MiB at 64K
+// positions, 4 KV heads) fits the last-level cache but not an XCD's 4 MiB L2.
+// The positions are therefore cut into segments of 2^shift positions (a KV
+// head's K and V of one segment: 8 MiB at 16384 positions; shorter segments
+// hit L2 more often but cost more partials, and 16384 measured fastest at
+// 64K positions), and the work units (row, KV head, segment) are ordered
+// segment-major with the KV head
+// fastest at workgroup granularity: workgroup w takes KV head w % Hkv, and
+// since the dispatcher deals workgroups round-robin over the 8 XCDs, each XCD
+// sees one KV head (Hkv dividing 8) and, at any time, the segment the grid
+// has reached: the gathers hit its L2.  Each unit attends over the index
+// entries of its row that fall in its segment (a contiguous run, index rows
+// being ascending) and writes an (O, m, l) partial; a row whose entries all
+// fall in one segment (short rows, or rows that are not ascending, which are
+// given one segment covering the whole row) writes its output directly.
+// k_seg_merge combines the partials (log-sum-exp merge, SSA article section 6).
+
+// bnd[row][j] (j = 0..nseg) = index entries of the row whose position lies
+// below segment j's start; bnd[row][nseg] = the row's valid entries.  Needs
+// the row ascending over its valid entries (positions in [0, L)) followed
+// only by -1; any other row gets {0, kk, ..., kk}: one segment, whole row.
+// One wave per row.
+__global__ __launch_bounds__(256) void k_seg_bounds(const int32_t* __restrict__ idx,
+                                                    int32_t* __restrict__ bnd, int64_t rows, int kk,
+                                                    int64_t L, int shift, int nseg) {
+  const int lane = threadIdx.x & 63;
+  const int64_t br = (int64_t)blockIdx.x * 4 + wave_id();
+  if (br >= rows) return;
+  const int32_t* ix = idx + br * kk;
+  int32_t* bb = bnd + br * (nseg + 1);
+  // pass 1: the row's shape (-2: before the first entry)
+  bool bad = false;
+  int carry = -2;
+  for (int c = 0; c < kk; c += 64) {
+    const int e = c + lane;
+    const int p = e < kk ? ix[e] : -1;
+    int prv = __shfl(p, (lane + 63) & 63, 64);
+    if (lane == 0) prv = carry;
+    carry = __shfl(p, 63, 64);
+    const bool valid = p >= 0 && (int64_t)p < L;
+    bool ok;
+    if (prv == -2) ok = valid || p == -1;
+    else if (prv == -1) ok = p == -1;
+    else ok = p == -1 || (valid && p > prv);
+    bad = bad || (e < kk && !ok);
+  }
+  if (__ballot(bad) != 0) {
+    for (int j = lane; j <= nseg; j += 64) bb[j] = j == 0 ? 0 : kk;
+    return;
+  }
+  // pass 2: entry e opens segments (key(e-1), key(e)]; key = segment of the
+  // position, nseg for -1 and for the virtual entry kk, -1 before entry 0
+  int kcarry = -1;
+  for (int c = 0; c <= kk; c += 64) {
+    const int e = c + lane;
+    const int p = e < kk ? ix[e] : -1;
+    const int key = (e >= kk || p < 0) ? nseg : (p >> shift);
+    int kprv = __shfl(key, (lane + 63) & 63, 64);
+    if (lane == 0) kprv = kcarry;
+    kcarry = __shfl(key, 63, 64);
+    if (e <= kk)
+      for (int j = kprv + 1; j <= key; ++j) bb[j] = e;
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn_seg(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ bnd, float* __restrict__ out, float* __restrict__ part,
+    int64_t rows, int64_t groups, int Lq, int Hq, int Hkv, int64_t L, int kk, float scale_log2,
+    int nseg) {
+  constexpr int D = ATT_D;
+  __shared__ __attribute__((aligned(16))) char vta[ATT_NW][2][4][1024];
+  __shared__ __attribute__((aligned(16))) char vtb[ATT_NW][2][4][1024];
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  // workgroup -> (segment, group of ATT_NW rows, KV head), KV head fastest
+  const int64_t wg = blockIdx.x;
+  const int kvh = (int)(wg % Hkv);
+  const int64_t t = wg / Hkv;
+  const int seg = (int)(t / groups);
+  const int64_t br = (t % groups) * ATT_NW + wid;  // b * Lq + r
+  if (br >= rows) return;  // the whole wave; nothing below waits on other waves
+  const int32_t* bb = bnd + br * (nseg + 1);
+  const int e_begin = bb[seg], e_end = bb[seg + 1], n = bb[nseg];
+  const bool whole = e_end - e_begin == n;  // the row's only non-empty segment
+  if (e_begin == e_end && !(n == 0 && seg == 0)) return;
+  const int64_t b = br / Lq;
+  const int hl = lane & 15, kg = lane >> 4;
+  const int32_t* ix = idx + br * kk;
+
+  int pos[4];
+  attn_entries(ix, e_begin, e_end > e_begin ? e_end : e_begin + 1, lane >> 2, pos);
+  bf16x8 qf[4];
+  attn_query<G>(q, br, Hq, kvh, hl, kg, qf);
+  float m = -INFINITY, lsum = 0.f;
+  floatx4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const size_t row_stride = (size_t)Hkv * D;
+  attn_span<G>(ix, e_begin, e_end, pos, qf, k + ((size_t)b * L * Hkv + kvh) * D,
+               v + ((size_t)b * L * Hkv + kvh) * D, row_stride, L, scale_log2, vta[wid], vtb[wid], lane, m,
+               lsum, o);
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (hl >= G) return;
+  if (whole) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    float* op = out + ((br * Hq) + kvh * G + hl) * D + kg * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(op + dt * 16) = o[dt] * inv;
+  } else {
+    float* pp = part + (((br * Hkv + kvh) * nseg + seg) * G + hl) * ATT_PS;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(pp + dt * 16 + kg * 4) = o[dt];
+    if (kg == 0) *reinterpret_cast<float2*>(pp + D) = float2{m, lsum};
+  }
+}
+
+// Merge of the segment partials of one row (one workgroup; wave w takes KV
+// heads w, w + 4, ...): O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j over
+// the row's non-empty segments, M = max_j m_j.  Rows written directly by
+// their only non-empty segment are skipped.
+template <int G>
+__global__ __launch_bounds__(256) void k_seg_merge(const float* __restrict__ part,
+                                                   const int32_t* __restrict__ bnd,
+                                                   float* __restrict__ out, int Hq, int Hkv,
+                                                   int nseg) {
+  constexpr int D = ATT_D;
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int64_t br = blockIdx.x;
+  const int32_t* bb = bnd + br * (nseg + 1);
+  const int n = bb[nseg];
+  const int cnt = lane < nseg ? bb[lane + 1] - bb[lane] : 0;
+  if (__ballot(lane < nseg && cnt == n) != 0) return;  // settled by one unit
+  const uint64_t live = __ballot(cnt > 0);
+  for (int h = wid; h < Hkv; h += 4) {
+    const float* pb = part + (br * Hkv + h) * (int64_t)nseg * G * ATT_PS;
+    for (int c = lane; c < G * (D / 4); c += 64) {
+      const int hq = c / (D / 4), d4 = 4 * (c % (D / 4));
+      float M = -INFINITY;
+      for (uint64_t w = live; w; w &= w - 1) {
+        const int j = __builtin_ctzll(w);
+        M = fmaxf(M, pb[(j * G + hq) * ATT_PS + D]);
+      }
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+      float lt = 0.f;
+      for (uint64_t w = live; w; w &= w - 1) {
+        const int j = __builtin_ctzll(w);
+        const float* pr = pb + (j * G + hq) * ATT_PS;
+        const float wt = exp2f(pr[D] - M);
+        lt += wt * pr[D + 1];
+        acc += wt * *reinterpret_cast<const floatx4*>(pr + d4);
+      }
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      *reinterpret_cast<floatx4*>(out + ((br * Hq) + h * G + hq) * D + d4) = acc * inv;
+    }
+  }
+}
+
+static hipError_t launch_sparse_attn_seg(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                         const int32_t* idx, float* out, int B, int Lq, int Hq,
+                                         int Hkv, int64_t L, int kk, float sl2, const AttnPlan& plan,
+                                         float* ws, hipStream_t st) {
+  const int G = Hq / Hkv;
+  const int64_t rows = (int64_t)B * Lq;
+  const int64_t groups = (rows + ATT_NW - 1) / ATT_NW;
+  float* part = ws;
+  int32_t* bnd = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + attn_bnd_offset(plan));
+  k_seg_bounds<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(idx, bnd, rows, kk, L, plan.seg_shift,
+                                                                  plan.nseg);
+  const int64_t wgs = (int64_t)plan.nseg * groups * Hkv;
+  if (wgs >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+#define LCT_ATT(GG)                                                                                \
+  k_sparse_attn_seg<GG><<<dim3((unsigned)wgs), ATT_NW * 64, 0, st>>>(q, k, v, idx, bnd, out, part, rows, \
+                                                                     groups, Lq, Hq, Hkv, L, kk, sl2,  \
+                                                                     plan.nseg);                       \
+  k_seg_merge<GG><<<dim3((unsigned)rows), 256, 0, st>>>(part, bnd, out, Hq, Hkv, plan.nseg)
+  switch (G) {
+    case 1: LCT_ATT(1); break;
+    case 2: LCT_ATT(2); break;
+    case 4: LCT_ATT(4); break;
+    case 8: LCT_ATT(8); break;
+    case 16: LCT_ATT(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef LCT_ATT
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* idx, float* out, int B, int Lq, int Hq, int Hkv,
                               int64_t L, int kk, float scale, const AttnPlan& plan,
                               float* partials, hipStream_t st) {
   const int G = Hq / Hkv;
+  const float sl2 = scale * LOG2E;
+  if (plan.nseg > 0) return launch_sparse_attn_seg(q, k, v, idx, out, B, Lq, Hq, Hkv, L, kk, sl2, plan,
+                                                   partials, st);
   const int64_t units = (int64_t)B * Lq * Hkv;
   const int64_t waves = units * plan.splits;
   const dim3 grid((unsigned)((waves + ATT_NW - 1) / ATT_NW));
-  const float sl2 = scale * LOG2E;
 #define LCT_ATT(GG)                                                                          \
   k_sparse_attn<GG><<<grid, ATT_NW * 64, 0, st>>>(q, k, v, idx, out, units, Lq, Hq, Hkv, L, kk, \
                                                   sl2, plan.splits, plan.per_split, partials)

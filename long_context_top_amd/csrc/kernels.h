@@ -82,8 +82,15 @@ struct AttnPlan {
   int splits;       // waves per (b, row, kv head)
   int per_split;    // index entries per wave (a multiple of 32)
   size_t part_bytes;
+  int nseg;         // > 0: segmented path with nseg position segments of 2^seg_shift
+  int seg_shift;
+  size_t bnd_bytes;  // segmented path: per-row segment bounds after the partials
 };
-AttnPlan attn_plan(int B, int Lq, int Hkv, int kk);
+AttnPlan attn_plan(int B, int Lq, int Hq, int Hkv, int kk, int64_t L);
+inline size_t attn_bnd_offset(const AttnPlan& p) { return (p.part_bytes + 255) / 256 * 256; }
+inline size_t attn_ws_bytes(const AttnPlan& p) {
+  return p.nseg > 0 ? attn_bnd_offset(p) + p.bnd_bytes : p.part_bytes;
+}
 // With plan.splits > 1 the kernel writes (O, m, l) partials and a merge
 // kernel combines them (log-sum-exp merge).
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -182,3 +182,18 @@ def test_prefill_index_validation_and_sizing():
     rc = L.lct_prefill_index_i8(None, None, None, 4096, 256, 64, None, 0, None, None)
     assert rc == lct.LCT_EINVAL
     assert "null" in lct.lib().lct_last_error().decode()
+
+
+def test_sparse_attn_workspace_sizes():
+    L = lct.lib()
+    nb = ctypes.c_size_t()
+    # one decode row per batch entry: split partials only
+    assert L.lct_sparse_attn_workspace_bytes(8, 1, 32, 4, 128, 131072, 2048, ctypes.byref(nb)) == 0
+    small = nb.value
+    assert small <= 8 * 4 * 64 * 16 * 132 * 4
+    # 64K causal prefill rows: position-segment partials (O, m, l per row, KV head,
+    # query head and segment; at least two segments) and per-row bounds
+    assert L.lct_sparse_attn_workspace_bytes(1, 65536, 32, 4, 128, 65536, 2048, ctypes.byref(nb)) == 0
+    assert nb.value >= 65536 * 4 * 2 * 8 * 130 * 4 + 65536 * 3 * 4
+    # Hq not a multiple of Hkv
+    assert L.lct_sparse_attn_workspace_bytes(1, 1, 6, 4, 128, 1000, 16, ctypes.byref(nb)) == lct.LCT_EINVAL

@@ -138,3 +138,18 @@ def test_causal_prefill_free_pattern():
     for l, g in ((1, 1), (2, 1)):
         ref = oracle.prefill_attention_rows(cfg, l, sample, idx[g][0][sample])
         assert np.abs(out[l][0, sample] - ref).max() < ATOL, l
+
+
+def test_causal_prefill_segmented_attention():
+    """33000 positions, 4 KV heads: the prefill attention takes the position-
+    segment path; rows inside the first segment and rows spanning several
+    are checked against the oracle."""
+    cfg = C.DecodeConfig("prefill_seg", 8181, B=1, Lq=33000, L=33000, n_layers=1, group=1, Hq=16,
+                         Hkv=4, D=128, H_idx=4, d_idx=64, topk=512, causal=True)
+    announce(cfg.name)
+    idx, out, _ = _run(cfg)
+    sample = [0, 1, 511, 512, 4095, 4096, 16383, 16384, 16385, 25000, 32767, 32768, 32999]
+    want = oracle.prefill_index_rows(cfg, 0, sample)
+    assert np.array_equal(idx[0][0][sample], want)
+    ref = oracle.prefill_attention_rows(cfg, 0, sample, want)
+    assert np.abs(out[0][0, sample] - ref).max() < ATOL

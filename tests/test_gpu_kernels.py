@@ -204,6 +204,57 @@ def test_sparse_attn_empty_rows_are_zero():
     assert np.all(got == 0.0)
 
 
+def test_sparse_attn_segmented_path_row_shapes():
+    """Many rows over a long cache take the position-segment path (16800
+    (row, KV head) pairs, 40000 positions: several segments).  Rows of every
+    shape: ascending with -1 padding, inside one segment, skipping a segment,
+    shuffled, with duplicates, with -1 in the middle, empty, full."""
+    B, Lq, Hq, Hkv, L, kk = 2, 2100, 8, 4, 40000, 200
+    announce(f"attn segmented B={B} Lq={Lq} Hkv={Hkv} L={L} kk={kk}")
+    r = _rng(77)
+    q, qh = dev_bf16(r.standard_normal((B, Lq, Hq, 128)))
+    k, kh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    v, vh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    idx = np.full((B, Lq, kk), -1, dtype=np.int32)
+    for b in range(B):
+        for j in range(Lq):
+            kind = (j + b) % 8
+            if kind == 0:
+                sel = np.sort(r.choice(L, size=kk - 1 - j % 50, replace=False))
+            elif kind == 1:
+                sel = np.sort(r.choice(np.arange(16384, 16384 + 4096), size=kk, replace=False))
+            elif kind == 2:
+                sel = r.choice(L, size=kk, replace=False)
+            elif kind == 3:
+                sel = np.zeros(0, dtype=np.int64)
+            elif kind == 4:
+                sel = np.sort(r.choice(L, size=kk // 2, replace=True))
+                sel = np.sort(np.concatenate([sel, sel[:10]]))
+            elif kind == 5:
+                pool = np.concatenate([np.arange(0, 4096), np.arange(32768, L)])
+                sel = np.sort(r.choice(pool, size=kk // 3, replace=False))
+            elif kind == 6:
+                sel = np.sort(r.choice(L, size=kk, replace=False))
+            else:
+                sel = np.sort(r.choice(L, size=kk - 5, replace=False))
+                sel = np.concatenate([sel[:40], [-1] * 5, sel[40:]])
+            idx[b, j, :sel.size] = sel
+    scale = 1.0 / math.sqrt(128)
+    got = host(lct.sparse_attn_gather(q, k, v, dev_i32(idx), scale))
+    nb = lct._sz()
+    lct._check(lct.lib().lct_sparse_attn_workspace_bytes(B, Lq, Hq, Hkv, 128, L, kk, lct._c.byref(nb)))
+    assert nb.value >= B * Lq * Hkv * 2 * Hq // Hkv * 130 * 4  # partials, two segments or more
+    for b in range(B):
+        for j in range(Lq):
+            sel = idx[b, j][idx[b, j] >= 0]
+            if sel.size == 0:
+                assert np.all(got[b, j] == 0.0), (b, j)
+                continue
+            want = oracle.sparse_attention_gqa(qh[b, j], kh[b, sel], vh[b, sel], scale)
+            err = np.abs(got[b, j] - want).max()
+            assert err < ATOL, (b, j, (j + b) % 8, err)
+
+
 # ------------------------------------------------------------------ GSA ----
 
 def _gsa_inputs(cfg, gist_vals=None):
