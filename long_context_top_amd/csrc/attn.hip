@@ -235,8 +235,11 @@ LCT_DEV void attn_iter(const int32_t* ix, int e0, int e_end, int64_t L, const At
                        int (&pos)[4], int (&pp)[4], uint64_t (&msk)[4], bf16x8 (&kr)[4][4],
                        const bf16x8 (&qf)[4], __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                        int row_bytes, float scale_log2, char (*vta)[4][1024],
-                       char (*vtb)[4][1024], float& m, float& lsum, floatx4 (&o)[ATT_D / 16]) {
+                       char (*vtb)[4][1024], float& m, floatx4& lacc, floatx4 (&o)[ATT_D / 16]) {
   constexpr int D = ATT_D;
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
   // S^T = K Q^T per 16-token block; sacc[j][e] = S^T[token 16j + 4kg + e][head hl]
   floatx4 sacc[4];
 #pragma unroll
@@ -256,39 +259,53 @@ LCT_DEV void attn_iter(const int32_t* ix, int e0, int e_end, int64_t L, const At
     attn_gather_k(krs, row_bytes, a.ck, ppn, kr);
     attn_entries(ix, e0 + 2 * ATT_STEP, e_end, a.tk, pos);
   }
-  float z[4][4];
+  // running maximum in the exp2 domain (scale_log2 > 0 commutes with max)
+  const bool full = (mskc[0] & mskc[1] & mskc[2] & mskc[3]) == ~0ull;  // uniform
+  uint32_t mk[4];  // this lane's tokens 4kg + e of block j: bit 4e
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mk[j] = (uint32_t)(mskc[j] >> (16 * a.kg));
   float tmax = -INFINITY;
+  if (full) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      z[j][e] = ((mskc[j] >> (16 * a.kg + 4 * e)) & 1) ? sacc[j][e] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, z[j][e]);
-    }
+      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sacc[j][e]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, ((mk[j] >> (4 * e)) & 1) ? sacc[j][e] : -INFINITY);
+  }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-  const float mnew = fmaxf(m, tmax);
+  const float mnew = fmaxf(m, tmax * scale_log2);
   // no valid token yet (a run of skipped entries): any finite reference
   // keeps alpha and the weights at 0 instead of NaN
   const float mref = mnew == -INFINITY ? 0.f : mnew;
   const float alpha = __builtin_amdgcn_exp2f(m - mref);
-  // the weights enter the PV product as bf16; the denominator sums the same
-  // rounded weights so that the normalisation is consistent
-  __bf16 pw[4][4];
-  float psum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pw[j][e] = (__bf16)__builtin_amdgcn_exp2f(z[j][e] - mref);
-      psum += (float)pw[j][e];
-    }
-  lsum = lsum * alpha + psum;
   m = mnew;
+  // weights 2^(s * scale_log2 - m), rounded to bf16 for the PV product; the
+  // denominator is the same MFMA over these rounded weights (a row of ones)
+  __bf16 pw[4][4];
+  if (full) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pw[j][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[j][e], scale_log2, -mref));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float w = __builtin_amdgcn_exp2f(fmaf(sacc[j][e], scale_log2, -mref));
+        pw[j][e] = (__bf16)(((mk[j] >> (4 * e)) & 1) ? w : 0.f);
+      }
+  }
   // the running maximum moves ever more rarely: rescale only when it did
   if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
+    lacc = lacc * alpha;
   }
   // O^T += V^T P^T, 32 tokens (blocks 2h, 2h+1: half h of the tile) per
   // MFMA: the MFMA's k = 8kg + jj is token 4kg + jj of block 2h (jj < 4) or
@@ -330,6 +347,7 @@ LCT_DEV void attn_iter(const int32_t* ix, int e0, int e_end, int64_t L, const At
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pf, o[dt], 0, 0, 0);
+    lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc, 0, 0, 0);
   }
   compiler_fence();
   if (NEXT) {
@@ -339,8 +357,9 @@ LCT_DEV void attn_iter(const int32_t* ix, int e0, int e_end, int64_t L, const At
 }
 
 // Online softmax attention of one query row's G heads over the index
-// entries [e_begin, e_end) of its row `ix`, 64 entries per iteration, into
-// the running (m, lsum, O^T).  `pos` holds the first iteration's entries
+// entries [e_begin, e_end) of its row `ix`, 64 entries per iteration: on
+// return m is the running maximum (exp2 domain), lsum the denominator of the
+// lane's head and o = O^T (unnormalised); called with m = -inf, o = 0.  `pos` holds the first iteration's entries
 // (attn_entries).  Entries that are -1 or outside [0, L) are skipped.
 template <int G>
 LCT_DEV void attn_span(const int32_t* ix, int e_begin, int e_end, int (&pos)[4],
@@ -363,12 +382,16 @@ LCT_DEV void attn_span(const int32_t* ix, int e_begin, int e_end, int (&pos)[4],
   attn_entries(ix, e_begin + ATT_STEP, e_end, a.tk, pos);  // the next iteration's entries
   attn_gather_v_half(vrs, row_bytes, a.cv, pp, 0, vta);
   attn_gather_v_half(vrs, row_bytes, a.cv, pp, 1, vtb);
+  // the softmax denominator accumulates on the MFMA (every row of lacc holds
+  // the sum of this lane's head)
+  floatx4 lacc = floatx4{0.f, 0.f, 0.f, 0.f};
   int e0 = e_begin;
   for (; e0 + ATT_STEP < e_end; e0 += ATT_STEP)
     attn_iter<G, true>(ix, e0, e_end, L, a, pos, pp, msk, kr, qf, krs, vrs, row_bytes, scale_log2, vta,
-                       vtb, m, lsum, o);
+                       vtb, m, lacc, o);
   attn_iter<G, false>(ix, e0, e_end, L, a, pos, pp, msk, kr, qf, krs, vrs, row_bytes, scale_log2, vta,
-                      vtb, m, lsum, o);
+                      vtb, m, lacc, o);
+  lsum = lacc[0];
 }
 
 template <int G>
@@ -414,9 +437,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn(
                v + ((size_t)b * L * Hkv + kvh) * D, row_stride, L, scale_log2, vta[wid], vtb[wid], lane, m,
                lsum, o);
 
-  // o[dt][e] = O^T[d = 16dt + 4kg + e][head hl]; lsum: this lane's share
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  // o[dt][e] = O^T[d = 16dt + 4kg + e][head hl]; lsum: head hl's denominator
   if (hl >= G) return;
   if (splits == 1) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
@@ -586,8 +607,6 @@ __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn_seg(
                v + ((size_t)b * L * Hkv + kvh) * D, row_stride, L, scale_log2, vta[wid], vtb[wid], lane, m,
                lsum, o);
 
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
   if (hl >= G) return;
   if (whole) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
