@@ -182,7 +182,8 @@ def _attn_case(B, Lq, Hq, Hkv, L, kk, seed, pad=0, shuffle=False, ones=False):
 
 @pytest.mark.parametrize("B,Lq,Hq,Hkv,L,kk", [(2, 3, 8, 2, 1000, 100), (1, 1, 32, 4, 5000, 2048),
                                                (1, 2, 16, 16, 300, 37), (3, 1, 16, 1, 700, 128),
-                                               (1, 1, 8, 8, 64, 64), (2, 1, 4, 2, 4000, 1000)])
+                                               (1, 1, 8, 8, 64, 64), (2, 1, 4, 2, 4000, 1000),
+                                               (1, 1, 16, 1, 5000, 2048), (8, 1, 32, 4, 9000, 2048)])
 def test_sparse_attn_matches_oracle(B, Lq, Hq, Hkv, L, kk):
     announce(f"attn B={B} Lq={Lq} Hq={Hq} Hkv={Hkv} L={L} kk={kk}")
     got, want = _attn_case(B, Lq, Hq, Hkv, L, kk, seed=L + kk, pad=kk // 7)
@@ -196,6 +197,27 @@ def test_sparse_attn_order_invariant_and_ones():
     assert np.abs(got - want).max() < ATOL
     got1, _ = _attn_case(2, 1, 32, 4, 3000, 2048, seed=4, ones=True)
     assert np.abs(got1 - 1.0).max() < 1e-5
+
+
+def test_sparse_attn_split_path_repeated_calls():
+    """The split path's workgroups count themselves in per (row, KV head) and
+    the last one merges; every call must leave the counters ready for the
+    next, on one workspace, with a different shape in between."""
+    announce("attn split path, repeated calls on one workspace")
+    ws = lct.Workspace()
+    r = _rng(21)
+    for it, (B, kk) in enumerate([(2, 2048), (2, 2048), (1, 700), (3, 2048)]):
+        L, Hq, Hkv = 6000, 32, 4
+        q, qh = dev_bf16(r.standard_normal((B, 1, Hq, 128)))
+        k, kh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+        v, vh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+        idx = np.stack([np.sort(r.choice(L, size=kk, replace=False)) for _ in range(B)])[:, None, :]
+        idx = idx.astype(np.int32)
+        scale = 1.0 / math.sqrt(128)
+        got = host(lct.sparse_attn_gather(q, k, v, dev_i32(idx), scale, ws=ws))
+        for b in range(B):
+            want = oracle.sparse_attention_gqa(qh[b, 0], kh[b, idx[b, 0]], vh[b, idx[b, 0]], scale)
+            assert np.abs(got[b, 0] - want).max() < ATOL, (it, b)
 
 
 def test_sparse_attn_empty_rows_are_zero():
