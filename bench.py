@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, vendor figure
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
 MIB = 1 << 20
 
 
@@ -318,12 +319,61 @@ def bench_prefill_indexer(cfg, steps, warmup):
     pairs = cfg.L * (cfg.L + 1) // 2
     ops = 2 * cfg.HD * pairs
     tops = ops / (ms * 1e-3) / 1e12
+    attn = bench_prefill_attention(cfg, out, steps, warmup)
+    # the whole prefill of the 28-layer stack: one index per group of layers,
+    # sparse attention in every layer
+    step_ms = cfg.n_groups * ms + cfg.n_layers * attn["ms_per_layer"]
     return {"workload": cfg.name + " indexer (one group, fused score filter + exact top-k)",
             "ms_per_group": ms, "int8_tops": tops, "rows_on_plain_path": stats.get("n_fallback"),
             "roofline": {"bound": "mfma", "kernel": "k_pf_filter + k_pf_select (+ short-row block)",
                          "achieved": tops, "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                          "frac": tops / INT8_PEAK_TOPS, "ops_per_launch": ops,
-                         "us_per_launch": ms * 1e3}}
+                         "us_per_launch": ms * 1e3},
+            "attention": attn,
+            "prefill_ms_all_layers": step_ms,
+            "prefill_tokens_per_s": cfg.L / (step_ms * 1e-3)}
+
+
+def bench_prefill_attention(cfg, idx, steps, warmup):
+    """Sparse attention of one layer over the causal index sets (every row
+    its own top-k positions): the position-segment path of
+    lct_sparse_attn_gather.  Throughput over the selected pairs' bf16 flops
+    (QK and PV, 4 flops per pair, query head and feature)."""
+    import torch
+
+    import long_context_top_amd as lct
+    import synth.device as sd
+
+    dev = idx.device
+    q = sd.make(cfg, cfg.q_spec(0), dev)
+    k = sd.make(cfg, cfg.k_spec(0), dev)
+    v = sd.make(cfg, cfg.v_spec(0), dev)
+    out = torch.empty((1, cfg.L, cfg.Hq, cfg.D), dtype=torch.float32, device=dev)
+    ws = lct.Workspace(dev)
+    ix = idx.view(1, cfg.L, cfg.topk)
+    f = lambda: lct.sparse_attn_gather(q, k, v, ix, cfg.scale, out=out, ws=ws)
+    for _ in range(max(warmup, 1)):
+        f()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        f()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    sel = sum(min(cfg.topk, r + 1) for r in range(cfg.L))
+    flops = 4.0 * cfg.Hq * cfg.D * sel
+    gathered = sel * cfg.Hkv * cfg.D * 2 * 2
+    del q, k, v, out, ws
+    return {"kernel": "k_seg_bounds + k_sparse_attn_seg + k_seg_merge", "ms_per_layer": ms,
+            "bf16_tflops": flops / (ms * 1e-3) / 1e12, "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "gathered_gb_per_s": gathered / (ms * 1e-3) / 1e9,
+            "note": "selected K/V rows are re-read by many rows: the gathers run from L2/MALL, "
+                    "bounded by the per-CU address rate (64 B/clk), not HBM"}
 
 
 def copy_calibration(steps):
