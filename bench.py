@@ -43,12 +43,15 @@ def decode_step_bytes(cfg) -> dict:
     """Algorithmic bytes of one decode step.
 
     Indexer keys are read once per group (B x L x HD bytes); each layer reads
-    the selected K and V rows (B x Lq x k x Hkv x D x 2 bytes x 2).  Queries,
+    the selected K and V rows (B x Lq x k x Hkv x D x 2 bytes x 2).  With one
+    KV cache for all layers the layers of a group gather the very same rows
+    (one index, one cache), so those bytes count once per group.  Queries,
     index sets, outputs and scratch are not counted.
     """
     idx_per_call = cfg.B * cfg.L * cfg.HD
     kv_per_layer = cfg.B * cfg.Lq * min(cfg.topk, cfg.L) * cfg.Hkv * cfg.D * 2 * 2
-    total = cfg.n_groups * idx_per_call + cfg.n_layers * kv_per_layer
+    kv_reads = cfg.n_groups if getattr(cfg, "shared_kv", False) else cfg.n_layers
+    total = cfg.n_groups * idx_per_call + kv_reads * kv_per_layer
     return {"indexer_per_call": idx_per_call, "kv_per_layer": kv_per_layer, "total": total}
 
 
@@ -183,8 +186,14 @@ def bench_decode(cfg, steps, warmup, want_cpu):
     qi = [sd.make(cfg, cfg.qi_spec(g), dev) for g in range(ng)]
     ki = [sd.make(cfg, cfg.ki_spec(g), dev) for g in range(ng)]
     q = [sd.make(cfg, cfg.q_spec(l), dev) for l in range(cfg.n_layers)]
-    k = [sd.make(cfg, cfg.k_spec(l), dev) for l in range(cfg.n_layers)]
-    v = [sd.make(cfg, cfg.v_spec(l), dev) for l in range(cfg.n_layers)]
+    # one cache tensor per distinct KV layer (all layers share layer 0's with shared_kv)
+    kv = {}
+    for l in range(cfg.n_layers):
+        j = cfg.kv_layer(l)
+        if j not in kv:
+            kv[j] = (sd.make(cfg, cfg.k_spec(l), dev), sd.make(cfg, cfg.v_spec(l), dev))
+    k = [kv[cfg.kv_layer(l)][0] for l in range(cfg.n_layers)]
+    v = [kv[cfg.kv_layer(l)][1] for l in range(cfg.n_layers)]
     out = [torch.empty((cfg.B, cfg.Lq, cfg.Hq, cfg.D), dtype=torch.float32, device=dev)
            for _ in range(cfg.n_layers)]
     idx_out = [torch.empty((cfg.B, cfg.Lq, cfg.topk), dtype=torch.int32, device=dev) for _ in range(ng)]
@@ -229,7 +238,8 @@ def bench_decode(cfg, steps, warmup, want_cpu):
         "config": {"workload": cfg.name, "global_batch": cfg.B, "seq_len": cfg.L,
                    "layers": cfg.n_layers, "layers_per_index": cfg.group, "q_heads": cfg.Hq,
                    "kv_heads": cfg.Hkv, "head_dim": cfg.D, "indexer": f"int8 {cfg.H_idx}x{cfg.d_idx}",
-                   "topk": cfg.topk, "parallelism": "single GPU"},
+                   "topk": cfg.topk, "kv_cache": "one shared by all layers" if cfg.shared_kv else "per layer",
+                   "parallelism": "single GPU"},
         "hbm_gbs_step": step_gbs, "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": bytes_["total"],
         "roofline": {"bound": "hbm", "kernel": "k_idx_score_stream (indexer scores, one group)",
@@ -488,7 +498,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode_128k",
-                    choices=["decode_128k", "decode_32k", "decode_1m", "gsa_128k", "prefill_64k", "tiny"])
+                    choices=["decode_128k", "decode_32k", "decode_1m", "gsa_128k", "prefill_64k", "tiny",
+                             "decode_128k_shared_kv"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy used to calibrate HBM byte counters")
@@ -514,7 +525,8 @@ def main():
         sys.exit(2)
     from synth import configs as C
     cfgs = {"decode_128k": C.DECODE_128K, "decode_32k": C.DECODE_32K, "decode_1m": C.DECODE_1M,
-            "gsa_128k": C.GSA_128K, "prefill_64k": C.PREFILL_64K, "tiny": C.TINY}
+            "gsa_128k": C.GSA_128K, "prefill_64k": C.PREFILL_64K, "tiny": C.TINY,
+            "decode_128k_shared_kv": C.DECODE_128K_SHARED_KV}
     cfg = cfgs[args.config]
     if args.config == "gsa_128k":
         res = bench_gsa(cfg, args.steps, args.warmup)

@@ -228,8 +228,13 @@ typedef struct lct_group_desc {
   const int8_t* const* qi;        /* host array [n_groups] of device [B, Lq, HD] */
   const int8_t* const* ki;        /* host array [n_groups] of device [B, L, HD]  */
   const uint16_t* const* q;       /* host array [n_layers] of device bf16 [B, Lq, Hq, D] */
-  const uint16_t* const* k;       /* host array [n_layers] of device bf16 [B, L, Hkv, D] */
-  const uint16_t* const* v;       /* host array [n_layers] of device bf16 [B, L, Hkv, D] */
+  const uint16_t* const* k;       /* host array [n_layers] of device bf16 [B, L, Hkv, D];
+                                     entries may repeat: layers sharing one KV cache
+                                     (YOCO / CLSA explainer section 2.1) pass the same
+                                     pointer, and then the layers of a group gather the
+                                     same rows, which the later layers find in cache   */
+  const uint16_t* const* v;       /* host array [n_layers] of device bf16 [B, L, Hkv, D];
+                                     may repeat like k                                  */
   float* const* out;              /* host array [n_layers] of device fp32 [B, Lq, Hq, D] */
   int32_t* const* idx_out;        /* NULL, or host array [n_groups] of device int32
                                      [B, Lq, topk] (NULL entries allowed): where each

@@ -36,7 +36,9 @@ class DecodeConfig:
     ``Lq`` query rows per batch entry all attend over the same ``L`` cached
     positions; each row has its own index set.  With ``causal`` set, query
     row ``r`` sits at position ``r`` (``Lq == L``) and may only see
-    positions ``<= r`` (causal prefill).
+    positions ``<= r`` (causal prefill).  With ``shared_kv`` every layer
+    reads the one KV cache of layer 0 (YOCO / CLSA cross-layer KV sharing);
+    the queries stay per layer.
     """
 
     name: str
@@ -53,6 +55,7 @@ class DecodeConfig:
     d_idx: int
     topk: int
     causal: bool = False
+    shared_kv: bool = False
 
     @property
     def HD(self) -> int:
@@ -76,11 +79,15 @@ class DecodeConfig:
     def q_spec(self, l):
         return BF16N, (self.B, self.Lq, self.Hq, self.D), tid(T_Q, l)
 
+    def kv_layer(self, l):
+        """The layer whose KV cache layer ``l`` reads."""
+        return 0 if self.shared_kv else l
+
     def k_spec(self, l):
-        return BF16N, (self.B, self.L, self.Hkv, self.D), tid(T_K, l)
+        return BF16N, (self.B, self.L, self.Hkv, self.D), tid(T_K, self.kv_layer(l))
 
     def v_spec(self, l):
-        return BF16N, (self.B, self.L, self.Hkv, self.D), tid(T_V, l)
+        return BF16N, (self.B, self.L, self.Hkv, self.D), tid(T_V, self.kv_layer(l))
 
     def with_(self, **kw) -> "DecodeConfig":
         return replace(self, **kw)
@@ -140,6 +147,8 @@ TINY = DecodeConfig("tiny_decode_2k", 1001, B=1, Lq=16, L=2048, n_layers=4, grou
 DECODE_32K = DecodeConfig("sparse_decode_32k_b8", 1002, B=8, Lq=1, L=32768, n_layers=28,
                           group=4, Hq=32, Hkv=4, D=128, H_idx=4, d_idx=64, topk=2048)
 DECODE_128K = DECODE_32K.with_(name="sparse_decode_128k_b8", L=131072)
+# the 128K decode with one KV cache for all 28 layers (YOCO / CLSA)
+DECODE_128K_SHARED_KV = DECODE_128K.with_(name="sparse_decode_128k_b8_shared_kv", shared_kv=True)
 PREFILL_64K = DecodeConfig("causal_prefill_64k", 1003, B=1, Lq=65536, L=65536, n_layers=28,
                            group=4, Hq=32, Hkv=4, D=128, H_idx=4, d_idx=64, topk=2048,
                            causal=True)
@@ -148,7 +157,8 @@ GSA_128K = GsaConfig("gsa_decode_128k_b16", 1004, B=16, H=16, D=128, Nc=8192, ch
 DECODE_1M = DecodeConfig("sparse_decode_1m_b1", 1005, B=1, Lq=1, L=1048576, n_layers=28,
                          group=4, Hq=32, Hkv=4, D=128, H_idx=4, d_idx=64, topk=2048)
 
-ALL = {c.name: c for c in (TINY, DECODE_32K, DECODE_128K, PREFILL_64K, GSA_128K, DECODE_1M)}
+ALL = {c.name: c for c in (TINY, DECODE_32K, DECODE_128K, PREFILL_64K, GSA_128K, DECODE_1M,
+                           DECODE_128K_SHARED_KV)}
 
 
 # ---- host-side generation helpers ----

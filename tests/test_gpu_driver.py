@@ -153,3 +153,25 @@ def test_causal_prefill_segmented_attention():
     assert np.array_equal(idx[0][0][sample], want)
     ref = oracle.prefill_attention_rows(cfg, 0, sample, want)
     assert np.abs(out[0][0, sample] - ref).max() < ATOL
+
+
+def test_decode_shared_kv_cache():
+    """One KV cache for every layer (YOCO / CLSA): the same K/V tensors are
+    handed to all layers; each layer still has its own queries."""
+    cfg = C.DecodeConfig("shared_kv", 9191, B=2, Lq=2, L=6000, n_layers=8, group=4, Hq=16, Hkv=4,
+                         D=128, H_idx=4, d_idx=64, topk=512, shared_kv=True)
+    announce(cfg.name)
+    qi = [sd.make(cfg, cfg.qi_spec(g)) for g in range(cfg.n_groups)]
+    ki = [sd.make(cfg, cfg.ki_spec(g)) for g in range(cfg.n_groups)]
+    q = [sd.make(cfg, cfg.q_spec(l)) for l in range(cfg.n_layers)]
+    k0, v0 = sd.make(cfg, cfg.k_spec(0)), sd.make(cfg, cfg.v_spec(0))
+    idx_out = [torch.empty((cfg.B, cfg.Lq, cfg.topk), dtype=torch.int32, device="cuda")
+               for _ in range(cfg.n_groups)]
+    out, _ = lct.group_run(qi, ki, q, [k0] * cfg.n_layers, [v0] * cfg.n_layers, cfg.topk, cfg.group,
+                           cfg.scale, idx_out=idx_out)
+    torch.cuda.synchronize()
+    ref_idx, ref_out = oracle.decode_step(cfg)
+    for g in range(cfg.n_groups):
+        assert np.array_equal(host(idx_out[g]), ref_idx[g]), g
+    for l in range(cfg.n_layers):
+        assert np.abs(host(out[l]) - ref_out[l]).max() < ATOL, l

@@ -46,3 +46,26 @@ def test_gsa_keeps_selected_gists_and_raw_only():
 
 def test_sizes_match_printed_values():
     P.pin_sizes(oracle.kv_cache_gib, oracle.kv_bytes_per_token, oracle.scored_pairs)
+
+
+def test_shared_kv_cache_reads_layer_zero():
+    """YOCO / CLSA: with one KV cache every layer attends over layer 0's K/V
+    (checked by dense softmax attention over the gathered rows, a different
+    routine from the GQA one the driver uses), with its own queries."""
+    import numpy as np
+    import synth
+    from synth import configs as C
+    cfg = P.small_decode_cfg(shared_kv=True, n_layers=4)
+    assert all(cfg.k_spec(l) == cfg.k_spec(0) and cfg.v_spec(l) == cfg.v_spec(0) for l in range(4))
+    idx, outs = oracle.decode_step(cfg, batch=[1], layers=[0, 3])
+    sel = idx[0][0, 2]
+    sel = sel[sel >= 0]
+    G = cfg.Hq // cfg.Hkv
+    k = synth.as_float(synth.BF16N, C.make(cfg, cfg.k_spec(0)))[1, sel]
+    v = synth.as_float(synth.BF16N, C.make(cfg, cfg.v_spec(0)))[1, sel]
+    for l in (0, 3):
+        q = synth.as_float(synth.BF16N, C.make(cfg, cfg.q_spec(l)))[1, 2]
+        for h in range(cfg.Hq):
+            want = oracle.softmax_attention(q[h][None], k[:, h // G], v[:, h // G], cfg.scale)[0]
+            assert np.allclose(outs[l][0, 2, h], want, atol=1e-12)
+    assert not np.allclose(outs[0], outs[3])  # the queries differ per layer
