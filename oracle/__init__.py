@@ -27,7 +27,8 @@ Sources (web pages on long-context sparse attention):
 * IndexCache article (arXiv 2603.12201) -- section 2 (Full / Shared layers),
   section 3 (the greedy search keeps Full layers at uneven places),
   section 6 (one conditional plus one temporary index buffer).
-* GSA summary page (gist.science) -- section 2.2 (selective unfolding).
+* GSA summary page (gist.science) -- section 2.2 (selective unfolding),
+  section 2.4 (hierarchical gist-of-gist routing).
 
 Pins: every function is checked against values the pages print, closed
 forms, library routines for the special cases the method reduces to, and
@@ -38,7 +39,7 @@ this package is "parity unpinned".
 from .indexer import index_scores, index_scores_row  # noqa: F401
 from .topk import select_topk  # noqa: F401
 from .attention import softmax_attention, sparse_attention_gqa  # noqa: F401
-from .gsa import gist_scores, gsa_key_positions, gsa_attention, gsa_select  # noqa: F401
+from .gsa import gist_scores, gsa_key_positions, gsa_attention, gsa_select, hgsa_select  # noqa: F401
 from .driver import (decode_group, decode_layers, decode_step, decode_step_pattern,  # noqa: F401
-                     gsa_step, layer_owner, prefill_attention_rows, prefill_index_rows)
+                     gsa_step, hgsa_step, layer_owner, prefill_attention_rows, prefill_index_rows)
 from .sizes import kv_cache_gib, kv_bytes_per_token, scored_pairs  # noqa: F401

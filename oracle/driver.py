@@ -175,3 +175,32 @@ def gsa_step(cfg: C.GsaConfig, pairs=None):
         gvs = _f(kgv, C.rows(cfg, cfg.gv_spec(), (gb, gh, gist_ids)))
         out[i] = gsa_attention(q, rk, rv, gks, gvs, cfg.scale)
     return idx, out
+
+
+def hgsa_step(cfg: C.GsaConfig, pairs=None):
+    """Hierarchically routed GSA decode for (b, h) pairs: ``(chunk_idx[P, kc], out[P, D])``."""
+    from .gsa import gsa_attention, gsa_key_positions, hgsa_select
+
+    pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.H)] if pairs is None else list(pairs)
+    kq, _, _ = cfg.q_spec()
+    kgk, _, _ = cfg.gk_spec()
+    kgv, _, _ = cfg.gv_spec()
+    kmk, _, _ = cfg.mk_spec()
+    krk, _, _ = cfg.rk_spec()
+    krv, _, _ = cfg.rv_spec()
+    idx = np.full((len(pairs), cfg.kc), -1, dtype=np.int32)
+    out = np.zeros((len(pairs), cfg.D))
+    for i, (b, h) in enumerate(pairs):
+        q = _f(kq, C.rows(cfg, cfg.q_spec(), (np.array(b), np.array(h))))
+        gk = _f(kgk, C.rows(cfg, cfg.gk_spec(), (np.array(b), np.array(h))))
+        mk = _f(kmk, C.rows(cfg, cfg.mk_spec(), (np.array(b), np.array(h))))
+        idx[i] = hgsa_select(q, mk, gk, cfg.group, cfg.km, cfg.kc)
+        raw_pos, gist_ids = gsa_key_positions(idx[i], cfg.chunk, cfg.Nc, cfg.tail_len)
+        bb, hh = np.full_like(raw_pos, b), np.full_like(raw_pos, h)
+        rk = _f(krk, C.rows(cfg, cfg.rk_spec(), (bb, hh, raw_pos)))
+        rv = _f(krv, C.rows(cfg, cfg.rv_spec(), (bb, hh, raw_pos)))
+        gb, gh = np.full_like(gist_ids, b), np.full_like(gist_ids, h)
+        gks = gk[gist_ids]
+        gvs = _f(kgv, C.rows(cfg, cfg.gv_spec(), (gb, gh, gist_ids)))
+        out[i] = gsa_attention(q, rk, rv, gks, gvs, cfg.scale)
+    return idx, out

@@ -22,6 +22,16 @@ Readings where the pages are silent or disagree:
 * The current token opens an unfinished chunk; its first ``tail_len`` raw
   positions (including the current token) are always attended.
 * The gist logit in attention is the same ``q . gK`` product, scaled.
+
+Hierarchical routing (H-GSA / H-SSA): SSA article section 5 (a meta-gist
+token after every few gist tokens summarises them; the query first picks the
+best meta-gists, then the best gists inside their groups, then unfolds those
+chunks' raw tokens) and the GSA summary page section 2.4 (gist-of-gist,
+coarse-to-fine selection, O(log N) routing).  Readings: meta-gist ``g``
+covers gists ``[g*group, (g+1)*group)`` (the last group may be short); its
+routing score is the unscaled ``q . mK`` like the gists'; ties go to the
+lower group, then to the lower chunk; meta-gists only route: the attention
+is the GSA one over the chosen chunks' raw tokens and gists plus the tail.
 """
 
 from __future__ import annotations
@@ -66,3 +76,22 @@ def gsa_attention(q: np.ndarray, raw_k: np.ndarray, raw_v: np.ndarray, gist_k: n
 def gsa_select(q: np.ndarray, gk: np.ndarray, kc: int) -> np.ndarray:
     """Chosen chunk ids ``[..., kc]`` (ascending, -1 padded)."""
     return select_topk(gist_scores(q, gk), kc)
+
+
+def hgsa_select(q: np.ndarray, mk: np.ndarray, gk: np.ndarray, group: int, km: int,
+                kc: int) -> np.ndarray:
+    """Coarse-to-fine chunk choice for one query: ``q[D]``, meta-gist keys
+    ``mk[Nm, D]``, gist keys ``gk[Nc, D]`` -> chosen chunk ids ``[kc]``
+    (ascending, -1 padded when the chosen groups hold fewer than kc chunks).
+    """
+    gk = np.asarray(gk)
+    nc = gk.shape[0]
+    groups = select_topk(gist_scores(q, mk), km)           # the km best meta-gists
+    groups = groups[groups >= 0]
+    cand = np.concatenate([np.arange(g * group, min((g + 1) * group, nc)) for g in groups])
+    s = gist_scores(q, gk[cand])
+    order = np.lexsort((cand, -s))                        # score desc, then chunk asc
+    chosen = np.sort(cand[order[:kc]])
+    out = np.full(kc, -1, dtype=np.int32)
+    out[:chosen.size] = chosen
+    return out

@@ -23,6 +23,7 @@ from . import BF16N, BF16U4, I8U4, tensor, values
 # tensor kind codes
 T_QI, T_KI, T_Q, T_K, T_V = 1, 2, 3, 4, 5
 T_GQ, T_GK, T_GV, T_RK, T_RV = 6, 7, 8, 9, 10
+T_MK = 11  # meta-gist keys (hierarchical GSA)
 
 
 def tid(kind_code: int, index: int = 0) -> int:
@@ -101,6 +102,10 @@ class GsaConfig:
     follows it.  The current token opens the unfinished chunk ``Nc``; its
     ``tail_len`` raw positions ``[Nc*chunk, Nc*chunk + tail_len)`` are always
     attended.  The raw arrays hold room for one full unfinished chunk.
+
+    Hierarchical routing (``group`` > 0): meta-gist ``g`` summarises gists
+    ``[g*group, (g+1)*group)``; the ``km`` best meta-gists are chosen first
+    and the ``kc`` chunks only among their gists.
     """
 
     name: str
@@ -113,6 +118,12 @@ class GsaConfig:
     kc: int
     tail_len: int
     gist_kind: int = BF16U4
+    group: int = 0
+    km: int = 0
+
+    @property
+    def Nm(self) -> int:
+        return -(-self.Nc // self.group) if self.group else 0
 
     @property
     def raw_cap(self) -> int:
@@ -130,6 +141,9 @@ class GsaConfig:
 
     def gv_spec(self):
         return BF16N, (self.B, self.H, self.Nc, self.D), tid(T_GV)
+
+    def mk_spec(self):
+        return self.gist_kind, (self.B, self.H, self.Nm, self.D), tid(T_MK)
 
     def rk_spec(self):
         return BF16N, (self.B, self.H, self.raw_cap, self.D), tid(T_RK)
@@ -154,11 +168,14 @@ PREFILL_64K = DecodeConfig("causal_prefill_64k", 1003, B=1, Lq=65536, L=65536, n
                            causal=True)
 GSA_128K = GsaConfig("gsa_decode_128k_b16", 1004, B=16, H=16, D=128, Nc=8192, chunk=16,
                      kc=64, tail_len=1)
+# GSA 128K with coarse-to-fine routing: 128 meta-gists of 64 gists each, 4
+# groups chosen, then the 64 best of their 256 chunks
+HGSA_128K = GSA_128K.with_(name="hgsa_decode_128k_b16", seed=1006, group=64, km=4)
 DECODE_1M = DecodeConfig("sparse_decode_1m_b1", 1005, B=1, Lq=1, L=1048576, n_layers=28,
                          group=4, Hq=32, Hkv=4, D=128, H_idx=4, d_idx=64, topk=2048)
 
 ALL = {c.name: c for c in (TINY, DECODE_32K, DECODE_128K, PREFILL_64K, GSA_128K, DECODE_1M,
-                           DECODE_128K_SHARED_KV)}
+                           DECODE_128K_SHARED_KV, HGSA_128K)}
 
 
 # ---- host-side generation helpers ----

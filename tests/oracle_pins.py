@@ -437,3 +437,40 @@ def pin_sizes(kv_cache_gib, kv_bytes_per_token, scored_pairs):
     gc = g["gist_count_at_1M"]
     n_gists = gc["n_tok"] // gc["chunk"]
     assert gc["printed_lower_bound"] <= n_gists <= gc["printed_upper_bound"]
+
+
+def pin_hgsa_select(hgsa_select, gsa_select):
+    """Coarse-to-fine routing: a hand-worked case with ties; brute force by
+    rank counting on small integer inputs (many ties, a short last group);
+    choosing every group reduces to the flat top-kc over all chunks."""
+    # hand-worked: D = 2, q = (1, 0), so a key's score is its first feature.
+    # Groups of 2 over 6 chunks: meta scores 5, 9, 9 (groups 1 and 2 tie).
+    q = np.array([1.0, 0.0])
+    mk = np.array([[5, 0], [9, 0], [9, 0]], dtype=float)
+    gk = np.array([[8, 0], [8, 0], [4, 0], [4, 0], [7, 0], [1, 0]], dtype=float)
+    assert list(hgsa_select(q, mk, gk, 2, 1, 1)) == [2]           # group 1 (tie -> lower), chunk 2 (tie)
+    assert list(hgsa_select(q, mk, gk, 2, 2, 2)) == [2, 4]        # chunks 2..5 score 4 4 7 1
+    assert list(hgsa_select(q, mk, gk, 2, 2, 5)) == [2, 3, 4, 5, -1]
+    assert list(hgsa_select(q, mk, gk, 2, 3, 2)) == [0, 1]        # every group: the flat choice
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        nc = int(rng.integers(1, 40))
+        group = int(rng.integers(1, 9))
+        nm = -(-nc // group)
+        km = int(rng.integers(1, nm + 2))
+        kc = int(rng.integers(1, 12))
+        d = 3
+        q = rng.integers(-2, 3, d).astype(float)
+        mk = rng.integers(-2, 3, (nm, d)).astype(float)
+        gk = rng.integers(-2, 3, (nc, d)).astype(float)
+        got = hgsa_select(q, mk, gk, group, km, kc)
+        ms, gs = mk @ q, gk @ q
+        gsel = [g for g in range(nm)
+                if sum(1 for h in range(nm) if ms[h] > ms[g] or (ms[h] == ms[g] and h < g)) < km]
+        cand = [c for c in range(nc) if c // group in gsel]
+        want = sorted(c for c in cand
+                      if sum(1 for e in cand if gs[e] > gs[c] or (gs[e] == gs[c] and e < c)) < kc)
+        want = want + [-1] * (kc - len(want))
+        assert list(got) == want, (trial, nc, group, km, kc)
+        if km >= nm:
+            assert list(got) == list(gsa_select(q, gk, kc)), trial

@@ -234,3 +234,39 @@ def test_gsa_gists_dropped_mutant_caught(monkeypatch):
 def test_sizes_mutant_caught():
     _fails(P.pin_sizes, lambda L, H, D, n, b=2: L * H * D * b * n / 1024**3,   # K only, V dropped
            oracle.kv_bytes_per_token, oracle.scored_pairs)
+
+
+# ---- hierarchical GSA ----
+
+def _hgsa_meta_ties_high(q, mk, gk, group, km, kc):
+    """Meta-gist ties go to the higher group."""
+    nm = len(mk)
+    ms = np.asarray(mk, float) @ np.asarray(q, float)
+    order = np.lexsort((-np.arange(nm), -ms))
+    groups = np.sort(order[:km])
+    nc = len(gk)
+    cand = np.concatenate([np.arange(g * group, min((g + 1) * group, nc)) for g in groups])
+    s = np.asarray(gk, float)[cand] @ np.asarray(q, float)
+    chosen = np.sort(cand[np.lexsort((cand, -s))[:kc]])
+    out = np.full(kc, -1, dtype=np.int32)
+    out[:chosen.size] = chosen
+    return out
+
+
+def _hgsa_flat(q, mk, gk, group, km, kc):
+    """Ignores the groups: the flat top-kc over every chunk."""
+    return GSA.gsa_select(q, gk, kc)
+
+
+def _hgsa_drops_short_group(q, mk, gk, group, km, kc):
+    """Leaves out the last group when it is short."""
+    nc = len(gk)
+    full = (nc // group) * group
+    if full == 0:
+        return GSA.hgsa_select(q, mk, gk, group, km, kc)
+    return GSA.hgsa_select(q, np.asarray(mk)[: nc // group], np.asarray(gk)[:full], group, km, kc)
+
+
+@pytest.mark.parametrize("mut", [_hgsa_meta_ties_high, _hgsa_flat, _hgsa_drops_short_group])
+def test_hgsa_mutants_caught(mut):
+    _fails(P.pin_hgsa_select, mut, GSA.gsa_select)

@@ -69,3 +69,7 @@ def test_shared_kv_cache_reads_layer_zero():
             want = oracle.softmax_attention(q[h][None], k[:, h // G], v[:, h // G], cfg.scale)[0]
             assert np.allclose(outs[l][0, 2, h], want, atol=1e-12)
     assert not np.allclose(outs[0], outs[3])  # the queries differ per layer
+
+
+def test_hgsa_coarse_to_fine_select():
+    P.pin_hgsa_select(oracle.hgsa_select, oracle.gsa_select)
