@@ -56,9 +56,12 @@ def decode_step_bytes(cfg) -> dict:
 
 
 def gsa_step_bytes(cfg) -> dict:
-    """Gist keys once, then per (b, h): chosen chunks' raw K and V, gist V, tail K and V."""
+    """Routing keys (every gist key; with coarse-to-fine routing the meta-gist
+    keys and the chosen groups' gist keys), then per (b, h): chosen chunks'
+    raw K and V, gist V, tail K and V."""
     BH = cfg.B * cfg.H
-    gk = BH * cfg.Nc * cfg.D * 2
+    rows = (cfg.Nm + cfg.km * cfg.group) if cfg.group else cfg.Nc
+    gk = BH * rows * cfg.D * 2
     sel = BH * cfg.kc * (cfg.chunk * 2 + 1) * cfg.D * 2 + BH * cfg.tail_len * 2 * cfg.D * 2
     return {"gist_keys": gk, "selected": sel, "total": gk + sel}
 
@@ -276,7 +279,13 @@ def bench_gsa(cfg, steps, warmup):
     out = torch.empty((BH, cfg.D), dtype=torch.float32, device=dev)
     cidx = torch.empty((BH, cfg.kc), dtype=torch.int32, device=dev)
     ws = lct.Workspace(dev)
-    step = lambda: lct.gsa_decode(qv, gk, gv, rk, rv, cfg.kc, cfg.tail_len, cfg.scale, idx_out=cidx, out=out, ws=ws)
+    if cfg.group:  # coarse-to-fine routing through the meta-gists
+        mkeys = mk(cfg.mk_spec())
+        step = lambda: lct.hgsa_decode(qv, mkeys, gk, gv, rk, rv, cfg.group, cfg.km, cfg.kc, cfg.tail_len,
+                                       cfg.scale, idx_out=cidx, out=out, ws=ws)
+    else:
+        step = lambda: lct.gsa_decode(qv, gk, gv, rk, rv, cfg.kc, cfg.tail_len, cfg.scale, idx_out=cidx,
+                                      out=out, ws=ws)
     step()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -287,12 +296,14 @@ def bench_gsa(cfg, steps, warmup):
     stream = torch.cuda.current_stream()
     ms = _timed_loop(g.replay, steps, stream)
     b = gsa_step_bytes(cfg)
-    gs = torch.empty((BH, cfg.Nc), dtype=torch.float32, device=dev)
-    ms_gs = _timed_graph(lambda: lct.gist_score(qv, gk, out=gs), max(10, steps), stream)
     gbs = b["total"] / (ms * 1e-3) / 1e9
-    return {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": BH // cfg.H * 1.0 / (ms * 1e-3),
-            "hbm_gbs_step": gbs, "hbm_frac_step": gbs / HBM_PEAK_GBS,
-            "gist_score_gbs": b["gist_keys"] / (ms_gs * 1e-3) / 1e9, "gist_score_us": ms_gs * 1e3}
+    res = {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": BH // cfg.H * 1.0 / (ms * 1e-3),
+           "hbm_gbs_step": gbs, "hbm_frac_step": gbs / HBM_PEAK_GBS, "routing_key_bytes": b["gist_keys"]}
+    if not cfg.group:
+        gs = torch.empty((BH, cfg.Nc), dtype=torch.float32, device=dev)
+        ms_gs = _timed_graph(lambda: lct.gist_score(qv, gk, out=gs), max(10, steps), stream)
+        res.update({"gist_score_gbs": b["gist_keys"] / (ms_gs * 1e-3) / 1e9, "gist_score_us": ms_gs * 1e3})
+    return res
 
 
 # --------------------------------------------------------------- prefill ----
@@ -499,7 +510,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode_128k",
                     choices=["decode_128k", "decode_32k", "decode_1m", "gsa_128k", "prefill_64k", "tiny",
-                             "decode_128k_shared_kv"])
+                             "decode_128k_shared_kv", "hgsa_128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy used to calibrate HBM byte counters")
@@ -526,9 +537,9 @@ def main():
     from synth import configs as C
     cfgs = {"decode_128k": C.DECODE_128K, "decode_32k": C.DECODE_32K, "decode_1m": C.DECODE_1M,
             "gsa_128k": C.GSA_128K, "prefill_64k": C.PREFILL_64K, "tiny": C.TINY,
-            "decode_128k_shared_kv": C.DECODE_128K_SHARED_KV}
+            "decode_128k_shared_kv": C.DECODE_128K_SHARED_KV, "hgsa_128k": C.HGSA_128K}
     cfg = cfgs[args.config]
-    if args.config == "gsa_128k":
+    if args.config in ("gsa_128k", "hgsa_128k"):
         res = bench_gsa(cfg, args.steps, args.warmup)
     elif args.config == "prefill_64k":
         res = bench_prefill_indexer(cfg, args.steps, args.warmup)

@@ -197,6 +197,31 @@ int lct_gsa_decode(const uint16_t* q, const uint16_t* gk, const uint16_t* gv,
 int lct_gsa_decode_workspace_bytes(int BH, int D, int64_t Nc, int kc, size_t* bytes);
 
 /*
+ * GSA decode step with coarse-to-fine (hierarchical) routing.  Source: SSA
+ * article section 5 (H-SSA: a meta-gist after every few gists summarises
+ * them; the query picks the best meta-gists, then the best gists inside
+ * their groups, then unfolds those chunks) and GSA summary page section 2.4
+ * (gist-of-gist, coarse-to-fine selection, logarithmic routing cost).
+ *   mk bf16 [BH, ceil(Nc/group), D]  meta-gist keys; meta-gist g covers
+ *                                    gists [g*group, (g+1)*group) (the last
+ *                                    group may be short)
+ *   the km best meta-gists by q . mk (unscaled; ties to the lower group) are
+ *   kept, then the kc best of their gists by q . gk (ties to the lower
+ *   chunk); chunk_idx_out gets them ascending, -1 padded when the chosen
+ *   groups hold fewer than kc chunks.  Meta-gists only route: the attention
+ *   is lct_gsa_attn's over the chosen chunks' raw tokens and gists plus the
+ *   tail.  Other arguments as lct_gsa_decode.  Requires 1 <= km <=
+ *   ceil(Nc/group), ceil(Nc/group) <= 4096, km <= 64, km*group <= 4096,
+ *   kc <= 1024 (LCT_EUNSUPPORTED otherwise).  Key rows read by the routing:
+ *   ceil(Nc/group) + km*group per (batch, head) instead of Nc.
+ */
+int lct_hgsa_decode(const uint16_t* q, const uint16_t* mk, const uint16_t* gk, const uint16_t* gv,
+                    const uint16_t* rk, const uint16_t* rv, int32_t* chunk_idx_out, float* out, int BH,
+                    int D, int64_t Nc, int64_t raw_cap, int chunk, int group, int km, int kc,
+                    int tail_len, float scale, void* ws, size_t ws_bytes, void* stream);
+int lct_hgsa_decode_workspace_bytes(int BH, int D, int64_t Nc, int kc, int tail_len, size_t* bytes);
+
+/*
  * Layer-group driver (step 4).  Sources: CLSA explainer section 2.3
  * workflow (indexer once, shared index to every layer's selector);
  * tutorial IndexShare (4 layers share one index); IndexCache article

@@ -66,6 +66,9 @@ _SIGS = {
                         _f32, _vp, _sz, _vp], _i32),
     "lct_gsa_decode_workspace_bytes": ([_i32, _i32, _i64, _i32, _c.POINTER(_sz)], _i32),
     "lct_gsa_attn_workspace_bytes": ([_i32, _i32, _i32, _i32, _c.POINTER(_sz)], _i32),
+    "lct_hgsa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32,
+                         _i32, _i32, _f32, _vp, _sz, _vp], _i32),
+    "lct_hgsa_decode_workspace_bytes": ([_i32, _i32, _i64, _i32, _i32, _c.POINTER(_sz)], _i32),
     "lct_group_run": ([_c.POINTER(GroupDesc), _vp, _sz, _vp], _i32),
     "lct_group_workspace_bytes": ([_c.POINTER(GroupDesc), _c.POINTER(_sz)], _i32),
 }
@@ -290,6 +293,30 @@ def gsa_decode(q, gk, gv, rk, rv, kc: int, tail_len: int, scale: float, chunk: i
     _check(lib().lct_gsa_decode(_p(q), _p(gk), _p(gv), _p(rk), _p(rv), _p(idx_out), _p(out), BH, D,
                                 Nc, raw_cap, chunk, kc, tail_len, scale, _p(buf), buf.numel(),
                                 _stream()))
+    return out, idx_out
+
+
+def hgsa_decode(q, mk, gk, gv, rk, rv, group: int, km: int, kc: int, tail_len: int, scale: float,
+                chunk: int = 16, idx_out=None, out=None, ws: Optional[Workspace] = None):
+    """Coarse-to-fine routing (meta-gists, then gists of the km chosen groups,
+    kc chunks), unfold attention.  Returns (out, chunk_idx)."""
+    for t, n in ((q, "q"), (mk, "mk"), (gk, "gk"), (gv, "gv"), (rk, "rk"), (rv, "rv")):
+        _need(t, torch.bfloat16, n)
+    BH, D = q.shape
+    Nc = gk.shape[1]
+    raw_cap = rk.shape[1]
+    if out is None:
+        out = torch.empty((BH, D), dtype=torch.float32, device=q.device)
+    if idx_out is None:
+        idx_out = torch.empty((BH, kc), dtype=torch.int32, device=q.device)
+    _need(out, torch.float32, "out")
+    _need(idx_out, torch.int32, "idx_out")
+    nb = _sz()
+    _check(lib().lct_hgsa_decode_workspace_bytes(BH, D, Nc, kc, tail_len, _c.byref(nb)))
+    buf = _ws(ws).get(nb.value)
+    _check(lib().lct_hgsa_decode(_p(q), _p(mk), _p(gk), _p(gv), _p(rk), _p(rv), _p(idx_out), _p(out), BH,
+                                 D, Nc, raw_cap, chunk, group, km, kc, tail_len, scale, _p(buf),
+                                 buf.numel(), _stream()))
     return out, idx_out
 
 

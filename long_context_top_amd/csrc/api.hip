@@ -423,6 +423,50 @@ int lct_gsa_decode(const uint16_t* q, const uint16_t* gk, const uint16_t* gv,
   return LCT_OK;
 }
 
+int lct_hgsa_decode_workspace_bytes(int BH, int D, int64_t Nc, int kc, int tail_len, size_t* bytes) {
+  LCT_REQUIRE(bytes, "bytes is null");
+  LCT_REQUIRE(BH >= 1 && D >= 1 && Nc >= 1 && kc >= 1 && tail_len >= 0, "bad shape");
+  // gist scores (only the candidates' are written) + chunk ids + attention partials
+  const GsaLayout l = gsa_layout(BH, Nc, kc, tail_len);
+  *bytes = l.total - up256(topk_scratch_bytes(BH, Nc));
+  return LCT_OK;
+}
+
+int lct_hgsa_decode(const uint16_t* q, const uint16_t* mk, const uint16_t* gk, const uint16_t* gv,
+                    const uint16_t* rk, const uint16_t* rv, int32_t* chunk_idx_out, float* out, int BH,
+                    int D, int64_t Nc, int64_t raw_cap, int chunk, int group, int km, int kc,
+                    int tail_len, float scale, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate_gsa(q, rk, rv, gv, out, BH, D, Nc, raw_cap, chunk, kc, tail_len, scale);
+  if (rc) return rc;
+  LCT_REQUIRE(gk && aligned(gk, 16) && mk && aligned(mk, 16), "gk and mk must be non-null and 16-byte aligned");
+  LCT_REQUIRE(aligned(chunk_idx_out, 4), "misaligned chunk_idx_out");
+  LCT_REQUIRE(group >= 1 && km >= 1, "group and km must be >= 1");
+  const int64_t Nm = (Nc + group - 1) / group;
+  LCT_REQUIRE(km <= Nm, "km must be <= the number of meta-gists (ceil(Nc / group))");
+  if (Nm > HG_MAX_ITEMS || km > HG_MAX_KM || (int64_t)km * group > HG_MAX_ITEMS || kc > HG_MAX_KC)
+    return fail(LCT_EUNSUPPORTED, "hgsa: needs ceil(Nc/group) <= %d, km <= %d, km*group <= %d, kc <= %d",
+                HG_MAX_ITEMS, HG_MAX_KM, HG_MAX_ITEMS, HG_MAX_KC);
+  LCT_REQUIRE(ws != nullptr && aligned(ws, 256), "workspace must be non-null and 256-byte aligned");
+  size_t need = 0;
+  lct_hgsa_decode_workspace_bytes(BH, D, Nc, kc, tail_len, &need);
+  if (ws_bytes < need) return fail(LCT_ENOWORKSPACE, "hgsa_decode needs %zu workspace bytes, got %zu", need, ws_bytes);
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = as_stream(stream);
+  // layout: [gist scores][chunk ids][attention partials]
+  char* w = reinterpret_cast<char*>(ws);
+  float* sc = reinterpret_cast<float*>(w);
+  const size_t cidx_off = up256((size_t)BH * Nc * sizeof(float));
+  const size_t part_off = cidx_off + up256((size_t)BH * kc * sizeof(int32_t));
+  int32_t* cidx = chunk_idx_out ? chunk_idx_out : reinterpret_cast<int32_t*>(w + cidx_off);
+  LCT_HIP(launch_hgsa_route(q, mk, gk, sc, cidx, BH, Nc, (int)Nm, group, km, kc, st), "hgsa_decode: route");
+  const GsaPlan plan = gsa_plan(BH, kc, tail_len);
+  LCT_HIP(launch_gsa_attn(q, rk, rv, gv, sc, cidx, out, BH, Nc, raw_cap, kc, tail_len, scale, plan,
+                          reinterpret_cast<float*>(w + part_off), st),
+          "hgsa_decode: gsa_attn");
+  return LCT_OK;
+}
+
 // ------------------------------------------------------------- driver ----
 namespace {
 

@@ -137,4 +137,25 @@ LCT_DEV uint32_t window_shift(uint32_t lo, uint32_t hi, int nb_log2) {
   return bits > nb_log2 ? (uint32_t)(bits - nb_log2) : 0u;
 }
 
+// Descending bitonic sort of n (power of two) 64-bit values in LDS by the
+// NT threads of a block (every thread calls it).
+template <int NT>
+LCT_DEV void bitonic_sort_desc(uint64_t* a, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (n >> 1); i += NT) {
+        int lo = 2 * i - (i & (stride - 1));
+        int hi = lo + stride;
+        bool desc = (lo & size) == 0;
+        uint64_t x = a[lo], y = a[hi];
+        if (desc ? (x < y) : (x > y)) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 }  // namespace lct

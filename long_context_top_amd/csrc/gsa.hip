@@ -15,6 +15,12 @@
 // contiguous each, plus the gist's V row) with an fp32 online softmax.  The
 // gist's logit reuses the routing score (q . gist_key) instead of re-reading
 // the gist key.
+//
+// Hierarchical routing (SSA article section 5, H-SSA; GSA summary page
+// section 2.4): k_hgsa_route, one workgroup per (batch, head), scores the
+// meta-gists, keeps the best km groups, scores only the gists of those
+// groups and keeps the best kc chunks; it reads (Nm + km*group) key rows
+// instead of Nc, so the routing cost no longer grows with the whole context.
 
 #include "common.h"
 #include "kernels.h"
@@ -25,6 +31,7 @@ constexpr int GS_TILE = 1024;   // gists per workgroup
 constexpr int GSA_D = 128;
 constexpr int GSA_MAX_SPLITS = 32;  // slices of one (b, head) row merged by k_split_merge
 constexpr float GSA_LOG2E = 1.4426950408889634f;
+constexpr int HG_RANK_MAX = 1024;  // items ranked by counting (else a bitonic sort)
 
 template <int P>
 __global__ __launch_bounds__(256) void k_gist_score(const uint16_t* __restrict__ q,
@@ -242,6 +249,157 @@ __global__ __launch_bounds__(256) void k_gsa_attn(
     pp[D] = M;
     pp[D + 1] = Ls;
   }
+}
+
+// ------------------------------------------------------ hierarchical ----
+
+// Dot products of n bf16 key rows (D = 128, 256 bytes each) with the query:
+// 16 lanes per row, 16 bytes per lane (a wave reads 4 rows = 1 KiB
+// contiguous pieces per instruction), partial sums reduced over the 16 lanes;
+// the workgroup's 4 waves take rows 4w .. 4w+3, then every 16th, eight rows
+// per lane loaded at once.  row_of(i) names the key row of item i (i < n);
+// sink(i, score) is called by one lane per item.
+template <class RowOf, class Sink>
+LCT_DEV void hg_score_rows(const uint16_t* base, int n, const float (&qv)[8], RowOf row_of, Sink sink) {
+  constexpr int BATCH = 8;  // rows per lane loaded before any is used (one memory round trip)
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int sub = lane & 15, r4 = lane >> 4;
+  for (int i0 = wid * 4; i0 < n; i0 += BATCH * (HG_NT / 16)) {
+    uint4 raw[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int i = i0 + b * (HG_NT / 16) + r4;
+      raw[b] = *reinterpret_cast<const uint4*>(base + (size_t)row_of(i < n ? i : n - 1) * GSA_D + sub * 8);
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int i = i0 + b * (HG_NT / 16) + r4;
+      const uint32_t w[4] = {raw[b].x, raw[b].y, raw[b].z, raw[b].w};
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        part = fmaf(bf16_to_f32(w[j] & 0xFFFFu), qv[2 * j], part);
+        part = fmaf(bf16_to_f32(w[j] >> 16), qv[2 * j + 1], part);
+      }
+      part += __shfl_xor(part, 8, 16);
+      part += __shfl_xor(part, 4, 16);
+      part += __shfl_xor(part, 2, 16);
+      part += __shfl_xor(part, 1, 16);
+      if (sub == 0 && i < n) sink(i, part);
+    }
+  }
+}
+
+// Selection key: order-preserving score above, the inverted item id below,
+// so a descending sort puts the higher score first and, among equal scores,
+// the lower id; never 0 (that marks padding).
+LCT_DEV uint64_t hg_key(float s, uint32_t id) { return ((uint64_t)key_of_f32(s) << 32) | (0xFFFFFFFFu - id); }
+LCT_DEV uint32_t hg_id(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)key; }
+
+LCT_DEV int hg_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Of the n items in keys[] (0 = not an item), the k with the largest keys,
+// listed by item index ascending into sel[] (min(k, items) entries); returns
+// how many.  Items' keys are distinct.  Up to HG_RANK_MAX items each thread
+// ranks its items by counting (two short loops over LDS); beyond that a
+// bitonic sort (keys[] padded to a power of two) and a rank among the first k.
+LCT_DEV int hg_select(uint64_t* keys, uint8_t* flag, int n, int k, int32_t* sel) {
+  __shared__ int s_cnt;
+  if (threadIdx.x == 0) s_cnt = 0;
+  if (n <= HG_RANK_MAX) {
+    for (int i = threadIdx.x; i < n; i += HG_NT) {
+      const uint64_t ki = keys[i];
+      int r = 0;
+      for (int j = 0; j < n; ++j) r += keys[j] > ki ? 1 : 0;
+      flag[i] = (ki != 0 && r < k) ? 1 : 0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += HG_NT) {
+      if (!flag[i]) continue;
+      int pos = 0;
+      for (int j = 0; j < i; ++j) pos += flag[j];
+      sel[pos] = i;
+      atomicAdd(&s_cnt, 1);
+    }
+  } else {
+    const int n2 = hg_pow2(n);
+    for (int i = n + threadIdx.x; i < n2; i += HG_NT) keys[i] = 0;
+    // the sort orders keys, so the item index travels in the key's low bits
+    __syncthreads();
+    bitonic_sort_desc<HG_NT>(keys, n2);
+    for (int t = threadIdx.x; t < k; t += HG_NT) {
+      if (keys[t] == 0) continue;
+      const uint32_t it = hg_id(keys[t]);
+      int r = 0;
+      for (int u = 0; u < k; ++u) r += (keys[u] != 0 && hg_id(keys[u]) < it) ? 1 : 0;
+      sel[r] = (int32_t)it;
+      atomicAdd(&s_cnt, 1);
+    }
+  }
+  __syncthreads();
+  return s_cnt;
+}
+
+__global__ __launch_bounds__(HG_NT) void k_hgsa_route(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ mk, const uint16_t* __restrict__ gk,
+    float* __restrict__ gscores, int32_t* __restrict__ cidx, int64_t Nc, int Nm, int group, int km,
+    int kc) {
+  __shared__ uint64_t keys[HG_MAX_ITEMS];
+  __shared__ uint8_t flag[HG_MAX_ITEMS];
+  __shared__ int32_t gsel[HG_MAX_KM];
+  __shared__ int32_t csel[HG_MAX_KC];
+  const int64_t bh = blockIdx.x;
+  const int sub = threadIdx.x & 15;
+  float qv[8];
+  {
+    const uint4 raw = *reinterpret_cast<const uint4*>(q + bh * GSA_D + sub * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qv[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+      qv[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+  }
+  // 1. the km best meta-gists (groups), ascending
+  for (int i = threadIdx.x; i < Nm; i += HG_NT) keys[i] = 0;
+  __syncthreads();
+  hg_score_rows(mk + (size_t)bh * Nm * GSA_D, Nm, qv, [](int i) { return i; },
+                [&](int i, float s) { keys[i] = hg_key(s, (uint32_t)i); });
+  __syncthreads();
+  hg_select(keys, flag, Nm, km, gsel);
+  // 2. the kc best chunks among the chosen groups' gists; candidate p is
+  // chunk gsel[p / group] * group + p % group (ascending in p; past Nc in a
+  // short last group: no item)
+  const int nc_items = km * group;
+  for (int i = threadIdx.x; i < nc_items; i += HG_NT) keys[i] = 0;
+  __syncthreads();
+  auto chunk_of = [&](int p) -> int64_t { return (int64_t)gsel[p / group] * group + p % group; };
+  hg_score_rows(gk + (size_t)bh * Nc * GSA_D, nc_items, qv,
+                [&](int p) { const int64_t c = chunk_of(p); return c < Nc ? c : Nc - 1; },
+                [&](int p, float s) {
+                  const int64_t c = chunk_of(p);
+                  if (c < Nc) {
+                    keys[p] = hg_key(s, (uint32_t)p);  // ties: lower p = lower chunk
+                    gscores[bh * Nc + c] = s;          // the gist logit of the attention
+                  }
+                });
+  __syncthreads();
+  const int nch = hg_select(keys, flag, nc_items, kc, csel);
+  for (int t = threadIdx.x; t < kc; t += HG_NT)
+    cidx[bh * kc + t] = t < nch ? (int32_t)chunk_of(csel[t]) : -1;
+}
+
+hipError_t launch_hgsa_route(const uint16_t* q, const uint16_t* mk, const uint16_t* gk, float* gscores,
+                             int32_t* cidx, int BH, int64_t Nc, int Nm, int group, int km, int kc,
+                             hipStream_t st) {
+  if (Nm > HG_MAX_ITEMS || km > HG_MAX_KM || km > Nm || (int64_t)km * group > HG_MAX_ITEMS || kc > HG_MAX_KC)
+    return hipErrorInvalidValue;
+  k_hgsa_route<<<dim3((unsigned)BH), HG_NT, 0, st>>>(q, mk, gk, gscores, cidx, Nc, Nm, group, km, kc);
+  return hipGetLastError();
 }
 
 hipError_t launch_gsa_attn(const uint16_t* q, const uint16_t* rk, const uint16_t* rv,

@@ -110,6 +110,15 @@ struct GsaPlan {
   size_t part_bytes;
 };
 GsaPlan gsa_plan(int BH, int kc, int tail_len);
+// Hierarchical routing: one workgroup per (batch, head); limits on the
+// meta-gists, the candidate chunks (km * group), km and kc.
+constexpr int HG_NT = 256;
+constexpr int HG_MAX_ITEMS = 4096;
+constexpr int HG_MAX_KM = 64;
+constexpr int HG_MAX_KC = 1024;
+hipError_t launch_hgsa_route(const uint16_t* q, const uint16_t* mk, const uint16_t* gk, float* gscores,
+                             int32_t* cidx, int BH, int64_t Nc, int Nm, int group, int km, int kc,
+                             hipStream_t st);
 hipError_t launch_gsa_attn(const uint16_t* q, const uint16_t* rk, const uint16_t* rv,
                            const uint16_t* gv, const float* gscores, const int32_t* cidx,
                            float* out, int BH, int64_t Nc, int64_t raw_cap, int kc, int tail_len,

@@ -41,26 +41,6 @@ LCT_DEV uint32_t lane_rank(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Descending bitonic sort of n (power of two) 64-bit values in LDS.
-template <int NT>
-LCT_DEV void bitonic_sort_desc(uint64_t* a, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (n >> 1); i += NT) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool desc = (lo & size) == 0;
-        uint64_t x = a[lo], y = a[hi];
-        if (desc ? (x < y) : (x > y)) {
-          a[lo] = y;
-          a[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 // Histogram bin of a key; keys outside the window are clamped into the end
 // bins (cannot happen when the window was taken over the same keys).
 LCT_DEV uint32_t bin_of(uint32_t key, uint32_t lo, uint32_t shift, uint32_t nb) {

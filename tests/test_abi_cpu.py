@@ -29,7 +29,8 @@ def test_every_declared_symbol_is_exported():
         "lct_version", "lct_last_error", "lct_idx_score_i8", "lct_gist_score_bf16",
         "lct_topk_select", "lct_topk_workspace_bytes", "lct_sparse_attn_gather",
         "lct_sparse_attn_workspace_bytes", "lct_gsa_attn", "lct_gsa_attn_workspace_bytes",
-        "lct_gsa_decode", "lct_gsa_decode_workspace_bytes", "lct_group_run",
+        "lct_gsa_decode", "lct_gsa_decode_workspace_bytes", "lct_hgsa_decode",
+        "lct_hgsa_decode_workspace_bytes", "lct_group_run",
         "lct_group_workspace_bytes", "lct_prefill_index_i8",
         "lct_prefill_index_workspace_bytes"]), names
     so = ctypes.CDLL(lct.LIB_PATH)
@@ -197,3 +198,21 @@ def test_sparse_attn_workspace_sizes():
     assert nb.value >= 65536 * 4 * 2 * 8 * 130 * 4 + 65536 * 3 * 4
     # Hq not a multiple of Hkv
     assert L.lct_sparse_attn_workspace_bytes(1, 1, 6, 4, 128, 1000, 16, ctypes.byref(nb)) == lct.LCT_EINVAL
+
+
+def test_hgsa_validation():
+    L = lct.lib()
+    p = [FAKE] * 8
+    ws = FAKE
+    # km above the number of meta-gists (ceil(1000 / 64) = 16)
+    assert L.lct_hgsa_decode(*p, 4, 128, 1000, 1000 * 16 + 16, 16, 64, 17, 8, 1, 0.1, ws, 1 << 26,
+                             None) == lct.LCT_EINVAL
+    # candidates km * group above 4096
+    assert L.lct_hgsa_decode(*p, 4, 128, 100000, 100000 * 16 + 16, 16, 128, 40, 8, 1, 0.1, ws, 1 << 30,
+                             None) == lct.LCT_EUNSUPPORTED
+    # group 0
+    assert L.lct_hgsa_decode(*p, 4, 128, 1000, 1000 * 16 + 16, 16, 0, 1, 8, 1, 0.1, ws, 1 << 26,
+                             None) == lct.LCT_EINVAL
+    nb = ctypes.c_size_t()
+    assert L.lct_hgsa_decode_workspace_bytes(16, 128, 8192, 64, 1, ctypes.byref(nb)) == 0
+    assert nb.value >= 16 * 8192 * 4 + 16 * 64 * 4

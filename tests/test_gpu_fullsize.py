@@ -155,3 +155,30 @@ def test_causal_prefill_64k_full_size():
     assert np.abs(host(out[2])[0, sample] - ref).max() < ATOL
     del qi, ki, q, k, v, out, idx_out, run
     _free()
+
+
+def test_hgsa_128k_b16_full_size():
+    cfg = C.HGSA_128K
+    announce(cfg.name)
+    BH = cfg.B * cfg.H
+
+    def mk(spec):
+        t = sd.make(cfg, spec)
+        return t.view((BH,) + tuple(t.shape[2:]))
+
+    qv, mkeys, gk, gv, rk, rv = (mk(cfg.q_spec()), mk(cfg.mk_spec()), mk(cfg.gk_spec()), mk(cfg.gv_spec()),
+                                 mk(cfg.rk_spec()), mk(cfg.rv_spec()))
+    out, cidx = lct.hgsa_decode(qv, mkeys, gk, gv, rk, rv, cfg.group, cfg.km, cfg.kc, cfg.tail_len,
+                                cfg.scale)
+    torch.cuda.synchronize()
+    got_idx, got = host(cidx), host(out)
+    for i in range(BH):
+        _check_index_rows(got_idx[i], cfg.Nc, cfg.kc, cfg.Nc)
+    pairs = [(0, 0), (3, 7), (9, 15), (15, 2)]
+    ref_idx, ref_out = oracle.driver.hgsa_step(cfg, pairs)
+    for j, (b, h) in enumerate(pairs):
+        i = b * cfg.H + h
+        assert np.array_equal(got_idx[i], ref_idx[j]), (b, h)
+        assert np.abs(got[i] - ref_out[j]).max() < ATOL, (b, h)
+    del qv, mkeys, gk, gv, rk, rv, out, cidx
+    _free()

@@ -309,6 +309,28 @@ def test_gist_score_and_gsa_decode(tail):
     assert np.abs(host(out) - ref_out).max() < ATOL
 
 
+@pytest.mark.parametrize("Nc,group,km,kc,tail", [(300, 16, 3, 8, 1), (300, 4, 2, 16, 0),
+                                                  (1000, 64, 4, 64, 16), (2049, 1, 64, 64, 5),
+                                                  (513, 512, 2, 100, 1)])
+def test_hgsa_decode(Nc, group, km, kc, tail):
+    """Coarse-to-fine routing against the oracle: short last groups, fewer
+    candidates than kc (-1 padding), groups of one gist, two groups only."""
+    from synth import configs as C
+    from tests.gpu_util import dev_bf16_bits
+    announce(f"hgsa decode Nc={Nc} group={group} km={km} kc={kc} tail={tail}")
+    cfg = C.GsaConfig("t_hgsa", 700 + Nc + group, B=2, H=3, D=128, Nc=Nc, chunk=16, kc=kc,
+                      tail_len=tail, group=group, km=km)
+    inp = _gsa_inputs(cfg)
+    inp["mk"] = C.make(cfg, cfg.mk_spec())
+    BH = cfg.B * cfg.H
+    dv = {k: dev_bf16_bits(v.reshape((BH,) + v.shape[2:])) for k, v in inp.items()}
+    out, cidx = lct.hgsa_decode(dv["q"], dv["mk"], dv["gk"], dv["gv"], dv["rk"], dv["rv"], group, km, kc,
+                                tail, cfg.scale)
+    ref_idx, ref_out = oracle.driver.hgsa_step(cfg)
+    assert np.array_equal(host(cidx), ref_idx)
+    assert np.abs(host(out) - ref_out).max() < ATOL
+
+
 def test_gsa_raw_path_sensitivity():
     """Ternary gist keys keep gist logits small so raw tokens carry real weight."""
     from tests.gpu_util import dev_bf16_bits
