@@ -306,6 +306,61 @@ def bench_gsa(cfg, steps, warmup):
     return res
 
 
+# ----------------------------------------------------------- GSA prefill ----
+
+def gsa_prefill_pairs(cfg) -> int:
+    """Visible (query, key) pairs under the gist mask for one (batch, head):
+    raw token i of chunk c sees c gists and i + 1 raw tokens, gist c sees
+    c + 1 gists and the chunk's raw tokens."""
+    nc, ch = cfg.Nc, cfg.chunk
+    raw = ch * nc * (nc - 1) // 2 + nc * ch * (ch + 1) // 2
+    gist = nc * (nc + 1) // 2 + nc * ch
+    return raw + gist
+
+
+def bench_gsa_prefill(cfg, steps, warmup):
+    """Every raw and gist token of the sequence attends under the gist mask
+    (lct_gsa_prefill).  Throughput: bf16 flops of the visible pairs (QK and
+    PV: 4 per pair and feature) against the dense bf16 MFMA peak."""
+    import torch
+
+    import long_context_top_amd as lct
+    import synth.device as sd
+
+    dev = torch.device("cuda", 0)
+    BH = cfg.B * cfg.H
+
+    def mk(spec):
+        t = sd.make(cfg, spec, dev)
+        return t.view((BH,) + tuple(t.shape[2:]))
+
+    qr, qg, rk, rv, gk, gv = (mk(cfg.qr_spec()), mk(cfg.qg_spec()), mk(cfg.rk_spec()), mk(cfg.rv_spec()),
+                              mk(cfg.gk_spec()), mk(cfg.gv_spec()))
+    out_r = torch.empty((BH, cfg.Nc * cfg.chunk, cfg.D), dtype=torch.float32, device=dev)
+    out_g = torch.empty((BH, cfg.Nc, cfg.D), dtype=torch.float32, device=dev)
+    f = lambda: lct.gsa_prefill(qr, qg, rk, rv, gk, gv, cfg.scale, out_raw=out_r, out_gist=out_g)
+    for _ in range(max(warmup, 1)):
+        f()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        f()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    flops = 4.0 * cfg.D * gsa_prefill_pairs(cfg) * BH
+    tf = flops / (ms * 1e-3) / 1e12
+    tokens = cfg.B * cfg.Nc * (cfg.chunk + 1)
+    return {"workload": cfg.name, "ms_per_prefill": ms, "tokens_per_s": tokens / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "kernel": "k_gsa_prefill (raw and gist queries)", "achieved": tf,
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                         "flops_per_launch": flops, "us_per_launch": ms * 1e3}}
+
+
 # --------------------------------------------------------------- prefill ----
 
 def bench_prefill_indexer(cfg, steps, warmup):
@@ -510,7 +565,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode_128k",
                     choices=["decode_128k", "decode_32k", "decode_1m", "gsa_128k", "prefill_64k", "tiny",
-                             "decode_128k_shared_kv", "hgsa_128k"])
+                             "decode_128k_shared_kv", "hgsa_128k", "gsa_prefill_128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy used to calibrate HBM byte counters")
@@ -537,10 +592,13 @@ def main():
     from synth import configs as C
     cfgs = {"decode_128k": C.DECODE_128K, "decode_32k": C.DECODE_32K, "decode_1m": C.DECODE_1M,
             "gsa_128k": C.GSA_128K, "prefill_64k": C.PREFILL_64K, "tiny": C.TINY,
-            "decode_128k_shared_kv": C.DECODE_128K_SHARED_KV, "hgsa_128k": C.HGSA_128K}
+            "decode_128k_shared_kv": C.DECODE_128K_SHARED_KV, "hgsa_128k": C.HGSA_128K,
+            "gsa_prefill_128k": C.GSA_PREFILL_128K}
     cfg = cfgs[args.config]
     if args.config in ("gsa_128k", "hgsa_128k"):
         res = bench_gsa(cfg, args.steps, args.warmup)
+    elif args.config == "gsa_prefill_128k":
+        res = bench_gsa_prefill(cfg, args.steps, args.warmup)
     elif args.config == "prefill_64k":
         res = bench_prefill_indexer(cfg, args.steps, args.warmup)
     else:

@@ -222,6 +222,27 @@ int lct_hgsa_decode(const uint16_t* q, const uint16_t* mk, const uint16_t* gk, c
 int lct_hgsa_decode_workspace_bytes(int BH, int D, int64_t Nc, int kc, int tail_len, size_t* bytes);
 
 /*
+ * GSA prefill: attention of every raw and gist token under the gist mask.
+ * Source: SSA article section 4 (a segment's raw tokens see one another and
+ * the gists of all earlier segments, never earlier segments' raw tokens) and
+ * section 6 (global key columns moved in front: a dense block of gists plus
+ * a diagonal band; softmax is unchanged by the key order).  Causal order is
+ * the interleaved one (chunk c's 16 raw tokens, then its gist): raw token i
+ * of chunk c attends to gists 0..c-1 and raw tokens 0..i of chunk c; gist c
+ * to gists 0..c and the 16 raw tokens of chunk c.  No attention anchors.
+ *   q_raw    bf16 [BH, Nc*chunk, D]   raw-token queries
+ *   q_gist   bf16 [BH, Nc, D]         gist-token queries
+ *   rk, rv   bf16 [BH, raw_cap, D]    raw keys/values (rows [0, Nc*chunk) used)
+ *   gk, gv   bf16 [BH, Nc, D]         gist keys/values
+ *   out_raw  fp32 [BH, Nc*chunk, D],  out_gist fp32 [BH, Nc, D]
+ * Requires chunk == 16, D == 128; one (batch, head) array < 2 GiB.  No
+ * workspace; fp32 online softmax, bf16 MFMA products.
+ */
+int lct_gsa_prefill(const uint16_t* q_raw, const uint16_t* q_gist, const uint16_t* rk, const uint16_t* rv,
+                    const uint16_t* gk, const uint16_t* gv, float* out_raw, float* out_gist, int BH, int D,
+                    int64_t Nc, int64_t raw_cap, int chunk, float scale, void* stream);
+
+/*
  * Layer-group driver (step 4).  Sources: CLSA explainer section 2.3
  * workflow (indexer once, shared index to every layer's selector);
  * tutorial IndexShare (4 layers share one index); IndexCache article

@@ -69,6 +69,7 @@ _SIGS = {
     "lct_hgsa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32,
                          _i32, _i32, _f32, _vp, _sz, _vp], _i32),
     "lct_hgsa_decode_workspace_bytes": ([_i32, _i32, _i64, _i32, _i32, _c.POINTER(_sz)], _i32),
+    "lct_gsa_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _f32, _vp], _i32),
     "lct_group_run": ([_c.POINTER(GroupDesc), _vp, _sz, _vp], _i32),
     "lct_group_workspace_bytes": ([_c.POINTER(GroupDesc), _c.POINTER(_sz)], _i32),
 }
@@ -318,6 +319,27 @@ def hgsa_decode(q, mk, gk, gv, rk, rv, group: int, km: int, kc: int, tail_len: i
                                  D, Nc, raw_cap, chunk, group, km, kc, tail_len, scale, _p(buf),
                                  buf.numel(), _stream()))
     return out, idx_out
+
+
+def gsa_prefill(q_raw, q_gist, rk, rv, gk, gv, scale: float, chunk: int = 16, out_raw=None, out_gist=None):
+    """Every raw and gist token's attention under the gist mask.
+    q_raw [BH, Nc*chunk, D], q_gist [BH, Nc, D], rk/rv [BH, raw_cap, D], gk/gv [BH, Nc, D]
+    -> (out_raw fp32 [BH, Nc*chunk, D], out_gist fp32 [BH, Nc, D])."""
+    for t, n in ((q_raw, "q_raw"), (q_gist, "q_gist"), (rk, "rk"), (rv, "rv"), (gk, "gk"), (gv, "gv")):
+        _need(t, torch.bfloat16, n)
+    BH, Nc, D = gk.shape
+    raw_cap = rk.shape[1]
+    if q_raw.shape != (BH, Nc * chunk, D) or q_gist.shape != (BH, Nc, D):
+        raise ValueError("q_raw must be [BH, Nc*chunk, D] and q_gist [BH, Nc, D]")
+    if out_raw is None:
+        out_raw = torch.empty((BH, Nc * chunk, D), dtype=torch.float32, device=gk.device)
+    if out_gist is None:
+        out_gist = torch.empty((BH, Nc, D), dtype=torch.float32, device=gk.device)
+    _need(out_raw, torch.float32, "out_raw")
+    _need(out_gist, torch.float32, "out_gist")
+    _check(lib().lct_gsa_prefill(_p(q_raw), _p(q_gist), _p(rk), _p(rv), _p(gk), _p(gv), _p(out_raw), _p(out_gist),
+                                 BH, D, Nc, raw_cap, chunk, scale, _stream()))
+    return out_raw, out_gist
 
 
 class GroupRun:

@@ -21,7 +21,8 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-LCT_SOURCES = ["api.hip", "topk.hip", "idx_score.hip", "attn.hip", "gsa.hip", "prefill.hip", "misc.hip"]
+LCT_SOURCES = ["api.hip", "topk.hip", "idx_score.hip", "attn.hip", "gsa.hip", "gsa_prefill.hip", "prefill.hip",
+               "misc.hip"]
 
 
 def _run(cmd):

@@ -467,6 +467,28 @@ int lct_hgsa_decode(const uint16_t* q, const uint16_t* mk, const uint16_t* gk, c
   return LCT_OK;
 }
 
+int lct_gsa_prefill(const uint16_t* q_raw, const uint16_t* q_gist, const uint16_t* rk, const uint16_t* rv,
+                    const uint16_t* gk, const uint16_t* gv, float* out_raw, float* out_gist, int BH, int D,
+                    int64_t Nc, int64_t raw_cap, int chunk, float scale, void* stream) {
+  LCT_REQUIRE(q_raw && q_gist && rk && rv && gk && gv && out_raw && out_gist, "null tensor pointer");
+  LCT_REQUIRE(aligned(q_raw, 16) && aligned(q_gist, 16) && aligned(rk, 16) && aligned(rv, 16) && aligned(gk, 16) &&
+                  aligned(gv, 16) && aligned(out_raw, 16) && aligned(out_gist, 16),
+              "misaligned tensor");
+  LCT_REQUIRE(BH >= 1 && Nc >= 1, "bad BH / Nc");
+  LCT_REQUIRE(raw_cap >= Nc * chunk, "raw_cap must hold Nc*chunk rows");
+  LCT_REQUIRE(std::isfinite(scale), "scale must be finite");
+  if (chunk != 16) return fail(LCT_EUNSUPPORTED, "chunk %d (only 16 is built)", chunk);
+  if (D != 128) return fail(LCT_EUNSUPPORTED, "head dim %d (only 128 is built)", D);
+  if (raw_cap * D * 2 >= ((int64_t)1 << 31) || Nc * D * 2 >= ((int64_t)1 << 31))
+    return fail(LCT_EUNSUPPORTED, "one (batch, head) K or V array must be < 2 GiB");
+  int rc = check_device();
+  if (rc) return rc;
+  LCT_HIP(launch_gsa_prefill(q_raw, q_gist, rk, rv, gk, gv, out_raw, out_gist, BH, Nc, raw_cap, scale,
+                             as_stream(stream)),
+          "gsa_prefill");
+  return LCT_OK;
+}
+
 // ------------------------------------------------------------- driver ----
 namespace {
 

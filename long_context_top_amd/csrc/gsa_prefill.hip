@@ -1,0 +1,292 @@
+// GSA prefill attention under the gist mask for gfx950.
+//
+// Sources: SSA article section 4 (the gist mask: a segment's raw tokens see
+// one another and every earlier segment's gist tokens, never the raw tokens
+// of earlier segments), section 6 (prefill kernel: the global key columns
+// are moved in front, which leaves softmax unchanged, so the pattern becomes
+// a dense thin block -- the gists -- plus a diagonal band -- the segment's
+// own raw tokens).
+//
+// The keys arrive already in that order: the gist keys and values are their
+// own arrays ([BH, Nc, D]) and so are the raw ones ([BH, raw_cap, D]).  A
+// raw query of chunk c attends to gists [0, c) (a prefix of the gist array,
+// no mask) and to its own chunk's raw tokens up to itself; a gist query of
+// chunk c to gists [0, c] and its chunk's 16 raw tokens.
+//
+// Work: one workgroup of 4 waves per 64 queries (raw: 4 chunks, one per
+// wave; gist: 64 gists, 16 per wave), each wave 16 queries as the columns of
+// v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, O^T += V^T P^T, as in the sparse
+// attention kernel).  The workgroup walks its key tiles of 64 rows (the gist
+// prefix, then the band) through two LDS buffers filled by buffer loads to
+// LDS, so each key row is read once per workgroup and serves its 4 waves;
+// rows are stored with their 16-byte chunks XOR-swizzled by row so that the
+// A-operand reads and the transposed V reads hit distinct banks.  Raw
+// queries and outputs are [BH, Nc*16, D], gist ones [BH, Nc, D].  Tiles a
+// wave cannot see are skipped by it, tiles it sees whole take an unmasked
+// softmax.  Workgroups are launched heaviest first (the gist prefix grows
+// with the chunk index).
+
+#include "common.h"
+#include "kernels.h"
+
+namespace lct {
+
+constexpr int GP_D = 128;
+constexpr int GP_CHUNK = 16;
+constexpr int GP_TILE = 64;                  // key rows per tile
+constexpr int GP_NW = 4;                     // waves per workgroup
+constexpr int GP_ROWB = GP_D * 2;            // bytes per key row
+constexpr int GP_TILEB = GP_TILE * GP_ROWB;  // 16 KiB
+constexpr float GP_LOG2E = 1.4426950408889634f;
+
+typedef __attribute__((address_space(3))) short4v gp_lds_short4v;
+typedef __attribute__((address_space(3))) void gp_lds_void;
+
+// s_waitcnt vmcnt(0), lgkmcnt(0) (expcnt left at its maximum)
+#define GP_WAIT_VM0() __builtin_amdgcn_s_waitcnt(0x0F70)
+#define GP_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+LCT_DEV void gp_fence() { __asm__ __volatile__("" ::: "memory"); }
+
+// Byte offset of 16-byte chunk c of tile row r: the chunk index is XORed
+// with s(r) = 2*(r % 8) + (r / 8) % 2, a permutation of 0..15 over 16 rows
+// (the A-operand reads: 16 rows, one chunk) that keeps the pairs of chunks
+// (2i, 2i+1) together and gives 4 consecutive rows different pairs (the
+// transposed V reads: 4 rows x 2 chunks per 16 lanes).
+LCT_DEV int gp_swz(int r, int c) { return r * GP_ROWB + 16 * (c ^ (((r & 7) << 1) | ((r >> 3) & 1))); }
+
+// DMA of key/value rows [row0, row0 + n) (n <= 64; rows past n repeat the
+// last one: finite data, masked out) into a tile.  16 instructions of 1 KiB
+// per array, 4 per wave: instruction i holds tile rows 4i .. 4i+3, lane l
+// the 16 bytes of row 4i + l/16 that the swizzle puts at slot l % 16.
+LCT_DEV void gp_dma(__amdgpu_buffer_rsrc_t rs, int row0, int n, char* tile, int wid, int lane) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = wid * 4 + u;
+    const int r = 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    const int rg = row0 + (r < n ? r : n - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gp_lds_void*)(tile + i * 1024), 16, rg * GP_ROWB + c * 16, 0, 0,
+                                             0);
+  }
+}
+
+// Mask of one tile for one wave: which (key row, query) pairs are visible.
+// seg 0: gist keys, seg 1: raw keys.  qid: raw -> the wave's chunk; gist ->
+// the wave's first gist (query hl is gist qid + hl).
+template <bool GQ>
+LCT_DEV bool gp_visible(int seg, int64_t key, int64_t qid, int hl) {
+  if (!GQ) {
+    if (seg == 0) return key < qid;                                        // earlier gists
+    return key / GP_CHUNK == qid && key % GP_CHUNK <= hl;                  // own chunk, causal
+  }
+  if (seg == 0) return key <= qid + hl;                                    // earlier gists and itself
+  return key / GP_CHUNK == qid + hl;                                       // its chunk's raw tokens
+}
+
+// 0: the wave sees no pair of the tile, 2: every pair, 1: some.
+template <bool GQ>
+LCT_DEV int gp_tile_class(int seg, int64_t r0, int n, int64_t qid) {
+  if (!GQ) {
+    if (seg == 0) return r0 >= qid ? 0 : (r0 + GP_TILE <= qid && n == GP_TILE ? 2 : 1);
+    return (r0 + n <= qid * GP_CHUNK || r0 >= (qid + 1) * GP_CHUNK) ? 0 : 1;
+  }
+  if (seg == 0) return r0 > qid + 15 ? 0 : (r0 + GP_TILE - 1 <= qid && n == GP_TILE ? 2 : 1);
+  return (r0 + n <= qid * GP_CHUNK || r0 >= (qid + 16) * GP_CHUNK) ? 0 : 1;
+}
+
+template <bool GQ>
+__global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ qg, const uint16_t* __restrict__ rk,
+    const uint16_t* __restrict__ rv, const uint16_t* __restrict__ gk, const uint16_t* __restrict__ gv,
+    float* __restrict__ outr, float* __restrict__ outg, int64_t Nc, int64_t raw_cap, float scale_log2,
+    int wg_per_bh) {
+  constexpr int D = GP_D;
+  __shared__ __attribute__((aligned(16))) char tk0[GP_TILEB];
+  __shared__ __attribute__((aligned(16))) char tv0[GP_TILEB];
+  __shared__ __attribute__((aligned(16))) char tk1[GP_TILEB];
+  __shared__ __attribute__((aligned(16))) char tv1[GP_TILEB];
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int hl = lane & 15, kg = lane >> 4;
+  const int64_t bh = blockIdx.x / wg_per_bh;
+  const int64_t j = wg_per_bh - 1 - (int64_t)(blockIdx.x % wg_per_bh);  // heaviest first
+  // queries: raw -> chunk qid's 16 tokens; gist -> gists qid .. qid+15
+  const int64_t qid = GQ ? 64 * j + 16 * wid : 4 * j + wid;
+  const bool wave_live = qid < Nc;
+  // key segments: the gist prefix the workgroup's last query sees, then the band
+  const int64_t na = GQ ? std::min<int64_t>(Nc, 64 * j + 64) : std::min<int64_t>(Nc, 4 * j + 3);
+  const int64_t b0 = GQ ? 64 * j * GP_CHUNK : 4 * j * GP_CHUNK;
+  const int64_t nb = GQ ? std::min<int64_t>(64 * GP_CHUNK, (Nc - 64 * j) * GP_CHUNK)
+                        : std::min<int64_t>(4 * GP_CHUNK, (Nc - 4 * j) * GP_CHUNK);
+  const int ta = (int)((na + GP_TILE - 1) / GP_TILE);
+  const int tb = (int)((nb + GP_TILE - 1) / GP_TILE);
+  const int nt = ta + tb;
+  const __amdgpu_buffer_rsrc_t grs_k = make_rsrc(gk + bh * Nc * D, Nc * GP_ROWB);
+  const __amdgpu_buffer_rsrc_t grs_v = make_rsrc(gv + bh * Nc * D, Nc * GP_ROWB);
+  const __amdgpu_buffer_rsrc_t rrs_k = make_rsrc(rk + bh * raw_cap * D, raw_cap * GP_ROWB);
+  const __amdgpu_buffer_rsrc_t rrs_v = make_rsrc(rv + bh * raw_cap * D, raw_cap * GP_ROWB);
+  auto tile_of = [&](int t, int& seg, int64_t& r0, int& n) {
+    if (t < ta) {
+      seg = 0;
+      r0 = (int64_t)t * GP_TILE;
+      n = (int)std::min<int64_t>(GP_TILE, na - r0);
+    } else {
+      seg = 1;
+      r0 = b0 + (int64_t)(t - ta) * GP_TILE;
+      n = (int)std::min<int64_t>(GP_TILE, b0 + nb - r0);
+    }
+  };
+  auto issue = [&](int t, char* tk, char* tv) {
+    int seg, n;
+    int64_t r0;
+    tile_of(t, seg, r0, n);
+    gp_dma(seg == 0 ? grs_k : rrs_k, (int)r0, n, tk, wid, lane);
+    gp_dma(seg == 0 ? grs_v : rrs_v, (int)r0, n, tv, wid, lane);
+  };
+
+  // query fragment (B operand): lane (hl, kg) holds query hl, features st*32 + kg*8 ..
+  bf16x8 qf[4];
+  {
+    const int64_t qrow = GQ ? std::min<int64_t>(qid + hl, Nc - 1) : std::min<int64_t>(qid, Nc - 1) * GP_CHUNK + hl;
+    const uint16_t* qp = (GQ ? qg + (bh * Nc + qrow) * D : qr + (bh * Nc * GP_CHUNK + qrow) * D) + kg * 8;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qp + st * 32);
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+  float m = -INFINITY;
+  floatx4 lacc = floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // transposed V read of this lane: token 4*kg + hl/4 of a block, features
+  // 16*dt + 4*(hl%4) .. +3 -> chunk 2*dt + (hl%4)/2, byte 8*(hl%2)
+  const int trt = 4 * kg + (hl >> 2);
+
+  auto compute = [&](int t, const char* tk, const char* tv) {
+    int seg, n;
+    int64_t r0;
+    tile_of(t, seg, r0, n);
+    const int cls = wave_live ? gp_tile_class<GQ>(seg, r0, n, qid) : 0;
+    if (cls == 0) return;  // uniform over the wave
+    // S^T = K Q^T: sacc[jb][e] = S^T[key 16jb + 4kg + e][query hl]
+    floatx4 sacc[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      sacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * jb + hl;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(tk + gp_swz(r, st * 4 + kg));
+        sacc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[st], sacc[jb], 0, 0, 0);
+      }
+    }
+    bool vis[4][4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kl = 16 * jb + 4 * kg + e;
+        vis[jb][e] = cls == 2 || (kl < n && gp_visible<GQ>(seg, r0 + kl, qid, hl));
+      }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, vis[jb][e] ? sacc[jb][e] : -INFINITY);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(m, tmax * scale_log2);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;  // a query with nothing visible yet
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);
+    m = mnew;
+    __bf16 pw[4][4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float w = __builtin_amdgcn_exp2f(fmaf(sacc[jb][e], scale_log2, -mref));
+        pw[jb][e] = (__bf16)(vis[jb][e] ? w : 0.f);
+      }
+    if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
+      lacc = lacc * alpha;
+    }
+    // O^T += V^T P^T, 32 keys (blocks 2h, 2h+1) per MFMA
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = pw[2 * h][e];
+        pf[4 + e] = pw[2 * h + 1][e];
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int c = 2 * dt + ((hl & 3) >> 1);
+        const int rlo = 16 * (2 * h) + trt, rhi = 16 * (2 * h + 1) + trt;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (gp_lds_short4v*)(tv + gp_swz(rlo, c) + 8 * (hl & 1)));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (gp_lds_short4v*)(tv + gp_swz(rhi, c) + 8 * (hl & 1)));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[dt], 0, 0, 0);
+      }
+      lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc, 0, 0, 0);
+    }
+  };
+
+  // two LDS buffers, the loop unrolled by two so every access names one of
+  // them; a tile's DMA is waited for by its issuing waves, then the barrier
+  // makes it visible to all and frees the other buffer for the next tile
+  if (nt > 0) issue(0, tk0, tv0);
+  for (int t = 0; t < nt; t += 2) {
+    GP_WAIT_VM0();
+    __syncthreads();
+    if (t + 1 < nt) issue(t + 1, tk1, tv1);
+    gp_fence();
+    compute(t, tk0, tv0);
+    gp_fence();
+    if (t + 1 >= nt) break;
+    GP_WAIT_VM0();
+    __syncthreads();
+    if (t + 2 < nt) issue(t + 2, tk0, tv0);
+    gp_fence();
+    compute(t + 1, tk1, tv1);
+    gp_fence();
+  }
+
+  // o[dt][e] = O^T[d = 16dt + 4kg + e][query hl]; lacc: query hl's denominator
+  if (!wave_live) return;
+  const float l = lacc[0];
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (GQ) {
+    if (qid + hl >= Nc) return;
+    float* op = outg + (bh * Nc + qid + hl) * D + kg * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(op + dt * 16) = o[dt] * inv;
+  } else {
+    float* op = outr + (bh * Nc * GP_CHUNK + qid * GP_CHUNK + hl) * D + kg * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(op + dt * 16) = o[dt] * inv;
+  }
+}
+
+hipError_t launch_gsa_prefill(const uint16_t* qr, const uint16_t* qg, const uint16_t* rk, const uint16_t* rv,
+                              const uint16_t* gk, const uint16_t* gv, float* outr, float* outg, int BH,
+                              int64_t Nc, int64_t raw_cap, float scale, hipStream_t st) {
+  const float sl2 = scale * GP_LOG2E;
+  const int wr = (int)((Nc + 3) / 4), wgq = (int)((Nc + 63) / 64);
+  if ((int64_t)BH * wr >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  k_gsa_prefill<false><<<dim3((unsigned)(BH * wr)), GP_NW * 64, 0, st>>>(qr, qg, rk, rv, gk, gv, outr, outg, Nc,
+                                                                        raw_cap, sl2, wr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_gsa_prefill<true><<<dim3((unsigned)(BH * wgq)), GP_NW * 64, 0, st>>>(qr, qg, rk, rv, gk, gv, outr, outg, Nc,
+                                                                        raw_cap, sl2, wgq);
+  return hipGetLastError();
+}
+
+}  // namespace lct

@@ -116,6 +116,11 @@ constexpr int HG_NT = 256;
 constexpr int HG_MAX_ITEMS = 4096;
 constexpr int HG_MAX_KM = 64;
 constexpr int HG_MAX_KC = 1024;
+// GSA prefill under the gist mask: raw queries/outputs [BH, Nc*16, D], gist
+// queries/outputs [BH, Nc, D], raw K/V [BH, raw_cap, D], gist K/V [BH, Nc, D].
+hipError_t launch_gsa_prefill(const uint16_t* qr, const uint16_t* qg, const uint16_t* rk, const uint16_t* rv,
+                              const uint16_t* gk, const uint16_t* gv, float* outr, float* outg, int BH,
+                              int64_t Nc, int64_t raw_cap, float scale, hipStream_t st);
 hipError_t launch_hgsa_route(const uint16_t* q, const uint16_t* mk, const uint16_t* gk, float* gscores,
                              int32_t* cidx, int BH, int64_t Nc, int Nm, int group, int km, int kc,
                              hipStream_t st);

@@ -22,8 +22,9 @@ Sources (web pages on long-context sparse attention):
   section (lightning indexer, top-k, 4 layers share one index), KV-cache
   volume section and the hands-on arithmetic section.
 * SSA article (arXiv 2604.20920) -- sections 2-3 (gist tokens, selective
-  unfolding, keep selected chunks' gists with their raw tokens), section 6
-  (key-order invariance, split decode with log-sum-exp merge).
+  unfolding, keep selected chunks' gists with their raw tokens), section 4
+  (the gist mask), section 5 (hierarchical gists), section 6 (key-order
+  invariance and the permuted prefill, split decode with log-sum-exp merge).
 * IndexCache article (arXiv 2603.12201) -- section 2 (Full / Shared layers),
   section 3 (the greedy search keeps Full layers at uneven places),
   section 6 (one conditional plus one temporary index buffer).
@@ -39,7 +40,8 @@ this package is "parity unpinned".
 from .indexer import index_scores, index_scores_row  # noqa: F401
 from .topk import select_topk  # noqa: F401
 from .attention import softmax_attention, sparse_attention_gqa  # noqa: F401
-from .gsa import gist_scores, gsa_key_positions, gsa_attention, gsa_select, hgsa_select  # noqa: F401
+from .gsa import (gist_scores, gsa_key_positions, gsa_attention, gsa_select, hgsa_select,  # noqa: F401
+                  gsa_prefill, gsa_prefill_rows, gsa_prefill_visible)
 from .driver import (decode_group, decode_layers, decode_step, decode_step_pattern,  # noqa: F401
                      gsa_step, hgsa_step, layer_owner, prefill_attention_rows, prefill_index_rows)
 from .sizes import kv_cache_gib, kv_bytes_per_token, scored_pairs  # noqa: F401

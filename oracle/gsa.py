@@ -23,6 +23,18 @@ Readings where the pages are silent or disagree:
   positions (including the current token) are always attended.
 * The gist logit in attention is the same ``q . gK`` product, scaled.
 
+Prefill under the gist mask: SSA article section 4 (continued pretraining:
+the text is cut into segments with gist tokens; a segment's raw tokens see
+one another and every earlier segment's gists, never earlier segments' raw
+tokens), section 6 (prefill kernel: the global columns -- gists and
+attention anchors -- are moved in front of the keys, which softmax does not
+mind, so the pattern becomes a dense thin block plus a diagonal band).
+Readings: causal order is the interleaved one (chunk c's raw tokens, then
+its gist); a segment's raw tokens see one another causally; a gist token
+sees its own segment's raw tokens, the earlier gists and itself; the
+attention anchors are the first ``n_sink`` raw positions of the sequence,
+seen by every later token (none in the workload).
+
 Hierarchical routing (H-GSA / H-SSA): SSA article section 5 (a meta-gist
 token after every few gist tokens summarises them; the query first picks the
 best meta-gists, then the best gists inside their groups, then unfolds those
@@ -95,3 +107,63 @@ def hgsa_select(q: np.ndarray, mk: np.ndarray, gk: np.ndarray, group: int, km: i
     out = np.full(kc, -1, dtype=np.int32)
     out[:chosen.size] = chosen
     return out
+
+
+def gsa_prefill_visible(n_chunks: int, chunk: int, n_sink: int = 0):
+    """The gist-mask pattern over the interleaved sequence: returns
+    ``(is_gist[T], chunk_of[T], raw_pos[T], vis[T, T])`` with T = n_chunks *
+    (chunk + 1); ``vis[t, s]`` is whether token t may attend to token s."""
+    T = n_chunks * (chunk + 1)
+    t = np.arange(T)
+    seg, off = t // (chunk + 1), t % (chunk + 1)
+    is_gist = off == chunk
+    raw_pos = np.where(is_gist, -1, seg * chunk + off)
+    earlier = t[None, :] <= t[:, None]                       # causal: s <= t
+    same_seg = seg[None, :] == seg[:, None]
+    sink = (~is_gist) & (raw_pos < n_sink)
+    vis = earlier & (is_gist[None, :] | same_seg | sink[None, :])
+    return is_gist, seg, raw_pos, vis
+
+
+def gsa_prefill(q_raw, q_gist, k_raw, v_raw, k_gist, v_gist, chunk: int, scale: float,
+                n_sink: int = 0):
+    """Attention of every raw and gist token under the gist mask.
+
+    Raw arrays ``[n_chunks*chunk, D]`` in token order, gist arrays
+    ``[n_chunks, D]``.  Returns ``(out_raw, out_gist)`` in float64.
+    """
+    n_chunks = np.asarray(k_gist).shape[0]
+    is_gist, seg, raw_pos, vis = gsa_prefill_visible(n_chunks, chunk, n_sink)
+    # the interleaved sequence's rows
+    idx_raw = np.where(is_gist, 0, raw_pos)
+    def seq(raw, gist):
+        raw, gist = np.asarray(raw, np.float64), np.asarray(gist, np.float64)
+        return np.where(is_gist[:, None], gist[seg], raw[idx_raw])
+    q, k, v = seq(q_raw, q_gist), seq(k_raw, k_gist), seq(v_raw, v_gist)
+    out = np.zeros((q.shape[0], v.shape[1]))
+    for t in range(q.shape[0]):
+        keys = np.nonzero(vis[t])[0]
+        out[t] = softmax_attention(q[t][None], k[keys], v[keys], scale)[0]
+    return out[~is_gist], out[is_gist]
+
+
+def gsa_prefill_rows(q_raw, q_gist, k_raw, v_raw, k_gist, v_gist, chunk: int, scale: float,
+                     raw_rows=(), gist_rows=(), n_sink: int = 0):
+    """Selected rows of :func:`gsa_prefill` (raw token ids, gist ids), each
+    from its own visible key list, without the full mask: raw token i of
+    chunk c sees the gists of chunks < c, the anchors before it and chunk c's
+    raw tokens up to itself; gist c sees the gists up to itself, the anchors
+    and chunk c's raw tokens."""
+    kr, vr = np.asarray(k_raw, np.float64), np.asarray(v_raw, np.float64)
+    kg, vg = np.asarray(k_gist, np.float64), np.asarray(v_gist, np.float64)
+
+    def run(q, c, last_raw, gists_upto):
+        raw_ids = set(range(c * chunk, last_raw + 1)) | set(range(min(n_sink, last_raw + 1)))
+        raw_ids = sorted(raw_ids)
+        keys = np.vstack([kg[:gists_upto], kr[raw_ids]])
+        vals = np.vstack([vg[:gists_upto], vr[raw_ids]])
+        return softmax_attention(np.asarray(q, np.float64)[None], keys, vals, scale)[0]
+
+    out_r = np.array([run(q_raw[t], t // chunk, t, t // chunk) for t in raw_rows]).reshape(-1, vr.shape[1])
+    out_g = np.array([run(q_gist[c], c, (c + 1) * chunk - 1, c + 1) for c in gist_rows]).reshape(-1, vg.shape[1])
+    return out_r, out_g

@@ -24,6 +24,7 @@ from . import BF16N, BF16U4, I8U4, tensor, values
 T_QI, T_KI, T_Q, T_K, T_V = 1, 2, 3, 4, 5
 T_GQ, T_GK, T_GV, T_RK, T_RV = 6, 7, 8, 9, 10
 T_MK = 11  # meta-gist keys (hierarchical GSA)
+T_QR, T_QG = 12, 13  # prefill queries of raw and gist tokens (GSA)
 
 
 def tid(kind_code: int, index: int = 0) -> int:
@@ -145,6 +146,14 @@ class GsaConfig:
     def mk_spec(self):
         return self.gist_kind, (self.B, self.H, self.Nm, self.D), tid(T_MK)
 
+    def qr_spec(self):
+        """Prefill: the raw tokens' queries."""
+        return BF16N, (self.B, self.H, self.Nc * self.chunk, self.D), tid(T_QR)
+
+    def qg_spec(self):
+        """Prefill: the gist tokens' queries."""
+        return BF16N, (self.B, self.H, self.Nc, self.D), tid(T_QG)
+
     def rk_spec(self):
         return BF16N, (self.B, self.H, self.raw_cap, self.D), tid(T_RK)
 
@@ -171,11 +180,15 @@ GSA_128K = GsaConfig("gsa_decode_128k_b16", 1004, B=16, H=16, D=128, Nc=8192, ch
 # GSA 128K with coarse-to-fine routing: 128 meta-gists of 64 gists each, 4
 # groups chosen, then the 64 best of their 256 chunks
 HGSA_128K = GSA_128K.with_(name="hgsa_decode_128k_b16", seed=1006, group=64, km=4)
+# GSA prefill under the gist mask: 128K raw tokens (8192 chunks + their
+# gists) for one sequence, 16 heads (the GSA decode workload's context)
+GSA_PREFILL_128K = GsaConfig("gsa_prefill_128k_h16", 1007, B=1, H=16, D=128, Nc=8192, chunk=16, kc=64,
+                             tail_len=0)
 DECODE_1M = DecodeConfig("sparse_decode_1m_b1", 1005, B=1, Lq=1, L=1048576, n_layers=28,
                          group=4, Hq=32, Hkv=4, D=128, H_idx=4, d_idx=64, topk=2048)
 
 ALL = {c.name: c for c in (TINY, DECODE_32K, DECODE_128K, PREFILL_64K, GSA_128K, DECODE_1M,
-                           DECODE_128K_SHARED_KV, HGSA_128K)}
+                           DECODE_128K_SHARED_KV, HGSA_128K, GSA_PREFILL_128K)}
 
 
 # ---- host-side generation helpers ----

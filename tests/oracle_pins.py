@@ -474,3 +474,67 @@ def pin_hgsa_select(hgsa_select, gsa_select):
         assert list(got) == want, (trial, nc, group, km, kc)
         if km >= nm:
             assert list(got) == list(gsa_select(q, gk, kc)), trial
+
+
+def _softmax_rows(q, k, v, scale):
+    """Direct softmax-weighted sum for one query (explicit exponentials)."""
+    z = (k @ q) * scale
+    w = np.exp(z - z.max())
+    return (w / w.sum()) @ v
+
+
+def pin_gsa_prefill(gsa_prefill, gsa_prefill_visible):
+    """The gist mask: one segment is plain causal attention; the gists-first
+    key order (the prefill kernel's permutation) gives the same outputs;
+    earlier segments' raw tokens and a raw token's own gist are invisible,
+    earlier gists visible; anchors are seen by every later token; the
+    visible counts per row have closed forms."""
+    rng = np.random.default_rng(17)
+    D, chunk, nc, scale = 8, 4, 5, 0.3
+    qr, kr, vr = (rng.standard_normal((nc * chunk, D)) for _ in range(3))
+    qg, kg, vg = (rng.standard_normal((nc, D)) for _ in range(3))
+    out_r, out_g = gsa_prefill(qr, qg, kr, vr, kg, vg, chunk, scale)
+    # one segment: causal attention over its raw tokens; its gist sees them all and itself
+    r1, g1 = gsa_prefill(qr[:chunk], qg[:1], kr[:chunk], vr[:chunk], kg[:1], vg[:1], chunk, scale)
+    for i in range(chunk):
+        assert np.allclose(r1[i], _softmax_rows(qr[i], kr[:i + 1], vr[:i + 1], scale), atol=1e-12)
+    assert np.allclose(g1[0], _softmax_rows(qg[0], np.vstack([kr[:chunk], kg[:1]]),
+                                            np.vstack([vr[:chunk], vg[:1]]), scale), atol=1e-12)
+    # gists first, then the segment's own raw tokens
+    for c in range(nc):
+        for i in range(chunk):
+            t = c * chunk + i
+            keys = np.vstack([kg[:c], kr[c * chunk:t + 1]])
+            vals = np.vstack([vg[:c], vr[c * chunk:t + 1]])
+            assert np.allclose(out_r[t], _softmax_rows(qr[t], keys, vals, scale), atol=1e-12), (c, i)
+        keys = np.vstack([kg[:c + 1], kr[c * chunk:(c + 1) * chunk]])
+        vals = np.vstack([vg[:c + 1], vr[c * chunk:(c + 1) * chunk]])
+        assert np.allclose(out_g[c], _softmax_rows(qg[c], keys, vals, scale), atol=1e-12), c
+    # earlier raw tokens invisible, earlier gists visible, own gist invisible to raw tokens
+    vr2 = vr.copy()
+    vr2[:chunk] += 1.0
+    o2, _ = gsa_prefill(qr, qg, kr, vr2, kg, vg, chunk, scale)
+    assert np.allclose(o2[chunk:], out_r[chunk:]) and not np.allclose(o2[:chunk], out_r[:chunk])
+    vg2 = vg.copy()
+    vg2[2] += 1.0
+    o3, _ = gsa_prefill(qr, qg, kr, vr, kg, vg2, chunk, scale)
+    assert np.allclose(o3[:3 * chunk], out_r[:3 * chunk]) and not np.allclose(o3[3 * chunk:], out_r[3 * chunk:])
+    # anchors: the first two raw positions are seen by every later token, not by earlier ones
+    vr3 = vr.copy()
+    vr3[1] += 1.0
+    o4, _ = gsa_prefill(qr, qg, kr, vr3, kg, vg, chunk, scale, n_sink=2)
+    o4b, _ = gsa_prefill(qr, qg, kr, vr, kg, vg, chunk, scale, n_sink=2)
+    assert np.allclose(o4[0], o4b[0]) and not np.allclose(o4[3 * chunk], o4b[3 * chunk])
+    # the per-row form (visible keys listed row by row) agrees with the mask form, anchors too
+    import oracle.gsa as G
+    for ns in (0, 3):
+        fr, fg = gsa_prefill(qr, qg, kr, vr, kg, vg, chunk, scale, n_sink=ns)
+        rr, rg = G.gsa_prefill_rows(qr, qg, kr, vr, kg, vg, chunk, scale, raw_rows=range(nc * chunk),
+                                    gist_rows=range(nc), n_sink=ns)
+        assert np.allclose(rr, fr, atol=1e-12) and np.allclose(rg, fg, atol=1e-12), ns
+    # visible keys per row: raw (c, i) sees c gists and i + 1 raw tokens; gist c sees c + 1 gists and chunk raw
+    is_gist, seg, raw_pos, vis = gsa_prefill_visible(nc, chunk)
+    for t in range(len(is_gist)):
+        c = seg[t]
+        want = c + 1 + chunk if is_gist[t] else c + (raw_pos[t] - c * chunk) + 1
+        assert vis[t].sum() == want, t

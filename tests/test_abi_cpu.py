@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
         "lct_topk_select", "lct_topk_workspace_bytes", "lct_sparse_attn_gather",
         "lct_sparse_attn_workspace_bytes", "lct_gsa_attn", "lct_gsa_attn_workspace_bytes",
         "lct_gsa_decode", "lct_gsa_decode_workspace_bytes", "lct_hgsa_decode",
-        "lct_hgsa_decode_workspace_bytes", "lct_group_run",
+        "lct_hgsa_decode_workspace_bytes", "lct_gsa_prefill", "lct_group_run",
         "lct_group_workspace_bytes", "lct_prefill_index_i8",
         "lct_prefill_index_workspace_bytes"]), names
     so = ctypes.CDLL(lct.LIB_PATH)
@@ -216,3 +216,13 @@ def test_hgsa_validation():
     nb = ctypes.c_size_t()
     assert L.lct_hgsa_decode_workspace_bytes(16, 128, 8192, 64, 1, ctypes.byref(nb)) == 0
     assert nb.value >= 16 * 8192 * 4 + 16 * 64 * 4
+
+
+def test_gsa_prefill_validation():
+    L = lct.lib()
+    p = [FAKE] * 8
+    # raw_cap too small
+    assert L.lct_gsa_prefill(*p, 2, 128, 100, 1599, 16, 0.1, None) == lct.LCT_EINVAL
+    # chunk other than 16, head dim other than 128
+    assert L.lct_gsa_prefill(*p, 2, 128, 100, 3200, 32, 0.1, None) == lct.LCT_EUNSUPPORTED
+    assert L.lct_gsa_prefill(*p, 2, 64, 100, 1600, 16, 0.1, None) == lct.LCT_EUNSUPPORTED

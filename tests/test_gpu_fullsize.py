@@ -182,3 +182,35 @@ def test_hgsa_128k_b16_full_size():
         assert np.abs(got[i] - ref_out[j]).max() < ATOL, (b, h)
     del qv, mkeys, gk, gv, rk, rv, out, cidx
     _free()
+
+
+def test_gsa_prefill_128k_h16_full_size():
+    cfg = C.GSA_PREFILL_128K
+    announce(cfg.name)
+    BH = cfg.B * cfg.H
+
+    def mk(spec):
+        t = sd.make(cfg, spec)
+        return t.view((BH,) + tuple(t.shape[2:]))
+
+    qr, qg, rk, rv, gk, gv = (mk(cfg.qr_spec()), mk(cfg.qg_spec()), mk(cfg.rk_spec()), mk(cfg.rv_spec()),
+                              mk(cfg.gk_spec()), mk(cfg.gv_spec()))
+    out_r, out_g = lct.gsa_prefill(qr, qg, rk, rv, gk, gv, cfg.scale)
+    torch.cuda.synchronize()
+    n_raw = cfg.Nc * cfg.chunk
+    raw_rows = [0, 1, 15, 16, 17, 1000, 16383, 16384, 70001, n_raw - 17, n_raw - 1]
+    gist_rows = [0, 1, 63, 64, 1000, 4097, cfg.Nc - 1]
+    f = synth.as_float
+    for h in (0, 9, 15):
+        idx = (np.array(0), np.array(h))
+        args = [f(spec[0], C.rows(cfg, spec, idx)) for spec in
+                (cfg.qr_spec(), cfg.qg_spec(), cfg.rk_spec(), cfg.rv_spec(), cfg.gk_spec(), cfg.gv_spec())]
+        args[2], args[3] = args[2][:n_raw], args[3][:n_raw]
+        want_r, want_g = oracle.gsa_prefill_rows(*args, cfg.chunk, cfg.scale, raw_rows=raw_rows,
+                                                 gist_rows=gist_rows)
+        got_r = host(out_r[h, raw_rows])
+        got_g = host(out_g[h, gist_rows])
+        assert np.abs(got_r - want_r).max() < ATOL, h
+        assert np.abs(got_g - want_g).max() < ATOL, h
+    del qr, qg, rk, rv, gk, gv, out_r, out_g
+    _free()

@@ -331,6 +331,31 @@ def test_hgsa_decode(Nc, group, km, kc, tail):
     assert np.abs(host(out) - ref_out).max() < ATOL
 
 
+@pytest.mark.parametrize("Nc,BH", [(1, 2), (3, 2), (4, 1), (5, 3), (67, 2), (130, 1)])
+def test_gsa_prefill_matches_oracle(Nc, BH):
+    """Every raw and gist token's output under the gist mask, against the
+    oracle's interleaved-sequence definition (partial workgroups of chunks
+    and of gists, one chunk, a few)."""
+    announce(f"gsa prefill Nc={Nc} BH={BH}")
+    r = _rng(900 + Nc)
+    chunk, D = 16, 128
+    raw_cap = Nc * chunk + 5  # room past the last chunk, unused
+    qr, qrh = dev_bf16(r.standard_normal((BH, Nc * chunk, D)))
+    qg, qgh = dev_bf16(r.standard_normal((BH, Nc, D)))
+    rk, rkh = dev_bf16(r.standard_normal((BH, raw_cap, D)))
+    rv, rvh = dev_bf16(r.standard_normal((BH, raw_cap, D)))
+    gk, gkh = dev_bf16(r.standard_normal((BH, Nc, D)))
+    gv, gvh = dev_bf16(r.standard_normal((BH, Nc, D)))
+    scale = 1.0 / math.sqrt(D)
+    out_r, out_g = lct.gsa_prefill(qr, qg, rk, rv, gk, gv, scale)
+    out_r, out_g = host(out_r), host(out_g)
+    for b in range(BH):
+        want_r, want_g = oracle.gsa_prefill(qrh[b], qgh[b], rkh[b, :Nc * chunk], rvh[b, :Nc * chunk], gkh[b],
+                                            gvh[b], chunk, scale)
+        assert np.abs(out_r[b] - want_r).max() < ATOL, b
+        assert np.abs(out_g[b] - want_g).max() < ATOL, b
+
+
 def test_gsa_raw_path_sensitivity():
     """Ternary gist keys keep gist logits small so raw tokens carry real weight."""
     from tests.gpu_util import dev_bf16_bits

@@ -270,3 +270,29 @@ def _hgsa_drops_short_group(q, mk, gk, group, km, kc):
 @pytest.mark.parametrize("mut", [_hgsa_meta_ties_high, _hgsa_flat, _hgsa_drops_short_group])
 def test_hgsa_mutants_caught(mut):
     _fails(P.pin_hgsa_select, mut, GSA.gsa_select)
+
+
+# ---- GSA prefill (gist mask) ----
+
+_VISIBLE = GSA.gsa_prefill_visible
+
+
+def _visible_mutant(kind):
+    def vis_fn(n_chunks, chunk, n_sink=0):
+        is_gist, seg, raw_pos, vis = _VISIBLE(n_chunks, chunk, n_sink)
+        T = len(is_gist)
+        t = np.arange(T)
+        if kind == "full_causal":        # earlier raw tokens visible
+            vis = t[None, :] <= t[:, None]
+        elif kind == "non_causal":       # future tokens of the segment visible
+            vis = vis | (seg[None, :] == seg[:, None])
+        elif kind == "gist_not_self":    # a gist does not see itself
+            vis = vis & ~(np.eye(T, dtype=bool) & is_gist[:, None])
+        return is_gist, seg, raw_pos, vis
+    return vis_fn
+
+
+@pytest.mark.parametrize("kind", ["full_causal", "non_causal", "gist_not_self"])
+def test_gsa_prefill_mask_mutants_caught(kind, monkeypatch):
+    monkeypatch.setattr(GSA, "gsa_prefill_visible", _visible_mutant(kind))
+    _fails(P.pin_gsa_prefill, GSA.gsa_prefill, GSA.gsa_prefill_visible)

@@ -73,3 +73,7 @@ def test_shared_kv_cache_reads_layer_zero():
 
 def test_hgsa_coarse_to_fine_select():
     P.pin_hgsa_select(oracle.hgsa_select, oracle.gsa_select)
+
+
+def test_gsa_prefill_gist_mask():
+    P.pin_gsa_prefill(oracle.gsa_prefill, oracle.gsa_prefill_visible)
