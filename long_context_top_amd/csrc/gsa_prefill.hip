@@ -14,9 +14,10 @@
 // chunk c to gists [0, c] and its chunk's 16 raw tokens.
 //
 // Work: one workgroup of 4 waves per 64 queries (raw: 4 chunks, one per
-// wave; gist: 64 gists, 16 per wave), each wave 16 queries as the columns of
-// v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, O^T += V^T P^T, as in the sparse
-// attention kernel).  The workgroup walks its key tiles of 64 rows (the gist
+// wave; gist: 64 gists, 16 per wave); each wave holds GP_QG groups of 16
+// queries as the columns of v_mfma_f32_16x16x32_bf16 (S^T = K Q^T,
+// O^T += V^T P^T, as in the sparse attention kernel), every K or V fragment
+// it reads from LDS feeding one MFMA per group.  The workgroup walks its key tiles of 64 rows (the gist
 // prefix, then the band) through two LDS buffers filled by buffer loads to
 // LDS, so each key row is read once per workgroup and serves its 4 waves;
 // rows are stored with their 16-byte chunks XOR-swizzled by row so that the
@@ -35,6 +36,8 @@ constexpr int GP_D = 128;
 constexpr int GP_CHUNK = 16;
 constexpr int GP_TILE = 64;                  // key rows per tile
 constexpr int GP_NW = 4;                     // waves per workgroup
+constexpr int GP_QG = 1;                     // query groups of 16 per wave (2 measured slower:
+                                             // 328 registers, one wave per SIMD)
 constexpr int GP_ROWB = GP_D * 2;            // bytes per key row
 constexpr int GP_TILEB = GP_TILE * GP_ROWB;  // 16 KiB
 constexpr float GP_LOG2E = 1.4426950408889634f;
@@ -53,7 +56,8 @@ LCT_DEV void gp_fence() { __asm__ __volatile__("" ::: "memory"); }
 // (the A-operand reads: 16 rows, one chunk) that keeps the pairs of chunks
 // (2i, 2i+1) together and gives 4 consecutive rows different pairs (the
 // transposed V reads: 4 rows x 2 chunks per 16 lanes).
-LCT_DEV int gp_swz(int r, int c) { return r * GP_ROWB + 16 * (c ^ (((r & 7) << 1) | ((r >> 3) & 1))); }
+LCT_DEV int gp_s(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+LCT_DEV int gp_swz(int r, int c) { return r * GP_ROWB + 16 * (c ^ gp_s(r)); }
 
 // DMA of key/value rows [row0, row0 + n) (n <= 64; rows past n repeat the
 // last one: finite data, masked out) into a tile.  16 instructions of 1 KiB
@@ -64,7 +68,7 @@ LCT_DEV void gp_dma(__amdgpu_buffer_rsrc_t rs, int row0, int n, char* tile, int 
   for (int u = 0; u < 4; ++u) {
     const int i = wid * 4 + u;
     const int r = 4 * i + (lane >> 4);
-    const int c = (lane & 15) ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    const int c = (lane & 15) ^ gp_s(r);
     const int rg = row0 + (r < n ? r : n - 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gp_lds_void*)(tile + i * 1024), 16, rg * GP_ROWB + c * 16, 0, 0,
                                              0);
@@ -102,6 +106,7 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
     float* __restrict__ outr, float* __restrict__ outg, int64_t Nc, int64_t raw_cap, float scale_log2,
     int wg_per_bh) {
   constexpr int D = GP_D;
+  constexpr int NG = GP_QG;  // query groups of 16 per wave
   __shared__ __attribute__((aligned(16))) char tk0[GP_TILEB];
   __shared__ __attribute__((aligned(16))) char tv0[GP_TILEB];
   __shared__ __attribute__((aligned(16))) char tk1[GP_TILEB];
@@ -110,14 +115,16 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   const int hl = lane & 15, kg = lane >> 4;
   const int64_t bh = blockIdx.x / wg_per_bh;
   const int64_t j = wg_per_bh - 1 - (int64_t)(blockIdx.x % wg_per_bh);  // heaviest first
-  // queries: raw -> chunk qid's 16 tokens; gist -> gists qid .. qid+15
-  const int64_t qid = GQ ? 64 * j + 16 * wid : 4 * j + wid;
-  const bool wave_live = qid < Nc;
+  // queries of group g: raw -> chunk qid[g]'s 16 tokens; gist -> gists qid[g] .. qid[g]+15
+  constexpr int QPW = GQ ? 16 * NG : NG;       // gists / chunks per wave
+  constexpr int QPG = GP_NW * QPW;             // per workgroup
+  int64_t qid[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) qid[g] = QPG * j + QPW * wid + (GQ ? 16 * g : g);
   // key segments: the gist prefix the workgroup's last query sees, then the band
-  const int64_t na = GQ ? std::min<int64_t>(Nc, 64 * j + 64) : std::min<int64_t>(Nc, 4 * j + 3);
-  const int64_t b0 = GQ ? 64 * j * GP_CHUNK : 4 * j * GP_CHUNK;
-  const int64_t nb = GQ ? std::min<int64_t>(64 * GP_CHUNK, (Nc - 64 * j) * GP_CHUNK)
-                        : std::min<int64_t>(4 * GP_CHUNK, (Nc - 4 * j) * GP_CHUNK);
+  const int64_t na = GQ ? std::min<int64_t>(Nc, QPG * j + QPG) : std::min<int64_t>(Nc, QPG * j + QPG - 1);
+  const int64_t b0 = QPG * j * GP_CHUNK;
+  const int64_t nb = std::min<int64_t>((int64_t)QPG * GP_CHUNK, (Nc - QPG * j) * GP_CHUNK);
   const int ta = (int)((na + GP_TILE - 1) / GP_TILE);
   const int tb = (int)((nb + GP_TILE - 1) / GP_TILE);
   const int nt = ta + tb;
@@ -144,22 +151,30 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
     gp_dma(seg == 0 ? grs_v : rrs_v, (int)r0, n, tv, wid, lane);
   };
 
-  // query fragment (B operand): lane (hl, kg) holds query hl, features st*32 + kg*8 ..
-  bf16x8 qf[4];
-  {
-    const int64_t qrow = GQ ? std::min<int64_t>(qid + hl, Nc - 1) : std::min<int64_t>(qid, Nc - 1) * GP_CHUNK + hl;
+  // query fragments (B operands): lane (hl, kg) holds query hl of group g,
+  // features st*32 + kg*8 ..
+  bf16x8 qf[NG][4];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int64_t qrow = GQ ? std::min<int64_t>(qid[g] + hl, Nc - 1)
+                            : std::min<int64_t>(qid[g], Nc - 1) * GP_CHUNK + hl;
     const uint16_t* qp = (GQ ? qg + (bh * Nc + qrow) * D : qr + (bh * Nc * GP_CHUNK + qrow) * D) + kg * 8;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qp + st * 32);
+    for (int st = 0; st < 4; ++st) qf[g][st] = *reinterpret_cast<const bf16x8*>(qp + st * 32);
   }
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
-  float m = -INFINITY;
-  floatx4 lacc = floatx4{0.f, 0.f, 0.f, 0.f};
-  floatx4 o[D / 16];
+  float m[NG];
+  floatx4 lacc[NG];
+  floatx4 o[NG][D / 16];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < NG; ++g) {
+    m[g] = -INFINITY;
+    lacc[g] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[g][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
   // transposed V read of this lane: token 4*kg + hl/4 of a block, features
   // 16*dt + 4*(hl%4) .. +3 -> chunk 2*dt + (hl%4)/2, byte 8*(hl%2)
   const int trt = 4 * kg + (hl >> 2);
@@ -168,61 +183,77 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
     int seg, n;
     int64_t r0;
     tile_of(t, seg, r0, n);
-    const int cls = wave_live ? gp_tile_class<GQ>(seg, r0, n, qid) : 0;
-    if (cls == 0) return;  // uniform over the wave
-    // S^T = K Q^T: sacc[jb][e] = S^T[key 16jb + 4kg + e][query hl]
-    floatx4 sacc[4];
+    int cls[NG];
+    bool any = false;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      cls[g] = qid[g] < Nc ? gp_tile_class<GQ>(seg, r0, n, qid[g]) : 0;
+      any = any || cls[g] != 0;
+    }
+    if (!any) return;  // uniform over the wave
+    // S^T = K Q^T: sacc[g][jb][e] = S^T[key 16jb + 4kg + e][query hl of group g];
+    // each K fragment read from LDS serves every query group
+    floatx4 sacc[NG][4];
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
-      sacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < NG; ++g) sacc[g][jb] = floatx4{0.f, 0.f, 0.f, 0.f};
       const int r = 16 * jb + hl;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(tk + gp_swz(r, st * 4 + kg));
-        sacc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[st], sacc[jb], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          sacc[g][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g][st], sacc[g][jb], 0, 0, 0);
       }
     }
-    bool vis[4][4];
+    __bf16 pw[NG][4][4];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
+    for (int g = 0; g < NG; ++g) {
+      bool vis[4][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kl = 16 * jb + 4 * kg + e;
-        vis[jb][e] = cls == 2 || (kl < n && gp_visible<GQ>(seg, r0 + kl, qid, hl));
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kl = 16 * jb + 4 * kg + e;
+          vis[jb][e] = cls[g] == 2 || (cls[g] == 1 && kl < n && gp_visible<GQ>(seg, r0 + kl, qid[g], hl));
+        }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, vis[jb][e] ? sacc[g][jb][e] : -INFINITY);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(m[g], tmax * scale_log2);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;  // a query with nothing visible yet
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - mref);
+      m[g] = mnew;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float w = __builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref));
+          pw[g][jb][e] = (__bf16)(vis[jb][e] ? w : 0.f);
+        }
+      if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[g][dt] = o[g][dt] * alpha;
+        lacc[g] = lacc[g] * alpha;
       }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, vis[jb][e] ? sacc[jb][e] : -INFINITY);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(m, tmax * scale_log2);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;  // a query with nothing visible yet
-    const float alpha = __builtin_amdgcn_exp2f(m - mref);
-    m = mnew;
-    __bf16 pw[4][4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float w = __builtin_amdgcn_exp2f(fmaf(sacc[jb][e], scale_log2, -mref));
-        pw[jb][e] = (__bf16)(vis[jb][e] ? w : 0.f);
-      }
-    if (__ballot(alpha != 1.f) != 0) {
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
-      lacc = lacc * alpha;
     }
-    // O^T += V^T P^T, 32 keys (blocks 2h, 2h+1) per MFMA
+    // O^T += V^T P^T, 32 keys (blocks 2h, 2h+1) per MFMA; each V fragment
+    // read from LDS serves every query group
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      bf16x8 pf;
+      bf16x8 pf[NG];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = pw[2 * h][e];
-        pf[4 + e] = pw[2 * h + 1][e];
-      }
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pf[g][e] = pw[g][2 * h][e];
+          pf[g][4 + e] = pw[g][2 * h + 1][e];
+        }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const int c = 2 * dt + ((hl & 3) >> 1);
@@ -232,9 +263,11 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (gp_lds_short4v*)(tv + gp_swz(rhi, c) + 8 * (hl & 1)));
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[dt], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) o[g][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[g], o[g][dt], 0, 0, 0);
       }
-      lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc, 0, 0, 0);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) lacc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[g], lacc[g], 0, 0, 0);
     }
   };
 
@@ -258,19 +291,21 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
     gp_fence();
   }
 
-  // o[dt][e] = O^T[d = 16dt + 4kg + e][query hl]; lacc: query hl's denominator
-  if (!wave_live) return;
-  const float l = lacc[0];
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (GQ) {
-    if (qid + hl >= Nc) return;
-    float* op = outg + (bh * Nc + qid + hl) * D + kg * 4;
+  // o[g][dt][e] = O^T[d = 16dt + 4kg + e][query hl of group g]; lacc: the denominator
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(op + dt * 16) = o[dt] * inv;
-  } else {
-    float* op = outr + (bh * Nc * GP_CHUNK + qid * GP_CHUNK + hl) * D + kg * 4;
+  for (int g = 0; g < NG; ++g) {
+    const float l = lacc[g][0];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* op;
+    if (GQ) {
+      if (qid[g] + hl >= Nc) continue;
+      op = outg + (bh * Nc + qid[g] + hl) * D + kg * 4;
+    } else {
+      if (qid[g] >= Nc) continue;
+      op = outr + (bh * Nc * GP_CHUNK + qid[g] * GP_CHUNK + hl) * D + kg * 4;
+    }
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(op + dt * 16) = o[dt] * inv;
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(op + dt * 16) = o[g][dt] * inv;
   }
 }
 
@@ -278,7 +313,8 @@ hipError_t launch_gsa_prefill(const uint16_t* qr, const uint16_t* qg, const uint
                               const uint16_t* gk, const uint16_t* gv, float* outr, float* outg, int BH,
                               int64_t Nc, int64_t raw_cap, float scale, hipStream_t st) {
   const float sl2 = scale * GP_LOG2E;
-  const int wr = (int)((Nc + 3) / 4), wgq = (int)((Nc + 63) / 64);
+  const int wr = (int)((Nc + GP_NW * GP_QG - 1) / (GP_NW * GP_QG));
+  const int wgq = (int)((Nc + GP_NW * GP_QG * 16 - 1) / (GP_NW * GP_QG * 16));
   if ((int64_t)BH * wr >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   k_gsa_prefill<false><<<dim3((unsigned)(BH * wr)), GP_NW * 64, 0, st>>>(qr, qg, rk, rv, gk, gv, outr, outg, Nc,
                                                                         raw_cap, sl2, wr);
