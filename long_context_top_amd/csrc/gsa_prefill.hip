@@ -75,6 +75,40 @@ LCT_DEV void gp_dma(__amdgpu_buffer_rsrc_t rs, int row0, int n, char* tile, int 
   }
 }
 
+// Tile t of a workgroup's key walk: the gist prefix [0, na) in tiles of 64,
+// then the band rows [b0, b0 + nb).  seg 0: gist keys, 1: raw keys.
+struct GpTile {
+  int seg, n;
+  int64_t r0;
+};
+LCT_DEV GpTile gp_tile(int t, int ta, int64_t na, int64_t b0, int64_t nb) {
+  GpTile x;
+  if (t < ta) {
+    x.seg = 0;
+    x.r0 = (int64_t)t * GP_TILE;
+    x.n = (int)(na - x.r0 < GP_TILE ? na - x.r0 : GP_TILE);
+  } else {
+    x.seg = 1;
+    x.r0 = b0 + (int64_t)(t - ta) * GP_TILE;
+    x.n = (int)(b0 + nb - x.r0 < GP_TILE ? b0 + nb - x.r0 : GP_TILE);
+  }
+  return x;
+}
+
+// The DMA of one tile's K and V rows; the buffer resources are made here from
+// uniform pointers (passed through a lambda's captures or selected as values
+// they are not known to be uniform and get re-made lane by lane).
+LCT_DEV void gp_issue(const GpTile& x, const uint16_t* gkb, const uint16_t* gvb, const uint16_t* rkb,
+                      const uint16_t* rvb, int64_t Nc, int64_t raw_cap, char* tk, char* tv, int wid, int lane) {
+  if (x.seg == 0) {
+    gp_dma(make_rsrc(gkb, Nc * GP_ROWB), (int)x.r0, x.n, tk, wid, lane);
+    gp_dma(make_rsrc(gvb, Nc * GP_ROWB), (int)x.r0, x.n, tv, wid, lane);
+  } else {
+    gp_dma(make_rsrc(rkb, raw_cap * GP_ROWB), (int)x.r0, x.n, tk, wid, lane);
+    gp_dma(make_rsrc(rvb, raw_cap * GP_ROWB), (int)x.r0, x.n, tv, wid, lane);
+  }
+}
+
 // Mask of one tile for one wave: which (key row, query) pairs are visible.
 // seg 0: gist keys, seg 1: raw keys.  qid: raw -> the wave's chunk; gist ->
 // the wave's first gist (query hl is gist qid + hl).
@@ -128,28 +162,10 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   const int ta = (int)((na + GP_TILE - 1) / GP_TILE);
   const int tb = (int)((nb + GP_TILE - 1) / GP_TILE);
   const int nt = ta + tb;
-  const __amdgpu_buffer_rsrc_t grs_k = make_rsrc(gk + bh * Nc * D, Nc * GP_ROWB);
-  const __amdgpu_buffer_rsrc_t grs_v = make_rsrc(gv + bh * Nc * D, Nc * GP_ROWB);
-  const __amdgpu_buffer_rsrc_t rrs_k = make_rsrc(rk + bh * raw_cap * D, raw_cap * GP_ROWB);
-  const __amdgpu_buffer_rsrc_t rrs_v = make_rsrc(rv + bh * raw_cap * D, raw_cap * GP_ROWB);
-  auto tile_of = [&](int t, int& seg, int64_t& r0, int& n) {
-    if (t < ta) {
-      seg = 0;
-      r0 = (int64_t)t * GP_TILE;
-      n = (int)std::min<int64_t>(GP_TILE, na - r0);
-    } else {
-      seg = 1;
-      r0 = b0 + (int64_t)(t - ta) * GP_TILE;
-      n = (int)std::min<int64_t>(GP_TILE, b0 + nb - r0);
-    }
-  };
-  auto issue = [&](int t, char* tk, char* tv) {
-    int seg, n;
-    int64_t r0;
-    tile_of(t, seg, r0, n);
-    gp_dma(seg == 0 ? grs_k : rrs_k, (int)r0, n, tk, wid, lane);
-    gp_dma(seg == 0 ? grs_v : rrs_v, (int)r0, n, tv, wid, lane);
-  };
+  const uint16_t* gkb = gk + bh * Nc * D;
+  const uint16_t* gvb = gv + bh * Nc * D;
+  const uint16_t* rkb = rk + bh * raw_cap * D;
+  const uint16_t* rvb = rv + bh * raw_cap * D;
 
   // query fragments (B operands): lane (hl, kg) holds query hl of group g,
   // features st*32 + kg*8 ..
@@ -180,9 +196,9 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   const int trt = 4 * kg + (hl >> 2);
 
   auto compute = [&](int t, const char* tk, const char* tv) {
-    int seg, n;
-    int64_t r0;
-    tile_of(t, seg, r0, n);
+    const GpTile x = gp_tile(t, ta, na, b0, nb);
+    const int seg = x.seg, n = x.n;
+    const int64_t r0 = x.r0;
     int cls[NG];
     bool any = false;
 #pragma unroll
@@ -210,32 +226,45 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
     __bf16 pw[NG][4][4];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      bool vis[4][4];
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kl = 16 * jb + 4 * kg + e;
-          vis[jb][e] = cls[g] == 2 || (cls[g] == 1 && kl < n && gp_visible<GQ>(seg, r0 + kl, qid[g], hl));
-        }
+      // a tile the group sees whole takes the unmasked path (uniform branch)
       float tmax = -INFINITY;
+      bool vis[4][4];
+      if (cls[g] == 2) {
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+        for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, vis[jb][e] ? sacc[g][jb][e] : -INFINITY);
+          for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sacc[g][jb][e]);
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kl = 16 * jb + 4 * kg + e;
+            vis[jb][e] = cls[g] == 1 && kl < n && gp_visible<GQ>(seg, r0 + kl, qid[g], hl);
+            tmax = fmaxf(tmax, vis[jb][e] ? sacc[g][jb][e] : -INFINITY);
+          }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mnew = fmaxf(m[g], tmax * scale_log2);
       const float mref = mnew == -INFINITY ? 0.f : mnew;  // a query with nothing visible yet
       const float alpha = __builtin_amdgcn_exp2f(m[g] - mref);
       m[g] = mnew;
+      if (cls[g] == 2) {
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+        for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float w = __builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref));
-          pw[g][jb][e] = (__bf16)(vis[jb][e] ? w : 0.f);
-        }
+          for (int e = 0; e < 4; ++e)
+            pw[g][jb][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref));
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float w = __builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref));
+            pw[g][jb][e] = (__bf16)(vis[jb][e] ? w : 0.f);
+          }
+      }
       if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[g][dt] = o[g][dt] * alpha;
@@ -274,18 +303,20 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   // two LDS buffers, the loop unrolled by two so every access names one of
   // them; a tile's DMA is waited for by its issuing waves, then the barrier
   // makes it visible to all and frees the other buffer for the next tile
-  if (nt > 0) issue(0, tk0, tv0);
+  if (nt > 0) gp_issue(gp_tile(0, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane);
   for (int t = 0; t < nt; t += 2) {
     GP_WAIT_VM0();
     __syncthreads();
-    if (t + 1 < nt) issue(t + 1, tk1, tv1);
+    if (t + 1 < nt)
+      gp_issue(gp_tile(t + 1, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk1, tv1, wid, lane);
     gp_fence();
     compute(t, tk0, tv0);
     gp_fence();
     if (t + 1 >= nt) break;
     GP_WAIT_VM0();
     __syncthreads();
-    if (t + 2 < nt) issue(t + 2, tk0, tv0);
+    if (t + 2 < nt)
+      gp_issue(gp_tile(t + 2, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane);
     gp_fence();
     compute(t + 1, tk1, tv1);
     gp_fence();
