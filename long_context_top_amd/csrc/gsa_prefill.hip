@@ -41,6 +41,7 @@ constexpr int GP_QG = 1;                     // query groups of 16 per wave (2 m
 constexpr int GP_ROWB = GP_D * 2;            // bytes per key row
 constexpr int GP_TILEB = GP_TILE * GP_ROWB;  // 16 KiB
 constexpr float GP_LOG2E = 1.4426950408889634f;
+constexpr float GP_SLACK = 8.f;              // log2 headroom of the softmax reference
 
 typedef __attribute__((address_space(3))) short4v gp_lds_short4v;
 typedef __attribute__((address_space(3))) void gp_lds_void;
@@ -246,7 +247,12 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mnew = fmaxf(m[g], tmax * scale_log2);
+      // the reference maximum moves only when a score exceeds it by more
+      // than 2^GP_SLACK: the weights stay <= 2^GP_SLACK (fine in fp32 and
+      // bf16) and O is rescaled far less often
+      const float cand = tmax * scale_log2;
+      const bool grow = cand > m[g] + GP_SLACK;
+      const float mnew = grow ? cand : m[g];
       const float mref = mnew == -INFINITY ? 0.f : mnew;  // a query with nothing visible yet
       const float alpha = __builtin_amdgcn_exp2f(m[g] - mref);
       m[g] = mnew;
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
             pw[g][jb][e] = (__bf16)(vis[jb][e] ? w : 0.f);
           }
       }
-      if (__ballot(alpha != 1.f) != 0) {
+      if (__ballot(grow) != 0) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[g][dt] = o[g][dt] * alpha;
         lacc[g] = lacc[g] * alpha;
