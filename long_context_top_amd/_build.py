@@ -21,6 +21,12 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
+# The attention kernels keep their MFMA accumulators in VGPRs: in AGPRs the
+# compiler copies the whole output tile out and back on every key tile to
+# serve the (rarely taken) softmax rescale branch.
+_VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCE_FLAGS = {"gsa_prefill.hip": _VGPR_MFMA, "attn.hip": _VGPR_MFMA}
+
 LCT_SOURCES = ["api.hip", "topk.hip", "idx_score.hip", "attn.hip", "gsa.hip", "gsa_prefill.hip", "prefill.hip",
                "misc.hip"]
 
@@ -34,7 +40,8 @@ def _run(cmd):
 
 
 def _compile(src, obj):
-    return _run([HIPCC, *DEVICE_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj])
+    extra = SOURCE_FLAGS.get(os.path.basename(src), [])
+    return _run([HIPCC, *DEVICE_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj])
 
 
 def build(verbose: bool = False) -> list[str]:
