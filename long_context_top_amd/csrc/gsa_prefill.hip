@@ -13,18 +13,21 @@
 // no mask) and to its own chunk's raw tokens up to itself; a gist query of
 // chunk c to gists [0, c] and its chunk's 16 raw tokens.
 //
-// Work: one workgroup of 4 waves per 64 queries (raw: 4 chunks, one per
-// wave; gist: 64 gists, 16 per wave); each wave holds GP_QG groups of 16
-// queries as the columns of v_mfma_f32_16x16x32_bf16 (S^T = K Q^T,
+// Work: one workgroup of 4 waves per 128 queries (raw: 8 chunks, two per
+// wave; gist: 128 gists, 32 per wave); each wave holds GP_QG = 2 groups of
+// 16 queries as the columns of v_mfma_f32_16x16x32_bf16 (S^T = K Q^T,
 // O^T += V^T P^T, as in the sparse attention kernel), every K or V fragment
-// it reads from LDS feeding one MFMA per group.  The workgroup walks its key tiles of 64 rows (the gist
-// prefix, then the band) through two LDS buffers filled by buffer loads to
-// LDS, so each key row is read once per workgroup and serves its 4 waves;
-// rows are stored with their 16-byte chunks XOR-swizzled by row so that the
-// A-operand reads and the transposed V reads hit distinct banks.  Raw
-// queries and outputs are [BH, Nc*16, D], gist ones [BH, Nc, D].  Tiles a
-// wave cannot see are skipped by it, tiles it sees whole take an unmasked
-// softmax.  Workgroups are launched heaviest first (the gist prefix grows
+// it reads from LDS feeding one MFMA per group.  The workgroup walks its key
+// tiles of 64 rows (the gist prefix, then the band) through two LDS buffers
+// filled by buffer loads to LDS, so each key row is read once per workgroup
+// and serves its 4 waves; rows are stored with their 16-byte chunks
+// XOR-swizzled by row so that the A-operand reads and the transposed V reads
+// hit distinct banks.  Raw queries and outputs are [BH, Nc*16, D], gist ones
+// [BH, Nc, D].  Tiles a query group cannot see are skipped by it, tiles it
+// sees whole take an unmasked softmax, the others mask one interval of rows
+// per query.  The running softmax reference moves only when a tile's
+// maximum exceeds it by 2^8, so the output is rarely rescaled.  Workgroups
+// are launched heaviest first (the gist prefix grows
 // with the chunk index).
 
 #include "common.h"
@@ -36,8 +39,9 @@ constexpr int GP_D = 128;
 constexpr int GP_CHUNK = 16;
 constexpr int GP_TILE = 64;                  // key rows per tile
 constexpr int GP_NW = 4;                     // waves per workgroup
-constexpr int GP_QG = 1;                     // query groups of 16 per wave (2 measured slower:
-                                             // 328 registers, one wave per SIMD)
+constexpr int GP_QG = 2;                     // query groups of 16 per wave: every K/V fragment
+                                             // read from LDS feeds two MFMAs (221 VGPRs, two
+                                             // waves per SIMD; one group: 6.8 vs 6.0 ms)
 constexpr int GP_ROWB = GP_D * 2;            // bytes per key row
 constexpr int GP_TILEB = GP_TILE * GP_ROWB;  // 16 KiB
 constexpr float GP_LOG2E = 1.4426950408889634f;
@@ -77,21 +81,21 @@ LCT_DEV void gp_dma(__amdgpu_buffer_rsrc_t rs, int row0, int n, char* tile, int 
 }
 
 // Tile t of a workgroup's key walk: the gist prefix [0, na) in tiles of 64,
-// then the band rows [b0, b0 + nb).  seg 0: gist keys, 1: raw keys.
+// then the band rows [b0, b0 + nb).  seg 0: gist keys, 1: raw keys.  Row
+// indices fit in 32 bits (a head's raw K array is < 2 GiB).
 struct GpTile {
-  int seg, n;
-  int64_t r0;
+  int seg, n, r0;
 };
-LCT_DEV GpTile gp_tile(int t, int ta, int64_t na, int64_t b0, int64_t nb) {
+LCT_DEV GpTile gp_tile(int t, int ta, int na, int b0, int nb) {
   GpTile x;
   if (t < ta) {
     x.seg = 0;
-    x.r0 = (int64_t)t * GP_TILE;
-    x.n = (int)(na - x.r0 < GP_TILE ? na - x.r0 : GP_TILE);
+    x.r0 = t * GP_TILE;
+    x.n = na - x.r0 < GP_TILE ? na - x.r0 : GP_TILE;
   } else {
     x.seg = 1;
-    x.r0 = b0 + (int64_t)(t - ta) * GP_TILE;
-    x.n = (int)(b0 + nb - x.r0 < GP_TILE ? b0 + nb - x.r0 : GP_TILE);
+    x.r0 = b0 + (t - ta) * GP_TILE;
+    x.n = b0 + nb - x.r0 < GP_TILE ? b0 + nb - x.r0 : GP_TILE;
   }
   return x;
 }
@@ -102,30 +106,40 @@ LCT_DEV GpTile gp_tile(int t, int ta, int64_t na, int64_t b0, int64_t nb) {
 LCT_DEV void gp_issue(const GpTile& x, const uint16_t* gkb, const uint16_t* gvb, const uint16_t* rkb,
                       const uint16_t* rvb, int64_t Nc, int64_t raw_cap, char* tk, char* tv, int wid, int lane) {
   if (x.seg == 0) {
-    gp_dma(make_rsrc(gkb, Nc * GP_ROWB), (int)x.r0, x.n, tk, wid, lane);
-    gp_dma(make_rsrc(gvb, Nc * GP_ROWB), (int)x.r0, x.n, tv, wid, lane);
+    gp_dma(make_rsrc(gkb, Nc * GP_ROWB), x.r0, x.n, tk, wid, lane);
+    gp_dma(make_rsrc(gvb, Nc * GP_ROWB), x.r0, x.n, tv, wid, lane);
   } else {
-    gp_dma(make_rsrc(rkb, raw_cap * GP_ROWB), (int)x.r0, x.n, tk, wid, lane);
-    gp_dma(make_rsrc(rvb, raw_cap * GP_ROWB), (int)x.r0, x.n, tv, wid, lane);
+    gp_dma(make_rsrc(rkb, raw_cap * GP_ROWB), x.r0, x.n, tk, wid, lane);
+    gp_dma(make_rsrc(rvb, raw_cap * GP_ROWB), x.r0, x.n, tv, wid, lane);
   }
 }
 
-// Mask of one tile for one wave: which (key row, query) pairs are visible.
-// seg 0: gist keys, seg 1: raw keys.  qid: raw -> the wave's chunk; gist ->
-// the wave's first gist (query hl is gist qid + hl).
+// The keys of a tile that query hl of a wave sees form one interval of tile
+// rows, [lo, hi) (empty when lo >= hi).  seg 0: gist keys, seg 1: raw keys;
+// qid: raw -> the wave's chunk, gist -> the wave's first gist (query hl is
+// gist qid + hl).
+//   raw query, gists:  the earlier gists, key < qid
+//   raw query, raws:   its chunk's tokens up to itself, 16 qid <= key <= 16 qid + hl
+//   gist query, gists: the earlier gists and itself, key <= qid + hl
+//   gist query, raws:  its chunk's 16 tokens, 16 (qid + hl) <= key < 16 (qid + hl + 1)
 template <bool GQ>
-LCT_DEV bool gp_visible(int seg, int64_t key, int64_t qid, int hl) {
+LCT_DEV void gp_interval(int seg, int r0, int n, int qid, int hl, int& lo, int& hi) {
+  int a, b;
   if (!GQ) {
-    if (seg == 0) return key < qid;                                        // earlier gists
-    return key / GP_CHUNK == qid && key % GP_CHUNK <= hl;                  // own chunk, causal
+    a = seg == 0 ? 0 : GP_CHUNK * qid;
+    b = seg == 0 ? qid : GP_CHUNK * qid + hl + 1;
+  } else {
+    a = seg == 0 ? 0 : GP_CHUNK * (qid + hl);
+    b = seg == 0 ? qid + hl + 1 : GP_CHUNK * (qid + hl + 1);
   }
-  if (seg == 0) return key <= qid + hl;                                    // earlier gists and itself
-  return key / GP_CHUNK == qid + hl;                                       // its chunk's raw tokens
+  lo = a - r0 > 0 ? a - r0 : 0;
+  hi = b - r0 < n ? b - r0 : n;
+  hi = hi > lo ? hi : lo;
 }
 
 // 0: the wave sees no pair of the tile, 2: every pair, 1: some.
 template <bool GQ>
-LCT_DEV int gp_tile_class(int seg, int64_t r0, int n, int64_t qid) {
+LCT_DEV int gp_tile_class(int seg, int r0, int n, int qid) {
   if (!GQ) {
     if (seg == 0) return r0 >= qid ? 0 : (r0 + GP_TILE <= qid && n == GP_TILE ? 2 : 1);
     return (r0 + n <= qid * GP_CHUNK || r0 >= (qid + 1) * GP_CHUNK) ? 0 : 1;
@@ -149,17 +163,18 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int hl = lane & 15, kg = lane >> 4;
   const int64_t bh = blockIdx.x / wg_per_bh;
-  const int64_t j = wg_per_bh - 1 - (int64_t)(blockIdx.x % wg_per_bh);  // heaviest first
+  const int j = wg_per_bh - 1 - (int)(blockIdx.x % wg_per_bh);  // heaviest first
+  const int nc = (int)Nc;
   // queries of group g: raw -> chunk qid[g]'s 16 tokens; gist -> gists qid[g] .. qid[g]+15
   constexpr int QPW = GQ ? 16 * NG : NG;       // gists / chunks per wave
   constexpr int QPG = GP_NW * QPW;             // per workgroup
-  int64_t qid[NG];
+  int qid[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) qid[g] = QPG * j + QPW * wid + (GQ ? 16 * g : g);
   // key segments: the gist prefix the workgroup's last query sees, then the band
-  const int64_t na = GQ ? std::min<int64_t>(Nc, QPG * j + QPG) : std::min<int64_t>(Nc, QPG * j + QPG - 1);
-  const int64_t b0 = QPG * j * GP_CHUNK;
-  const int64_t nb = std::min<int64_t>((int64_t)QPG * GP_CHUNK, (Nc - QPG * j) * GP_CHUNK);
+  const int na = GQ ? min(nc, QPG * j + QPG) : min(nc, QPG * j + QPG - 1);
+  const int b0 = QPG * j * GP_CHUNK;
+  const int nb = min(QPG * GP_CHUNK, (nc - QPG * j) * GP_CHUNK);
   const int ta = (int)((na + GP_TILE - 1) / GP_TILE);
   const int tb = (int)((nb + GP_TILE - 1) / GP_TILE);
   const int nt = ta + tb;
@@ -173,8 +188,7 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   bf16x8 qf[NG][4];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const int64_t qrow = GQ ? std::min<int64_t>(qid[g] + hl, Nc - 1)
-                            : std::min<int64_t>(qid[g], Nc - 1) * GP_CHUNK + hl;
+    const int qrow = GQ ? min(qid[g] + hl, nc - 1) : min(qid[g], nc - 1) * GP_CHUNK + hl;
     const uint16_t* qp = (GQ ? qg + (bh * Nc + qrow) * D : qr + (bh * Nc * GP_CHUNK + qrow) * D) + kg * 8;
 #pragma unroll
     for (int st = 0; st < 4; ++st) qf[g][st] = *reinterpret_cast<const bf16x8*>(qp + st * 32);
@@ -198,13 +212,12 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
 
   auto compute = [&](int t, const char* tk, const char* tv) {
     const GpTile x = gp_tile(t, ta, na, b0, nb);
-    const int seg = x.seg, n = x.n;
-    const int64_t r0 = x.r0;
+    const int seg = x.seg, n = x.n, r0 = x.r0;
     int cls[NG];
     bool any = false;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      cls[g] = qid[g] < Nc ? gp_tile_class<GQ>(seg, r0, n, qid[g]) : 0;
+      cls[g] = qid[g] < nc ? gp_tile_class<GQ>(seg, r0, n, qid[g]) : 0;
       any = any || cls[g] != 0;
     }
     if (!any) return;  // uniform over the wave
@@ -230,6 +243,12 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
       // a tile the group sees whole takes the unmasked path (uniform branch)
       float tmax = -INFINITY;
       bool vis[4][4];
+      int lo = 0, hi = 0;
+      if (cls[g] == 1) {
+        gp_interval<GQ>(seg, r0, n, qid[g], hl, lo, hi);
+        lo -= 4 * kg;  // row 16 jb + 4 kg + e is visible iff lo <= 16 jb + e < hi
+        hi = max(hi - 4 * kg, lo);
+      }
       if (cls[g] == 2) {
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
@@ -240,8 +259,7 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
         for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int kl = 16 * jb + 4 * kg + e;
-            vis[jb][e] = cls[g] == 1 && kl < n && gp_visible<GQ>(seg, r0 + kl, qid[g], hl);
+            vis[jb][e] = (unsigned)(16 * jb + e - lo) < (unsigned)(hi - lo);
             tmax = fmaxf(tmax, vis[jb][e] ? sacc[g][jb][e] : -INFINITY);
           }
       }
@@ -335,10 +353,10 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
     const float inv = l > 0.f ? 1.f / l : 0.f;
     float* op;
     if (GQ) {
-      if (qid[g] + hl >= Nc) continue;
+      if (qid[g] + hl >= nc) continue;
       op = outg + (bh * Nc + qid[g] + hl) * D + kg * 4;
     } else {
-      if (qid[g] >= Nc) continue;
+      if (qid[g] >= nc) continue;
       op = outr + (bh * Nc * GP_CHUNK + qid[g] * GP_CHUNK + hl) * D + kg * 4;
     }
 #pragma unroll
