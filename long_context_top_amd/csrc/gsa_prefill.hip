@@ -56,6 +56,24 @@ typedef __attribute__((address_space(3))) void gp_lds_void;
 
 LCT_DEV void gp_fence() { __asm__ __volatile__("" ::: "memory"); }
 
+typedef __bf16 gp_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float gp_floatx2 __attribute__((ext_vector_type(2)));
+
+// Two weights rounded to bf16 and packed (one v_cvt_pk_bf16_f32).
+LCT_DEV uint32_t gp_pack(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((gp_floatx2){a, b}, gp_bf16x2));
+}
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the 64 keys of a
+// tile for one query): the permlane swaps pair every lane with lane ^ 32,
+// then with lane ^ 16.
+LCT_DEV float gp_max4(float t) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  t = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Byte offset of 16-byte chunk c of tile row r: the chunk index is XORed
 // with s(r) = 2*(r % 8) + (r / 8) % 2, a permutation of 0..15 over 16 rows
 // (the A-operand reads: 16 rows, one chunk) that keeps the pairs of chunks
@@ -237,7 +255,7 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
           sacc[g][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g][st], sacc[g][jb], 0, 0, 0);
       }
     }
-    __bf16 pw[NG][4][4];
+    uint32_t pw[NG][4][2];  // bf16 weight pairs: keys 16 jb + 4 kg + (2i, 2i+1)
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       // a tile the group sees whole takes the unmasked path (uniform branch)
@@ -263,8 +281,7 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
             tmax = fmaxf(tmax, vis[jb][e] ? sacc[g][jb][e] : -INFINITY);
           }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = gp_max4(tmax);
       // the reference maximum moves only when a score exceeds it by more
       // than 2^GP_SLACK: the weights stay <= 2^GP_SLACK (fine in fp32 and
       // bf16) and O is rescaled far less often
@@ -274,20 +291,16 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
       const float mref = mnew == -INFINITY ? 0.f : mnew;  // a query with nothing visible yet
       const float alpha = __builtin_amdgcn_exp2f(m[g] - mref);
       m[g] = mnew;
-      if (cls[g] == 2) {
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
+      for (int jb = 0; jb < 4; ++jb) {
+        float w[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pw[g][jb][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref));
-      } else {
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float w = __builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref));
-            pw[g][jb][e] = (__bf16)(vis[jb][e] ? w : 0.f);
-          }
+        for (int e = 0; e < 4; ++e) {
+          w[e] = __builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref));
+          if (cls[g] != 2) w[e] = vis[jb][e] ? w[e] : 0.f;
+        }
+        pw[g][jb][0] = gp_pack(w[0], w[1]);
+        pw[g][jb][1] = gp_pack(w[2], w[3]);
       }
       if (__ballot(grow) != 0) {
 #pragma unroll
@@ -302,11 +315,8 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
       bf16x8 pf[NG];
 #pragma unroll
       for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pf[g][e] = pw[g][2 * h][e];
-          pf[g][4 + e] = pw[g][2 * h + 1][e];
-        }
+        pf[g] = __builtin_bit_cast(bf16x8, (uintx4){pw[g][2 * h][0], pw[g][2 * h][1], pw[g][2 * h + 1][0],
+                                                     pw[g][2 * h + 1][1]});
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const int c = 2 * dt + ((hl & 3) >> 1);
