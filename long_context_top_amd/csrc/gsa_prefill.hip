@@ -98,6 +98,15 @@ LCT_DEV void gp_dma(__amdgpu_buffer_rsrc_t rs, int row0, int n, char* tile, int 
   }
 }
 
+// DMA of a whole tile (rows [row0, row0 + 64)): the same slots as gp_dma,
+// the row base in the scalar offset and the lane part precomputed (off[u]).
+LCT_DEV void gp_dma_whole(__amdgpu_buffer_rsrc_t rs, int row0, char* tile, int wid, const int* off) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gp_lds_void*)(tile + (wid * 4 + u) * 1024), 16, off[u],
+                                             row0 * GP_ROWB, 0, 0);
+}
+
 // Tile t of a workgroup's key walk: the gist prefix [0, na) in tiles of 64,
 // then the band rows [b0, b0 + nb).  seg 0: gist keys, 1: raw keys.  Row
 // indices fit in 32 bits (a head's raw K array is < 2 GiB).
@@ -122,8 +131,17 @@ LCT_DEV GpTile gp_tile(int t, int ta, int na, int b0, int nb) {
 // uniform pointers (passed through a lambda's captures or selected as values
 // they are not known to be uniform and get re-made lane by lane).
 LCT_DEV void gp_issue(const GpTile& x, const uint16_t* gkb, const uint16_t* gvb, const uint16_t* rkb,
-                      const uint16_t* rvb, int64_t Nc, int64_t raw_cap, char* tk, char* tv, int wid, int lane) {
-  if (x.seg == 0) {
+                      const uint16_t* rvb, int64_t Nc, int64_t raw_cap, char* tk, char* tv, int wid, int lane,
+                      const int* off) {
+  if (x.n == GP_TILE) {
+    if (x.seg == 0) {
+      gp_dma_whole(make_rsrc(gkb, Nc * GP_ROWB), x.r0, tk, wid, off);
+      gp_dma_whole(make_rsrc(gvb, Nc * GP_ROWB), x.r0, tv, wid, off);
+    } else {
+      gp_dma_whole(make_rsrc(rkb, raw_cap * GP_ROWB), x.r0, tk, wid, off);
+      gp_dma_whole(make_rsrc(rvb, raw_cap * GP_ROWB), x.r0, tv, wid, off);
+    }
+  } else if (x.seg == 0) {
     gp_dma(make_rsrc(gkb, Nc * GP_ROWB), x.r0, x.n, tk, wid, lane);
     gp_dma(make_rsrc(gvb, Nc * GP_ROWB), x.r0, x.n, tv, wid, lane);
   } else {
@@ -224,6 +242,12 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[g][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  int doff[4];  // this lane's byte offsets in a whole tile's DMA (gp_dma's slots)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 4 * (wid * 4 + u) + (lane >> 4);
+    doff[u] = r * GP_ROWB + 16 * ((lane & 15) ^ gp_s(r));
+  }
   // transposed V read of this lane: token 4*kg + hl/4 of a block, features
   // 16*dt + 4*(hl%4) .. +3 -> chunk 2*dt + (hl%4)/2, byte 8*(hl%2)
   const int trt = 4 * kg + (hl >> 2);
@@ -291,16 +315,25 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
       const float mref = mnew == -INFINITY ? 0.f : mnew;  // a query with nothing visible yet
       const float alpha = __builtin_amdgcn_exp2f(m[g] - mref);
       m[g] = mnew;
+      if (cls[g] == 2) {
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        float w[4];
+        for (int jb = 0; jb < 4; ++jb) {
+          float w[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[e] = __builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref));
-          if (cls[g] != 2) w[e] = vis[jb][e] ? w[e] : 0.f;
+          for (int e = 0; e < 4; ++e) w[e] = __builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref));
+          pw[g][jb][0] = gp_pack(w[0], w[1]);
+          pw[g][jb][1] = gp_pack(w[2], w[3]);
         }
-        pw[g][jb][0] = gp_pack(w[0], w[1]);
-        pw[g][jb][1] = gp_pack(w[2], w[3]);
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          float w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = vis[jb][e] ? __builtin_amdgcn_exp2f(fmaf(sacc[g][jb][e], scale_log2, -mref)) : 0.f;
+          pw[g][jb][0] = gp_pack(w[0], w[1]);
+          pw[g][jb][1] = gp_pack(w[2], w[3]);
+        }
       }
       if (__ballot(grow) != 0) {
 #pragma unroll
@@ -337,12 +370,12 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   // two LDS buffers, the loop unrolled by two so every access names one of
   // them; a tile's DMA is waited for by its issuing waves, then the barrier
   // makes it visible to all and frees the other buffer for the next tile
-  if (nt > 0) gp_issue(gp_tile(0, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane);
+  if (nt > 0) gp_issue(gp_tile(0, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane, doff);
   for (int t = 0; t < nt; t += 2) {
     GP_WAIT_VM0();
     __syncthreads();
     if (t + 1 < nt)
-      gp_issue(gp_tile(t + 1, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk1, tv1, wid, lane);
+      gp_issue(gp_tile(t + 1, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk1, tv1, wid, lane, doff);
     gp_fence();
     compute(t, tk0, tv0);
     gp_fence();
@@ -350,7 +383,7 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
     GP_WAIT_VM0();
     __syncthreads();
     if (t + 2 < nt)
-      gp_issue(gp_tile(t + 2, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane);
+      gp_issue(gp_tile(t + 2, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane, doff);
     gp_fence();
     compute(t + 1, tk1, tv1);
     gp_fence();
