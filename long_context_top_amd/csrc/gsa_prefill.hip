@@ -75,23 +75,31 @@ LCT_DEV float gp_max4(float t) {
 }
 
 // Byte offset of 16-byte chunk c of tile row r: the chunk index is XORed
-// with s(r) = 2*(r % 8) + (r / 8) % 2, a permutation of 0..15 over 16 rows
-// (the A-operand reads: 16 rows, one chunk) that keeps the pairs of chunks
-// (2i, 2i+1) together and gives 4 consecutive rows different pairs (the
-// transposed V reads: 4 rows x 2 chunks per 16 lanes).
-LCT_DEV int gp_s(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-LCT_DEV int gp_swz(int r, int c) { return r * GP_ROWB + 16 * (c ^ gp_s(r)); }
+// with a permutation s(r) of 0..15 over 16 rows, one per array.  V tiles:
+// s(r) = 2*(r % 8) + (r / 8) % 2 keeps the pairs of chunks (2i, 2i+1)
+// together and gives 4 consecutive rows different pairs (the transposed V
+// reads: 4 rows x 2 chunks per 16 lanes).  K tiles: s(r) = 8*(r % 2) +
+// (r / 2) % 8 (the A-operand reads: 16 rows, one chunk per 16 lanes).  Both
+// were measured free of LDS bank conflicts on gfx950 for their reads (bank
+// conflict counter); the V form leaves the A-operand reads 2-way conflicted.
+template <bool KT>
+LCT_DEV int gp_s(int r) {
+  return KT ? ((r & 1) << 3) | ((r >> 1) & 7) : ((r & 7) << 1) | ((r >> 3) & 1);
+}
+template <bool KT>
+LCT_DEV int gp_swz(int r, int c) { return r * GP_ROWB + 16 * (c ^ gp_s<KT>(r)); }
 
 // DMA of key/value rows [row0, row0 + n) (n <= 64; rows past n repeat the
 // last one: finite data, masked out) into a tile.  16 instructions of 1 KiB
 // per array, 4 per wave: instruction i holds tile rows 4i .. 4i+3, lane l
 // the 16 bytes of row 4i + l/16 that the swizzle puts at slot l % 16.
+template <bool KT>
 LCT_DEV void gp_dma(__amdgpu_buffer_rsrc_t rs, int row0, int n, char* tile, int wid, int lane) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = wid * 4 + u;
     const int r = 4 * i + (lane >> 4);
-    const int c = (lane & 15) ^ gp_s(r);
+    const int c = (lane & 15) ^ gp_s<KT>(r);
     const int rg = row0 + (r < n ? r : n - 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gp_lds_void*)(tile + i * 1024), 16, rg * GP_ROWB + c * 16, 0, 0,
                                              0);
@@ -132,21 +140,21 @@ LCT_DEV GpTile gp_tile(int t, int ta, int na, int b0, int nb) {
 // they are not known to be uniform and get re-made lane by lane).
 LCT_DEV void gp_issue(const GpTile& x, const uint16_t* gkb, const uint16_t* gvb, const uint16_t* rkb,
                       const uint16_t* rvb, int64_t Nc, int64_t raw_cap, char* tk, char* tv, int wid, int lane,
-                      const int* off) {
+                      const int* offk, const int* offv) {
   if (x.n == GP_TILE) {
     if (x.seg == 0) {
-      gp_dma_whole(make_rsrc(gkb, Nc * GP_ROWB), x.r0, tk, wid, off);
-      gp_dma_whole(make_rsrc(gvb, Nc * GP_ROWB), x.r0, tv, wid, off);
+      gp_dma_whole(make_rsrc(gkb, Nc * GP_ROWB), x.r0, tk, wid, offk);
+      gp_dma_whole(make_rsrc(gvb, Nc * GP_ROWB), x.r0, tv, wid, offv);
     } else {
-      gp_dma_whole(make_rsrc(rkb, raw_cap * GP_ROWB), x.r0, tk, wid, off);
-      gp_dma_whole(make_rsrc(rvb, raw_cap * GP_ROWB), x.r0, tv, wid, off);
+      gp_dma_whole(make_rsrc(rkb, raw_cap * GP_ROWB), x.r0, tk, wid, offk);
+      gp_dma_whole(make_rsrc(rvb, raw_cap * GP_ROWB), x.r0, tv, wid, offv);
     }
   } else if (x.seg == 0) {
-    gp_dma(make_rsrc(gkb, Nc * GP_ROWB), x.r0, x.n, tk, wid, lane);
-    gp_dma(make_rsrc(gvb, Nc * GP_ROWB), x.r0, x.n, tv, wid, lane);
+    gp_dma<true>(make_rsrc(gkb, Nc * GP_ROWB), x.r0, x.n, tk, wid, lane);
+    gp_dma<false>(make_rsrc(gvb, Nc * GP_ROWB), x.r0, x.n, tv, wid, lane);
   } else {
-    gp_dma(make_rsrc(rkb, raw_cap * GP_ROWB), x.r0, x.n, tk, wid, lane);
-    gp_dma(make_rsrc(rvb, raw_cap * GP_ROWB), x.r0, x.n, tv, wid, lane);
+    gp_dma<true>(make_rsrc(rkb, raw_cap * GP_ROWB), x.r0, x.n, tk, wid, lane);
+    gp_dma<false>(make_rsrc(rvb, raw_cap * GP_ROWB), x.r0, x.n, tv, wid, lane);
   }
 }
 
@@ -242,11 +250,12 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[g][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  int doff[4];  // this lane's byte offsets in a whole tile's DMA (gp_dma's slots)
+  int doffk[4], doffv[4];  // this lane's byte offsets in a whole tile's DMA (gp_dma's slots)
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 4 * (wid * 4 + u) + (lane >> 4);
-    doff[u] = r * GP_ROWB + 16 * ((lane & 15) ^ gp_s(r));
+    doffk[u] = r * GP_ROWB + 16 * ((lane & 15) ^ gp_s<true>(r));
+    doffv[u] = r * GP_ROWB + 16 * ((lane & 15) ^ gp_s<false>(r));
   }
   // transposed V read of this lane: token 4*kg + hl/4 of a block, features
   // 16*dt + 4*(hl%4) .. +3 -> chunk 2*dt + (hl%4)/2, byte 8*(hl%2)
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
       const int r = 16 * jb + hl;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(tk + gp_swz(r, st * 4 + kg));
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(tk + gp_swz<true>(r, st * 4 + kg));
 #pragma unroll
         for (int g = 0; g < NG; ++g)
           sacc[g][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g][st], sacc[g][jb], 0, 0, 0);
@@ -355,9 +364,9 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
         const int c = 2 * dt + ((hl & 3) >> 1);
         const int rlo = 16 * (2 * h) + trt, rhi = 16 * (2 * h + 1) + trt;
         const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (gp_lds_short4v*)(tv + gp_swz(rlo, c) + 8 * (hl & 1)));
+            (gp_lds_short4v*)(tv + gp_swz<false>(rlo, c) + 8 * (hl & 1)));
         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (gp_lds_short4v*)(tv + gp_swz(rhi, c) + 8 * (hl & 1)));
+            (gp_lds_short4v*)(tv + gp_swz<false>(rhi, c) + 8 * (hl & 1)));
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int g = 0; g < NG; ++g) o[g][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[g], o[g][dt], 0, 0, 0);
@@ -370,12 +379,12 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   // two LDS buffers, the loop unrolled by two so every access names one of
   // them; a tile's DMA is waited for by its issuing waves, then the barrier
   // makes it visible to all and frees the other buffer for the next tile
-  if (nt > 0) gp_issue(gp_tile(0, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane, doff);
+  if (nt > 0) gp_issue(gp_tile(0, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane, doffk, doffv);
   for (int t = 0; t < nt; t += 2) {
     GP_WAIT_VM0();
     __syncthreads();
     if (t + 1 < nt)
-      gp_issue(gp_tile(t + 1, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk1, tv1, wid, lane, doff);
+      gp_issue(gp_tile(t + 1, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk1, tv1, wid, lane, doffk, doffv);
     gp_fence();
     compute(t, tk0, tv0);
     gp_fence();
@@ -383,7 +392,7 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
     GP_WAIT_VM0();
     __syncthreads();
     if (t + 2 < nt)
-      gp_issue(gp_tile(t + 2, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane, doff);
+      gp_issue(gp_tile(t + 2, ta, na, b0, nb), gkb, gvb, rkb, rvb, Nc, raw_cap, tk0, tv0, wid, lane, doffk, doffv);
     gp_fence();
     compute(t + 1, tk1, tv1);
     gp_fence();
