@@ -356,6 +356,32 @@ def test_gsa_prefill_matches_oracle(Nc, BH):
         assert np.abs(out_g[b] - want_g).max() < ATOL, b
 
 
+@pytest.mark.parametrize("scale", [1.0, 4.0])
+def test_gsa_prefill_large_logits(scale):
+    """Logits of tens to hundreds with key norms growing along the sequence:
+    the running softmax reference keeps moving (the output is rescaled on
+    many tiles) and a tile's weights reach the 2^8 headroom; outputs stay
+    within the bar."""
+    announce(f"gsa prefill large logits scale={scale}")
+    r = _rng(77)
+    BH, Nc, chunk, D = 1, 67, 16, 128
+    n_raw = Nc * chunk
+    ramp_r = np.linspace(0.2, 2.0, n_raw)[None, :, None]
+    ramp_g = np.linspace(0.2, 2.0, Nc)[None, :, None]
+    qr, qrh = dev_bf16(r.standard_normal((BH, n_raw, D)))
+    qg, qgh = dev_bf16(r.standard_normal((BH, Nc, D)))
+    rk, rkh = dev_bf16(r.standard_normal((BH, n_raw, D)) * ramp_r)
+    rv, rvh = dev_bf16(r.standard_normal((BH, n_raw, D)))
+    gk, gkh = dev_bf16(r.standard_normal((BH, Nc, D)) * ramp_g)
+    gv, gvh = dev_bf16(r.standard_normal((BH, Nc, D)))
+    out_r, out_g = lct.gsa_prefill(qr, qg, rk, rv, gk, gv, scale)
+    out_r, out_g = host(out_r), host(out_g)
+    want_r, want_g = oracle.gsa_prefill(qrh[0], qgh[0], rkh[0], rvh[0], gkh[0], gvh[0], chunk, scale)
+    assert np.isfinite(out_r).all() and np.isfinite(out_g).all()
+    assert np.abs(out_r[0] - want_r).max() < ATOL
+    assert np.abs(out_g[0] - want_g).max() < ATOL
+
+
 def test_gsa_raw_path_sensitivity():
     """Ternary gist keys keep gist logits small so raw tokens carry real weight."""
     from tests.gpu_util import dev_bf16_bits
