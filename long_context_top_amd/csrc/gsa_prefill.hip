@@ -21,13 +21,13 @@
 // tiles of 64 rows (the gist prefix, then the band) through two LDS buffers
 // filled by buffer loads to LDS, so each key row is read once per workgroup
 // and serves its 4 waves; rows are stored with their 16-byte chunks
-// XOR-swizzled by row so that the A-operand reads and the transposed V reads
-// hit distinct banks.  Raw queries and outputs are [BH, Nc*16, D], gist ones
-// [BH, Nc, D].  Tiles a query group cannot see are skipped by it, tiles it
-// sees whole take an unmasked softmax, the others mask one interval of rows
-// per query.  The running softmax reference moves only when a tile's
-// maximum exceeds it by 2^8, so the output is rarely rescaled.  Workgroups
-// are launched heaviest first (the gist prefix grows
+// XOR-swizzled by row so that the A-operand reads (K tiles) and the
+// transposed reads (V tiles) hit distinct banks.  Raw queries and outputs are
+// [BH, Nc*16, D], gist ones [BH, Nc, D].  Tiles a query group cannot see are
+// skipped by it, tiles it sees whole take an unmasked softmax, the others
+// mask one interval of rows per query.  The running softmax reference moves
+// only when a tile's maximum exceeds it by 2^8, so the output is rarely
+// rescaled.  Workgroups are launched heaviest first (the gist prefix grows
 // with the chunk index).
 
 #include "common.h"
@@ -40,8 +40,8 @@ constexpr int GP_CHUNK = 16;
 constexpr int GP_TILE = 64;                  // key rows per tile
 constexpr int GP_NW = 4;                     // waves per workgroup
 constexpr int GP_QG = 2;                     // query groups of 16 per wave: every K/V fragment
-                                             // read from LDS feeds two MFMAs (221 VGPRs, two
-                                             // waves per SIMD; one group: 6.8 vs 6.0 ms)
+                                             // read from LDS feeds two MFMAs (two waves per
+                                             // SIMD; one group measured 6.8 against 6.0 ms)
 constexpr int GP_ROWB = GP_D * 2;            // bytes per key row
 constexpr int GP_TILEB = GP_TILE * GP_ROWB;  // 16 KiB
 constexpr float GP_LOG2E = 1.4426950408889634f;
