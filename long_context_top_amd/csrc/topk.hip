@@ -574,6 +574,7 @@ constexpr int ROW_NT = 512;
 constexpr int ROW_NB_LOG2 = 11;
 constexpr int ROW_NB = 1 << ROW_NB_LOG2;
 constexpr int ROW_CAP = 2048;
+constexpr int ROW_RC = 16;  // keys per thread kept in registers (rows up to 8192 keys)
 
 template <int DT>
 __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ scores, int64_t n,
@@ -605,12 +606,33 @@ __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ s
     for (uint32_t j = threadIdx.x; j < (uint32_t)k; j += NT) out[j] = j < nv ? (int32_t)j : -1;
     return;
   }
+  // rows of up to NT * ROW_RC keys are read once into registers (key j*NT +
+  // threadIdx.x in kr[j]: the order every pass below walks the row in);
+  // longer rows are read again by each pass
+  const bool cached = nv <= (uint32_t)(NT * ROW_RC);
+  uint32_t kr[ROW_RC];
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < ROW_RC; ++j) {
+      const uint32_t p = (uint32_t)(j * NT) + threadIdx.x;
+      kr[j] = p < nv ? load_key<DT>(rp, p) : 0u;
+    }
+  }
   // 1. window
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (uint32_t p = threadIdx.x; p < nv; p += NT) {
-    uint32_t key = load_key<DT>(rp, p);
-    mn = min(mn, key);
-    mx = max(mx, key);
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < ROW_RC; ++j)
+      if ((uint32_t)(j * NT) + threadIdx.x < nv) {
+        mn = min(mn, kr[j]);
+        mx = max(mx, kr[j]);
+      }
+  } else {
+    for (uint32_t p = threadIdx.x; p < nv; p += NT) {
+      uint32_t key = load_key<DT>(rp, p);
+      mn = min(mn, key);
+      mx = max(mx, key);
+    }
   }
   block_minmax<NT>(mn, mx, lds);
   const uint32_t lo = mn, shift = window_shift(mn, mx, ROW_NB_LOG2);
@@ -618,8 +640,14 @@ __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ s
   for (int i = threadIdx.x; i < ROW_NB; i += NT) h[i] = 0;
   if (threadIdx.x == 0) s_fill = 0;
   __syncthreads();
-  for (uint32_t p = threadIdx.x; p < nv; p += NT)
-    atomicAdd(&h[bin_of(load_key<DT>(rp, p), lo, shift, ROW_NB)], 1u);
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < ROW_RC; ++j)
+      if ((uint32_t)(j * NT) + threadIdx.x < nv) atomicAdd(&h[bin_of(kr[j], lo, shift, ROW_NB)], 1u);
+  } else {
+    for (uint32_t p = threadIdx.x; p < nv; p += NT)
+      atomicAdd(&h[bin_of(load_key<DT>(rp, p), lo, shift, ROW_NB)], 1u);
+  }
   __syncthreads();
   // 3. threshold bin: suffix sums, each thread owns ROW_NB / NT consecutive bins
   constexpr int BPT = ROW_NB / NT;
@@ -647,25 +675,37 @@ __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ s
   __syncthreads();
   const uint32_t tb = lds[0], need = lds[1], ccount = lds[2];
   __syncthreads();
-  // 4. bitmap of bins above tb, candidates of bin tb
-  for (uint32_t cb = wid * 64; cb < nv; cb += NT) {
-    uint32_t p = cb + lane;
-    bool valid = p < nv;
-    uint32_t key = valid ? load_key<DT>(rp, p) : 0u;
-    uint32_t bin = bin_of(key, lo, shift, ROW_NB);
-    bool ab = valid && bin > tb;
-    bool cand = valid && bin == tb;
-    uint64_t am = __ballot(ab);
+  // 4. bitmap of bins above tb, candidates of bin tb (a wave takes 64
+  // consecutive positions cb .. cb + 63)
+  auto mark = [&](uint32_t cb, uint32_t key) {
+    const uint32_t p = cb + lane;
+    const bool valid = p < nv;
+    const uint32_t bin = bin_of(key, lo, shift, ROW_NB);
+    const bool ab = valid && bin > tb;
+    const bool cand = valid && bin == tb;
+    const uint64_t am = __ballot(ab);
     if (lane == 0) {
       bm[cb >> 5] = (uint32_t)am;
       if ((cb >> 5) + 1 < (TOPK_ROW_MAX_N / 32)) bm[(cb >> 5) + 1] = (uint32_t)(am >> 32);
     }
-    uint64_t cm = __ballot(cand);
+    const uint64_t cm = __ballot(cand);
     if (cm && ccount <= ROW_CAP) {
       uint32_t b0 = 0;
       if (lane == 0) b0 = atomicAdd(&s_fill, (uint32_t)__popcll(cm));
       b0 = __shfl(b0, 0, 64);
       if (cand) sc[b0 + lane_rank(cm)] = ((uint64_t)key << 32) | (uint32_t)(~p);
+    }
+  };
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < ROW_RC; ++j) {
+      const uint32_t cb = (uint32_t)(j * NT + wid * 64);
+      if (cb < nv) mark(cb, kr[j]);  // wave-uniform
+    }
+  } else {
+    for (uint32_t cb = wid * 64; cb < nv; cb += NT) {
+      const uint32_t p = cb + lane;
+      mark(cb, p < nv ? load_key<DT>(rp, p) : 0u);
     }
   }
   __syncthreads();
