@@ -457,10 +457,12 @@ __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn(
 // One workgroup per (unit, head), one thread per output feature; all split
 // partials of a thread are loaded at once (one memory round trip).
 
+template <int SPL>
 __global__ __launch_bounds__(256) void k_split_merge(const float* __restrict__ part,
                                                      float* __restrict__ out, int splits, int hs,
                                                      int G, int D, int rs) {
-  __shared__ float wts[MERGE_MAX_SPLITS];
+  static_assert(SPL <= 64, "one wave weighs the splits");
+  __shared__ float wts[SPL];
   __shared__ float s_inv;
   const int64_t unit = blockIdx.x;
   const int h = blockIdx.y;
@@ -470,9 +472,9 @@ __global__ __launch_bounds__(256) void k_split_merge(const float* __restrict__ p
   // all loads are issued together: this thread's feature of every split
   // (unconditional; split indices past `splits` re-read the last split and get
   // weight 0) and, in the first wave, one split's (m, l) per lane
-  float o[MERGE_MAX_SPLITS];
+  float o[SPL];
 #pragma unroll
-  for (int s = 0; s < MERGE_MAX_SPLITS; ++s) o[s] = base[(size_t)(s < splits ? s : splits - 1) * stride + d];
+  for (int s = 0; s < SPL; ++s) o[s] = base[(size_t)(s < splits ? s : splits - 1) * stride + d];
   if (threadIdx.x < 64) {
     const int s = threadIdx.x < splits ? threadIdx.x : splits - 1;
     const float m = base[(size_t)s * stride + D];
@@ -480,13 +482,13 @@ __global__ __launch_bounds__(256) void k_split_merge(const float* __restrict__ p
     const float M = wave_max(m);
     const float w = (M == -INFINITY || (int)threadIdx.x >= splits) ? 0.f : exp2f(m - M);
     const float L = wave_sum(w * l);
-    if (threadIdx.x < MERGE_MAX_SPLITS) wts[threadIdx.x] = w;
+    if (threadIdx.x < SPL) wts[threadIdx.x] = w;
     if (threadIdx.x == 0) s_inv = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
   float acc = 0.f;
 #pragma unroll
-  for (int s = 0; s < MERGE_MAX_SPLITS; ++s) acc += wts[s] * o[s];
+  for (int s = 0; s < SPL; ++s) acc += wts[s] * o[s];
   if (threadIdx.x < D) out[((size_t)unit * G + h) * D + d] = acc * s_inv;
 }
 
@@ -494,7 +496,12 @@ hipError_t launch_split_merge(const float* part, float* out, int64_t units, int 
                               int G, int D, int rs, hipStream_t st) {
   if (splits > MERGE_MAX_SPLITS || D > 256 || rs < D + 2) return hipErrorInvalidValue;
   const int threads = D < 64 ? 64 : D;
-  k_split_merge<<<dim3((unsigned)units, G), threads, 0, st>>>(part, out, splits, hs, G, D, rs);
+  const dim3 grid((unsigned)units, G);
+  // the load slots per thread: the next power of two of the split count
+  if (splits <= 8) k_split_merge<8><<<grid, threads, 0, st>>>(part, out, splits, hs, G, D, rs);
+  else if (splits <= 16) k_split_merge<16><<<grid, threads, 0, st>>>(part, out, splits, hs, G, D, rs);
+  else if (splits <= 32) k_split_merge<32><<<grid, threads, 0, st>>>(part, out, splits, hs, G, D, rs);
+  else k_split_merge<64><<<grid, threads, 0, st>>>(part, out, splits, hs, G, D, rs);
   return hipGetLastError();
 }
 
