@@ -586,7 +586,7 @@ def main():
         print(json.dumps(copy_calibration(args.steps)))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(every workload runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
     from synth import configs as C
