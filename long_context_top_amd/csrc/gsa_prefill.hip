@@ -192,22 +192,21 @@ LCT_DEV int gp_tile_class(int seg, int r0, int n, int qid) {
   return (r0 + n <= qid * GP_CHUNK || r0 >= (qid + 16) * GP_CHUNK) ? 0 : 1;
 }
 
+// One workgroup's work: workgroup `blk` of the raw (GQ false) or gist (GQ
+// true) queries; the four tile buffers are the kernel's LDS objects.
 template <bool GQ>
-__global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
-    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ qg, const uint16_t* __restrict__ rk,
-    const uint16_t* __restrict__ rv, const uint16_t* __restrict__ gk, const uint16_t* __restrict__ gv,
-    float* __restrict__ outr, float* __restrict__ outg, int64_t Nc, int64_t raw_cap, float scale_log2,
-    int wg_per_bh) {
+LCT_DEV void gp_workgroup(const uint16_t* __restrict__ qr, const uint16_t* __restrict__ qg,
+                          const uint16_t* __restrict__ rk, const uint16_t* __restrict__ rv,
+                          const uint16_t* __restrict__ gk, const uint16_t* __restrict__ gv,
+                          float* __restrict__ outr, float* __restrict__ outg, int64_t Nc, int64_t raw_cap,
+                          float scale_log2, int blk, int wg_per_bh, char* tk0, char* tv0, char* tk1,
+                          char* tv1) {
   constexpr int D = GP_D;
   constexpr int NG = GP_QG;  // query groups of 16 per wave
-  __shared__ __attribute__((aligned(16))) char tk0[GP_TILEB];
-  __shared__ __attribute__((aligned(16))) char tv0[GP_TILEB];
-  __shared__ __attribute__((aligned(16))) char tk1[GP_TILEB];
-  __shared__ __attribute__((aligned(16))) char tv1[GP_TILEB];
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int hl = lane & 15, kg = lane >> 4;
-  const int64_t bh = blockIdx.x / wg_per_bh;
-  const int j = wg_per_bh - 1 - (int)(blockIdx.x % wg_per_bh);  // heaviest first
+  const int64_t bh = blk / wg_per_bh;
+  const int j = wg_per_bh - 1 - blk % wg_per_bh;  // heaviest first
   const int nc = (int)Nc;
   // queries of group g: raw -> chunk qid[g]'s 16 tokens; gist -> gists qid[g] .. qid[g]+15
   constexpr int QPW = GQ ? 16 * NG : NG;       // gists / chunks per wave
@@ -416,19 +415,37 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   }
 }
 
+// Both query kinds in one launch: the gist workgroups (the heavier ones on
+// average) first, then the raw ones, each kind heaviest first within a head,
+// so the light raw workgroups fill the tail.
+__global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
+    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ qg, const uint16_t* __restrict__ rk,
+    const uint16_t* __restrict__ rv, const uint16_t* __restrict__ gk, const uint16_t* __restrict__ gv,
+    float* __restrict__ outr, float* __restrict__ outg, int64_t Nc, int64_t raw_cap, float scale_log2,
+    int n_gist_wg, int wg_gist_per_bh, int wg_raw_per_bh) {
+  __shared__ __attribute__((aligned(16))) char tk0[GP_TILEB];
+  __shared__ __attribute__((aligned(16))) char tv0[GP_TILEB];
+  __shared__ __attribute__((aligned(16))) char tk1[GP_TILEB];
+  __shared__ __attribute__((aligned(16))) char tv1[GP_TILEB];
+  const int blk = (int)blockIdx.x;
+  if (blk < n_gist_wg)
+    gp_workgroup<true>(qr, qg, rk, rv, gk, gv, outr, outg, Nc, raw_cap, scale_log2, blk, wg_gist_per_bh, tk0, tv0,
+                       tk1, tv1);
+  else
+    gp_workgroup<false>(qr, qg, rk, rv, gk, gv, outr, outg, Nc, raw_cap, scale_log2, blk - n_gist_wg,
+                        wg_raw_per_bh, tk0, tv0, tk1, tv1);
+}
+
 hipError_t launch_gsa_prefill(const uint16_t* qr, const uint16_t* qg, const uint16_t* rk, const uint16_t* rv,
                               const uint16_t* gk, const uint16_t* gv, float* outr, float* outg, int BH,
                               int64_t Nc, int64_t raw_cap, float scale, hipStream_t st) {
   const float sl2 = scale * GP_LOG2E;
   const int wr = (int)((Nc + GP_NW * GP_QG - 1) / (GP_NW * GP_QG));
   const int wgq = (int)((Nc + GP_NW * GP_QG * 16 - 1) / (GP_NW * GP_QG * 16));
-  if ((int64_t)BH * wr >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  k_gsa_prefill<false><<<dim3((unsigned)(BH * wr)), GP_NW * 64, 0, st>>>(qr, qg, rk, rv, gk, gv, outr, outg, Nc,
-                                                                        raw_cap, sl2, wr);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  k_gsa_prefill<true><<<dim3((unsigned)(BH * wgq)), GP_NW * 64, 0, st>>>(qr, qg, rk, rv, gk, gv, outr, outg, Nc,
-                                                                        raw_cap, sl2, wgq);
+  if ((int64_t)BH * (wr + wgq) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int ngist = BH * wgq;
+  k_gsa_prefill<<<dim3((unsigned)(ngist + BH * wr)), GP_NW * 64, 0, st>>>(qr, qg, rk, rv, gk, gv, outr, outg, Nc,
+                                                                         raw_cap, sl2, ngist, wgq, wr);
   return hipGetLastError();
 }
 
