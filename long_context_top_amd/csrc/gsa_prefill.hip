@@ -27,8 +27,9 @@
 // skipped by it, tiles it sees whole take an unmasked softmax, the others
 // mask one interval of rows per query.  The running softmax reference moves
 // only when a tile's maximum exceeds it by 2^8, so the output is rarely
-// rescaled.  Workgroups are launched heaviest first (the gist prefix grows
-// with the chunk index).
+// rescaled.  One launch holds both kinds: the gist workgroups first, then the
+// raw ones, each kind heaviest first within a head (the gist prefix grows with
+// the chunk index), so the light raw workgroups fill the tail.
 
 #include "common.h"
 #include "kernels.h"
