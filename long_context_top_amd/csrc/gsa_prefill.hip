@@ -28,8 +28,8 @@
 // mask one interval of rows per query.  The running softmax reference moves
 // only when a tile's maximum exceeds it by 2^8, so the output is rarely
 // rescaled.  One launch holds both kinds: the gist workgroups first, then the
-// raw ones, each kind heaviest first within a head (the gist prefix grows with
-// the chunk index), so the light raw workgroups fill the tail.
+// raw ones, each kind heaviest first over all heads (the gist prefix grows
+// with the chunk index), so the light raw workgroups fill the tail.
 
 #include "common.h"
 #include "kernels.h"
@@ -194,20 +194,22 @@ LCT_DEV int gp_tile_class(int seg, int r0, int n, int qid) {
 }
 
 // One workgroup's work: workgroup `blk` of the raw (GQ false) or gist (GQ
-// true) queries; the four tile buffers are the kernel's LDS objects.
+// true) queries of nbh (batch, head) pairs, taken heaviest first over all
+// pairs (blk / nbh counts down the query blocks, blk % nbh picks the pair);
+// the four tile buffers are the kernel's LDS objects.
 template <bool GQ>
 LCT_DEV void gp_workgroup(const uint16_t* __restrict__ qr, const uint16_t* __restrict__ qg,
                           const uint16_t* __restrict__ rk, const uint16_t* __restrict__ rv,
                           const uint16_t* __restrict__ gk, const uint16_t* __restrict__ gv,
                           float* __restrict__ outr, float* __restrict__ outg, int64_t Nc, int64_t raw_cap,
                           float scale_log2, int blk, int wg_per_bh, char* tk0, char* tv0, char* tk1,
-                          char* tv1) {
+                          char* tv1, int nbh) {
   constexpr int D = GP_D;
   constexpr int NG = GP_QG;  // query groups of 16 per wave
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int hl = lane & 15, kg = lane >> 4;
-  const int64_t bh = blk / wg_per_bh;
-  const int j = wg_per_bh - 1 - blk % wg_per_bh;  // heaviest first
+  const int64_t bh = blk % nbh;
+  const int j = wg_per_bh - 1 - blk / nbh;  // heaviest first over all heads
   const int nc = (int)Nc;
   // queries of group g: raw -> chunk qid[g]'s 16 tokens; gist -> gists qid[g] .. qid[g]+15
   constexpr int QPW = GQ ? 16 * NG : NG;       // gists / chunks per wave
@@ -417,7 +419,7 @@ LCT_DEV void gp_workgroup(const uint16_t* __restrict__ qr, const uint16_t* __res
 }
 
 // Both query kinds in one launch: the gist workgroups (the heavier ones on
-// average) first, then the raw ones, each kind heaviest first within a head,
+// average) first, then the raw ones, each kind heaviest first over all heads,
 // so the light raw workgroups fill the tail.
 __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
     const uint16_t* __restrict__ qr, const uint16_t* __restrict__ qg, const uint16_t* __restrict__ rk,
@@ -431,10 +433,10 @@ __global__ __launch_bounds__(GP_NW * 64) void k_gsa_prefill(
   const int blk = (int)blockIdx.x;
   if (blk < n_gist_wg)
     gp_workgroup<true>(qr, qg, rk, rv, gk, gv, outr, outg, Nc, raw_cap, scale_log2, blk, wg_gist_per_bh, tk0, tv0,
-                       tk1, tv1);
+                       tk1, tv1, n_gist_wg / wg_gist_per_bh);
   else
     gp_workgroup<false>(qr, qg, rk, rv, gk, gv, outr, outg, Nc, raw_cap, scale_log2, blk - n_gist_wg,
-                        wg_raw_per_bh, tk0, tv0, tk1, tv1);
+                        wg_raw_per_bh, tk0, tv0, tk1, tv1, n_gist_wg / wg_gist_per_bh);
 }
 
 hipError_t launch_gsa_prefill(const uint16_t* qr, const uint16_t* qg, const uint16_t* rk, const uint16_t* rv,
