@@ -27,7 +27,7 @@
 
 namespace lct {
 
-constexpr int GS_TILE = 1024;   // gists per workgroup
+constexpr int GS_TILE = 512;    // gists per workgroup (1024: 93-95 us, 2048: 106 us at 8192 x 256 rows)
 constexpr int GSA_D = 128;
 constexpr int GSA_MAX_SPLITS = 32;  // slices of one (b, head) row merged by k_split_merge
 constexpr float GSA_LOG2E = 1.4426950408889634f;
