@@ -65,7 +65,8 @@ constexpr int PF_NT = (PF_CW + 2) * 64;
 constexpr int PF_CHUNKS = (PF_TK / 16) * PF_KS;  // 1 KiB fragments per key tile
 constexpr int PF_RING = 128;               // candidate ring entries per row (LDS)
 constexpr int PF_LCAP = 512;               // select: entries of the k-th bin a wave can hold
-constexpr int PF_SEL_W = 4;                // select: waves (rows) per workgroup
+constexpr int PF_SEL_W = 1;                // select: waves (rows) per workgroup (one: more rows
+                                           // resident per CU; 4 measured 2.59 against 2.33 ms)
 static_assert(PF_RB * PF_RING <= PF_RB * PF_NBIN, "the rings reuse the sample histogram");
 
 typedef __attribute__((address_space(3))) void pf_lds_void;
