@@ -576,7 +576,9 @@ constexpr int ROW_NB = 1 << ROW_NB_LOG2;
 constexpr int ROW_CAP = 2048;
 constexpr int ROW_RC = 16;  // keys per thread kept in registers (rows up to 8192 keys)
 
-template <int DT>
+// BMW: bitmap words in LDS (rows of up to 32 * BMW keys); a short-row
+// instance keeps LDS small so that more rows are resident per CU.
+template <int DT, int BMW>
 __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ scores, int64_t n,
                                                       int64_t ld, int k,
                                                       const int32_t* valid_len, int vl_div,
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ s
   constexpr int NT = ROW_NT;
   __shared__ uint32_t h[ROW_NB];
   __shared__ uint64_t sc[ROW_CAP];
-  __shared__ uint32_t bm[TOPK_ROW_MAX_N / 32];
+  __shared__ uint32_t bm[BMW];
   __shared__ uint32_t lds_scan[NT / 64 + 2];
   __shared__ uint32_t lds[32];
   __shared__ uint32_t s_fill;
@@ -686,7 +688,7 @@ __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ s
     const uint64_t am = __ballot(ab);
     if (lane == 0) {
       bm[cb >> 5] = (uint32_t)am;
-      if ((cb >> 5) + 1 < (TOPK_ROW_MAX_N / 32)) bm[(cb >> 5) + 1] = (uint32_t)(am >> 32);
+      if ((cb >> 5) + 1 < BMW) bm[(cb >> 5) + 1] = (uint32_t)(am >> 32);
     }
     const uint64_t cm = __ballot(cand);
     if (cm && ccount <= ROW_CAP) {
@@ -741,10 +743,19 @@ __global__ __launch_bounds__(ROW_NT) void k_topk_rows(const void* __restrict__ s
 hipError_t launch_topk_rows(const void* scores, int dtype, int32_t* idx, int rows, int64_t n,
                             int64_t ld, int k, const int32_t* valid_len, int vl_div,
                             int64_t causal_pos0, hipStream_t s) {
-  if (dtype == 0)
-    k_topk_rows<0><<<rows, ROW_NT, 0, s>>>(scores, n, ld, k, valid_len, vl_div, causal_pos0, idx);
-  else
-    k_topk_rows<1><<<rows, ROW_NT, 0, s>>>(scores, n, ld, k, valid_len, vl_div, causal_pos0, idx);
+  constexpr int SHORT = ROW_NT * ROW_RC / 32;  // bitmap words of the register-cached rows
+  if (n <= (int64_t)SHORT * 32) {
+    if (dtype == 0)
+      k_topk_rows<0, SHORT><<<rows, ROW_NT, 0, s>>>(scores, n, ld, k, valid_len, vl_div, causal_pos0, idx);
+    else
+      k_topk_rows<1, SHORT><<<rows, ROW_NT, 0, s>>>(scores, n, ld, k, valid_len, vl_div, causal_pos0, idx);
+  } else if (dtype == 0) {
+    k_topk_rows<0, TOPK_ROW_MAX_N / 32><<<rows, ROW_NT, 0, s>>>(scores, n, ld, k, valid_len, vl_div, causal_pos0,
+                                                               idx);
+  } else {
+    k_topk_rows<1, TOPK_ROW_MAX_N / 32><<<rows, ROW_NT, 0, s>>>(scores, n, ld, k, valid_len, vl_div, causal_pos0,
+                                                               idx);
+  }
   return hipGetLastError();
 }
 
