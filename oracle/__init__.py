@@ -31,10 +31,34 @@ Sources (web pages on long-context sparse attention):
 * GSA summary page (gist.science) -- section 2.2 (selective unfolding),
   section 2.4 (hierarchical gist-of-gist routing).
 
-Pins: every function is checked against values the pages print, closed
-forms, library routines for the special cases the method reduces to, and
-brute force on tiny inputs (``tests/test_oracle_pins.py``).  No function in
-this package is "parity unpinned".
+Pins (``tests/oracle_pins.py``, run by ``tests/test_oracle_pins.py``; each
+pin is also run against copies with planted mistakes in
+``tests/test_oracle_mutants.py``, which must fail it):
+
+* ``index_scores``: one-hot keys, per-head block keys, the closed-form
+  maximising key, additivity in the key (``pin_index_scores``);
+* ``index_scores_row``: one-hot keys, closed-form maximum and minimum at the
+  int8 extremes, a pure-Python sum of products (``pin_index_scores_row``);
+* ``select_topk``: rank counting by brute force over tiny rows with massive
+  ties and short valid lengths (``pin_topk``);
+* ``softmax_attention`` / ``sparse_attention_gqa``: torch's
+  ``scaled_dot_product_attention`` in float64, row sums, V = 1
+  (``pin_attention``);
+* the driver functions: one index computation per group, the Full/Shared
+  pattern, dense equivalence when k covers the cache, planted needles,
+  causal prefill rows below k against dense causal attention
+  (``pin_driver_sharing``, ``pin_layer_pattern``, ``pin_dense_when_k_covers``,
+  ``pin_needles``, ``pin_prefill``);
+* the GSA functions: every chunk chosen equals dense attention over the whole
+  cache, a planted chunk unfolds exactly its raw tokens, its gist and the
+  tail (``pin_gsa_dense``, ``pin_gsa_sg_sr``); ``hgsa_select`` by brute force
+  (``pin_hgsa_select``); ``hgsa_step`` equal to the flat step when every
+  group is kept and a planted coarse-to-fine case (``pin_hgsa_step``); the
+  gist-mask prefill against explicit softmax over the visible keys
+  (``pin_gsa_prefill``);
+* the sizes: the values printed on the tutorial page (``pin_sizes``).
+
+Every function exported here has such a pin.
 """
 
 from .indexer import index_scores, index_scores_row  # noqa: F401

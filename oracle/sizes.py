@@ -15,11 +15,16 @@ from __future__ import annotations
 
 
 def kv_bytes_per_token(n_layers: int, kv_heads: int, head_dim: int, bytes_per: int = 2) -> int:
-    return n_layers * kv_heads * head_dim * 2 * bytes_per
+    """Cache bytes one token adds: a K row and a V row of every KV head of every layer."""
+    one_row = head_dim * bytes_per            # one head's K (or V) vector
+    per_layer = 2 * kv_heads * one_row        # K and V for every KV head
+    return n_layers * per_layer
 
 
 def kv_cache_gib(n_layers: int, kv_heads: int, head_dim: int, n_tok: int, bytes_per: int = 2) -> float:
-    return kv_bytes_per_token(n_layers, kv_heads, head_dim, bytes_per) * n_tok / 1024**3
+    """Whole cache for ``n_tok`` tokens, in GiB (2**30 bytes)."""
+    total = n_tok * kv_bytes_per_token(n_layers, kv_heads, head_dim, bytes_per)
+    return total / float(1 << 30)
 
 
 def scored_pairs(n_tok: int, per_query: int | None = None) -> int:

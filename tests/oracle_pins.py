@@ -96,6 +96,37 @@ def pin_index_scores(index_scores):
                           np.asarray(index_scores(q1, a, H)) + np.asarray(index_scores(q1, b2, H)))
 
 
+def pin_index_scores_row(index_scores_row):
+    """One query row against a key matrix ``[L, HD]``.
+
+    One-hot keys return single query coordinates; the maximising key has the
+    closed-form score sum_j max(127 q_j, -128 q_j), here at the int8 extremes
+    (a query of -128 everywhere and a key of -128 everywhere give
+    256 x 16384 = 4194304, which wraps in any int8 or int16 accumulation);
+    a pure-Python sum of products over the features agrees on random rows.
+    """
+    rng = np.random.default_rng(23)
+    HD = 256
+    for q in (np.full(HD, -128, np.int8), rng.integers(-128, 128, HD).astype(np.int8)):
+        q64 = [int(x) for x in q]
+        onehot = np.eye(HD, dtype=np.int8)[::17]                       # 16 one-hot keys
+        best = np.where(q.astype(np.int64) >= 0, 127, -128).astype(np.int8)[None]
+        worst = np.where(q.astype(np.int64) >= 0, -128, 127).astype(np.int8)[None]
+        rand = rng.integers(-128, 128, size=(12, HD)).astype(np.int8)
+        ki = np.concatenate([onehot, best, worst, rand])
+        s = np.asarray(index_scores_row(q, ki))
+        assert s.shape == (ki.shape[0],), s.shape
+        assert [int(x) for x in s[:16]] == q64[::17], "one-hot key must return that query coordinate"
+        want_best = sum(max(127 * x, -128 * x) for x in q64)
+        assert int(s[16]) == want_best, ("closed-form maximum", int(s[16]), want_best)
+        assert int(s[17]) == sum(min(127 * x, -128 * x) for x in q64), "closed-form minimum"
+        assert all(int(v) <= want_best for v in s), "no key may beat the maximising key"
+        for t in range(18, ki.shape[0]):
+            assert int(s[t]) == sum(a * int(b) for a, b in zip(q64, ki[t])), ("brute force", t)
+    assert int(np.asarray(index_scores_row(np.full(HD, -128, np.int8),
+                                           np.full((1, HD), -128, np.int8)))[0]) == 4194304
+
+
 # --------------------------------------------------------------------------
 # top-k
 # --------------------------------------------------------------------------
@@ -474,6 +505,69 @@ def pin_hgsa_select(hgsa_select, gsa_select):
         assert list(got) == want, (trial, nc, group, km, kc)
         if km >= nm:
             assert list(got) == list(gsa_select(q, gk, kc)), trial
+
+
+def small_hgsa_cfg(**kw):
+    base = small_gsa_cfg(Nc=14, kc=3, group=4, km=2)   # meta-gists 0..3, the last one short
+    return base.with_(**kw)
+
+
+def pin_hgsa_step(hgsa_step, gsa_step):
+    """Hierarchical GSA decode step (routing, then the gathers and attention).
+
+    (a) With every meta-gist kept (km = number of groups) the coarse step
+    chooses nothing away, so the step equals the flat GSA step, which has its
+    own pins (dense equivalence, the SG+SR key set).
+    (b) A planted case written out from the pages' rule: query and keys are
+    overridden with ternary values; meta-gist ``gp`` and gist ``planted`` (in
+    group ``gp``) equal the query, so their scores ||q||^2 are the unique
+    maxima; with km = kc = 1 the step must unfold exactly chunk ``planted``:
+    its 16 raw rows, its own gist (key and value), and the tail, and nothing
+    else (compared with textbook attention over that key list).
+    """
+    import synth
+    for tail in (0, 2):
+        cfg = small_hgsa_cfg(km=4, tail_len=tail)
+        assert cfg.km >= cfg.Nm
+        ih, oh = hgsa_step(cfg)
+        ig, og = gsa_step(cfg)
+        assert np.array_equal(np.asarray(ih), np.asarray(ig)), "all groups kept: flat selection"
+        assert np.allclose(oh, og, rtol=1e-12, atol=1e-12), "all groups kept: flat attention"
+
+    cfg = small_hgsa_cfg(km=1, kc=1, tail_len=3)
+    _, _, gv, rk, rv = _gsa_inputs(cfg)
+    rng = np.random.default_rng(19)
+    q2 = rng.choice([-1.0, 1.0], size=(cfg.B, cfg.H, cfg.D))
+    gk2 = rng.choice([-1.0, 0.0, 1.0], size=(cfg.B, cfg.H, cfg.Nc, cfg.D))
+    mk2 = rng.choice([-1.0, 0.0, 1.0], size=(cfg.B, cfg.H, cfg.Nm, cfg.D))
+    gp, planted = 2, 10                      # chunk 10 lies in group 2 (chunks 8..11)
+    assert planted // cfg.group == gp
+    mk2[:, :, gp] = q2
+    gk2[:, :, planted] = q2
+    gk2[:, :, 1] = q2                        # an equal gist outside the chosen group is not seen
+
+    import oracle.driver as drv
+    real_rows = drv.C.rows
+    override = {cfg.q_spec(): q2, cfg.gk_spec(): gk2, cfg.mk_spec(): mk2}
+
+    def rows_patched(c, spec, lead):
+        if spec in override:
+            idxs = np.broadcast_arrays(*[np.asarray(a) for a in lead])
+            return synth.f32_to_bf16_bits(override[spec][tuple(idxs)].astype(np.float32))
+        return real_rows(c, spec, lead)
+
+    drv.C.rows = rows_patched
+    try:
+        idx, out = hgsa_step(cfg)
+    finally:
+        drv.C.rows = real_rows
+    for i, (b, h) in enumerate([(b, h) for b in range(cfg.B) for h in range(cfg.H)]):
+        assert list(idx[i]) == [planted], (b, h, list(idx[i]))
+        raw_pos = list(range(planted * 16, planted * 16 + 16)) + [cfg.Nc * 16 + t for t in range(3)]
+        keys = np.concatenate([rk[b, h, raw_pos], gk2[b, h, planted][None]])
+        vals = np.concatenate([rv[b, h, raw_pos], gv[b, h, planted][None]])
+        ref = _sdpa(q2[b, h][None, None], keys[None], vals[None], cfg.scale)[0, 0]
+        assert np.allclose(out[i], ref, rtol=1e-12, atol=1e-12), (b, h)
 
 
 def _softmax_rows(q, k, v, scale):

@@ -296,3 +296,74 @@ def _visible_mutant(kind):
 def test_gsa_prefill_mask_mutants_caught(kind, monkeypatch):
     monkeypatch.setattr(GSA, "gsa_prefill_visible", _visible_mutant(kind))
     _fails(P.pin_gsa_prefill, GSA.gsa_prefill, GSA.gsa_prefill_visible)
+
+
+# ---- one-row indexer scores ----
+
+def _row_no_upcast(qi_row, ki):
+    return np.asarray(ki) @ np.asarray(qi_row)          # int8 accumulation wraps
+
+
+def _row_int16(qi_row, ki):
+    return np.asarray(ki, np.int16) @ np.asarray(qi_row, np.int16)
+
+
+def _row_drops_last_feature(qi_row, ki):
+    return IDX.index_scores_row(np.asarray(qi_row)[:-1], np.asarray(ki)[:, :-1])
+
+
+def _row_transposed_key(qi_row, ki):
+    k = np.asarray(ki).astype(np.int64)
+    return (k[:, ::-1] @ np.asarray(qi_row, np.int64))
+
+
+@pytest.mark.parametrize("mutant", [_row_no_upcast, _row_int16, _row_drops_last_feature, _row_transposed_key])
+def test_index_scores_row_mutants_caught(mutant):
+    _fails(P.pin_index_scores_row, mutant)
+
+
+# ---- hierarchical GSA step ----
+
+def _hgsa_step_mutant(slip):
+    """hgsa_step with one planted slip in its gathers."""
+    from synth import configs as C
+
+    def step(cfg, pairs=None):
+        pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.H)] if pairs is None else list(pairs)
+        f = DRV._f
+        kq, kgk, kgv, kmk = cfg.q_spec()[0], cfg.gk_spec()[0], cfg.gv_spec()[0], cfg.mk_spec()[0]
+        krk, krv = cfg.rk_spec()[0], cfg.rv_spec()[0]
+        idx = np.full((len(pairs), cfg.kc), -1, dtype=np.int32)
+        out = np.zeros((len(pairs), cfg.D))
+        for i, (b, h) in enumerate(pairs):
+            q = f(kq, C.rows(cfg, cfg.q_spec(), (np.array(b), np.array(h))))
+            gk = f(kgk, C.rows(cfg, cfg.gk_spec(), (np.array(b), np.array(h))))
+            mk = f(kmk, C.rows(cfg, cfg.mk_spec(), (np.array(b), np.array(h))))
+            idx[i] = GSA.hgsa_select(q, mk, gk, cfg.group, cfg.km, cfg.kc)
+            tail = 0 if slip == "tail_dropped" else cfg.tail_len
+            raw_pos, gist_ids = GSA.gsa_key_positions(idx[i], cfg.chunk, cfg.Nc, tail)
+            bb, hh = np.full_like(raw_pos, b), np.full_like(raw_pos, h)
+            rk = f(krk, C.rows(cfg, cfg.rk_spec(), (bb, hh, raw_pos)))
+            rv = f(krv, C.rows(cfg, cfg.rv_spec(), (bb, hh, raw_pos)))
+            gv_ids = np.minimum(gist_ids + 1, cfg.Nc - 1) if slip == "gist_value_shifted" else gist_ids
+            gb, gh = np.full_like(gv_ids, b), np.full_like(gv_ids, h)
+            if slip == "gist_key_from_meta":
+                gks = mk[np.minimum(gist_ids // cfg.group, cfg.Nm - 1)]
+            elif slip == "gist_key_shifted":
+                gks = gk[np.maximum(gist_ids - 1, 0)]
+            else:
+                gks = gk[gist_ids]
+            gvs = f(kgv, C.rows(cfg, cfg.gv_spec(), (gb, gh, gv_ids)))
+            out[i] = GSA.gsa_attention(q, rk, rv, gks, gvs, cfg.scale)
+        return idx, out
+    return step
+
+
+@pytest.mark.parametrize("slip", ["tail_dropped", "gist_value_shifted", "gist_key_from_meta", "gist_key_shifted"])
+def test_hgsa_step_mutants_caught(slip):
+    _fails(P.pin_hgsa_step, _hgsa_step_mutant(slip), oracle.gsa_step)
+
+
+def test_hgsa_step_mutant_harness_is_faithful():
+    """The mutant copy without a slip passes, so each caught slip is the slip."""
+    P.pin_hgsa_step(_hgsa_step_mutant("none"), oracle.gsa_step)

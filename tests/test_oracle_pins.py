@@ -8,6 +8,10 @@ def test_index_scores_closed_forms():
     P.pin_index_scores(oracle.index_scores)
 
 
+def test_index_scores_row_closed_forms():
+    P.pin_index_scores_row(oracle.index_scores_row)
+
+
 def test_topk_bruteforce_ranks():
     P.pin_topk(oracle.select_topk)
 
@@ -77,3 +81,7 @@ def test_hgsa_coarse_to_fine_select():
 
 def test_gsa_prefill_gist_mask():
     P.pin_gsa_prefill(oracle.gsa_prefill, oracle.gsa_prefill_visible)
+
+
+def test_hgsa_step_gathers_and_attention():
+    P.pin_hgsa_step(oracle.hgsa_step, oracle.gsa_step)
