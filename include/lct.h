@@ -97,18 +97,19 @@ int lct_idx_score_i8(const int8_t* q, const int8_t* k, int32_t* scores, int B, i
  *                          position, ascending, padded with -1.
  * HD = 256, L <= 65536, topk <= 2048: the scores are never stored; they are
  * filtered to per-row candidate lists on the fly and an exact select runs
- * on those; rows the lists cannot settle go through the plain path.  This
- * synchronizes `stream` once (the number of such rows sizes the plain work)
- * and writes it to *n_fallback (host pointer, may be NULL).  Other shapes
- * (HD a power of two in [64, 512], L <= 2^18) score blocks of rows into the
- * workspace and select per row; *n_fallback is then 0.
+ * on those; rows the lists cannot settle are listed on the device and get a
+ * whole-row select from a fixed grid that reads their count on the device,
+ * so the call is asynchronous like every other.  n_fallback (DEVICE int32,
+ * may be NULL) receives the number of such rows when the stream reaches it.
+ * Other shapes (HD a power of two in [64, 512], L <= 2^18) score blocks of
+ * rows into the workspace and select per row; n_fallback then receives 0.
  * ws: at least lct_prefill_index_workspace_bytes(L, HD, topk) bytes, 256-byte
  * aligned, device memory owned by the caller.  q, k 16-byte aligned.
  * Errors: LCT_EINVAL (null / misaligned / bad sizes), LCT_EUNSUPPORTED
  * (shape), LCT_ENOWORKSPACE, LCT_EHIP.
  */
 int lct_prefill_index_i8(const int8_t* q, const int8_t* k, int32_t* idx, int64_t L, int HD,
-                         int topk, void* ws, size_t ws_bytes, int* n_fallback, void* stream);
+                         int topk, void* ws, size_t ws_bytes, int32_t* n_fallback, void* stream);
 int lct_prefill_index_workspace_bytes(int64_t L, int HD, int topk, size_t* bytes);
 
 /*

@@ -50,8 +50,7 @@ _SIGS = {
     "lct_version": ([], _c.c_char_p),
     "lct_last_error": ([], _c.c_char_p),
     "lct_idx_score_i8": ([_vp, _vp, _vp, _i32, _i32, _i64, _i32, _i64, _vp], _i32),
-    "lct_prefill_index_i8": ([_vp, _vp, _vp, _i64, _i32, _i32, _vp, _sz, _c.POINTER(_i32), _vp],
-                             _i32),
+    "lct_prefill_index_i8": ([_vp, _vp, _vp, _i64, _i32, _i32, _vp, _sz, _vp, _vp], _i32),
     "lct_prefill_index_workspace_bytes": ([_i64, _i32, _i32, _c.POINTER(_sz)], _i32),
     "lct_gist_score_bf16": ([_vp, _vp, _vp, _i32, _i64, _i32, _vp], _i32),
     "lct_topk_select": ([_vp, _i32, _vp, _i32, _i64, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
@@ -175,7 +174,8 @@ def prefill_index(q: torch.Tensor, k: torch.Tensor, topk: int, out: Optional[tor
     Row i lists the min(topk, i + 1) positions t <= i with the largest
     q[i].k[t] (ties to the lower position), ascending, -1 padded.  With
     ``stats`` given, ``stats["n_fallback"]`` receives the number of rows the
-    fused filter left to the plain path.
+    fused filter left to the whole-row select (read after the stream is done:
+    the call itself never waits).
     """
     _need(q, torch.int8, "q")
     _need(k, torch.int8, "k")
@@ -188,11 +188,11 @@ def prefill_index(q: torch.Tensor, k: torch.Tensor, topk: int, out: Optional[tor
     nb = _sz()
     _check(lib().lct_prefill_index_workspace_bytes(L, HD, topk, _c.byref(nb)))
     buf = _ws(ws).get(nb.value)
-    nf = _i32(0)
+    nf = None if stats is None else torch.zeros(1, dtype=torch.int32, device=q.device)
     _check(lib().lct_prefill_index_i8(_p(q), _p(k), _p(out), L, HD, topk, _p(buf), buf.numel(),
-                                      _c.byref(nf), _stream()))
+                                      _p(nf), _stream()))
     if stats is not None:
-        stats["n_fallback"] = int(nf.value)
+        stats["n_fallback"] = int(nf.item())   # waits for the stream (only when asked)
     return out
 
 

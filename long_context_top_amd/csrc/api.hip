@@ -147,9 +147,8 @@ int validate_prefill(int64_t L, int HD, int kk) {
 }
 
 int run_prefill(const int8_t* q, const int8_t* k, int32_t* idx, int64_t L, int HD, int kk,
-                char* ws, int* n_fallback, hipStream_t st) {
+                char* ws, int32_t* n_fallback, hipStream_t st) {
   const PrefillPlan p = prefill_plan(L, HD, kk);
-  if (n_fallback) *n_fallback = 0;
   if (p.fused) {
     LCT_HIP(launch_pf_fused(q, k, L, HD, kk, idx, ws, st, n_fallback), "prefill index (fused)");
     return LCT_OK;
@@ -162,6 +161,7 @@ int run_prefill(const int8_t* q, const int8_t* k, int32_t* idx, int64_t L, int H
     LCT_HIP(launch_topk_rows(scores, LCT_I32, idx + r0 * kk, (int)nr, L, L, kk, nullptr, 1, r0, st),
             "prefill index: topk rows");
   }
+  if (n_fallback) LCT_HIP(launch_zero(n_fallback, sizeof(int32_t), st), "prefill index: n_fallback");
   return LCT_OK;
 }
 
@@ -208,9 +208,9 @@ int lct_prefill_index_workspace_bytes(int64_t L, int HD, int topk, size_t* bytes
 }
 
 int lct_prefill_index_i8(const int8_t* q, const int8_t* k, int32_t* idx, int64_t L, int HD,
-                         int topk, void* ws, size_t ws_bytes, int* n_fallback, void* stream) {
+                         int topk, void* ws, size_t ws_bytes, int32_t* n_fallback, void* stream) {
   LCT_REQUIRE(q && k && idx, "null tensor pointer");
-  LCT_REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(idx, 4), "misaligned tensor");
+  LCT_REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(idx, 4) && aligned(n_fallback, 4), "misaligned tensor");
   int rc = validate_prefill(L, HD, topk);
   if (rc) return rc;
   const size_t need = prefill_plan(L, HD, topk).bytes;

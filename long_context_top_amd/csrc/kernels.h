@@ -133,20 +133,21 @@ hipError_t launch_gsa_attn(const uint16_t* q, const uint16_t* rk, const uint16_t
 // Fused causal prefill score + select (B = 1, Lq = L, HD = 256, L <= 2^16,
 // k <= 2048): scores are filtered to per-row candidate lists (PF_CROW
 // entries), an exact select runs on those, rows with few earlier positions
-// take one plain block, and rows the lists cannot settle go through the
-// plain path in batches of PF_FAIL_CAP.  Synchronizes `st` once (the count
-// of such rows sizes the plain work); *n_failed (if not null) receives it.
+// take one plain block, and rows the lists cannot settle are listed on the
+// device and taken by a fixed grid of whole-row selects (PF_FB_GRID
+// workgroups), so nothing is read back to the host.  n_failed (device int32,
+// may be null) receives the number of such rows.
 constexpr int PF_CROW = 5120;
 constexpr int PF_META = 4;  // words per row: candidates, overflow flag, threshold
-constexpr int PF_FAIL_CAP = 256;
+constexpr int PF_FB_GRID = 256;
 constexpr int64_t PF_MAX_L = (int64_t)1 << 16;
 constexpr int PF_MAX_K = 2048;
 struct PfLayout {
-  size_t list, meta, fails, short_scores, qc, vlen, fscores, fidx, total;
+  size_t list, meta, fails, short_scores, fb_scores, total;
 };
 size_t pf_workspace_layout(int64_t L, int HD, int kk, PfLayout* lay);
 hipError_t launch_pf_fused(const int8_t* q, const int8_t* k, int64_t L, int HD, int kk,
-                           int32_t* idx, char* ws, hipStream_t st, int* n_failed);
+                           int32_t* idx, char* ws, hipStream_t st, int32_t* n_failed);
 
 // --------------------------------------------------------------- misc ----
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);

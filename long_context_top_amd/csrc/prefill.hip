@@ -47,6 +47,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "topk_dev.h"
 
 namespace lct {
 
@@ -811,25 +812,46 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
   for (uint32_t j = lane; j < (uint32_t)kk; j += 64) out[j] = j < tot ? (int32_t)stage[j] : -1;
 }
 
-// ---- plain path for the rows the lists could not settle -----------------
+// ---- whole-row select for the rows the lists could not settle ----------
 
-// compact the queries of failed rows [b0, b0 + nb) of the list
-__global__ __launch_bounds__(256) void k_pf_fb_gather(const int8_t* __restrict__ q,
-                                                      const int32_t* __restrict__ rows,
-                                                      int8_t* __restrict__ qc,
-                                                      int32_t* __restrict__ vlen) {
-  const int slot = blockIdx.x;
-  const int64_t row = rows[slot];
-  for (int i = threadIdx.x; i < PF_HD; i += 256) qc[(size_t)slot * PF_HD + i] = q[row * PF_HD + i];
-  if (threadIdx.x == 0) vlen[slot] = (int32_t)(row + 1);
-}
-
-__global__ __launch_bounds__(256) void k_pf_fb_scatter(const int32_t* __restrict__ fidx, int kk,
-                                                       const int32_t* __restrict__ rows,
-                                                       int32_t* __restrict__ idx) {
-  const int slot = blockIdx.x;
-  const int64_t row = rows[slot];
-  for (int j = threadIdx.x; j < kk; j += 256) idx[row * kk + j] = fidx[(size_t)slot * kk + j];
+// A fixed grid takes the rows k_pf_select listed, in turn: workgroup w takes
+// list slots w, w + grid, ... below the count the list holds on the device
+// (the host never reads it, so the call stays asynchronous), scores its row
+// against every earlier key into its own slice of the workspace (one key per
+// lane, the query row broadcast from LDS) and runs the one-row select on it.
+__global__ __launch_bounds__(ROW_NT) void k_pf_fallback(const int8_t* __restrict__ q,
+                                                        const int8_t* __restrict__ k, int kk,
+                                                        const int32_t* __restrict__ fails,
+                                                        int32_t* __restrict__ scratch, int L,
+                                                        int32_t* __restrict__ idx,
+                                                        int32_t* __restrict__ n_out) {
+  __shared__ RowSelSmem<PF_MAX_L / 32> sm;
+  __shared__ uintx4 qrow[PF_HD / 16];
+  const int nf = fails[0];
+  if (n_out && blockIdx.x == 0 && threadIdx.x == 0) *n_out = nf;
+  int32_t* const sc = scratch + (size_t)blockIdx.x * L;
+  for (int slot = blockIdx.x; slot < nf; slot += gridDim.x) {
+    const int row = fails[1 + slot];
+    __syncthreads();  // the previous row is done with the LDS and the slice
+    if (threadIdx.x < PF_HD / 16)
+      qrow[threadIdx.x] = reinterpret_cast<const uintx4*>(q + (size_t)row * PF_HD)[threadIdx.x];
+    __syncthreads();
+    for (int t = threadIdx.x; t <= row; t += ROW_NT) {
+      const uintx4* kp = reinterpret_cast<const uintx4*>(k + (size_t)t * PF_HD);
+      int32_t acc = 0;
+#pragma unroll
+      for (int w = 0; w < PF_HD / 16; ++w) {
+        const uintx4 kv = kp[w], qv = qrow[w];
+        acc = __builtin_amdgcn_sdot4((int)qv.x, (int)kv.x, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)qv.y, (int)kv.y, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)qv.z, (int)kv.z, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)qv.w, (int)kv.w, acc, false);
+      }
+      sc[t] = acc;
+    }
+    __syncthreads();  // the whole row is stored (same workgroup, same L1)
+    row_select<0, PF_MAX_L / 32>(sc, (uint32_t)row + 1u, kk, idx + (size_t)row * kk, sm);
+  }
 }
 
 __global__ void k_pf_zero_fails(int32_t* fails) {
@@ -848,6 +870,9 @@ static void pf_params(int64_t L, int kk, int* m_s, int* r_all) {
   *r_all = (int)ra;
 }
 
+// Workgroups of the whole-row fallback (one row at a time each).
+static int pf_fallback_grid(int64_t L) { return (int)(L < PF_FB_GRID ? L : PF_FB_GRID); }
+
 size_t pf_workspace_layout(int64_t L, int HD, int kk, PfLayout* lay) {
   (void)HD;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -863,21 +888,15 @@ size_t pf_workspace_layout(int64_t L, int HD, int kk, PfLayout* lay) {
   off += up((size_t)(1 + L) * 4);
   l.short_scores = off;
   off += up((size_t)(r_all - kk > 0 ? r_all - kk : 0) * r_all * 4);
-  l.qc = off;
-  off += up((size_t)PF_FAIL_CAP * PF_HD);
-  l.vlen = off;
-  off += up((size_t)PF_FAIL_CAP * 4);
-  l.fscores = off;
-  off += up((size_t)PF_FAIL_CAP * L * 4);
-  l.fidx = off;
-  off += up((size_t)PF_FAIL_CAP * kk * 4);
+  l.fb_scores = off;
+  off += up((size_t)pf_fallback_grid(L) * L * 4);
   l.total = off;
   if (lay) *lay = l;
   return off;
 }
 
 hipError_t launch_pf_fused(const int8_t* q, const int8_t* k, int64_t L, int HD, int kk,
-                           int32_t* idx, char* ws, hipStream_t st, int* n_failed) {
+                           int32_t* idx, char* ws, hipStream_t st, int32_t* n_failed) {
   if (HD != PF_HD || L < 1 || L > PF_MAX_L || kk < 1 || kk > PF_MAX_K) return hipErrorInvalidValue;
   PfLayout l;
   pf_workspace_layout(L, HD, kk, &l);
@@ -904,25 +923,10 @@ hipError_t launch_pf_fused(const int8_t* q, const int8_t* k, int64_t L, int HD, 
   k_pf_select<<<dim3((unsigned)((L + PF_SEL_W - 1) / PF_SEL_W)), PF_SEL_W * 64, 0, st>>>(
       q, k, (int)L, kk, r_all, list, meta, idx, fails);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // rows the lists could not settle: the count decides how much plain work follows
-  int32_t nf = 0;
-  if ((e = hipMemcpyAsync(&nf, fails, sizeof(nf), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
-  if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
-  if (n_failed) *n_failed = nf;
-  auto qc = reinterpret_cast<int8_t*>(ws + l.qc);
-  auto vlen = reinterpret_cast<int32_t*>(ws + l.vlen);
-  auto fscores = reinterpret_cast<int32_t*>(ws + l.fscores);
-  auto fidx = reinterpret_cast<int32_t*>(ws + l.fidx);
-  for (int b0 = 0; b0 < nf; b0 += PF_FAIL_CAP) {
-    const int nb = nf - b0 < PF_FAIL_CAP ? nf - b0 : PF_FAIL_CAP;
-    const int32_t* rows = fails + 1 + b0;
-    k_pf_fb_gather<<<nb, 256, 0, st>>>(q, rows, qc, vlen);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_idx_score_mfma(qc, k, fscores, 1, nb, L, PF_HD, -1, st)) != hipSuccess) return e;
-    if ((e = launch_topk_rows(fscores, 0, fidx, nb, L, L, kk, vlen, 1, -1, st)) != hipSuccess) return e;
-    k_pf_fb_scatter<<<nb, 256, 0, st>>>(fidx, kk, rows, idx);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  // rows the lists could not settle: a fixed grid reads their count on the device
+  k_pf_fallback<<<pf_fallback_grid(L), ROW_NT, 0, st>>>(q, k, kk, fails, reinterpret_cast<int32_t*>(ws + l.fb_scores),
+                                                       (int)L, idx, n_failed);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   return hipSuccess;
 }
 

@@ -39,8 +39,12 @@ pin is also run against copies with planted mistakes in
   maximising key, additivity in the key (``pin_index_scores``);
 * ``index_scores_row``: one-hot keys, closed-form maximum and minimum at the
   int8 extremes, a pure-Python sum of products (``pin_index_scores_row``);
-* ``select_topk``: rank counting by brute force over tiny rows with massive
-  ties and short valid lengths (``pin_topk``);
+* ``index_scores_f32``: equal to a pure-Python sum of products on random
+  full-range int8 rows and at the int8 extremes, refusing head dims past
+  its exactness bound (``pin_index_scores_f32``);
+* ``select_topk`` and ``select_topk_threshold``: rank counting by brute
+  force over tiny rows with massive ties and short valid lengths
+  (``pin_topk``);
 * ``softmax_attention`` / ``sparse_attention_gqa``: torch's
   ``scaled_dot_product_attention`` in float64, row sums, V = 1
   (``pin_attention``);
@@ -61,8 +65,8 @@ pin is also run against copies with planted mistakes in
 Every function exported here has such a pin.
 """
 
-from .indexer import index_scores, index_scores_row  # noqa: F401
-from .topk import select_topk  # noqa: F401
+from .indexer import index_scores, index_scores_f32, index_scores_row  # noqa: F401
+from .topk import select_topk, select_topk_threshold  # noqa: F401
 from .attention import softmax_attention, sparse_attention_gqa  # noqa: F401
 from .gsa import (gist_scores, gsa_key_positions, gsa_attention, gsa_select, hgsa_select,  # noqa: F401
                   gsa_prefill, gsa_prefill_rows, gsa_prefill_visible)

@@ -47,3 +47,21 @@ def index_scores_row(qi_row: np.ndarray, ki: np.ndarray) -> np.ndarray:
     Provided for sampled checks at full size: it touches only one query row.
     """
     return ki.astype(np.int64) @ qi_row.astype(np.int64)
+
+
+def index_scores_f32(qi: np.ndarray, ki: np.ndarray) -> np.ndarray:
+    """Scores ``[R, L]`` (int64) of query rows ``qi[R, HD]`` against ``ki[L, HD]``
+    through a float32 matrix product.
+
+    Exact, not approximate: every product of two int8 values and every partial
+    sum of at most ``HD`` of them is an integer of magnitude at most
+    ``HD * 128 * 128``, and while that stays below 2**24 float32 represents
+    each of them exactly, so any summation order gives the exact integer.  The
+    bound is checked.  Used for whole-group checks at the large workloads,
+    where the int64 product is too slow.
+    """
+    HD = qi.shape[-1]
+    if HD * 128 * 128 >= (1 << 24):
+        raise ValueError("float32 sums are exact only for HD * 2**14 < 2**24")
+    s = qi.astype(np.float32) @ ki.astype(np.float32).T
+    return s.astype(np.int64)

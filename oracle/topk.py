@@ -46,3 +46,39 @@ def select_topk(scores: np.ndarray, k: int, valid_len=None) -> np.ndarray:
         take = np.sort(order[: min(k, nv)])
         out[r, : take.size] = take
     return out.reshape(lead + (k,))
+
+
+def select_topk_threshold(scores: np.ndarray, k: int, valid_len=None) -> np.ndarray:
+    """The same index sets as :func:`select_topk`, found without a full sort.
+
+    For score rows ``[R, n]`` (integer or float): the k-th largest valid value T comes
+    from a partition; every valid position scoring above T is chosen, and of
+    the positions scoring exactly T the lowest-numbered ones fill the rest
+    (the tie rule).  Rows with at most k valid positions keep all of them.
+    Used for whole-group checks at the large workloads.
+    """
+    scores = np.asarray(scores)
+    R, n = scores.shape
+    vl = np.broadcast_to(np.asarray(n if valid_len is None else valid_len, dtype=np.int64), (R,))
+    vl = np.clip(vl, 0, n)
+    out = np.full((R, k), -1, dtype=np.int32)
+    if scores.dtype.kind == "f":
+        masked, low = scores.astype(np.float64, copy=True), -np.inf
+    else:
+        masked, low = scores.astype(np.int64, copy=True), np.iinfo(np.int64).min
+    pos = np.arange(n)
+    masked[pos[None, :] >= vl[:, None]] = low
+    short = vl <= k
+    for r in np.where(short)[0]:
+        out[r, : vl[r]] = np.arange(vl[r])
+    long_rows = np.where(~short)[0]
+    if long_rows.size:
+        m = masked[long_rows]
+        T = np.partition(m, n - k, axis=1)[:, n - k]                 # k-th largest value
+        above = m > T[:, None]
+        need = k - above.sum(axis=1)                                 # ties at T to take
+        eq = m == T[:, None]
+        take = above | (eq & (np.cumsum(eq, axis=1) <= need[:, None]))
+        for j, r in enumerate(long_rows):
+            out[r] = np.nonzero(take[j])[0]
+    return out

@@ -127,6 +127,31 @@ def pin_index_scores_row(index_scores_row):
                                            np.full((1, HD), -128, np.int8)))[0]) == 4194304
 
 
+def pin_index_scores_f32(index_scores_f32):
+    """The float32 product path: exact integers on full-range int8 rows (a
+    pure-Python sum of products), at the extremes (-128 everywhere: 4194304),
+    and a refusal past the exactness bound (HD = 1024 could reach 2**24)."""
+    rng = np.random.default_rng(31)
+    HD = 256
+    q = rng.integers(-128, 128, size=(5, HD)).astype(np.int8)
+    k = rng.integers(-128, 128, size=(9, HD)).astype(np.int8)
+    q[0] = -128
+    k[0] = -128
+    k[1] = 127
+    s = np.asarray(index_scores_f32(q, k))
+    assert s.shape == (5, 9) and s.dtype.kind == "i"
+    for i in range(5):
+        for t in range(9):
+            assert int(s[i, t]) == sum(int(a) * int(b) for a, b in zip(q[i], k[t])), (i, t)
+    assert int(s[0, 0]) == 4194304 and int(s[0, 1]) == -128 * 127 * 256
+    try:
+        index_scores_f32(np.zeros((1, 1024), np.int8), np.zeros((1, 1024), np.int8))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("HD = 1024 is past the float32 exactness bound")
+
+
 # --------------------------------------------------------------------------
 # top-k
 # --------------------------------------------------------------------------

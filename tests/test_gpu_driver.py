@@ -94,6 +94,43 @@ def test_causal_prefill_small():
     assert np.abs(out[3][0, sample] - ref).max() < ATOL
 
 
+def test_causal_prefill_graph_capture():
+    """Causal group_run (index with rows for the whole-row select, then
+    attention) captured in a HIP graph and replayed three times with eager
+    work in between; index sets and sampled outputs checked each time."""
+    cfg = C.DecodeConfig("prefill_graph", 5353, B=1, Lq=1300, L=1300, n_layers=4, group=4, Hq=8, Hkv=2,
+                         D=128, H_idx=4, d_idx=64, topk=64, causal=True)
+    announce(cfg.name)
+    qi, ki, q, k, v = _inputs(cfg)
+    qi[0][0, 3::4] = 0                       # all-zero rows: every score equal
+    idx_out = [torch.full((1, cfg.L, cfg.topk), -7, dtype=torch.int32, device="cuda")]
+    out = [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in q]
+    run = lct.GroupRun(qi, ki, q, k, v, out, cfg.topk, cfg.group, cfg.scale, causal=True, idx_out=idx_out)
+    run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    qh = host(qi[0])[0]
+    kh = host(ki[0])[0]
+    sc = oracle.index_scores(qh[None], kh[None], cfg.H_idx)[0]
+    want = oracle.select_topk(sc, cfg.topk, np.arange(cfg.L) + 1)
+    sample = [0, 3, 63, 64, 67, 700, 1299]
+    ref = oracle.prefill_attention_rows(cfg, 2, sample, want[sample])
+    for rep in range(3):
+        idx_out[0].fill_(-7)
+        out[2].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(idx_out[0])[0], want), rep
+        assert np.abs(host(out[2])[0, sample] - ref).max() < ATOL, rep
+
+
 def _run_pattern(cfg, layer_full):
     n_full = sum(layer_full)
     qi = [sd.make(cfg, cfg.qi_spec(g)) for g in range(n_full)]

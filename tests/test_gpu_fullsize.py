@@ -1,12 +1,18 @@
 """Parity at the full workload sizes (MI355X), in the launch configuration the
-benchmark times, on outputs the oracle computes one sampled row at a time.
+benchmark times.
 
-Every index set is also checked for properties that hold at any size
-(ascending, unique, in range, exactly min(k, valid) entries, one buffer per
-group).  Inputs are generated in HBM by the device filler; the oracle
-regenerates only the rows it reads.
+Every index set of every workload is compared with the oracle: all
+(group, sequence) sets of the decode workloads, all (batch, head) pairs of the
+GSA workloads, every row of the 64K causal index.  Attention outputs are
+compared on sampled layers and rows (each costs the oracle a float64 softmax
+over gathered rows).  Every index set is also checked for properties that hold
+at any size (ascending, unique, in range, exactly min(k, valid) entries, one
+buffer per group).  Inputs are generated in HBM by the device filler; the
+oracle regenerates the rows it reads with the host generator (threads over
+independent rows).
 """
 
+import concurrent.futures as cf
 import gc
 
 import numpy as np
@@ -38,18 +44,27 @@ def _check_index_rows(idx, L, k, valid):
     assert idx[n - 1] < valid
 
 
-def _oracle_scores_row(cfg, g, b, qrow=0, chunk=1 << 16):
-    """Exact int64 indexer scores of one query row over all L positions, chunked."""
-    qi = C.rows(cfg, cfg.qi_spec(g), (np.array([b]), np.array([qrow])))[0].astype(np.int64)
-    out = np.empty(cfg.L, dtype=np.int64)
-    for t0 in range(0, cfg.L, chunk):
+def _pool(fn, items, workers=8):
+    with cf.ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, items))
+
+
+def _oracle_set(cfg, g, b):
+    """The oracle's index set of sequence b in group g (exact int64 scores of
+    the one query row, chunks of keys regenerated in parallel)."""
+    qi = C.rows(cfg, cfg.qi_spec(g), (np.array([b]), np.array([0])))[0]
+    chunk = 1 << 17
+    starts = list(range(0, cfg.L, chunk))
+
+    def part(t0):
         t = np.arange(t0, min(cfg.L, t0 + chunk))
-        ki = C.rows(cfg, cfg.ki_spec(g), (np.full_like(t, b), t)).astype(np.int64)
-        out[t0:t0 + t.size] = oracle.index_scores_row(qi, ki)
-    return out
+        return oracle.index_scores_row(qi, C.rows(cfg, cfg.ki_spec(g), (np.full_like(t, b), t)))
+
+    s = np.concatenate(_pool(part, starts))
+    return oracle.select_topk_threshold(s[None], cfg.topk)[0]
 
 
-def _decode_full(cfg, sample_groups, sample_rows, sample_layers):
+def _decode_full(cfg, sample_rows, sample_layers):
     announce(cfg.name)
     ng = cfg.n_groups
     qi = [sd.make(cfg, cfg.qi_spec(g)) for g in range(ng)]
@@ -70,11 +85,14 @@ def _decode_full(cfg, sample_groups, sample_rows, sample_layers):
     for g in range(ng):
         for b in range(cfg.B):
             _check_index_rows(idx[g][b, 0], cfg.L, cfg.topk, cfg.L)
-    for g in sample_groups:
-        for b in sample_rows:
-            s = _oracle_scores_row(cfg, g, b)
-            want = oracle.select_topk(s, cfg.topk, cfg.L)
-            assert np.array_equal(idx[g][b, 0], want), (g, b)
+    sets = [(g, b) for g in range(ng) for b in range(cfg.B)]
+    if cfg.L >= (1 << 20):
+        wants = [_oracle_set(cfg, g, b) for g, b in sets]       # chunks in parallel inside
+    else:
+        wants = _pool(lambda gb: _oracle_set(cfg, *gb), sets)
+    bad = [gb for gb, w in zip(sets, wants) if not np.array_equal(idx[gb[0]][gb[1], 0], w)]
+    assert not bad, f"{len(bad)} of {len(sets)} (group, sequence) index sets differ: {bad[:6]}"
+    print(f"  all {len(sets)} (group, sequence) index sets equal the oracle's", flush=True)
     for l in sample_layers:
         g = l // cfg.group
         ref = oracle.decode_layers(cfg, l, idx[g][sample_rows], batch=sample_rows)
@@ -86,15 +104,32 @@ def _decode_full(cfg, sample_groups, sample_rows, sample_layers):
 
 
 def test_decode_128k_b8_full_size():
-    _decode_full(C.DECODE_128K, sample_groups=[0, 6], sample_rows=[0, 7], sample_layers=[0, 3, 27])
+    _decode_full(C.DECODE_128K, sample_rows=[0, 7], sample_layers=[0, 3, 27])
 
 
 def test_decode_32k_b8_full_size():
-    _decode_full(C.DECODE_32K, sample_groups=[2], sample_rows=[3, 5], sample_layers=[9, 10])
+    _decode_full(C.DECODE_32K, sample_rows=[3, 5], sample_layers=[9, 10])
 
 
 def test_decode_1m_b1_full_size():
-    _decode_full(C.DECODE_1M, sample_groups=[0, 5], sample_rows=[0], sample_layers=[1, 22])
+    _decode_full(C.DECODE_1M, sample_rows=[0], sample_layers=[1, 22])
+
+
+def _check_all_pairs(cfg, step, got_idx, got):
+    """Every (batch, head) pair: chunk set bit-exact, output within ATOL."""
+    pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    parts = _pool(lambda ps: step(cfg, ps), [pairs[i::16] for i in range(16)])
+    ref_idx = np.zeros((len(pairs), cfg.kc), dtype=np.int64)
+    ref_out = np.zeros((len(pairs), cfg.D))
+    for i in range(16):
+        ref_idx[i::16], ref_out[i::16] = parts[i]
+    rows = [b * cfg.H + h for b, h in pairs]
+    bad = [p for p, r, w in zip(pairs, rows, ref_idx) if not np.array_equal(got_idx[r], w)]
+    assert not bad, f"{len(bad)} of {len(pairs)} chunk sets differ: {bad[:6]}"
+    err = np.abs(got[rows] - ref_out).max()
+    print(f"  all {len(pairs)} (batch, head) chunk sets equal the oracle's; max |out - oracle| = {err:.2e}",
+          flush=True)
+    assert err < ATOL
 
 
 def test_gsa_128k_b16_full_size():
@@ -113,20 +148,14 @@ def test_gsa_128k_b16_full_size():
     got_idx, got = host(cidx), host(out)
     for i in range(BH):
         _check_index_rows(got_idx[i], cfg.Nc, cfg.kc, cfg.Nc)
-    pairs = [(0, 0), (3, 7), (9, 15), (15, 2)]
-    ref_idx, ref_out = oracle.driver.gsa_step(cfg, pairs)
-    for j, (b, h) in enumerate(pairs):
-        i = b * cfg.H + h
-        assert np.array_equal(got_idx[i], ref_idx[j]), (b, h)
-        assert np.abs(got[i] - ref_out[j]).max() < ATOL, (b, h)
+    _check_all_pairs(cfg, oracle.driver.gsa_step, got_idx, got)
     del qv, gk, gv, rk, rv, out, cidx
     _free()
 
 
 def test_causal_prefill_64k_full_size():
-    """One group (4 layers) of the 64K causal prefill; index sets checked on
-    every row for the structural properties and against the oracle on rows
-    below k (all of them) and a spread of longer rows."""
+    """One group (4 layers) of the 64K causal prefill; every index row against
+    the oracle, attention outputs on sampled rows."""
     cfg = C.PREFILL_64K.with_(n_layers=4)
     announce(cfg.name)
     qi = [sd.make(cfg, cfg.qi_spec(0))]
@@ -146,7 +175,21 @@ def test_causal_prefill_64k_full_size():
     below = np.arange(cfg.topk)  # rows whose set is every earlier position
     for r in below[::37]:
         assert np.array_equal(idx[r][: r + 1], np.arange(r + 1))
-    rows = [2047, 2048, 2049, 4095, 10000, 33333, 50001, 65535]
+    # every row against the exact float32-product scorer + partition select
+    # (both pinned against the int64 / sort definitions on the CPU)
+    qh = C.rows(cfg, cfg.qi_spec(0), (np.array([0]),))[0]
+    kh = C.rows(cfg, cfg.ki_spec(0), (np.array([0]),))[0]
+    blocks = [np.arange(r0, min(cfg.L, r0 + 512)) for r0 in range(0, cfg.L, 512)]
+
+    def block_bad(rb):
+        s = oracle.index_scores_f32(qh[rb], kh[: rb[-1] + 1])
+        w = oracle.select_topk_threshold(s, cfg.topk, rb + 1)
+        return [int(r) for r, a, b in zip(rb, idx[rb], w) if not np.array_equal(a, b)]
+
+    bad = [r for rs in _pool(block_bad, blocks) for r in rs]
+    assert not bad, f"{len(bad)} of {cfg.L} rows differ from the oracle: {bad[:8]}"
+    print(f"  all {cfg.L} index rows equal the oracle's", flush=True)
+    rows = [2047, 2048, 2049, 33333, 65535]     # the int64 / sort definition on a few rows
     want = oracle.prefill_index_rows(cfg, 0, rows)
     for j, r in enumerate(rows):
         assert np.array_equal(idx[r], want[j]), r
@@ -174,12 +217,7 @@ def test_hgsa_128k_b16_full_size():
     got_idx, got = host(cidx), host(out)
     for i in range(BH):
         _check_index_rows(got_idx[i], cfg.Nc, cfg.kc, cfg.Nc)
-    pairs = [(0, 0), (3, 7), (9, 15), (15, 2)]
-    ref_idx, ref_out = oracle.driver.hgsa_step(cfg, pairs)
-    for j, (b, h) in enumerate(pairs):
-        i = b * cfg.H + h
-        assert np.array_equal(got_idx[i], ref_idx[j]), (b, h)
-        assert np.abs(got[i] - ref_out[j]).max() < ATOL, (b, h)
+    _check_all_pairs(cfg, oracle.driver.hgsa_step, got_idx, got)
     del qv, mkeys, gk, gv, rk, rv, out, cidx
     _free()
 

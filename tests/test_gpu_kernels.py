@@ -127,6 +127,27 @@ def test_topk_rows_kernel(case):
     _check_topk(s if s.dtype.kind == "f" else s.astype(np.int64), k, vl)
 
 
+@pytest.mark.parametrize("n", [8192, 8193, 20000, 100000])
+@pytest.mark.parametrize("case", ["random", "allequal", "valid"])
+def test_topk_rows_kernel_long_rows(n, case):
+    """More than 64 rows of up to 100000 keys: the one-workgroup-per-row
+    select, its full-bitmap instance above 8192 keys and the rows it reads
+    again per pass (above 8192 keys it cannot keep in registers)."""
+    announce(f"topk rows long n={n} {case}")
+    r = _rng(n + len(case))
+    rows, k = 65, 512
+    vl = None
+    if case == "random":
+        s = r.integers(-3000, 3000, size=(rows, n))
+    elif case == "allequal":
+        s = np.full((rows, n), -11)
+    else:
+        s = r.integers(-100, 100, size=(rows, n))
+        vl = r.integers(0, n + 5, size=rows)
+        vl[:6] = [0, 1, 511, 512, 8192, 8193]
+    _check_topk(s.astype(np.int64), k, vl)
+
+
 @pytest.mark.parametrize("case", ["normal", "allequal", "outlier", "valid", "float", "many_rows_long"])
 def test_topk_multi_kernel(case):
     announce(f"topk multi {case}")

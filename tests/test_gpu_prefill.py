@@ -102,3 +102,117 @@ def test_prefill_index_unfused_shape():
     got, nf = _run(q, k, topk)
     assert nf == 0
     assert np.array_equal(got, _want(q, k, topk))
+
+
+# ---- every row at k = 2048, where the fused path runs -------------------
+
+def _want_fast(q, k, topk, rows):
+    """All listed rows through the exact float32-product scorer and the
+    partition select (both pinned on the CPU), in blocks, keys cut to the
+    block's last row."""
+    import concurrent.futures as cf
+    rows = np.asarray(rows)
+    blocks = [rows[i:i + 256] for i in range(0, rows.size, 256)]
+
+    def one(b):
+        n = int(b.max()) + 1
+        s = oracle.index_scores_f32(q[b], k[:n])
+        return oracle.select_topk_threshold(s, topk, b + 1)
+
+    with cf.ThreadPoolExecutor(8) as ex:
+        return np.concatenate(list(ex.map(one, blocks)))
+
+
+def _m_s(topk):
+    # the filter's sample target (every 16th key): k/16 + 6 sqrt(k/16), + 4
+    ks = topk / 16.0
+    return int(np.ceil(ks + 6.0 * np.sqrt(ks))) + 4
+
+
+def test_prefill_index_fused_k2048_every_row():
+    """16384 rows at k = 2048: rows from 32 m_s = 6400 on take the fused
+    filter + list select at the workload's k; every row is compared."""
+    L, topk = 16384, 2048
+    announce(f"prefill_index fused every row L={L} k={topk}")
+    q, k = _synth_qk(20480, L)
+    got, nf = _run(q, k, topk)
+    assert 2 * 16 * _m_s(topk) == 6400
+    want = _want_fast(q, k, topk, np.arange(L))
+    bad = np.where(~np.all(got == want, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:8]}"
+    assert nf < L // 100
+
+
+@pytest.mark.parametrize("topk", [16, 256])
+def test_prefill_index_full_range_int8(topk):
+    """q, k uniform over all int8 values: candidates lie far above the
+    threshold, so their stored score offsets saturate at 65535 and the list
+    select re-scores the k-th bin exactly (the clamped branch).  The input is
+    checked to force that branch: in many rows the k-th largest score lies
+    more than 65535 above the m_s-th largest sampled score, hence above the
+    row's threshold by more than the offset can hold.  Every row compared."""
+    L = 4100
+    announce(f"prefill_index full-range int8 L={L} k={topk}")
+    r = np.random.default_rng(topk)
+    q = r.integers(-128, 128, size=(L, HD)).astype(np.int8)
+    k = r.integers(-128, 128, size=(L, HD)).astype(np.int8)
+    got, nf = _run(q, k, topk)
+    want = _want_fast(q, k, topk, np.arange(L))
+    bad = np.where(~np.all(got == want, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:8]}"
+    assert nf < L // 4
+    ms = _m_s(topk)
+    r_all = max(2 * 16 * ms, topk)
+    rows = np.arange(r_all, L, 37)
+    s = oracle.index_scores_f32(q[rows], k)
+    forced = 0
+    for j, i in enumerate(rows):
+        row = s[j, : i + 1]
+        kth = np.partition(row, row.size - topk)[row.size - topk]
+        samp = np.sort(row[::16])[::-1]
+        forced += int(kth - samp[ms - 1] > 65535)
+    print(f"  rows forced onto the clamped branch: {forced} of {rows.size}", flush=True)
+    if topk == 16:
+        assert forced > rows.size // 4
+
+
+def test_prefill_index_unfused_long_rows():
+    """HD = 128 (blocked scores + row select) with rows longer than 8192 keys:
+    the row select's full-bitmap instance; sampled rows checked."""
+    L, topk = 9000, 300
+    announce(f"prefill_index HD=128 L={L} k={topk}")
+    q = synth.tensor(synth.I8U4, 19, 1, (L, 128))
+    k = synth.tensor(synth.I8U4, 19, 2, (L, 128))
+    got, nf = _run(q, k, topk)
+    assert nf == 0
+    rows = np.array([0, 299, 300, 8191, 8192, 8193, 8999])
+    assert np.array_equal(got[rows], _want(q, k, topk, rows))
+
+
+def test_prefill_index_graph_replays():
+    """The causal index is asynchronous: it is captured in a HIP graph
+    (including rows that go to the whole-row select: half the query rows are
+    zero) and replayed with eager work in between; every replay is checked."""
+    L, topk = 2500, 128
+    announce(f"prefill_index graph capture L={L} k={topk}")
+    q, k = _synth_qk(5150, L)
+    q[1::2] = 0
+    qd, kd = dev_i8(q), dev_i8(k)
+    out = torch.full((L, topk), -7, dtype=torch.int32, device="cuda")
+    ws = lct.Workspace()
+    lct.prefill_index(qd, kd, topk, out=out, ws=ws)      # sizes the workspace outside the capture
+    torch.cuda.synchronize()
+    want = _want(q, k, topk)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            lct.prefill_index(qd, kd, topk, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), want), rep

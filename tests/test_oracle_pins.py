@@ -12,8 +12,16 @@ def test_index_scores_row_closed_forms():
     P.pin_index_scores_row(oracle.index_scores_row)
 
 
+def test_index_scores_f32_exact():
+    P.pin_index_scores_f32(oracle.index_scores_f32)
+
+
 def test_topk_bruteforce_ranks():
     P.pin_topk(oracle.select_topk)
+
+
+def test_topk_threshold_bruteforce_ranks():
+    P.pin_topk(oracle.select_topk_threshold)
 
 
 def test_attention_textbook_cases():
