@@ -301,6 +301,25 @@ typedef struct lct_group_desc {
 int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stream);
 int lct_group_workspace_bytes(const lct_group_desc* d, size_t* bytes);
 
+/*
+ * lct_group_run without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP-graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The scratch memory
+ * is a fixed array of LCT_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * per GPU, placed when the library's code is loaded on that device and held
+ * until the process ends; the call allocates and frees nothing.  Same
+ * descriptor, semantics and outputs as lct_group_run.  A step whose workspace
+ * (lct_group_workspace_bytes) exceeds LCT_NOALLOC_SCRATCH_BYTES is rejected
+ * with LCT_ENOWORKSPACE before anything is enqueued (decode steps of the
+ * 128K x 8 and 1M x 1 workloads need about 9 MiB and 5 MiB; a causal prefill
+ * of thousands of rows does not fit).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads) race
+ * and must be serialised by the caller.  The array needs no initialisation
+ * (as for lct_group_run's workspace).
+ */
+#define LCT_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int lct_group_run_noalloc(const lct_group_desc* d, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,7 @@ __all__ = [
 LCT_OK, LCT_EINVAL, LCT_EUNSUPPORTED, LCT_ENOWORKSPACE, LCT_ENODEV, LCT_EHIP = range(6)
 LCT_I32, LCT_F32 = 0, 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblct.so")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # LCT_NOALLOC_SCRATCH_BYTES in lct.h
 
 _c = ctypes
 _vp, _i32, _i64, _f32, _sz = _c.c_void_p, _c.c_int, _c.c_int64, _c.c_float, _c.c_size_t
@@ -71,6 +72,7 @@ _SIGS = {
     "lct_gsa_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _f32, _vp], _i32),
     "lct_group_run": ([_c.POINTER(GroupDesc), _vp, _sz, _vp], _i32),
     "lct_group_workspace_bytes": ([_c.POINTER(GroupDesc), _c.POINTER(_sz)], _i32),
+    "lct_group_run_noalloc": ([_c.POINTER(GroupDesc), _vp], _i32),
 }
 
 _lib = None
@@ -411,6 +413,11 @@ class GroupRun:
 
     def __call__(self):
         _check(lib().lct_group_run(_c.byref(self.desc), _p(self.buf), self.buf.numel(), _stream()))
+
+    def call_noalloc(self):
+        """The same step through ``lct_group_run_noalloc`` (the library's own
+        fixed scratch array instead of this object's workspace)."""
+        _check(lib().lct_group_run_noalloc(_c.byref(self.desc), _stream()))
 
     def layer_index_addresses(self):
         """Device address of the index set each layer read in the last call."""

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "lct.h"
@@ -644,3 +645,47 @@ int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stre
 }
 
 }  // extern "C"
+
+// ------------------------------------------------- no-allocation driver ----
+// Scratch memory of lct_group_run_noalloc: one array per GPU, part of the code
+// object (placed when the library's code is loaded on a device, never by a
+// call) and held until the process ends.  Host code never uses the array's
+// name as an address: the device address comes from hipGetSymbolAddress,
+// once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[LCT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(LCT_ENODEV, "no HIP device is available");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(LCT_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LCT_OK;
+}
+}  // namespace
+
+extern "C" int lct_group_run_noalloc(const lct_group_desc* d, void* stream) {
+  int rc = validate_group(d);
+  if (rc) return rc;
+  const size_t need = group_layout(d).total;
+  if (need > LCT_NOALLOC_SCRATCH_BYTES)
+    return fail(LCT_ENOWORKSPACE,
+                "group_run_noalloc: this step needs %zu bytes of scratch, the built-in array holds %zu "
+                "(use lct_group_run with a workspace)", need, (size_t)LCT_NOALLOC_SCRATCH_BYTES);
+  rc = check_device();
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return lct_group_run(d, ws, LCT_NOALLOC_SCRATCH_BYTES, stream);
+}

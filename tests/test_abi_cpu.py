@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
         "lct_sparse_attn_workspace_bytes", "lct_gsa_attn", "lct_gsa_attn_workspace_bytes",
         "lct_gsa_decode", "lct_gsa_decode_workspace_bytes", "lct_hgsa_decode",
         "lct_hgsa_decode_workspace_bytes", "lct_gsa_prefill", "lct_group_run",
-        "lct_group_workspace_bytes", "lct_prefill_index_i8",
+        "lct_group_workspace_bytes", "lct_group_run_noalloc", "lct_prefill_index_i8",
         "lct_prefill_index_workspace_bytes"]), names
     so = ctypes.CDLL(lct.LIB_PATH)
     for n in names:
@@ -153,6 +153,30 @@ def test_group_validation_and_sizes():
     assert L.lct_group_workspace_bytes(ctypes.byref(free), ctypes.byref(nb)) == 0
     pat[0] = 0
     assert L.lct_group_workspace_bytes(ctypes.byref(free), ctypes.byref(nb)) == lct.LCT_EINVAL
+
+
+def test_group_noalloc_limit():
+    """The no-allocation driver: the header's limit matches the binding's, the
+    decode workloads fit it, and a step that does not fit is refused before
+    any device work."""
+    text = open(HEADER).read()
+    m = re.search(r"#define LCT_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == lct.NOALLOC_SCRATCH_BYTES
+    L = lct.lib()
+    nb = ctypes.c_size_t()
+    P = ctypes.POINTER(ctypes.c_void_p)
+    arr = (ctypes.c_void_p * 28)(*([FAKE.value] * 28))
+    for Lc, B in ((131072, 8), (32768, 8), (1 << 20, 1)):
+        d = _desc(B=B, L=Lc, Hq=32, Hkv=4, topk=2048, n_layers=28)
+        d.qi = d.ki = d.q = d.k = d.v = d.out = ctypes.cast(arr, P)
+        assert L.lct_group_workspace_bytes(ctypes.byref(d), ctypes.byref(nb)) == 0
+        assert nb.value <= lct.NOALLOC_SCRATCH_BYTES, (Lc, B, nb.value)
+    big = _desc(B=1, Lq=65536, L=65536, Hq=32, Hkv=4, topk=2048, n_layers=28, causal=1)
+    big.qi = big.ki = big.q = big.k = big.v = big.out = ctypes.cast(arr, P)
+    assert L.lct_group_workspace_bytes(ctypes.byref(big), ctypes.byref(nb)) == 0
+    assert nb.value > lct.NOALLOC_SCRATCH_BYTES
+    assert L.lct_group_run_noalloc(ctypes.byref(big), None) == lct.LCT_ENOWORKSPACE
+    assert b"scratch" in L.lct_last_error()
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
