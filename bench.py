@@ -7,7 +7,10 @@ int8 indexer (4 heads x 64) with top-2048 and one index per group of 4
 layers (7 indexer calls per step).  One step = the whole hot path for one
 new token per sequence: 7 x (indexer scores + top-k select) + 28 x sparse
 attention, captured in a HIP graph and replayed.  value = tokens/s = B /
-step time.  Inputs are seeded synthetic tensors generated directly in HBM.
+step time (median over the timed replays).  Inputs are seeded synthetic
+tensors generated directly in HBM.  The same line carries the metric's second
+half, ``prefill_indexer``: the causal index of one 64K-token group (int8 TOP/s
+against the int8 MFMA peak).
 
 Prints one JSON line.  Other workloads (``--config``) are for exploration:
 ``decode_32k``, ``decode_1m``, ``gsa_128k`` and ``prefill_64k`` (indexer int8
@@ -85,19 +88,72 @@ def _timed_loop(fn, iters, stream):
     return s.elapsed_time(e) / iters  # ms
 
 
+def _timed_each(fn, iters, stream):
+    """Per-call ms of ``iters`` back-to-back calls of ``fn``: an event on
+    ``stream`` between consecutive calls (no host wait in between), so each
+    interval is one call as the stream runs it.  Returns (median, mean)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record(stream)
+    for i in range(iters):
+        fn()
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+    return t[len(t) // 2], ev[0].elapsed_time(ev[-1]) / iters
+
+
+def _graph_of(fns, stream):
+    """One HIP graph holding the calls ``fns`` in order (each already run once)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
 def _timed_graph(fn, iters, stream):
     """Average ms per call of ``fn`` with ``iters`` calls captured in one HIP
     graph (no host launch overhead); events on the capturing stream."""
     import torch
     fn()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(iters):
-            fn()
-    g.replay()
-    torch.cuda.synchronize()
+    g = _graph_of([fn] * iters, stream)
     return _timed_loop(g.replay, 1, stream) / iters
+
+
+def _rotating_ms(fns, reps, stream):
+    """ms per call when ``fns`` (calls on different data, e.g. the 7 groups'
+    indexer keys) run back to back in one graph, so that each call finds its
+    data cold in the 256 MiB Infinity Cache, as inside a step.  Median over
+    ``reps`` replays of the whole rotation."""
+    import torch
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = _graph_of(fns, stream)
+    med, _ = _timed_each(g.replay, reps, stream)
+    return med / len(fns)
+
+
+def host_info():
+    """CPU model and the number of threads this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
 
 
 def _flush(buf):
@@ -136,57 +192,127 @@ def scorer_traffic():
         return None
 
 
-def cpu_baseline_decode(cfg, budget_s=10.0):
-    """The oracle, as it stands, on one whole decode step of one sequence
-    (b = 0): every group's indexer scores and top-k select and every layer's
-    sparse attention, i.e. one token.  The step is computed again until the
-    oracle's own compute time reaches budget_s; tokens/s = steps / that time.
-    Inputs are generated once, outside the timed calls (regenerating each
-    sequence's 32 MiB of indexer keys per group costs the host far more than
-    the oracle itself).  The oracle is single-threaded numpy (its int64
-    products do not use BLAS; BLAS is pinned to one thread for attention).
-    """
+def _decode_oracle_inputs(cfg, b=0):
+    """Host copies of one sequence's inputs (generated once, outside any timing)."""
+    import concurrent.futures as cf
+
     import numpy as np
-    from threadpoolctl import threadpool_limits
+
+    import synth
+    from synth import configs as C
+
+    with cf.ThreadPoolExecutor(8) as ex:
+        qi = list(ex.map(lambda g: C.rows(cfg, cfg.qi_spec(g), (np.array([b]),)), range(cfg.n_groups)))
+        ki = list(ex.map(lambda g: C.rows(cfg, cfg.ki_spec(g), (np.array([b]),)), range(cfg.n_groups)))
+    q = [synth.as_float(synth.BF16N, C.rows(cfg, cfg.q_spec(l), (np.array(b), np.array(0))))
+         for l in range(cfg.n_layers)]
+    return qi, ki, q
+
+
+def _decode_oracle_step(cfg, qi, ki, q, kv_cache, b=0):
+    """One whole decode step of the oracle for one sequence: every group's
+    indexer scores and top-k select, every layer's sparse attention.  The
+    gathered K/V rows are generated on first use and kept (kv_cache)."""
+    import numpy as np
 
     import oracle
     import synth
     from synth import configs as C
 
-    b = 0
-    qi = [C.rows(cfg, cfg.qi_spec(g), (np.array([b]),)) for g in range(cfg.n_groups)]
-    ki = [C.rows(cfg, cfg.ki_spec(g), (np.array([b]),)) for g in range(cfg.n_groups)]
-    q = [synth.as_float(synth.BF16N, C.rows(cfg, cfg.q_spec(l), (np.array(b), np.array(0))))
-         for l in range(cfg.n_layers)]
-    t_sel = t_att = 0.0
-    steps = 0
+    idx_all = []
+    for g in range(cfg.n_groups):
+        s = oracle.index_scores(qi[g], ki[g], cfg.H_idx)
+        idx_all.append(oracle.select_topk(s[0], cfg.topk, cfg.L))
+    if not kv_cache:
+        for l in range(cfg.n_layers):
+            idx = idx_all[l // cfg.group]
+            sel = idx[0][idx[0] >= 0].astype(np.int64)
+            lead = (np.full_like(sel, b), sel)
+            kv_cache.append((synth.as_float(synth.BF16N, C.rows(cfg, cfg.k_spec(l), lead)),
+                             synth.as_float(synth.BF16N, C.rows(cfg, cfg.v_spec(l), lead))))
+    for l in range(cfg.n_layers):
+        oracle.sparse_attention_gqa(q[l], kv_cache[l][0], kv_cache[l][1], cfg.scale)
+
+
+def cpu_baseline_decode(cfg, budget_s=6.0):
+    """The oracle, as it stands (int64 scores, stable-sort top-k, float64
+    attention), on whole decode steps of one sequence, timed on this host:
+    once on one thread (steps in a row until budget_s), once on every
+    thread this process may use (that many steps at a time in a thread pool,
+    numpy releasing the interpreter lock inside its loops, until budget_s).
+    tokens/s = steps / wall time.  Inputs are generated once, outside the
+    timing (regenerating a sequence's 32 MiB of indexer keys per group costs
+    the host more than the oracle itself)."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+
+    model, nthreads = host_info()
+    qi, ki, q = _decode_oracle_inputs(cfg)
+    kv = []
     with threadpool_limits(limits=1):
-        kv = None
-        while steps == 0 or t_sel + t_att < budget_s:
-            idx_all = []
-            for g in range(cfg.n_groups):
-                t0 = time.perf_counter()
-                s = oracle.index_scores(qi[g], ki[g], cfg.H_idx)
-                idx_all.append(oracle.select_topk(s[0], cfg.topk, cfg.L))
-                t_sel += time.perf_counter() - t0
-            if kv is None:  # the selected K/V rows (the same on every repeat)
-                kv = []
-                for l in range(cfg.n_layers):
-                    idx = idx_all[l // cfg.group]
-                    sel = idx[0][idx[0] >= 0].astype(np.int64)
-                    lead = (np.full_like(sel, b), sel)
-                    kv.append((synth.as_float(synth.BF16N, C.rows(cfg, cfg.k_spec(l), lead)),
-                               synth.as_float(synth.BF16N, C.rows(cfg, cfg.v_spec(l), lead))))
-            for l in range(cfg.n_layers):
-                t0 = time.perf_counter()
-                oracle.sparse_attention_gqa(q[l], kv[l][0], kv[l][1], cfg.scale)
-                t_att += time.perf_counter() - t0
-            steps += 1
-    total = t_sel + t_att
-    return {"value": steps / total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"sequence b=0, one whole decode step ({cfg.n_groups} groups: indexer scores over {cfg.L} "
-                       f"positions + top-{cfg.topk} select; {cfg.n_layers} layers of sparse attention), computed "
-                       f"{steps} times: {t_sel:.1f} s scoring and select, {t_att:.1f} s attention")}
+        _decode_oracle_step(cfg, qi, ki, q, kv)        # gathers the K/V rows once (untimed)
+        steps1, t0 = 0, time.perf_counter()
+        while steps1 == 0 or time.perf_counter() - t0 < budget_s:
+            _decode_oracle_step(cfg, qi, ki, q, kv)
+            steps1 += 1
+        t1 = time.perf_counter() - t0
+        stepsn, t0 = 0, time.perf_counter()
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            while stepsn == 0 or time.perf_counter() - t0 < budget_s:
+                list(ex.map(lambda _: _decode_oracle_step(cfg, qi, ki, q, kv), range(nthreads)))
+                stepsn += nthreads
+        tn = time.perf_counter() - t0
+    return {"value": stepsn / tn, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": model, "one_thread": {"value": steps1 / t1, "unit": "tokens/s", "cores": 1},
+            "sample": (f"sequence b=0, whole decode steps ({cfg.n_groups} groups: int64 indexer scores over "
+                       f"{cfg.L} positions + stable-sort top-{cfg.topk}; {cfg.n_layers} layers of float64 sparse "
+                       f"attention), one token each: {steps1} steps in {t1:.1f} s on 1 thread, {stepsn} steps "
+                       f"in {tn:.1f} s on {nthreads} threads ({nthreads} steps at a time)")}
+
+
+def cpu_baseline_prefill(cfg, n_rows=16, budget_rows=None):
+    """The oracle (int64 scores of a query row against every key, stable-sort
+    top-k with the causal valid length) on a sample of the 64K group's rows,
+    spread over the sequence, on one thread and on every thread; its cost per
+    row does not depend on the row (it scores all L keys), so the group's
+    time is the sample's time x L / n_rows, and the figure is the group's
+    int8 ops (the causal pairs') over that extrapolated time."""
+    import concurrent.futures as cf
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from synth import configs as C
+
+    model, nthreads = host_info()
+    qi = C.rows(cfg, cfg.qi_spec(0), (np.array([0]),))          # [1, L, HD]
+    ki = C.rows(cfg, cfg.ki_spec(0), (np.array([0]),))
+    rows = (np.arange(n_rows) * (cfg.L // n_rows) + cfg.L // (2 * n_rows)).astype(np.int64)
+    ops = 2 * cfg.HD * causal_pairs(cfg.L)
+
+    def block(rs):
+        s = oracle.index_scores(qi[:, rs], ki, cfg.H_idx)[0]
+        return oracle.select_topk(s, cfg.topk, rs + 1)
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for r in rows:
+            block(np.array([r]))
+        t1 = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(lambda r: block(np.array([r])), list(rows) * nthreads))
+        tn = (time.perf_counter() - t0) / nthreads
+    g1, gn = t1 * cfg.L / n_rows, tn * cfg.L / n_rows
+    return {"value": ops / gn / 1e12, "unit": "int8 TOP/s (causal-pair ops of the group / extrapolated time)",
+            "cores": nthreads, "kind": "oracle", "cpu_model": model,
+            "one_thread": {"value": ops / g1 / 1e12, "cores": 1, "s_per_group_extrapolated": g1},
+            "s_per_group_extrapolated": gn,
+            "sample": (f"{n_rows} query rows spread over the {cfg.L} (one every {cfg.L // n_rows}), each scored "
+                       f"against all {cfg.L} keys and selected: {t1:.1f} s on 1 thread, {tn * nthreads:.1f} s for "
+                       f"{nthreads} x the sample on {nthreads} threads; extrapolated x{cfg.L // n_rows} to the group")}
 
 
 # ---------------------------------------------------------------- decode ----
@@ -223,25 +349,27 @@ def bench_decode(cfg, steps, warmup, want_cpu):
     run()
     torch.cuda.synchronize()
 
-    # one step as a HIP graph (42 kernels for 28 layers / 7 groups)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        run()
+    # one step as a HIP graph (84 kernels for 28 layers / 7 groups)
+    g = _graph_of([run], stream)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
     log(f"warmup done ({warmup} steps)")
-    ms = _timed_loop(g.replay, steps, stream)
+    ms, ms_mean = _timed_each(g.replay, steps, stream)
     torch.cuda.synchronize()
 
-    # per-kernel timing of the dominant kernels, standalone launches on this stream
+    # the dominant kernels as they run inside a step: rotations over the 7
+    # groups' indexer keys (1.75 GiB) and the 28 layers' KV caches, so that every
+    # launch reads cold data as in the step (not the warm 256 MiB Infinity Cache)
     bytes_ = decode_step_bytes(cfg)
     scores = torch.empty((cfg.B, cfg.Lq, cfg.L), dtype=torch.int32, device=dev)
-    n_k = max(10, steps)
-    ms_score = _timed_graph(lambda: lct.idx_score(qi[0], ki[0], out=scores), n_k, stream)
+    rot = 7
+    ms_score = _rotating_ms([lambda g=g_: lct.idx_score(qi[g % ng], ki[g % ng], out=scores)
+                             for g_ in range(3 * rot)], max(5, steps // 10), stream)
     ws = lct.Workspace(dev)
-    ms_attn = _timed_graph(lambda: lct.sparse_attn_gather(q[0], k[0], v[0], idx_out[0], cfg.scale,
-                                                          out=out[0], ws=ws), n_k, stream)
+    ms_attn = _rotating_ms([lambda l=l_: lct.sparse_attn_gather(q[l], k[l], v[l], idx_out[l // cfg.group],
+                                                                cfg.scale, out=out[l], ws=ws)
+                            for l_ in range(cfg.n_layers)], max(5, steps // 10), stream)
     torch.cuda.synchronize()
     score_gbs = bytes_["indexer_per_call"] / (ms_score * 1e-3) / 1e9
     attn_gbs = bytes_["kv_per_layer"] / (ms_attn * 1e-3) / 1e9
@@ -250,7 +378,8 @@ def bench_decode(cfg, steps, warmup, want_cpu):
         "metric": "sparse-decode tokens/s + HBM GB/s at 128K ctx; prefill indexer int8 TOPS",
         "value": cfg.B * cfg.Lq / (ms * 1e-3),
         "unit": "tokens/s",
-        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms, "ms_per_step_mean": ms_mean,
+        "timing": f"median of {steps} graph replays of one step, an event between consecutive replays",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded SplitMix64 inputs generated in HBM; random-init, no trained weights)",
         "config": {"workload": cfg.name, "global_batch": cfg.B, "seq_len": cfg.L,
@@ -264,11 +393,14 @@ def bench_decode(cfg, steps, warmup, want_cpu):
                      "achieved": score_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": score_gbs / HBM_PEAK_GBS, "traffic": scorer_traffic(),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "us_per_launch": ms_score * 1e3, "bytes_per_launch": bytes_["indexer_per_call"]},
+                     "us_per_launch": ms_score * 1e3, "bytes_per_launch": bytes_["indexer_per_call"],
+                     "timing": "launches rotating over the 7 groups' keys (cold Infinity Cache), graph-replayed"},
         "attention_kernel": {"kernel": "k_sparse_attn + k_split_merge (one layer)", "achieved": attn_gbs,
                              "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
-                             "us_per_launch": ms_attn * 1e3, "bytes_per_launch": bytes_["kv_per_layer"]},
+                             "us_per_launch": ms_attn * 1e3, "bytes_per_launch": bytes_["kv_per_layer"],
+                             "timing": "launches rotating over the 28 layers' KV caches, graph-replayed"},
     }
+    del g, scores, ws
     if want_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline_decode(cfg)
@@ -378,7 +510,7 @@ def bench_gsa_prefill(cfg, steps, warmup):
 
 # --------------------------------------------------------------- prefill ----
 
-def bench_prefill_indexer(cfg, steps, warmup):
+def bench_prefill_indexer(cfg, steps, warmup, want_cpu=False, attention=True):
     """Causal index of one group at full length: int8 MFMA scores of every
     earlier position, filtered on the fly, exact top-k per row
     (lct_prefill_index_i8).  Throughput over the causal pairs' int8 ops."""
@@ -393,36 +525,40 @@ def bench_prefill_indexer(cfg, steps, warmup):
     out = torch.empty((cfg.L, cfg.topk), dtype=torch.int32, device=dev)
     ws = lct.Workspace(dev)
     stats = {}
-    f = lambda: lct.prefill_index(qi, ki, cfg.topk, out=out, ws=ws, stats=stats)
-    for _ in range(max(warmup, 1)):
-        f()
+    lct.prefill_index(qi, ki, cfg.topk, out=out, ws=ws, stats=stats)      # rows on the whole-row path
     torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        f()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    ms = sorted(times)[len(times) // 2]
-    pairs = cfg.L * (cfg.L + 1) // 2
+    f = lambda: lct.prefill_index(qi, ki, cfg.topk, out=out, ws=ws)
+    stream = torch.cuda.current_stream()
+    g = _graph_of([f], stream)
+    for _ in range(max(warmup, 1)):
+        g.replay()
+    torch.cuda.synchronize()
+    ms, ms_mean = _timed_each(g.replay, steps, stream)
+    pairs = causal_pairs(cfg.L)
     ops = 2 * cfg.HD * pairs
     tops = ops / (ms * 1e-3) / 1e12
-    attn = bench_prefill_attention(cfg, out, steps, warmup)
-    # the whole prefill of the 28-layer stack: one index per group of layers,
-    # sparse attention in every layer
-    step_ms = cfg.n_groups * ms + cfg.n_layers * attn["ms_per_layer"]
-    return {"workload": cfg.name + " indexer (one group, fused score filter + exact top-k)",
-            "ms_per_group": ms, "int8_tops": tops, "rows_on_plain_path": stats.get("n_fallback"),
-            "roofline": {"bound": "mfma", "kernel": "k_pf_filter + k_pf_select (+ short-row block)",
-                         "achieved": tops, "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                         "frac": tops / INT8_PEAK_TOPS, "ops_per_launch": ops,
-                         "us_per_launch": ms * 1e3},
-            "attention": attn,
-            "prefill_ms_all_layers": step_ms,
-            "prefill_tokens_per_s": cfg.L / (step_ms * 1e-3)}
+    res = {"workload": cfg.name + " indexer (one group, fused score filter + exact top-k)",
+           "ms_per_group": ms, "ms_per_group_mean": ms_mean, "int8_tops": tops,
+           "rows_on_plain_path": stats.get("n_fallback"),
+           "timing": f"median of {steps} graph replays of one call, an event between consecutive replays",
+           "roofline": {"bound": "mfma", "kernel": "k_pf_filter + k_pf_select (+ short-row block)",
+                        "achieved": tops, "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                        "frac": tops / INT8_PEAK_TOPS, "ops_per_launch": ops,
+                        "us_per_launch": ms * 1e3}}
+    del g
+    if attention:
+        attn = bench_prefill_attention(cfg, out, max(5, steps // 5), warmup)
+        # the whole prefill of the 28-layer stack: one index per group of layers,
+        # sparse attention in every layer
+        step_ms = cfg.n_groups * ms + cfg.n_layers * attn["ms_per_layer"]
+        res.update({"attention": attn, "prefill_ms_all_layers": step_ms,
+                    "prefill_tokens_per_s": cfg.L / (step_ms * 1e-3)})
+    del qi, ki, out, ws
+    torch.cuda.empty_cache()
+    if want_cpu:
+        log("timing the CPU oracle on sampled prefill rows ...")
+        res["cpu_baseline"] = cpu_baseline_prefill(cfg)
+    return res
 
 
 def bench_prefill_attention(cfg, idx, steps, warmup):
@@ -576,12 +712,14 @@ def step_breakdown(trace_csv, n_steps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_128k",
                     choices=["decode_128k", "decode_32k", "decode_1m", "gsa_128k", "prefill_64k", "tiny",
                              "decode_128k_shared_kv", "hgsa_128k", "gsa_prefill_128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode_128k: leave out the prefill indexer object of the default line")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy used to calibrate HBM byte counters")
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
@@ -615,10 +753,20 @@ def main():
     elif args.config == "gsa_prefill_128k":
         res = bench_gsa_prefill(cfg, args.steps, args.warmup)
     elif args.config == "prefill_64k":
-        res = bench_prefill_indexer(cfg, args.steps, args.warmup)
+        res = bench_prefill_indexer(cfg, args.steps, args.warmup, want_cpu=not args.no_cpu_baseline)
     else:
-        res = bench_decode(cfg, args.steps, args.warmup,
-                           want_cpu=not args.no_cpu_baseline and args.config == "decode_128k")
+        headline = args.config == "decode_128k"
+        res = bench_decode(cfg, args.steps, args.warmup, want_cpu=not args.no_cpu_baseline and headline)
+        if headline and not args.no_prefill:
+            # the metric's second half: the causal prefill indexer at 64K
+            import gc
+
+            import torch
+            gc.collect()
+            torch.cuda.empty_cache()
+            log("prefill indexer, one 64K group ...")
+            res["prefill_indexer"] = bench_prefill_indexer(C.PREFILL_64K, args.steps, args.warmup,
+                                                           want_cpu=not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
 
