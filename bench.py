@@ -595,8 +595,30 @@ def bench_prefill_attention(cfg, idx, steps, warmup):
     sel = sum(min(cfg.topk, r + 1) for r in range(cfg.L))
     flops = 4.0 * cfg.Hq * cfg.D * sel
     gathered = sel * cfg.Hkv * cfg.D * 2 * 2
-    del q, k, v, out, ws
-    return {"kernel": "k_seg_bounds + k_sparse_attn_seg + k_seg_merge", "ms_per_layer": ms,
+    # the same layer when neighbouring queries share their sets: every row of
+    # a 16-row block reuses the set its first row selected (valid for every
+    # row of the block: those positions precede the block)
+    ix_sh = ix[:, ::16].repeat_interleave(16, dim=1)[:, : cfg.L].contiguous()
+    f2 = lambda: lct.sparse_attn_gather(q, k, v, ix_sh, cfg.scale, out=out, ws=ws)
+    f2()
+    torch.cuda.synchronize()
+    t2 = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        f2()
+        e1.record()
+        torch.cuda.synchronize()
+        t2.append(e0.elapsed_time(e1))
+    ms2 = sorted(t2)[len(t2) // 2]
+    sel2 = int((ix_sh >= 0).sum().item())
+    del q, k, v, out, ws, ix_sh
+    return {"kernel": "k_seg_bounds + k_union_plan + k_union_attn + k_sparse_attn_seg + k_seg_merge",
+            "ms_per_layer": ms,
+            "shared_sets_ms_per_layer": ms2,
+            "shared_sets_bf16_tflops": 4.0 * cfg.Hq * cfg.D * sel2 / (ms2 * 1e-3) / 1e12,
+            "shared_sets_note": "every row of a 16-row block attends over its first row's set: the block-union path",
             "bf16_tflops": flops / (ms * 1e-3) / 1e12, "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "gathered_gb_per_s": gathered / (ms * 1e-3) / 1e9,
             "note": "selected K/V rows are re-read by many rows: the gathers run from L2/MALL, "

@@ -43,6 +43,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 #define ATT_SEG_SHIFT 14                 // log2 positions per segment (segmented path)
 #endif
 constexpr int ATT_SEG_MAX = 64;          // segments per row at most (the segment grows)
+constexpr int UA_R = 16;                 // rows per block of the block-union path
 constexpr int64_t ATT_SEG_MIN_UNITS = 16384;  // (row, KV head) pairs that take the segmented path
 
 typedef __attribute__((address_space(3))) short4v lds_short4v;
@@ -67,6 +68,7 @@ AttnPlan attn_plan(int B, int Lq, int Hq, int Hkv, int kk, int64_t L) {
   p.nseg = 0;
   p.seg_shift = 0;
   p.bnd_bytes = 0;
+  p.ua_blocks = 0;
   // many rows over a long cache: position segments (see k_sparse_attn_seg)
   if (units >= ATT_SEG_MIN_UNITS && L > ((int64_t)2 << ATT_SEG_SHIFT)) {
     int shift = ATT_SEG_SHIFT;
@@ -77,6 +79,8 @@ AttnPlan attn_plan(int B, int Lq, int Hq, int Hkv, int kk, int64_t L) {
     p.per_split = kk;
     p.part_bytes = (size_t)units * p.nseg * G * ATT_PS * sizeof(float);
     p.bnd_bytes = (size_t)rows * (p.nseg + 1) * sizeof(int32_t);
+    // blocks of UA_R rows that may take the block-union path (one flag each)
+    p.ua_blocks = (G == 4 || G == 8 || G == 16) ? rows / UA_R : 0;
     return p;
   }
   const int64_t pieces = (kk + 31) / 32;  // 32-position pieces of an index row
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn_seg(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ bnd, float* __restrict__ out, float* __restrict__ part,
     int64_t rows, int64_t groups, int Lq, int Hq, int Hkv, int64_t L, int kk, float scale_log2,
-    int nseg) {
+    int nseg, const int32_t* __restrict__ uflag, int64_t nblk) {
   constexpr int D = ATT_D;
   __shared__ __attribute__((aligned(16))) char vta[ATT_NW][2][4][1024];
   __shared__ __attribute__((aligned(16))) char vtb[ATT_NW][2][4][1024];
@@ -593,6 +597,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn_seg(
   const int seg = (int)(t / groups);
   const int64_t br = (t % groups) * ATT_NW + wid;  // b * Lq + r
   if (br >= rows) return;  // the whole wave; nothing below waits on other waves
+  if (uflag && br / UA_R < nblk && uflag[br / UA_R]) return;  // a union block's row
   const int32_t* bb = bnd + br * (nseg + 1);
   const int e_begin = bb[seg], e_end = bb[seg + 1], n = bb[nseg];
   const bool whole = e_end - e_begin == n;  // the row's only non-empty segment
@@ -636,10 +641,12 @@ template <int G>
 __global__ __launch_bounds__(256) void k_seg_merge(const float* __restrict__ part,
                                                    const int32_t* __restrict__ bnd,
                                                    float* __restrict__ out, int Hq, int Hkv,
-                                                   int nseg) {
+                                                   int nseg, const int32_t* __restrict__ uflag,
+                                                   int64_t nblk) {
   constexpr int D = ATT_D;
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int64_t br = blockIdx.x;
+  if (uflag && br / UA_R < nblk && uflag[br / UA_R]) return;  // written by the union path
   const int32_t* bb = bnd + br * (nseg + 1);
   const int n = bb[nseg];
   const int cnt = lane < nseg ? bb[lane + 1] - bb[lane] : 0;
@@ -669,6 +676,432 @@ __global__ __launch_bounds__(256) void k_seg_merge(const float* __restrict__ par
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block-union path for rows whose index sets overlap (neighbouring queries of
+// a causal prefill).  The per-row paths read every (row, selected position)
+// pair's K and V through the address unit; when the sets of neighbouring
+// rows overlap, a block of UA_R consecutive rows can instead gather the union
+// of their sets once into LDS and attend with a membership mask (a key of the
+// union counts for a row only if that row selected it), so each shared
+// position is fetched once per block instead of once per row, at the price of
+// MFMA work on the union for every row of the block.  k_union_plan decides per
+// block from the union's size; k_union_attn does the union blocks; the
+// segment path skips their rows.
+constexpr int UA_WIN = 4096;  // positions per membership window
+constexpr int UA_CH = 64;     // union positions per chunk
+// Union mode when the block's rows select each union position UA_SHARE x G / 8
+// times on average (sum of n_r >= that x |U|).  A union chunk costs its
+// workgroup G waves of MFMA and softmax work whoever selected its positions,
+// while the per-row path pays per (row, position) pair at the address unit:
+// measured on the 64K causal prefill, about 5 pairs per union position at 8
+// heads per KV head break even.
+#ifndef UA_SHARE
+#define UA_SHARE 6
+#endif
+
+// Workgroup barrier that drains LDS operations but not the vector memory
+// counter (a __syncthreads() would also wait for the LDS DMA in flight).
+LCT_DEV void ua_barrier() {
+  __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// One workgroup (256 threads) per block of UA_R rows: flag[block] = 1 if its
+// rows lie in one batch entry, each is ascending over its valid entries (in
+// [0, L)) followed only by -1, and the rows share its positions enough
+// (UA_SHARE).
+__global__ __launch_bounds__(256) void k_union_plan(const int32_t* __restrict__ idx, int64_t rows, int Lq,
+                                                    int kk, int64_t L, int G, int32_t* __restrict__ flag) {
+  __shared__ uint32_t bm[1024];  // one 32768-position window
+  __shared__ int32_t s_n[UA_R];
+  __shared__ uint32_t s_bad, s_u;
+  const int64_t blk = blockIdx.x;
+  const int64_t r0 = blk * UA_R;
+  const int rr = threadIdx.x >> 4, t = threadIdx.x & 15;
+  if (threadIdx.x == 0) {
+    s_bad = (r0 + UA_R > rows || r0 / Lq != (r0 + UA_R - 1) / Lq) ? 1u : 0u;
+    s_u = 0u;
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (threadIdx.x == 0) flag[blk] = 0;
+    return;
+  }
+  const int32_t* ix = idx + (r0 + rr) * kk;
+  bool bad = false;
+  int n = 0, pmax = -1;
+  for (int e = t; e < kk; e += 16) {
+    const int p = ix[e];
+    const int prv = e > 0 ? ix[e - 1] : -2;
+    bool ok;
+    if (prv == -2) ok = p == -1 || (p >= 0 && (int64_t)p < L);
+    else if (prv == -1) ok = p == -1;
+    else ok = p == -1 || (p > prv && (int64_t)p < L);
+    bad = bad || !ok;
+    n += p >= 0 ? 1 : 0;
+    pmax = max(pmax, p);
+  }
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) {
+    n += __shfl_xor(n, d, 64);
+    pmax = max(pmax, __shfl_xor(pmax, d, 64));
+    bad = bad || __shfl_xor((int)bad, d, 64);
+  }
+  if (t == 0) {
+    s_n[rr] = n;
+    if (bad) atomicOr(&s_bad, 1u);
+  }
+  __shared__ int32_t s_pmax;
+  if (threadIdx.x == 0) s_pmax = -1;
+  __syncthreads();
+  if (t == 0) atomicMax(&s_pmax, pmax);
+  __syncthreads();
+  if (s_bad) {
+    if (threadIdx.x == 0) flag[blk] = 0;
+    return;
+  }
+  const int nr = s_n[rr];
+  for (int w0 = 0; w0 <= s_pmax; w0 += 32768) {
+    for (int i = threadIdx.x; i < 1024; i += 256) bm[i] = 0u;
+    __syncthreads();
+    for (int e = t; e < nr; e += 16) {
+      const int p = ix[e] - w0;
+      if (p >= 0 && p < 32768) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+    uint32_t c = 0;
+    for (int i = threadIdx.x; i < 1024; i += 256) c += __popc(bm[i]);
+    c = wave_sum(c);
+    if ((threadIdx.x & 63) == 0) atomicAdd(&s_u, c);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int64_t sum_n = 0;
+    for (int r = 0; r < UA_R; ++r) sum_n += s_n[r];
+    flag[blk] = (sum_n > 0 && (int64_t)s_u * UA_SHARE * G <= sum_n * 8) ? 1 : 0;
+  }
+}
+
+// P^T V^T product of one half (two 16-token blocks) of a landed V tile.
+LCT_DEV void ua_pv_half(const char (&vh)[2][4][1024], const AttnLanes& a, const __bf16 (&pw)[4][4], int h,
+                        floatx4 (&o)[ATT_D / 16], floatx4& lacc) {
+  constexpr int D = ATT_D;
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+  // the 16 transposed reads in one asm block with their wait: the compiler
+  // cannot tell these LDS reads from the next chunk's DMA into the other
+  // buffer set and would otherwise drain that DMA first (the chunk's own DMA
+  // was waited for before the barrier that precedes this)
+  short4v r[16];
+  const uint32_t b0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&vh[0][0][a.tr0];
+  const uint32_t b1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&vh[0][0][a.tr1];
+  __asm__ volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %2, %17 offset:0\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %5, %16 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %6, %17 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %7, %17 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %10, %17 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %13, %16 offset:7168\n\t"
+      "ds_read_b64_tr_b16 %14, %17 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %15, %17 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
+        "=&v"(r[14]), "=&v"(r[15])
+      : "v"(b0), "v"(b1)
+      : "memory");
+  static_assert(sizeof(vh[0]) == 4096 && sizeof(vh[0][0]) == 1024, "offsets above: block 4096, slice 1024");
+  bf16x8 vv[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    vv[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[2 * dt], r[2 * dt + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+  bf16x8 pf;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pf[e] = pw[2 * h][e];
+    pf[4 + e] = pw[2 * h + 1][e];
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[dt], pf, o[dt], 0, 0, 0);
+  lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc, 0, 0, 0);
+}
+
+// Online-softmax attention of one wave's 16 columns over one landed chunk of
+// 64 union positions (base: the chunk's first union slot): S^T = K Q^T from
+// the swizzled K tile, the membership mask of each column's row, weights,
+// O^T += V^T P^T.
+LCT_DEV void ua_chunk(int base, const char (&kt)[UA_CH * 256], const char (&va)[2][4][1024],
+                      const char (&vb)[2][4][1024], const uint16_t* umask, const AttnLanes& a,
+                      const bf16x8 (&qf)[4], int rbit, float scale_log2, float& m, floatx4& lacc,
+                      floatx4 (&o)[ATT_D / 16]) {
+  constexpr int D = ATT_D;
+  const int hl = a.hl, kg = a.kg;
+  floatx4 sacc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int tok = 16 * j + hl;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kt[tok * 256 + (((st * 4 + kg) ^ hl) << 4)]);
+      sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[st], sacc[j], 0, 0, 0);
+    }
+  }
+  // membership of this lane's tokens 16j + 4kg + e for its column's row
+  uint32_t mk[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t0 = base + 16 * j + 4 * kg;
+    const uint2 w2 = *reinterpret_cast<const uint2*>(&umask[t0]);  // 4 masks (padding: 0)
+    const uint32_t ms[4] = {w2.x & 0xFFFFu, w2.x >> 16, w2.y & 0xFFFFu, w2.y >> 16};
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bits |= ((ms[e] >> rbit) & 1u) << (4 * e);
+    mk[j] = bits;
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, ((mk[j] >> (4 * e)) & 1) ? sacc[j][e] : -INFINITY);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  const float mnew = fmaxf(m, tmax * scale_log2);
+  const float mref = mnew == -INFINITY ? 0.f : mnew;
+  const float alpha = __builtin_amdgcn_exp2f(m - mref);
+  m = mnew;
+  __bf16 pw[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float w = __builtin_amdgcn_exp2f(fmaf(sacc[j][e], scale_log2, -mref));
+      pw[j][e] = (__bf16)(((mk[j] >> (4 * e)) & 1) ? w : 0.f);
+    }
+  if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
+    lacc = lacc * alpha;
+  }
+  ua_pv_half(va, a, pw, 0, o, lacc);
+  ua_pv_half(vb, a, pw, 1, o, lacc);
+}
+
+// Union attention of one (block, KV head) in union mode; G waves, wave w
+// takes rows w*(16/G) .. (w+1)*(16/G) - 1 of the block with their G heads as
+// its 16 MFMA columns (column c: row c / G, head c % G).  Per window of
+// UA_WIN positions: each row's entries in the window (a contiguous run of its
+// ascending list, from a cursor) set its membership bits; the union of the
+// rows is compacted to positions + 16-bit row masks; chunks of 64 union
+// positions are gathered into LDS (two buffers: the next chunk's DMA overlaps
+// this chunk's MFMA work) and attended by every wave with its rows' masks.
+// K is stored 16-byte-chunk swizzled (chunk s of token t at s ^ (t % 16)), so
+// the A-operand reads (16 tokens of one chunk) fall on distinct banks; V uses
+// the layout of the per-row path for the transposed reads.
+template <int G>
+__global__ __launch_bounds__(G * 64) void k_union_attn(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ flag, float* __restrict__ out, int Lq,
+    int Hq, int Hkv, int64_t L, int kk, float scale_log2) {
+  constexpr int D = ATT_D;
+  constexpr int NT = G * 64;
+  constexpr int RW = UA_R / G;  // rows per wave
+  static_assert(G >= 4 && G <= 16 && UA_R % G == 0, "union path for 4 to 16 heads per KV head");
+  __shared__ uint32_t mem[UA_R][UA_WIN / 32];
+  __shared__ int32_t upos[UA_WIN];
+  __shared__ __attribute__((aligned(8))) uint16_t umask[UA_WIN];
+  __shared__ __attribute__((aligned(16))) char kt0[UA_CH * 256];
+  __shared__ __attribute__((aligned(16))) char kt1[UA_CH * 256];
+  __shared__ __attribute__((aligned(16))) char va0[2][4][1024];
+  __shared__ __attribute__((aligned(16))) char vb0[2][4][1024];
+  __shared__ __attribute__((aligned(16))) char va1[2][4][1024];
+  __shared__ __attribute__((aligned(16))) char vb1[2][4][1024];
+  __shared__ int32_t cur[UA_R], nrow[UA_R];
+  __shared__ uint32_t scan[NT / 64 + 2];
+  const int64_t blk = blockIdx.x / Hkv;
+  const int kvh = (int)(blockIdx.x % Hkv);
+  if (flag[blk] == 0) return;  // uniform: the segment path takes this block
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int64_t r0 = blk * UA_R;
+  const int64_t b = r0 / Lq;
+  const int hl = lane & 15, kg = lane >> 4;
+  const AttnLanes a = attn_lanes(lane);
+  // this wave's columns: row r0 + wid*RW + hl / G, head kvh*G + hl % G
+  const int rbit = wid * RW + hl / G;
+  bf16x8 qf[4];
+  {
+    const int64_t row = r0 + rbit;
+    const uint16_t* qp = q + ((row * Hq) + kvh * G + hl % G) * D + kg * 8;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qp + st * 32);
+  }
+  // row lengths (valid entries: ascending, then -1) and cursors
+  if (threadIdx.x < UA_R) {
+    const int32_t* ix = idx + (r0 + threadIdx.x) * kk;
+    int lo = 0, hi = kk;  // first -1 by bisection (the row is ascending, then -1)
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (ix[mid] >= 0) lo = mid + 1;
+      else hi = mid;
+    }
+    nrow[threadIdx.x] = lo;
+    cur[threadIdx.x] = 0;
+  }
+  __syncthreads();
+  int plast = -1;
+  for (int r = 0; r < UA_R; ++r)
+    if (nrow[r] > 0) plast = max(plast, idx[(r0 + r) * kk + nrow[r] - 1]);
+  const int row_bytes = Hkv * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (size_t)b * L * Hkv * D + kvh * D, L * (int64_t)row_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (size_t)b * L * Hkv * D + kvh * D, L * (int64_t)row_bytes);
+  float m = -INFINITY;
+  floatx4 lacc = floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // DMA of chunk c (union positions c*64 ..) into buffer set (kt, va, vb):
+  // 16 K and 16 V instructions per chunk, 32 / G per wave (i = wid + ii * G)
+  auto issue = [&](int c, int nu, char* kt, char (*va)[4][1024], char (*vb)[4][1024]) {
+    const int base = c * UA_CH;
+#pragma unroll
+    for (int ii = 0; ii < 32 / G; ++ii) {
+      const int i = wid + ii * G;
+      if (i < 16) {
+        const int tok = 4 * i + (lane >> 4), s = lane & 15;
+        const int up = base + tok < nu ? base + tok : base;
+        const int roff = upos[up] * row_bytes + ((s ^ (tok & 15)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kt + i * 1024), 16, roff, 0, 0, 0);
+      } else {
+        const int j = (i - 16) >> 2, st = (i - 16) & 3;
+        const int tok = 16 * j + a.tk;
+        const int up = base + tok < nu ? base + tok : base;
+        const int roff = upos[up] * row_bytes + st * 64 + a.cv * 16;
+        char* dst = j < 2 ? &va[j][st][0] : &vb[j - 2][st][0];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)dst, 16, roff, 0, 0, 0);
+      }
+    }
+  };
+  constexpr int NDMA = 32 / G;  // DMA instructions per wave and chunk
+
+  auto compute = [&](int c, const char (&kt)[UA_CH * 256], const char (&va)[2][4][1024],
+                     const char (&vb)[2][4][1024]) {
+    ua_chunk(c * UA_CH, kt, va, vb, umask, a, qf, rbit, scale_log2, m, lacc, o);
+  };
+
+  constexpr int RT = NT / UA_R;  // threads per row in the membership pass
+  constexpr int BPT = UA_WIN / NT;  // union bits per thread
+  for (int p0 = 0; p0 <= plast; p0 += UA_WIN) {
+    // ---- membership of the window
+    for (int i = threadIdx.x; i < UA_R * (UA_WIN / 32); i += NT) (&mem[0][0])[i] = 0u;
+    __syncthreads();
+    {
+      const int rr = threadIdx.x / RT, t = threadIdx.x % RT;
+      const int32_t* ix = idx + (r0 + rr) * kk;
+      const int n = nrow[rr];
+      int c0 = cur[rr];
+      int taken = 0;
+      bool more = true;
+      while (more) {
+        const int e = c0 + t;
+        const int p = e < n ? ix[e] : INT32_MAX;
+        const bool in = p < p0 + UA_WIN;
+        if (in) atomicOr(&mem[rr][(p - p0) >> 5], 1u << ((p - p0) & 31));
+        // entries are ascending: the run in the window is a prefix
+        const uint64_t bl = __ballot(in);
+        const uint64_t gm = RT >= 64 ? ~0ull : (((1ull << RT) - 1ull) << ((threadIdx.x & 63) / RT * RT));
+        const uint32_t cnt = (uint32_t)__popcll(bl & gm);
+        taken += (int)cnt;
+        more = cnt == (uint32_t)RT;
+        c0 += RT;
+      }
+      __syncthreads();
+      if (t == 0) cur[rr] += taken;
+    }
+    __syncthreads();
+    // ---- union of the window: positions and row masks, ascending
+    uint32_t cnt = 0;
+    const int bit0 = (int)threadIdx.x * BPT;
+    uint32_t ubits = 0;  // BPT <= 32 bits of this thread
+    {
+      const int wd = bit0 >> 5, sh = bit0 & 31;
+      uint32_t u = 0;
+#pragma unroll
+      for (int r = 0; r < UA_R; ++r) u |= mem[r][wd];
+      ubits = BPT >= 32 ? u : (u >> sh) & ((1u << BPT) - 1u);
+      cnt = __popc(ubits);
+    }
+    uint32_t nu;
+    const uint32_t off = block_excl_scan<NT>(cnt, scan, nu);
+    {
+      const int wd = bit0 >> 5, sh = bit0 & 31;
+      uint32_t rw[UA_R];
+#pragma unroll
+      for (int r = 0; r < UA_R; ++r) rw[r] = mem[r][wd] >> sh;
+      uint32_t o2 = off, x = ubits;
+      while (x) {
+        const int bbit = __ffs(x) - 1;
+        x &= x - 1;
+        uint32_t msk = 0;
+#pragma unroll
+        for (int r = 0; r < UA_R; ++r) msk |= ((rw[r] >> bbit) & 1u) << r;
+        upos[o2] = p0 + bit0 + bbit;
+        umask[o2] = (uint16_t)msk;
+        ++o2;
+      }
+    }
+    // padding of the last chunk: no row takes it
+    const int nch = ((int)nu + UA_CH - 1) / UA_CH;
+    for (int i = (int)nu + (int)threadIdx.x; i < nch * UA_CH; i += NT) umask[i] = 0;
+    __syncthreads();
+    if (nu == 0) continue;
+    // ---- chunks, two buffer sets; DMA of chunk c + 1 overlaps chunk c.
+    // Plain barriers (ua_barrier): each wave waits for its own DMA with an
+    // explicit count, so the barrier need not drain the DMA in flight.
+    __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+    issue(0, (int)nu, kt0, va0, vb0);
+    for (int c = 0; c < nch; c += 2) {
+      if (c + 1 < nch) {
+        issue(c + 1, (int)nu, kt1, va1, vb1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
+      } else {
+        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+      }
+      ua_barrier();
+      compute(c, kt0, va0, vb0);
+      ua_barrier();  // buffer set 0 is free
+      if (c + 1 >= nch) break;
+      if (c + 2 < nch) {
+        issue(c + 2, (int)nu, kt0, va0, vb0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
+      } else {
+        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+      }
+      ua_barrier();
+      compute(c + 1, kt1, va1, vb1);
+      ua_barrier();  // buffer set 1 is free
+    }
+    __syncthreads();
+  }
+  // o[dt][e] = O^T[d = 16dt + 4kg + e][column hl]; every row of lacc holds
+  // the column's denominator
+  const float inv = lacc[0] > 0.f ? 1.f / lacc[0] : 0.f;
+  const int64_t row = r0 + rbit;
+  float* op = out + ((row * Hq) + kvh * G + hl % G) * D + kg * 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(op + dt * 16) = o[dt] * inv;
+}
+
 static hipError_t launch_sparse_attn_seg(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                          const int32_t* idx, float* out, int B, int Lq, int Hq,
                                          int Hkv, int64_t L, int kk, float sl2, const AttnPlan& plan,
@@ -678,15 +1111,28 @@ static hipError_t launch_sparse_attn_seg(const uint16_t* q, const uint16_t* k, c
   const int64_t groups = (rows + ATT_NW - 1) / ATT_NW;
   float* part = ws;
   int32_t* bnd = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + attn_bnd_offset(plan));
+  int32_t* uflag = plan.ua_blocks > 0 ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + attn_ua_offset(plan))
+                                      : nullptr;
+  const int64_t nblk = plan.ua_blocks;
   k_seg_bounds<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(idx, bnd, rows, kk, L, plan.seg_shift,
                                                                   plan.nseg);
+  if (nblk > 0) {
+    k_union_plan<<<dim3((unsigned)nblk), 256, 0, st>>>(idx, rows, Lq, kk, L, G, uflag);
+    const dim3 ug((unsigned)(nblk * Hkv));
+    switch (G) {
+      case 4: k_union_attn<4><<<ug, 4 * 64, 0, st>>>(q, k, v, idx, uflag, out, Lq, Hq, Hkv, L, kk, sl2); break;
+      case 8: k_union_attn<8><<<ug, 8 * 64, 0, st>>>(q, k, v, idx, uflag, out, Lq, Hq, Hkv, L, kk, sl2); break;
+      case 16: k_union_attn<16><<<ug, 16 * 64, 0, st>>>(q, k, v, idx, uflag, out, Lq, Hq, Hkv, L, kk, sl2); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   const int64_t wgs = (int64_t)plan.nseg * groups * Hkv;
   if (wgs >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
 #define LCT_ATT(GG)                                                                                \
   k_sparse_attn_seg<GG><<<dim3((unsigned)wgs), ATT_NW * 64, 0, st>>>(q, k, v, idx, bnd, out, part, rows, \
                                                                      groups, Lq, Hq, Hkv, L, kk, sl2,  \
-                                                                     plan.nseg);                       \
-  k_seg_merge<GG><<<dim3((unsigned)rows), 256, 0, st>>>(part, bnd, out, Hq, Hkv, plan.nseg)
+                                                                     plan.nseg, uflag, nblk);          \
+  k_seg_merge<GG><<<dim3((unsigned)rows), 256, 0, st>>>(part, bnd, out, Hq, Hkv, plan.nseg, uflag, nblk)
   switch (G) {
     case 1: LCT_ATT(1); break;
     case 2: LCT_ATT(2); break;

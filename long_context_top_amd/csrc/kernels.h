@@ -85,11 +85,16 @@ struct AttnPlan {
   int nseg;         // > 0: segmented path with nseg position segments of 2^seg_shift
   int seg_shift;
   size_t bnd_bytes;  // segmented path: per-row segment bounds after the partials
+  int64_t ua_blocks;  // segmented path: row blocks that may take the block-union path
+                      // (an int32 flag each, after the bounds)
 };
 AttnPlan attn_plan(int B, int Lq, int Hq, int Hkv, int kk, int64_t L);
 inline size_t attn_bnd_offset(const AttnPlan& p) { return (p.part_bytes + 255) / 256 * 256; }
+inline size_t attn_ua_offset(const AttnPlan& p) { return (attn_bnd_offset(p) + p.bnd_bytes + 255) / 256 * 256; }
 inline size_t attn_ws_bytes(const AttnPlan& p) {
-  return p.nseg > 0 ? attn_bnd_offset(p) + p.bnd_bytes : p.part_bytes;
+  if (p.nseg == 0) return p.part_bytes;
+  return p.ua_blocks > 0 ? attn_ua_offset(p) + (size_t)p.ua_blocks * sizeof(int32_t)
+                         : attn_bnd_offset(p) + p.bnd_bytes;
 }
 // With plan.splits > 1 the kernel writes (O, m, l) partials and a merge
 // kernel combines them (log-sum-exp merge).

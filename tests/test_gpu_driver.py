@@ -185,8 +185,17 @@ def test_causal_prefill_segmented_attention():
                          Hkv=4, D=128, H_idx=4, d_idx=64, topk=512, causal=True)
     announce(cfg.name)
     idx, out, _ = _run(cfg)
-    sample = [0, 1, 511, 512, 4095, 4096, 16383, 16384, 16385, 25000, 32767, 32768, 32999]
-    want = oracle.prefill_index_rows(cfg, 0, sample)
+    # rows below k keep every earlier position (nested prefixes: the block-union
+    # path); all of them and every row below 2048, then a spread
+    sample = np.array(list(range(0, 2048)) + [4095, 4096, 16383, 16384, 16385, 25000, 32767, 32768, 32999])
+    # index sets: the exact float32-product scorer and partition select (both
+    # pinned on the CPU against the int64 / sort definitions), then the
+    # definition itself on a few rows
+    qh = C.rows(cfg, cfg.qi_spec(0), (np.zeros_like(sample), sample))
+    kh = C.rows(cfg, cfg.ki_spec(0), (np.array([0]),))[0]
+    want = oracle.select_topk_threshold(oracle.index_scores_f32(qh, kh), cfg.topk, sample + 1)
+    few = [0, 511, 512, 2047, 32999]
+    assert np.array_equal(want[[0, 511, 512, 2047, len(sample) - 1]], oracle.prefill_index_rows(cfg, 0, few))
     assert np.array_equal(idx[0][0][sample], want)
     ref = oracle.prefill_attention_rows(cfg, 0, sample, want)
     assert np.abs(out[0][0, sample] - ref).max() < ATOL

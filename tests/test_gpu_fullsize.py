@@ -193,7 +193,9 @@ def test_causal_prefill_64k_full_size():
     want = oracle.prefill_index_rows(cfg, 0, rows)
     for j, r in enumerate(rows):
         assert np.array_equal(idx[r], want[j]), r
-    sample = [0, 5, 2047, 2048, 33333, 65535]
+    # every row below 2048 (nested prefixes and fast-growing overlaps: the
+    # block-union path) and a spread of long rows
+    sample = list(range(0, 2048)) + [2048, 4097, 33333, 65535]
     ref = oracle.prefill_attention_rows(cfg, 2, sample, idx[sample])
     assert np.abs(host(out[2])[0, sample] - ref).max() < ATOL
     del qi, ki, q, k, v, out, idx_out, run

@@ -312,6 +312,85 @@ def _gsa_inputs(cfg, gist_vals=None):
 
 
 @pytest.mark.parametrize("tail", [0, 1, 7, 15, 16])
+def _union_flags(ws, B, Lq, Hq, Hkv, L, kk):
+    """The block-union decisions the last call left in its workspace (int32
+    per block of 16 rows, after the segment partials and bounds)."""
+    G = Hq // Hkv
+    shift = 14
+    while ((L - 1) >> shift) + 1 > 64:
+        shift += 1
+    nseg = ((L - 1) >> shift) + 1
+    rows = B * Lq
+    up = lambda x: (x + 255) // 256 * 256
+    part = rows * Hkv * nseg * G * 132 * 4
+    off = up(up(part) + rows * (nseg + 1) * 4)
+    n = rows // 16
+    return ws.buf[off:off + 4 * n].view(torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 4), (16, 4)])
+def test_sparse_attn_block_union_path(Hq, Hkv):
+    """Many rows over a long cache whose neighbours share positions: blocks
+    of 16 rows with one common set, with nested prefix sets (the causal
+    prefill's short rows), with half-shared sets, take the block-union path
+    (checked in the decisions the call leaves in its workspace); blocks of
+    independent random sets, with a row that is not ascending, or with an
+    empty row among shared ones, are decided per block.  Every row is
+    compared with the oracle."""
+    B, Lq, L, kk = 1, 4096, 40000, 256        # 16384 (row, KV head) pairs: the segment path
+    announce(f"attn block union Hq={Hq} Hkv={Hkv} Lq={Lq} L={L} kk={kk}")
+    r = _rng(Hq)
+    q, qh = dev_bf16(r.standard_normal((B, Lq, Hq, 128)))
+    k, kh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    v, vh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    idx = np.full((B, Lq, kk), -1, dtype=np.int32)
+    kinds = []
+    for blk in range(Lq // 16):
+        kind = blk % 6
+        kinds.append(kind)
+        common = np.sort(r.choice(L, size=kk, replace=False))
+        for i in range(16):
+            j = blk * 16 + i
+            if kind == 0:                       # one common set
+                sel = common
+            elif kind == 1:                     # nested prefixes 0..m
+                m = (blk * 7 + i * 13) % kk + 1
+                sel = np.arange(m)
+            elif kind == 2:                     # half shared, half own
+                own = r.choice(L, size=kk // 2, replace=False)
+                sel = np.unique(np.concatenate([common[: kk // 2], own]))[:kk]
+            elif kind == 3:                     # independent random sets
+                sel = np.sort(r.choice(L, size=kk - (i % 3), replace=False))
+            elif kind == 4:                     # common set, one row not ascending
+                sel = common.copy()
+                if i == 5:
+                    sel = sel[::-1].copy()
+            else:                               # common set, one empty row, one short row
+                sel = common if i not in (3, 9) else (np.zeros(0, np.int64) if i == 3 else common[:17])
+            idx[0, j, :sel.size] = sel
+    scale = 1.0 / math.sqrt(128)
+    ws = lct.Workspace()
+    got = host(lct.sparse_attn_gather(q, k, v, dev_i32(idx), scale, ws=ws))
+    flags = _union_flags(ws, B, Lq, Hq, Hkv, L, kk)
+    kinds = np.array(kinds)
+    assert np.all(flags[kinds == 0] == 1) and np.all(flags[kinds == 1] == 1) and np.all(flags[kinds == 5] == 1)
+    assert np.all(flags[kinds == 4] == 0)          # a row that is not ascending
+    if Hq // Hkv == 8:  # independent sets: twice the per-row MFMA columns at least
+        assert np.all(flags[kinds == 3] == 0)
+    print(f"  union blocks: {int(flags.sum())} of {flags.size}", flush=True)
+    worst = 0.0
+    for j in range(Lq):
+        sel = idx[0, j][idx[0, j] >= 0]
+        if sel.size == 0:
+            assert np.all(got[0, j] == 0.0), j
+            continue
+        want = oracle.sparse_attention_gqa(qh[0, j], kh[0, sel], vh[0, sel], scale)
+        err = np.abs(got[0, j] - want).max()
+        worst = max(worst, err)
+        assert err < ATOL, (j, kinds[j // 16], err)
+    print(f"  max |out - oracle| = {worst:.2e}", flush=True)
+
+
 def test_gist_score_and_gsa_decode(tail):
     from synth import configs as C
     from tests.gpu_util import dev_bf16_bits
