@@ -311,7 +311,6 @@ def _gsa_inputs(cfg, gist_vals=None):
                 rv=C.make(cfg, cfg.rv_spec()))
 
 
-@pytest.mark.parametrize("tail", [0, 1, 7, 15, 16])
 def _union_flags(ws, B, Lq, Hq, Hkv, L, kk):
     """The block-union decisions the last call left in its workspace (int32
     per block of 16 rows, after the segment partials and bounds)."""
@@ -391,6 +390,7 @@ def test_sparse_attn_block_union_path(Hq, Hkv):
     print(f"  max |out - oracle| = {worst:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("tail", [0, 1, 7, 15, 16])
 def test_gist_score_and_gsa_decode(tail):
     from synth import configs as C
     from tests.gpu_util import dev_bf16_bits
