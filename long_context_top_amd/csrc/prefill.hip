@@ -66,8 +66,7 @@ constexpr int PF_NT = (PF_CW + 2) * 64;
 constexpr int PF_CHUNKS = (PF_TK / 16) * PF_KS;  // 1 KiB fragments per key tile
 constexpr int PF_RING = 128;               // candidate ring entries per row (LDS)
 constexpr int PF_LCAP = 512;               // select: entries of the k-th bin a wave can hold
-constexpr int PF_SEL_W = 1;                // select: waves (rows) per workgroup (one: more rows
-                                           // resident per CU; 4 measured 2.59 against 2.33 ms)
+constexpr int PF_SEL_NT = 256;             // select: threads of the one workgroup per row
 static_assert(PF_RB * PF_RING <= PF_RB * PF_NBIN, "the rings reuse the sample histogram");
 
 typedef __attribute__((address_space(3))) void pf_lds_void;
@@ -545,7 +544,7 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
 
 // ---- exact select per row from the candidate lists ----------------------
 
-struct PfSelWave {
+struct PfSelShared {
   uint32_t bm[2048];  // position bitmap (65536 positions)
   union {
     struct {
@@ -557,21 +556,14 @@ struct PfSelWave {
   uint32_t hist[PF_NBIN];
   uint32_t sub[256];  // exact-score histogram of the k-th bin, then its ties
   uint32_t qrow[PF_HD / 4];
+  uint32_t scan[PF_SEL_NT / 64 + 2];
+  uint32_t v[8];  // bin, above, count, status, list fill, clamped, cut value, tie fill
 };
 static_assert(sizeof(uint16_t) * PF_MAX_K <= 2 * sizeof(uint32_t) * PF_LCAP, "output staging fits");
-struct PfSelShared {
-  PfSelWave w[PF_SEL_W];
-};
 
-LCT_DEV void pf_wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// LDS slot of bitmap word w: lane l reads words 32 l + j together, so the
-// low five bits are XORed with l to spread those reads over the banks
-LCT_DEV uint32_t pf_bw(uint32_t w) { return w ^ ((w >> 5) & 31u); }
+// LDS slot of bitmap word w: the words a thread expands (8 in a row) are
+// spread over the banks
+LCT_DEV uint32_t pf_bw(uint32_t w) { return w ^ ((w >> 3) & 31u); }
 
 LCT_DEV uint32_t pf_mbcnt(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -579,7 +571,7 @@ LCT_DEV uint32_t pf_mbcnt(uint64_t m) {
 
 // Over the counts c(b) of bins b = top .. 0 held two per lane (lane l: bins
 // top - 2l and top - 2l - 1), find the bin that holds the need-th largest
-// entry.  Returns false if the counts sum to less than need.
+// entry.  Returns false if the counts sum to less than need.  One wave.
 LCT_DEV bool pf_find_bin(uint32_t c_hi, uint32_t c_lo, int top, uint32_t need, int lane,
                          uint32_t& bin, uint32_t& above, uint32_t& cnt) {
   const uint32_t tot = c_hi + c_lo;
@@ -605,170 +597,189 @@ LCT_DEV bool pf_find_bin(uint32_t c_hi, uint32_t c_lo, int top, uint32_t need, i
   return bal != 0;
 }
 
-__global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
+// Exact top-k of one row from its candidate list: one workgroup of
+// PF_SEL_NT threads per row.  The list is read once into registers (entry
+// 1024 m + 4 t + u in element u of e[m] of thread t); a histogram of
+// score - t_r names the bin holding the k-th largest; higher bins go to the
+// position bitmap, that bin to an LDS list, which is settled exactly (an
+// exact-score histogram and the ties at the cut ranked by position, or, for
+// a top bin or clamped offsets, every entry ranked); the bitmap is expanded
+// into the ascending row (a block-wide prefix sum of popcounts, eight words
+// per thread).  Rows the list cannot settle are listed for the whole-row
+// select.
+__global__ __launch_bounds__(PF_SEL_NT) void k_pf_select(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, int L, int kk, int r_all,
     const uint32_t* __restrict__ list, const uint32_t* __restrict__ meta,
     int32_t* __restrict__ idx, int32_t* __restrict__ fails) {
+  constexpr int NT = PF_SEL_NT;
+  constexpr int EM = PF_CROW / (4 * NT);  // 16-byte loads per thread
+  static_assert(EM * 4 * NT == PF_CROW, "the list fits the registers exactly");
   __shared__ __attribute__((aligned(16))) PfSelShared sh;
-  const int lane = threadIdx.x & 63, wid = wave_id();
-  const int row = blockIdx.x * PF_SEL_W + wid;
-  if (row >= L) return;
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
+  const int row = blockIdx.x;
   int32_t* out = idx + (size_t)row * kk;
   if (row < kk) {
-    for (int j = lane; j < kk; j += 64) out[j] = j <= row ? j : -1;
+    for (int j = tid; j < kk; j += NT) out[j] = j <= row ? j : -1;
     return;
   }
   if (row < r_all) return;  // the plain path writes these rows
-  const uint4 m = *reinterpret_cast<const uint4*>(meta + (size_t)row * PF_META);
-  const uint32_t c = m.x;
-  const int32_t base = (int32_t)m.z;
-  const int sf = (int)m.w;
-  if (m.y != 0u || c < (uint32_t)kk || c > (uint32_t)PF_CROW) {
-    if (lane == 0) fails[1 + atomicAdd(&fails[0], 1)] = row;
+  const uint4 m4 = *reinterpret_cast<const uint4*>(meta + (size_t)row * PF_META);
+  const uint32_t c = m4.x;
+  const int32_t base = (int32_t)m4.z;
+  const int sf = (int)m4.w;
+  if (m4.y != 0u || c < (uint32_t)kk || c > (uint32_t)PF_CROW) {
+    if (tid == 0) fails[1 + atomicAdd(&fails[0], 1)] = row;
     return;
   }
   // entry = position << 16 | min(score - base, 65535); bin = min(value >> sf, 127)
   const uint32_t* lp = list + (size_t)row * PF_CROW;
   auto bin_of = [&](uint32_t e) { return min((e & 0xFFFFu) >> sf, (uint32_t)(PF_NBIN - 1)); };
-  PfSelWave& sw = sh.w[wid];
-  uint32_t* hh = sw.hist;
-  for (int i = lane; i < PF_NBIN; i += 64) hh[i] = 0u;
-  pf_wave_sync();
-  // 2048 entries per round: eight 16-byte loads in flight per lane; a lane
-  // holds entries i0 + 256 m + 4 lane + u
-  auto load_round = [&](uint32_t i0, uintx4 (&e)[8]) {
+  uintx4 e[EM];
 #pragma unroll
-    for (int m8 = 0; m8 < 8; ++m8) {
-      const uint32_t i = i0 + 256u * m8 + 4u * lane;
-      e[m8] = i < c ? *reinterpret_cast<const uintx4*>(lp + i) : uintx4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  for (int m = 0; m < EM; ++m) {
+    const uint32_t i = 1024u * m + 4u * tid;
+    e[m] = i < c ? *reinterpret_cast<const uintx4*>(lp + i) : uintx4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (i + u >= c) e[m8][u] = 0xFFFFFFFFu;
-    }
-  };
-  // pass 1: the bin histogram
-  for (uint32_t i0 = 0; i0 < c; i0 += 2048) {
-    uintx4 e[8];
-    load_round(i0, e);
-#pragma unroll
-    for (int m8 = 0; m8 < 8; ++m8)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (e[m8][u] != 0xFFFFFFFFu) atomicAdd(&hh[bin_of(e[m8][u])], 1u);
+    for (int u = 0; u < 4; ++u)
+      if (i + u >= c) e[m][u] = 0xFFFFFFFFu;
   }
-  pf_wave_sync();
-  uint32_t bsel, above, nsel;
-  {
-    const uint2 hw = reinterpret_cast<const uint2*>(hh)[63 - lane];
-    // hw.y = bin 127 - 2 lane, hw.x = bin 126 - 2 lane
-    const bool ok = pf_find_bin(hw.y, hw.x, PF_NBIN - 1, (uint32_t)kk, lane, bsel, above, nsel);
-    if (!ok || nsel > (uint32_t)PF_LCAP) {
-      if (lane == 0) fails[1 + atomicAdd(&fails[0], 1)] = row;
-      return;
-    }
-  }
-  const uint32_t need1 = (uint32_t)kk - above;  // taken from the k-th bin, 1..nsel
-  uint32_t* bm = sw.bm;
-  uint32_t* lpos = sw.u.l.lpos;
-  int32_t* lsc = sw.u.l.lsc;
   const uint32_t nwords = (uint32_t)((row + 1 + 31) / 32);
-  for (uint32_t w = lane; w < nwords; w += 64) bm[pf_bw(w)] = 0u;
-  pf_wave_sync();
-  // pass 2: bins above bsel are in; bin bsel goes to the list with its value
-  bool clamped = false;
-  {
-    uint32_t lcount = 0;
-    for (uint32_t i0 = 0; i0 < c; i0 += 2048) {
-      uintx4 e[8];
-      load_round(i0, e);
+  for (int i = tid; i < PF_NBIN; i += NT) sh.hist[i] = 0u;
+  for (uint32_t w = tid; w < nwords; w += NT) sh.bm[pf_bw(w)] = 0u;
+  if (tid < 8) sh.v[tid] = 0u;
+  __syncthreads();
+  // the bin histogram
 #pragma unroll
-      for (int m8 = 0; m8 < 8; ++m8)
+  for (int m = 0; m < EM; ++m)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t x = e[m8][u];
-          const bool valid = x != 0xFFFFFFFFu;
-          const uint32_t d = x & 0xFFFFu, p = x >> 16, b = bin_of(x);
-          if (valid && b > bsel) atomicOr(&bm[pf_bw(p >> 5)], 1u << (p & 31));
-          const bool inl = valid && b == bsel;
-          const uint64_t bl = __ballot(inl);
-          if (inl) {
-            const uint32_t slot = lcount + pf_mbcnt(bl);
-            if (slot < (uint32_t)PF_LCAP) {  // the bin holds exactly nsel entries
-              lpos[slot] = p;
-              lsc[slot] = (int32_t)d;
-            }
-            clamped = clamped || d == 0xFFFFu;
-          }
-          lcount += (uint32_t)__popcll(bl);
-        }
+    for (int u = 0; u < 4; ++u)
+      if (e[m][u] != 0xFFFFFFFFu) atomicAdd(&sh.hist[bin_of(e[m][u])], 1u);
+  __syncthreads();
+  if (wid == 0) {
+    const uint2 hw = reinterpret_cast<const uint2*>(sh.hist)[63 - lane];
+    // hw.y = bin 127 - 2 lane, hw.x = bin 126 - 2 lane
+    uint32_t bsel, above, nsel;
+    const bool ok = pf_find_bin(hw.y, hw.x, PF_NBIN - 1, (uint32_t)kk, lane, bsel, above, nsel);
+    if (lane == 0) {
+      sh.v[0] = bsel;
+      sh.v[1] = above;
+      sh.v[2] = nsel;
+      sh.v[3] = (!ok || nsel > (uint32_t)PF_LCAP) ? 1u : 0u;
     }
   }
-  clamped = __ballot(clamped) != 0;
-  pf_wave_sync();
+  __syncthreads();
+  if (sh.v[3]) {  // uniform
+    if (tid == 0) fails[1 + atomicAdd(&fails[0], 1)] = row;
+    return;
+  }
+  const uint32_t bsel = sh.v[0], nsel = sh.v[2];
+  const uint32_t need1 = (uint32_t)kk - sh.v[1];  // taken from the k-th bin, 1..nsel
+  uint32_t* lpos = sh.u.l.lpos;
+  int32_t* lsc = sh.u.l.lsc;
+  // bins above bsel are in; bin bsel goes to the list with its offset
+  {
+    bool clamped = false;
+#pragma unroll
+    for (int m = 0; m < EM; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t x = e[m][u];
+        const bool valid = x != 0xFFFFFFFFu;
+        const uint32_t b = bin_of(x), p = x >> 16, d = x & 0xFFFFu;
+        if (valid && b > bsel) atomicOr(&sh.bm[pf_bw(p >> 5)], 1u << (p & 31));
+        const bool inl = valid && b == bsel;
+        const uint64_t bl = __ballot(inl);
+        if (bl) {  // uniform over the wave
+          uint32_t s0 = 0;
+          if (lane == 0) s0 = atomicAdd(&sh.v[4], (uint32_t)__popcll(bl));
+          s0 = __shfl(s0, 0, 64);
+          if (inl) {
+            const uint32_t slot = s0 + pf_mbcnt(bl);  // < nsel <= PF_LCAP
+            lpos[slot] = p;
+            lsc[slot] = (int32_t)d;
+          }
+        }
+        clamped = clamped || (inl && d == 0xFFFFu);
+      }
+    if (__ballot(clamped) != 0 && lane == 0) sh.v[5] = 1u;
+  }
+  __syncthreads();
+  const bool clamped = sh.v[5] != 0u;
   if (clamped) {
-    // values clamped at 65535 are not exact: recompute the bin's scores
-    sw.qrow[lane] = reinterpret_cast<const uint32_t*>(q + (size_t)row * PF_HD)[lane];
-    pf_wave_sync();
-    for (uint32_t j = lane; j < nsel; j += 64) {
+    // offsets clamped at 65535 are not exact: recompute the bin's scores
+    if (tid < PF_HD / 4) sh.qrow[tid] = reinterpret_cast<const uint32_t*>(q + (size_t)row * PF_HD)[tid];
+    __syncthreads();
+    for (uint32_t j = tid; j < nsel; j += NT) {
       const int8_t* kp = k + (size_t)lpos[j] * PF_HD;
-      int32_t s = 0;
+      int32_t sacc = 0;
 #pragma unroll
       for (int w = 0; w < PF_HD / 16; ++w) {
         const uintx4 kv = *reinterpret_cast<const uintx4*>(kp + w * 16);
-        const uintx4 qv = *reinterpret_cast<const uintx4*>(&sw.qrow[w * 4]);
-        s = __builtin_amdgcn_sdot4((int)qv.x, (int)kv.x, s, false);
-        s = __builtin_amdgcn_sdot4((int)qv.y, (int)kv.y, s, false);
-        s = __builtin_amdgcn_sdot4((int)qv.z, (int)kv.z, s, false);
-        s = __builtin_amdgcn_sdot4((int)qv.w, (int)kv.w, s, false);
+        const uintx4 qv = *reinterpret_cast<const uintx4*>(&sh.qrow[w * 4]);
+        sacc = __builtin_amdgcn_sdot4((int)qv.x, (int)kv.x, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)qv.y, (int)kv.y, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)qv.z, (int)kv.z, sacc, false);
+        sacc = __builtin_amdgcn_sdot4((int)qv.w, (int)kv.w, sacc, false);
       }
-      lsc[j] = s - base;
+      lsc[j] = sacc - base;
     }
-    pf_wave_sync();
+    __syncthreads();
   }
-  // the need1 best of the bin by (score desc, position asc).  Below the
-  // top bin and with sf <= 7 the bin spans 2^sf consecutive exact values
-  // from bsel << sf: a 128-counter histogram finds the cut value T, and only
-  // the ties at T are ranked by position.
+  // the need1 best of the bin by (score desc, position asc).  Below the top
+  // bin and with sf <= 7 the bin spans 2^sf consecutive exact values from
+  // bsel << sf: a 128-counter histogram finds the cut value T, and only the
+  // ties at T are ranked by position.
   bool ranked = false;
-  if (!clamped && sf <= 7 && bsel < (uint32_t)(PF_NBIN - 1)) {
+  if (!clamped && sf <= 7 && bsel < (uint32_t)(PF_NBIN - 1)) {  // uniform
     const int32_t lo_b = (int32_t)(bsel << sf);
-    uint32_t* sh_sub = sw.sub;
-    for (int i = lane; i < 128; i += 64) sh_sub[i] = 0u;
-    pf_wave_sync();
-    for (uint32_t j = lane; j < nsel; j += 64) atomicAdd(&sh_sub[lsc[j] - lo_b], 1u);
-    pf_wave_sync();
-    const uint2 hw = reinterpret_cast<const uint2*>(sh_sub)[63 - lane];
-    uint32_t tb, ab2, n_eq;
-    const bool found = pf_find_bin(hw.y, hw.x, 127, need1, lane, tb, ab2, n_eq);
-    const int32_t T = lo_b + (int32_t)tb;
-    const uint32_t need_eq = need1 - ab2;  // ties at T to take, 1..n_eq
-    pf_wave_sync();
-    if (found && n_eq <= 256) {
-      // ties at T compacted into sh_sub, then ranked by position
-      uint32_t tcount = 0;
-      for (uint32_t j0 = 0; j0 < nsel; j0 += 64) {
-        const uint32_t j = j0 + lane;
+    for (int i = tid; i < 128; i += NT) sh.sub[i] = 0u;
+    __syncthreads();
+    for (uint32_t j = tid; j < nsel; j += NT) atomicAdd(&sh.sub[lsc[j] - lo_b], 1u);
+    __syncthreads();
+    if (wid == 0) {
+      const uint2 hw = reinterpret_cast<const uint2*>(sh.sub)[63 - lane];
+      uint32_t tb, ab2, n_eq;
+      const bool found = pf_find_bin(hw.y, hw.x, 127, need1, lane, tb, ab2, n_eq);
+      if (lane == 0) {
+        sh.v[6] = (uint32_t)(lo_b + (int32_t)tb);
+        sh.v[7] = need1 - ab2;                 // ties at T to take, 1..n_eq
+        sh.v[3] = (found && n_eq <= 256) ? n_eq : 0xFFFFFFFFu;
+        sh.v[4] = 0u;                           // tie fill
+      }
+    }
+    __syncthreads();
+    const uint32_t n_eq = sh.v[3];
+    if (n_eq != 0xFFFFFFFFu) {  // uniform
+      const int32_t T = (int32_t)sh.v[6];
+      const uint32_t need_eq = sh.v[7];
+      // ties at T compacted into sh.sub, the rest above T straight to the bitmap
+      for (uint32_t j0 = 0; j0 < nsel; j0 += NT) {
+        const uint32_t j = j0 + tid;
         const bool in = j < nsel;
         const int32_t sv = in ? lsc[j] : INT32_MIN;
         const uint32_t p = in ? lpos[j] : 0u;
-        if (in && sv > T) atomicOr(&bm[pf_bw(p >> 5)], 1u << (p & 31));
+        if (in && sv > T) atomicOr(&sh.bm[pf_bw(p >> 5)], 1u << (p & 31));
         const uint64_t bl = __ballot(in && sv == T);
-        if (in && sv == T) sh_sub[tcount + pf_mbcnt(bl)] = p;
-        tcount += (uint32_t)__popcll(bl);
+        if (bl) {
+          uint32_t s0 = 0;
+          if (lane == 0) s0 = atomicAdd(&sh.v[4], (uint32_t)__popcll(bl));
+          s0 = __shfl(s0, 0, 64);
+          if (in && sv == T) sh.sub[s0 + pf_mbcnt(bl)] = p;
+        }
       }
-      pf_wave_sync();
-      for (uint32_t j = lane; j < n_eq; j += 64) {
-        const uint32_t p = sh_sub[j];
+      __syncthreads();
+      for (uint32_t j = tid; j < n_eq; j += NT) {
+        const uint32_t p = sh.sub[j];
         uint32_t r = 0;
-        for (uint32_t mm = 0; mm < n_eq; ++mm) r += sh_sub[mm] < p ? 1u : 0u;
-        if (r < need_eq) atomicOr(&bm[pf_bw(p >> 5)], 1u << (p & 31));
+        for (uint32_t mm = 0; mm < n_eq; ++mm) r += sh.sub[mm] < p ? 1u : 0u;
+        if (r < need_eq) atomicOr(&sh.bm[pf_bw(p >> 5)], 1u << (p & 31));
       }
       ranked = true;
     }
   }
   if (!ranked) {
     // any bin: rank every entry of the bin against all the others
-    for (uint32_t j = lane; j < nsel; j += 64) {
+    for (uint32_t j = tid; j < nsel; j += NT) {
       const int32_t sv = lsc[j];
       const uint32_t p = lpos[j];
       uint32_t r = 0;
@@ -777,39 +788,36 @@ __global__ __launch_bounds__(PF_SEL_W * 64) void k_pf_select(
         const uint32_t pm = lpos[mm];
         r += (sm > sv || (sm == sv && pm < p)) ? 1u : 0u;
       }
-      if (r < need1) atomicOr(&bm[pf_bw(p >> 5)], 1u << (p & 31));
+      if (r < need1) atomicOr(&sh.bm[pf_bw(p >> 5)], 1u << (p & 31));
     }
   }
-  pf_wave_sync();
-  // ascending: lane l expands words [32l, 32l + 32) into the LDS stage (the
+  __syncthreads();
+  // ascending: thread t expands words [8t, 8t + 8) into the LDS stage (the
   // k-th bin's list is dead now), then the row goes out in coalesced stores
-  // (the lane's 32 words are read once, all loads in flight together)
-  uint32_t wv[32], cnt = 0;
+  constexpr int WPT = 2048 / NT;
+  uint32_t wv[WPT], cnt = 0;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t w = lane * 32 + j;
-    wv[j] = w < nwords ? bm[pf_bw(w)] : 0u;
+  for (int j = 0; j < WPT; ++j) {
+    const uint32_t w = tid * WPT + j;
+    wv[j] = w < nwords ? sh.bm[pf_bw(w)] : 0u;
+    cnt += __popc(wv[j]);
   }
+  uint32_t tot;
+  uint32_t off = block_excl_scan<NT>(cnt, sh.scan, tot);
+  uint16_t* stage = sh.u.stage;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) cnt += __popc(wv[j]);
-  const uint32_t incl = wave_incl_scan(cnt);
-  uint32_t off = incl - cnt;
-  uint16_t* stage = sw.u.stage;
-  pf_wave_sync();
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t w = lane * 32 + j;
-    uint32_t v = wv[j];
-    while (v) {
-      const uint32_t b = __ffs(v) - 1;
-      v &= v - 1;
+  for (int j = 0; j < WPT; ++j) {
+    const uint32_t w = tid * WPT + j;
+    uint32_t x = wv[j];
+    while (x) {
+      const uint32_t b = __ffs(x) - 1;
+      x &= x - 1;
       if (off < (uint32_t)kk) stage[off] = (uint16_t)(w * 32 + b);
       ++off;
     }
   }
-  const uint32_t tot = __shfl(incl, 63, 64);
-  pf_wave_sync();
-  for (uint32_t j = lane; j < (uint32_t)kk; j += 64) out[j] = j < tot ? (int32_t)stage[j] : -1;
+  __syncthreads();
+  for (uint32_t j = tid; j < (uint32_t)kk; j += NT) out[j] = j < tot ? (int32_t)stage[j] : -1;
 }
 
 // ---- whole-row select for the rows the lists could not settle ----------
@@ -920,8 +928,7 @@ hipError_t launch_pf_fused(const int8_t* q, const int8_t* k, int64_t L, int HD, 
   const int64_t NB = (L + PF_RB - 1) / PF_RB;
   k_pf_filter<<<dim3((unsigned)((NB + 1) / 2)), PF_NT, 0, st>>>(q, k, (int)L, kk, r_all, list, meta, m_s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_pf_select<<<dim3((unsigned)((L + PF_SEL_W - 1) / PF_SEL_W)), PF_SEL_W * 64, 0, st>>>(
-      q, k, (int)L, kk, r_all, list, meta, idx, fails);
+  k_pf_select<<<dim3((unsigned)L), PF_SEL_NT, 0, st>>>(q, k, (int)L, kk, r_all, list, meta, idx, fails);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // rows the lists could not settle: a fixed grid reads their count on the device
   k_pf_fallback<<<pf_fallback_grid(L), ROW_NT, 0, st>>>(q, k, kk, fails, reinterpret_cast<int32_t*>(ws + l.fb_scores),
