@@ -161,6 +161,25 @@ def _flush(buf):
     buf.add_(1)
 
 
+def _timed_flushed(fn, iters, stream, flush_buf):
+    """Median ms of ``iters`` calls of ``fn``, each timed alone with events on
+    ``stream`` after a 1 GiB write has evicted the Infinity Cache (the flush
+    is outside the timed interval)."""
+    import torch
+    t = []
+    for _ in range(iters):
+        _flush(flush_buf)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        t.append(e0.elapsed_time(e1))
+    t.sort()
+    return t[len(t) // 2]
+
+
 SCORER_SOURCES = ["long_context_top_amd/csrc/idx_score.hip", "long_context_top_amd/csrc/common.h",
                   "long_context_top_amd/csrc/kernels.h"]
 PROFILE_128K = os.path.join(ROOT, "profiles", "decode_128k_b8_kernels.txt")
@@ -409,7 +428,11 @@ def bench_decode(cfg, steps, warmup, want_cpu):
 
 # ------------------------------------------------------------------- GSA ----
 
-def bench_gsa(cfg, steps, warmup):
+def bench_gsa(cfg, steps, warmup, want_cpu=False):
+    """One GSA decode step (gist scores, chunk select, unfold attention), or
+    the coarse-to-fine H-GSA step, captured in a HIP graph; each replay timed
+    alone after the Infinity Cache has been evicted (the step's gist keys are
+    512 MiB, the selected rows 132 MiB: a warm cache would serve part of them)."""
     import torch
 
     import long_context_top_amd as lct
@@ -435,22 +458,61 @@ def bench_gsa(cfg, steps, warmup):
                                       out=out, ws=ws)
     step()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
+    stream = torch.cuda.current_stream()
+    g = _graph_of([step], stream)
     for _ in range(warmup):
         g.replay()
-    stream = torch.cuda.current_stream()
-    ms = _timed_loop(g.replay, steps, stream)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    ms = _timed_flushed(g.replay, steps, stream, flush)
     b = gsa_step_bytes(cfg)
     gbs = b["total"] / (ms * 1e-3) / 1e9
     res = {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": BH // cfg.H * 1.0 / (ms * 1e-3),
-           "hbm_gbs_step": gbs, "hbm_frac_step": gbs / HBM_PEAK_GBS, "routing_key_bytes": b["gist_keys"]}
+           "hbm_gbs_step": gbs, "hbm_frac_step": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": b["total"],
+           "routing_key_bytes": b["gist_keys"],
+           "timing": f"median of {steps} graph replays, each alone after a 1 GiB write evicted the Infinity Cache"}
     if not cfg.group:
         gs = torch.empty((BH, cfg.Nc), dtype=torch.float32, device=dev)
-        ms_gs = _timed_graph(lambda: lct.gist_score(qv, gk, out=gs), max(10, steps), stream)
-        res.update({"gist_score_gbs": b["gist_keys"] / (ms_gs * 1e-3) / 1e9, "gist_score_us": ms_gs * 1e3})
+        lct.gist_score(qv, gk, out=gs)
+        ms_gs = _timed_flushed(lambda: lct.gist_score(qv, gk, out=gs), max(5, steps // 2), stream, flush)
+        res["roofline"] = {"bound": "hbm", "kernel": "k_gist_score (every gist key once)",
+                           "achieved": b["gist_keys"] / (ms_gs * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": b["gist_keys"] / (ms_gs * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "us_per_launch": ms_gs * 1e3, "bytes_per_launch": b["gist_keys"]}
+    del g, flush, qv, gk, gv, rk, rv, out, cidx, ws
+    torch.cuda.empty_cache()
+    if want_cpu:
+        res["cpu_baseline"] = cpu_baseline_gsa(cfg)
     return res
+
+
+def cpu_baseline_gsa(cfg, n_pairs=16):
+    """The oracle's GSA (or H-GSA) decode on a sample of (batch, head) pairs,
+    on one thread and on every thread; every pair costs the oracle the same
+    (it regenerates and scores the pair's gist keys, then unfolds its chunks),
+    so the step's time is the sample's x (B x H) / n_pairs."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    model, nthreads = host_info()
+    step = oracle.driver.hgsa_step if cfg.group else oracle.driver.gsa_step
+    pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.H)][:: (cfg.B * cfg.H) // n_pairs][:n_pairs]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        step(cfg, pairs)
+        t1 = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(lambda p: step(cfg, [p]), pairs * max(1, nthreads // 4)))
+        tn = (time.perf_counter() - t0) / max(1, nthreads // 4)
+    scale = cfg.B * cfg.H / len(pairs)
+    return {"value": cfg.B / (tn * scale), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": model, "one_thread": {"value": cfg.B / (t1 * scale), "unit": "tokens/s", "cores": 1},
+            "sample": (f"{len(pairs)} (batch, head) pairs of the {cfg.B * cfg.H}: {t1:.1f} s on 1 thread; "
+                       f"{max(1, nthreads // 4)} x the sample on {nthreads} threads in {tn * max(1, nthreads // 4):.1f} s; "
+                       f"a step is {cfg.B * cfg.H} pairs (extrapolated x{scale:.0f})")}
 
 
 # ----------------------------------------------------------- GSA prefill ----
@@ -489,16 +551,9 @@ def bench_gsa_prefill(cfg, steps, warmup):
     for _ in range(max(warmup, 1)):
         f()
     torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        f()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    ms = sorted(times)[len(times) // 2]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    ms = _timed_flushed(f, steps, torch.cuda.current_stream(), flush)
+    del flush
     flops = 4.0 * cfg.D * gsa_prefill_pairs(cfg) * BH
     tf = flops / (ms * 1e-3) / 1e12
     tokens = cfg.B * cfg.Nc * (cfg.chunk + 1)
@@ -742,6 +797,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode_128k: leave out the prefill indexer object of the default line")
+    ap.add_argument("--no-gsa", action="store_true",
+                    help="decode_128k: leave out the GSA / H-GSA / GSA-prefill objects of the default line")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain 1 GiB device copy used to calibrate HBM byte counters")
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
@@ -771,7 +828,7 @@ def main():
             "gsa_prefill_128k": C.GSA_PREFILL_128K}
     cfg = cfgs[args.config]
     if args.config in ("gsa_128k", "hgsa_128k"):
-        res = bench_gsa(cfg, args.steps, args.warmup)
+        res = bench_gsa(cfg, args.steps, args.warmup, want_cpu=not args.no_cpu_baseline)
     elif args.config == "gsa_prefill_128k":
         res = bench_gsa_prefill(cfg, args.steps, args.warmup)
     elif args.config == "prefill_64k":
@@ -789,6 +846,19 @@ def main():
             log("prefill indexer, one 64K group ...")
             res["prefill_indexer"] = bench_prefill_indexer(C.PREFILL_64K, args.steps, args.warmup,
                                                            want_cpu=not args.no_cpu_baseline)
+        if headline and not args.no_gsa:
+            # the gist-chunk workloads beside it (the select-and-unfold decode, its
+            # coarse-to-fine variant, the prefill under the gist mask)
+            import gc
+
+            import torch
+            gc.collect()
+            torch.cuda.empty_cache()
+            log("GSA workloads ...")
+            gsteps = max(10, args.steps // 2)
+            res["gsa_decode"] = bench_gsa(C.GSA_128K, gsteps, 2, want_cpu=not args.no_cpu_baseline)
+            res["hgsa_decode"] = bench_gsa(C.HGSA_128K, gsteps, 2)
+            res["gsa_prefill"] = bench_gsa_prefill(C.GSA_PREFILL_128K, max(5, args.steps // 10), 1)
     print(json.dumps(res), flush=True)
 
 
