@@ -689,6 +689,7 @@ __global__ __launch_bounds__(256) void k_seg_merge(const float* __restrict__ par
 // segment path skips their rows.
 constexpr int UA_WIN = 4096;  // positions per membership window
 constexpr int UA_CH = 64;     // union positions per chunk
+constexpr int UA_LD = 8;      // index entries per thread and round of the membership pass
 // Union mode when the block's rows select each union position UA_SHARE x G / 8
 // times on average (sum of n_r >= that x |U|).  A union chunk costs its
 // workgroup G waves of MFMA and softmax work whoever selected its positions,
@@ -1012,18 +1013,27 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
       int c0 = cur[rr];
       int taken = 0;
       bool more = true;
+      const uint64_t gm = RT >= 64 ? ~0ull : (((1ull << RT) - 1ull) << ((threadIdx.x & 63) / RT * RT));
       while (more) {
-        const int e = c0 + t;
-        const int p = e < n ? ix[e] : INT32_MAX;
-        const bool in = p < p0 + UA_WIN;
-        if (in) atomicOr(&mem[rr][(p - p0) >> 5], 1u << ((p - p0) & 31));
-        // entries are ascending: the run in the window is a prefix
-        const uint64_t bl = __ballot(in);
-        const uint64_t gm = RT >= 64 ? ~0ull : (((1ull << RT) - 1ull) << ((threadIdx.x & 63) / RT * RT));
-        const uint32_t cnt = (uint32_t)__popcll(bl & gm);
+        // UA_LD entries per thread per round, all loads issued before any is used
+        int pv[UA_LD];
+#pragma unroll
+        for (int j = 0; j < UA_LD; ++j) {
+          const int e = c0 + t + j * RT;
+          pv[j] = e < n ? ix[e] : INT32_MAX;
+        }
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < UA_LD; ++j) {
+          const int p = pv[j];
+          const bool in = p < p0 + UA_WIN;
+          if (in) atomicOr(&mem[rr][(p - p0) >> 5], 1u << ((p - p0) & 31));
+          // entries are ascending: the run in the window is a prefix
+          cnt += (uint32_t)__popcll(__ballot(in) & gm);
+        }
         taken += (int)cnt;
-        more = cnt == (uint32_t)RT;
-        c0 += RT;
+        more = cnt == (uint32_t)(RT * UA_LD);
+        c0 += RT * UA_LD;
       }
       __syncthreads();
       if (t == 0) cur[rr] += taken;
