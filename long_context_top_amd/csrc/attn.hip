@@ -687,9 +687,12 @@ __global__ __launch_bounds__(256) void k_seg_merge(const float* __restrict__ par
 // MFMA work on the union for every row of the block.  k_union_plan decides per
 // block from the union's size; k_union_attn does the union blocks; the
 // segment path skips their rows.
-constexpr int UA_WIN = 4096;  // positions per membership window
-constexpr int UA_CH = 64;     // union positions per chunk
-constexpr int UA_LD = 8;      // index entries per thread and round of the membership pass
+constexpr int UA_WIN = 16384;  // positions per membership window (16 rows x 2 KiB of bits)
+constexpr int UA_CH = 64;      // union positions per chunk
+constexpr int UA_LD = 8;       // index entries per thread and round of the membership pass
+constexpr int UA_UCAP = 4096;  // largest union of a union-mode block
+constexpr int UA_NBUF = 4;     // staging buffers of the chunk ring
+constexpr int UA_SET = UA_CH * 256 * 2;  // one staging buffer: the chunk's K and V tiles
 // Union mode when the block's rows select each union position UA_SHARE x G / 8
 // times on average (sum of n_r >= that x |U|).  A union chunk costs its
 // workgroup G waves of MFMA and softmax work whoever selected its positions,
@@ -711,8 +714,8 @@ LCT_DEV void ua_barrier() {
 
 // One workgroup (256 threads) per block of UA_R rows: flag[block] = 1 if its
 // rows lie in one batch entry, each is ascending over its valid entries (in
-// [0, L)) followed only by -1, and the rows share its positions enough
-// (UA_SHARE).
+// [0, L)) followed only by -1, the union holds at most UA_UCAP positions and
+// the rows share its positions enough (UA_SHARE).
 __global__ __launch_bounds__(256) void k_union_plan(const int32_t* __restrict__ idx, int64_t rows, int Lq,
                                                     int kk, int64_t L, int G, int32_t* __restrict__ flag) {
   __shared__ uint32_t bm[1024];  // one 32768-position window
@@ -781,7 +784,7 @@ __global__ __launch_bounds__(256) void k_union_plan(const int32_t* __restrict__ 
   if (threadIdx.x == 0) {
     int64_t sum_n = 0;
     for (int r = 0; r < UA_R; ++r) sum_n += s_n[r];
-    flag[blk] = (sum_n > 0 && (int64_t)s_u * UA_SHARE * G <= sum_n * 8) ? 1 : 0;
+    flag[blk] = (sum_n > 0 && s_u <= (uint32_t)UA_UCAP && (int64_t)s_u * UA_SHARE * G <= sum_n * 8) ? 1 : 0;
   }
 }
 
@@ -848,15 +851,58 @@ LCT_DEV void ua_chunk(int base, const char (&kt)[UA_CH * 256], const char (&va)[
                       floatx4 (&o)[ATT_D / 16]) {
   constexpr int D = ATT_D;
   const int hl = a.hl, kg = a.kg;
+  // K: lane (hl, kg) reads 16-byte chunk st*4 + kg of token 16j + hl, stored
+  // as chunk (st*4 + kg) ^ hl = (st ^ (hl / 4))*4 + (kg ^ (hl % 4)).  The reads
+  // are written out with their wait, two token blocks per asm block: the
+  // compiler cannot tell them from the DMA into the other staging buffers and
+  // would otherwise drain that DMA first.
   floatx4 sacc[4];
+  const uint32_t kb = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&kt[0] + hl * 256 +
+                      ((kg ^ (hl & 3)) << 4);
+  const uint32_t k0 = kb + ((0 ^ (hl >> 2)) << 6), k1 = kb + ((1 ^ (hl >> 2)) << 6);
+  const uint32_t k2 = kb + ((2 ^ (hl >> 2)) << 6), k3 = kb + ((3 ^ (hl >> 2)) << 6);
+  static_assert(sizeof(kt) == 4 * 4096, "K tile: four 16-token blocks of 4096 bytes");
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int tok = 16 * j + hl;
+  for (int jp = 0; jp < 2; ++jp) {
+    intx4 r[8];  // [token block jj][st]
+    if (jp == 0)
+      __asm__ volatile(
+          "ds_read_b128 %0, %8 offset:0\n\t"
+          "ds_read_b128 %1, %9 offset:0\n\t"
+          "ds_read_b128 %2, %10 offset:0\n\t"
+          "ds_read_b128 %3, %11 offset:0\n\t"
+          "ds_read_b128 %4, %8 offset:4096\n\t"
+          "ds_read_b128 %5, %9 offset:4096\n\t"
+          "ds_read_b128 %6, %10 offset:4096\n\t"
+          "ds_read_b128 %7, %11 offset:4096\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+            "=&v"(r[7])
+          : "v"(k0), "v"(k1), "v"(k2), "v"(k3)
+          : "memory");
+    else
+      __asm__ volatile(
+          "ds_read_b128 %0, %8 offset:8192\n\t"
+          "ds_read_b128 %1, %9 offset:8192\n\t"
+          "ds_read_b128 %2, %10 offset:8192\n\t"
+          "ds_read_b128 %3, %11 offset:8192\n\t"
+          "ds_read_b128 %4, %8 offset:12288\n\t"
+          "ds_read_b128 %5, %9 offset:12288\n\t"
+          "ds_read_b128 %6, %10 offset:12288\n\t"
+          "ds_read_b128 %7, %11 offset:12288\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+            "=&v"(r[7])
+          : "v"(k0), "v"(k1), "v"(k2), "v"(k3)
+          : "memory");
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kt[tok * 256 + (((st * 4 + kg) ^ hl) << 4)]);
-      sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[st], sacc[j], 0, 0, 0);
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * jp + jj;
+      sacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r[4 * jj + st]), qf[st],
+                                                          sacc[j], 0, 0, 0);
     }
   }
   // membership of this lane's tokens 16j + 4kg + e for its column's row
@@ -901,15 +947,18 @@ LCT_DEV void ua_chunk(int base, const char (&kt)[UA_CH * 256], const char (&va)[
 
 // Union attention of one (block, KV head) in union mode; G waves, wave w
 // takes rows w*(16/G) .. (w+1)*(16/G) - 1 of the block with their G heads as
-// its 16 MFMA columns (column c: row c / G, head c % G).  Per window of
-// UA_WIN positions: each row's entries in the window (a contiguous run of its
-// ascending list, from a cursor) set its membership bits; the union of the
-// rows is compacted to positions + 16-bit row masks; chunks of 64 union
-// positions are gathered into LDS (two buffers: the next chunk's DMA overlaps
-// this chunk's MFMA work) and attended by every wave with its rows' masks.
-// K is stored 16-byte-chunk swizzled (chunk s of token t at s ^ (t % 16)), so
-// the A-operand reads (16 tokens of one chunk) fall on distinct banks; V uses
-// the layout of the per-row path for the transposed reads.
+// its 16 MFMA columns (column c: row c / G, head c % G).
+// Phase 1 builds the block's whole union: per window of UA_WIN positions, each
+// row's entries in the window (a contiguous run of its ascending list, from a
+// cursor) set its membership bits; the window's union is appended to a list of
+// positions + 16-bit row masks (at most UA_UCAP entries: the plan flags no
+// larger union).  The bitmaps live in the first staging buffer, free then.
+// Phase 2 gathers chunks of 64 union positions into a ring of UA_NBUF staging
+// buffers (UA_NBUF - 1 chunks in flight while one is attended) and every wave
+// attends each chunk with its rows' masks.  K is stored 16-byte-chunk swizzled
+// (chunk s of token t at s ^ (t % 16)), so the A-operand reads (16 tokens of
+// one chunk) fall on distinct banks; V uses the layout of the per-row path
+// for the transposed reads.
 template <int G>
 __global__ __launch_bounds__(G * 64) void k_union_attn(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -919,17 +968,14 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
   constexpr int NT = G * 64;
   constexpr int RW = UA_R / G;  // rows per wave
   static_assert(G >= 4 && G <= 16 && UA_R % G == 0, "union path for 4 to 16 heads per KV head");
-  __shared__ uint32_t mem[UA_R][UA_WIN / 32];
-  __shared__ int32_t upos[UA_WIN];
-  __shared__ __attribute__((aligned(8))) uint16_t umask[UA_WIN];
-  __shared__ __attribute__((aligned(16))) char kt0[UA_CH * 256];
-  __shared__ __attribute__((aligned(16))) char kt1[UA_CH * 256];
-  __shared__ __attribute__((aligned(16))) char va0[2][4][1024];
-  __shared__ __attribute__((aligned(16))) char vb0[2][4][1024];
-  __shared__ __attribute__((aligned(16))) char va1[2][4][1024];
-  __shared__ __attribute__((aligned(16))) char vb1[2][4][1024];
-  __shared__ int32_t cur[UA_R], nrow[UA_R];
+  static_assert(UA_R * (UA_WIN / 32) * 4 <= UA_SET, "membership bitmaps fit one staging buffer");
+  static_assert(UA_UCAP % UA_CH == 0, "the last chunk's padding stays in the list");
+  __shared__ int32_t upos[UA_UCAP];
+  __shared__ __attribute__((aligned(8))) uint16_t umask[UA_UCAP];
+  __shared__ __attribute__((aligned(16))) char stage[UA_NBUF][UA_SET];
+  __shared__ int32_t cur[UA_R], nrow[UA_R], plst[UA_R];
   __shared__ uint32_t scan[NT / 64 + 2];
+  uint32_t (*mem)[UA_WIN / 32] = reinterpret_cast<uint32_t (*)[UA_WIN / 32]>(&stage[0][0]);
   const int64_t blk = blockIdx.x / Hkv;
   const int kvh = (int)(blockIdx.x % Hkv);
   if (flag[blk] == 0) return;  // uniform: the segment path takes this block
@@ -947,73 +993,57 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
 #pragma unroll
     for (int st = 0; st < 4; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qp + st * 32);
   }
-  // row lengths (valid entries: ascending, then -1) and cursors
-  if (threadIdx.x < UA_R) {
-    const int32_t* ix = idx + (r0 + threadIdx.x) * kk;
-    int lo = 0, hi = kk;  // first -1 by bisection (the row is ascending, then -1)
+  // row lengths (valid entries: ascending, then -1), cursors and last
+  // positions: RT threads per row narrow the first -1 down together, RT
+  // probes per round
+  constexpr int RT = NT / UA_R;  // threads per row (a power of two, 16 to 64)
+  const int rr = threadIdx.x / RT, t = threadIdx.x % RT;
+  const int gsh = (threadIdx.x & 63) / RT * RT;  // the row's first lane in its wave
+  const uint64_t gm = RT >= 64 ? ~0ull : (((1ull << RT) - 1ull) << gsh);
+  {
+    const int32_t* ix = idx + (r0 + rr) * kk;
+    int lo = 0, hi = kk;  // the first -1 (kk: none) lies in [lo, hi]
     while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (ix[mid] >= 0) lo = mid + 1;
-      else hi = mid;
+      const int step = (hi - lo + RT - 1) / RT;
+      const int pr = lo + t * step;
+      const bool neg = pr >= hi || ix[pr] < 0;
+      const uint64_t bl = (__ballot(neg) & gm) >> gsh;
+      if (bl == 0) {
+        lo += (RT - 1) * step + 1;  // past the last probe, which is < hi
+      } else {
+        const int f = __ffsll((unsigned long long)bl) - 1;
+        if (f == 0) {
+          hi = lo;
+        } else {
+          hi = min(hi, lo + f * step);
+          lo += (f - 1) * step + 1;
+        }
+      }
     }
-    nrow[threadIdx.x] = lo;
-    cur[threadIdx.x] = 0;
+    if (t == 0) {
+      nrow[rr] = lo;
+      cur[rr] = 0;
+      plst[rr] = lo > 0 ? ix[lo - 1] : -1;
+    }
   }
   __syncthreads();
   int plast = -1;
-  for (int r = 0; r < UA_R; ++r)
-    if (nrow[r] > 0) plast = max(plast, idx[(r0 + r) * kk + nrow[r] - 1]);
-  const int row_bytes = Hkv * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (size_t)b * L * Hkv * D + kvh * D, L * (int64_t)row_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (size_t)b * L * Hkv * D + kvh * D, L * (int64_t)row_bytes);
-  float m = -INFINITY;
-  floatx4 lacc = floatx4{0.f, 0.f, 0.f, 0.f};
-  floatx4 o[D / 16];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // DMA of chunk c (union positions c*64 ..) into buffer set (kt, va, vb):
-  // 16 K and 16 V instructions per chunk, 32 / G per wave (i = wid + ii * G)
-  auto issue = [&](int c, int nu, char* kt, char (*va)[4][1024], char (*vb)[4][1024]) {
-    const int base = c * UA_CH;
-#pragma unroll
-    for (int ii = 0; ii < 32 / G; ++ii) {
-      const int i = wid + ii * G;
-      if (i < 16) {
-        const int tok = 4 * i + (lane >> 4), s = lane & 15;
-        const int up = base + tok < nu ? base + tok : base;
-        const int roff = upos[up] * row_bytes + ((s ^ (tok & 15)) << 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kt + i * 1024), 16, roff, 0, 0, 0);
-      } else {
-        const int j = (i - 16) >> 2, st = (i - 16) & 3;
-        const int tok = 16 * j + a.tk;
-        const int up = base + tok < nu ? base + tok : base;
-        const int roff = upos[up] * row_bytes + st * 64 + a.cv * 16;
-        char* dst = j < 2 ? &va[j][st][0] : &vb[j - 2][st][0];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)dst, 16, roff, 0, 0, 0);
-      }
-    }
-  };
-  constexpr int NDMA = 32 / G;  // DMA instructions per wave and chunk
+  for (int r = 0; r < UA_R; ++r) plast = max(plast, plst[r]);
 
-  auto compute = [&](int c, const char (&kt)[UA_CH * 256], const char (&va)[2][4][1024],
-                     const char (&vb)[2][4][1024]) {
-    ua_chunk(c * UA_CH, kt, va, vb, umask, a, qf, rbit, scale_log2, m, lacc, o);
-  };
-
-  constexpr int RT = NT / UA_R;  // threads per row in the membership pass
-  constexpr int BPT = UA_WIN / NT;  // union bits per thread
+  // ---- phase 1: the union, window by window
+  constexpr int BPT = UA_WIN / NT < 32 ? UA_WIN / NT : 32;  // union bits per thread and pass
+  constexpr int NPASS = UA_WIN / (NT * BPT);           // passes over the window's bitmap
+  uint32_t ucount = 0;                                 // union entries so far (block-uniform)
   for (int p0 = 0; p0 <= plast; p0 += UA_WIN) {
-    // ---- membership of the window
     for (int i = threadIdx.x; i < UA_R * (UA_WIN / 32); i += NT) (&mem[0][0])[i] = 0u;
     __syncthreads();
     {
-      const int rr = threadIdx.x / RT, t = threadIdx.x % RT;
       const int32_t* ix = idx + (r0 + rr) * kk;
       const int n = nrow[rr];
       int c0 = cur[rr];
       int taken = 0;
       bool more = true;
-      const uint64_t gm = RT >= 64 ? ~0ull : (((1ull << RT) - 1ull) << ((threadIdx.x & 63) / RT * RT));
       while (more) {
         // UA_LD entries per thread per round, all loads issued before any is used
         int pv[UA_LD];
@@ -1039,69 +1069,110 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
       if (t == 0) cur[rr] += taken;
     }
     __syncthreads();
-    // ---- union of the window: positions and row masks, ascending
-    uint32_t cnt = 0;
-    const int bit0 = (int)threadIdx.x * BPT;
-    uint32_t ubits = 0;  // BPT <= 32 bits of this thread
-    {
-      const int wd = bit0 >> 5, sh = bit0 & 31;
-      uint32_t u = 0;
+    // the window's union appended in ascending order, BPT bits per thread
+    // and pass
 #pragma unroll
-      for (int r = 0; r < UA_R; ++r) u |= mem[r][wd];
-      ubits = BPT >= 32 ? u : (u >> sh) & ((1u << BPT) - 1u);
-      cnt = __popc(ubits);
-    }
-    uint32_t nu;
-    const uint32_t off = block_excl_scan<NT>(cnt, scan, nu);
-    {
+    for (int pass = 0; pass < NPASS; ++pass) {
+      const int bit0 = (pass * NT + (int)threadIdx.x) * BPT;
       const int wd = bit0 >> 5, sh = bit0 & 31;
-      uint32_t rw[UA_R];
+      uint32_t rw[UA_R], ubits = 0;
 #pragma unroll
-      for (int r = 0; r < UA_R; ++r) rw[r] = mem[r][wd] >> sh;
-      uint32_t o2 = off, x = ubits;
+      for (int r = 0; r < UA_R; ++r) {
+        rw[r] = mem[r][wd] >> sh;
+        ubits |= rw[r];
+      }
+      if (BPT < 32) ubits &= (1u << BPT) - 1u;
+      uint32_t nu;
+      uint32_t o2 = ucount + block_excl_scan<NT>(__popc(ubits), scan, nu);
+      uint32_t x = ubits;
       while (x) {
         const int bbit = __ffs(x) - 1;
         x &= x - 1;
         uint32_t msk = 0;
 #pragma unroll
         for (int r = 0; r < UA_R; ++r) msk |= ((rw[r] >> bbit) & 1u) << r;
-        upos[o2] = p0 + bit0 + bbit;
-        umask[o2] = (uint16_t)msk;
+        if (o2 < (uint32_t)UA_UCAP) {  // the plan admits no larger union
+          upos[o2] = p0 + bit0 + bbit;
+          umask[o2] = (uint16_t)msk;
+        }
         ++o2;
       }
+      ucount += nu;
     }
-    // padding of the last chunk: no row takes it
-    const int nch = ((int)nu + UA_CH - 1) / UA_CH;
-    for (int i = (int)nu + (int)threadIdx.x; i < nch * UA_CH; i += NT) umask[i] = 0;
-    __syncthreads();
-    if (nu == 0) continue;
-    // ---- chunks, two buffer sets; DMA of chunk c + 1 overlaps chunk c.
-    // Plain barriers (ua_barrier): each wave waits for its own DMA with an
-    // explicit count, so the barrier need not drain the DMA in flight.
-    __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
-    issue(0, (int)nu, kt0, va0, vb0);
-    for (int c = 0; c < nch; c += 2) {
-      if (c + 1 < nch) {
-        issue(c + 1, (int)nu, kt1, va1, vb1);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
+    __syncthreads();  // the bitmaps are read before the next window clears them
+  }
+  const int nu = (int)min(ucount, (uint32_t)UA_UCAP);
+  // padding of the last chunk: no row takes it
+  const int nch = (nu + UA_CH - 1) / UA_CH;
+  for (int i = nu + (int)threadIdx.x; i < nch * UA_CH; i += NT) umask[i] = 0;
+  __syncthreads();
+
+  // ---- phase 2: the chunks, UA_NBUF - 1 in flight
+  const int row_bytes = Hkv * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (size_t)b * L * Hkv * D + kvh * D, L * (int64_t)row_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (size_t)b * L * Hkv * D + kvh * D, L * (int64_t)row_bytes);
+  float m = -INFINITY;
+  floatx4 lacc = floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // staging buffer: K tile (64 x 256 B, swizzled), then the two V halves
+  auto kt_of = [&](int sb) -> char (&)[UA_CH * 256] {
+    return *reinterpret_cast<char (*)[UA_CH * 256]>(&stage[sb][0]);
+  };
+  auto va_of = [&](int sb) -> char (&)[2][4][1024] {
+    return *reinterpret_cast<char (*)[2][4][1024]>(&stage[sb][UA_CH * 256]);
+  };
+  auto vb_of = [&](int sb) -> char (&)[2][4][1024] {
+    return *reinterpret_cast<char (*)[2][4][1024]>(&stage[sb][UA_CH * 256 + 8192]);
+  };
+  // DMA of chunk c (union positions c*64 ..) into staging buffer c % UA_NBUF:
+  // 16 K and 16 V instructions per chunk, 32 / G per wave (i = wid + ii * G)
+  auto issue = [&](int c) {
+    const int sb = c % UA_NBUF;
+    char* kt = &kt_of(sb)[0];
+    char (*va)[4][1024] = va_of(sb);
+    char (*vb)[4][1024] = vb_of(sb);
+    const int base = c * UA_CH;
+#pragma unroll
+    for (int ii = 0; ii < 32 / G; ++ii) {
+      const int i = wid + ii * G;
+      if (i < 16) {
+        const int tok = 4 * i + (lane >> 4), s = lane & 15;
+        const int up = base + tok < nu ? base + tok : base;
+        const int roff = upos[up] * row_bytes + ((s ^ (tok & 15)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kt + i * 1024), 16, roff, 0, 0, 0);
       } else {
-        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+        const int j = (i - 16) >> 2, st = (i - 16) & 3;
+        const int tok = 16 * j + a.tk;
+        const int up = base + tok < nu ? base + tok : base;
+        const int roff = upos[up] * row_bytes + st * 64 + a.cv * 16;
+        char* dst = j < 2 ? &va[j][st][0] : &vb[j - 2][st][0];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)dst, 16, roff, 0, 0, 0);
       }
-      ua_barrier();
-      compute(c, kt0, va0, vb0);
-      ua_barrier();  // buffer set 0 is free
-      if (c + 1 >= nch) break;
-      if (c + 2 < nch) {
-        issue(c + 2, (int)nu, kt0, va0, vb0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
-      } else {
-        __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
-      }
-      ua_barrier();
-      compute(c + 1, kt1, va1, vb1);
-      ua_barrier();  // buffer set 1 is free
     }
-    __syncthreads();
+  };
+  constexpr int NDMA = 32 / G;  // DMA instructions per wave and chunk
+  static_assert((UA_NBUF - 2) * NDMA <= 63, "vector memory counter range");
+  // Plain barriers (ua_barrier): each wave waits for its own DMA with an
+  // explicit count, so the barrier need not drain the DMA in flight.
+  __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+#pragma unroll
+  for (int c = 0; c < UA_NBUF - 1; ++c)
+    if (c < nch) issue(c);
+  for (int c = 0; c < nch; ++c) {
+    // this wave's DMA of chunk c has landed once at most min(UA_NBUF - 2,
+    // nch - 1 - c) later chunks are outstanding
+    const int later = min(UA_NBUF - 2, nch - 1 - c);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
+    else __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+    // every wave's DMA of chunk c has landed, and every wave is done with
+    // chunk c - 1, whose buffer takes chunk c + UA_NBUF - 1
+    ua_barrier();
+    if (c + UA_NBUF - 1 < nch) issue(c + UA_NBUF - 1);
+    const int sb = c % UA_NBUF;
+    ua_chunk(c * UA_CH, kt_of(sb), va_of(sb), vb_of(sb), umask, a, qf, rbit, scale_log2, m, lacc, o);
   }
   // o[dt][e] = O^T[d = 16dt + 4kg + e][column hl]; every row of lacc holds
   // the column's denominator

@@ -390,6 +390,50 @@ def test_sparse_attn_block_union_path(Hq, Hkv):
     print(f"  max |out - oracle| = {worst:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(32, 4), (16, 4)])
+def test_sparse_attn_block_union_large_unions(Hq, Hkv):
+    """Blocks of 16 rows of 2048 positions drawn from a common pool: a pool of
+    3000 and one of exactly 4096 (rows 0 and 1 take its even and odd
+    positions; 64 chunks, the largest union the block-union path holds) take
+    that path; a pool of 5000 shares enough but its union is too large, and
+    independent random sets share too little: both are decided per row.
+    Rows of every kind are compared with the oracle."""
+    B, Lq, L, kk = 1, 4096, 40000, 2048
+    announce(f"attn block union large Hq={Hq} Hkv={Hkv} Lq={Lq} L={L} kk={kk}")
+    r = _rng(Hq + 7)
+    q, qh = dev_bf16(r.standard_normal((B, Lq, Hq, 128)))
+    k, kh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    v, vh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    idx = np.full((B, Lq, kk), -1, dtype=np.int32)
+    pools = {0: 3000, 1: 4096, 2: 5000}
+    kinds = np.arange(Lq // 16) % 4
+    for blk, kind in enumerate(kinds):
+        pool = np.sort(r.choice(L, size=pools[kind], replace=False)) if kind in pools else None
+        for i in range(16):
+            if kind == 1 and i < 2:
+                sel = pool[i::2]
+            elif pool is not None:
+                sel = np.sort(r.choice(pool, size=kk, replace=False))
+            else:
+                sel = np.sort(r.choice(L, size=kk, replace=False))
+            idx[0, blk * 16 + i] = sel
+    scale = 1.0 / math.sqrt(128)
+    ws = lct.Workspace()
+    got = host(lct.sparse_attn_gather(q, k, v, dev_i32(idx), scale, ws=ws))
+    flags = _union_flags(ws, B, Lq, Hq, Hkv, L, kk)
+    assert np.all(flags[kinds == 0] == 1) and np.all(flags[kinds == 1] == 1)
+    assert np.all(flags[kinds == 2] == 0) and np.all(flags[kinds == 3] == 0)
+    rows = [j for j in range(Lq) if j // 16 < 64 or j % 37 == 0]
+    worst = 0.0
+    for j in rows:
+        sel = idx[0, j]
+        want = oracle.sparse_attention_gqa(qh[0, j], kh[0, sel], vh[0, sel], scale)
+        err = np.abs(got[0, j] - want).max()
+        worst = max(worst, err)
+        assert err < ATOL, (j, int(kinds[j // 16]), err)
+    print(f"  {len(rows)} rows, max |out - oracle| = {worst:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("tail", [0, 1, 7, 15, 16])
 def test_gist_score_and_gsa_decode(tail):
     from synth import configs as C
