@@ -535,48 +535,59 @@ hipError_t launch_split_merge(const float* part, float* out, int64_t units, int 
 // below segment j's start; bnd[row][nseg] = the row's valid entries.  Needs
 // the row ascending over its valid entries (positions in [0, L)) followed
 // only by -1; any other row gets {0, kk, ..., kk}: one segment, whole row.
-// One wave per row.
+// One wave per row, one pass: the shape check and the bounds (staged in LDS
+// until the shape is known) over SB_LD x 64 entries per round, all loads of a
+// round issued first.  Rows of blocks on the block-union path are skipped:
+// nothing reads their bounds.
+constexpr int SB_LD = 8;
 __global__ __launch_bounds__(256) void k_seg_bounds(const int32_t* __restrict__ idx,
                                                     int32_t* __restrict__ bnd, int64_t rows, int kk,
-                                                    int64_t L, int shift, int nseg) {
-  const int lane = threadIdx.x & 63;
-  const int64_t br = (int64_t)blockIdx.x * 4 + wave_id();
+                                                    int64_t L, int shift, int nseg,
+                                                    const int32_t* __restrict__ uflag, int64_t nblk) {
+  __shared__ int32_t sb[4][ATT_SEG_MAX + 1];
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int64_t br = (int64_t)blockIdx.x * 4 + w;
   if (br >= rows) return;
+  if (uflag && br / UA_R < nblk && uflag[br / UA_R]) return;
   const int32_t* ix = idx + br * kk;
   int32_t* bb = bnd + br * (nseg + 1);
-  // pass 1: the row's shape (-2: before the first entry)
+  int32_t* s = sb[w];
   bool bad = false;
-  int carry = -2;
-  for (int c = 0; c < kk; c += 64) {
-    const int e = c + lane;
-    const int p = e < kk ? ix[e] : -1;
-    int prv = __shfl(p, (lane + 63) & 63, 64);
-    if (lane == 0) prv = carry;
-    carry = __shfl(p, 63, 64);
-    const bool valid = p >= 0 && (int64_t)p < L;
-    bool ok;
-    if (prv == -2) ok = valid || p == -1;
-    else if (prv == -1) ok = p == -1;
-    else ok = p == -1 || (valid && p > prv);
-    bad = bad || (e < kk && !ok);
+  int carry = -2;   // the previous entry (-2: before the first)
+  int kcarry = -1;  // its segment key (-1 before entry 0)
+  for (int c0 = 0; c0 <= kk; c0 += 64 * SB_LD) {
+    int pv[SB_LD];
+#pragma unroll
+    for (int j = 0; j < SB_LD; ++j) {
+      const int e = c0 + 64 * j + lane;
+      pv[j] = e < kk ? ix[e] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < SB_LD; ++j) {
+      const int e = c0 + 64 * j + lane;
+      const int p = pv[j];
+      int prv = __shfl(p, (lane + 63) & 63, 64);
+      if (lane == 0) prv = carry;
+      carry = __shfl(p, 63, 64);
+      const bool valid = p >= 0 && (int64_t)p < L;
+      bool ok;
+      if (prv == -2) ok = valid || p == -1;
+      else if (prv == -1) ok = p == -1;
+      else ok = p == -1 || (valid && p > prv);
+      bad = bad || (e < kk && !ok);
+      // entry e opens segments (key(e-1), key(e)]; key = segment of the
+      // position, nseg for -1 and for the virtual entry kk
+      const int key = (e >= kk || p < 0) ? nseg : min(p >> shift, nseg);
+      int kprv = __shfl(key, (lane + 63) & 63, 64);
+      if (lane == 0) kprv = kcarry;
+      kcarry = __shfl(key, 63, 64);
+      if (e <= kk)
+        for (int jj = kprv + 1; jj <= key; ++jj) s[jj] = e;
+    }
   }
-  if (__ballot(bad) != 0) {
-    for (int j = lane; j <= nseg; j += 64) bb[j] = j == 0 ? 0 : kk;
-    return;
-  }
-  // pass 2: entry e opens segments (key(e-1), key(e)]; key = segment of the
-  // position, nseg for -1 and for the virtual entry kk, -1 before entry 0
-  int kcarry = -1;
-  for (int c = 0; c <= kk; c += 64) {
-    const int e = c + lane;
-    const int p = e < kk ? ix[e] : -1;
-    const int key = (e >= kk || p < 0) ? nseg : (p >> shift);
-    int kprv = __shfl(key, (lane + 63) & 63, 64);
-    if (lane == 0) kprv = kcarry;
-    kcarry = __shfl(key, 63, 64);
-    if (e <= kk)
-      for (int j = kprv + 1; j <= key; ++j) bb[j] = e;
-  }
+  __builtin_amdgcn_wave_barrier();
+  const bool rbad = __ballot(bad) != 0;
+  for (int j = lane; j <= nseg; j += 64) bb[j] = rbad ? (j == 0 ? 0 : kk) : s[j];
 }
 
 template <int G>
@@ -689,8 +700,7 @@ __global__ __launch_bounds__(256) void k_seg_merge(const float* __restrict__ par
 // segment path skips their rows.
 constexpr int UA_WIN = 16384;  // positions per membership window (16 rows x 2 KiB of bits)
 constexpr int UA_CH = 64;      // union positions per chunk
-constexpr int UA_LD = 8;       // index entries per thread and round of the membership pass
-constexpr int UA_UCAP = 4096;  // largest union of a union-mode block
+constexpr int UA_LD = 16;      // index entries per thread and round of the membership pass
 constexpr int UA_NBUF = 4;     // staging buffers of the chunk ring
 constexpr int UA_SET = UA_CH * 256 * 2;  // one staging buffer: the chunk's K and V tiles
 // Union mode when the block's rows select each union position UA_SHARE x G / 8
@@ -712,21 +722,32 @@ LCT_DEV void ua_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-// One workgroup (256 threads) per block of UA_R rows: flag[block] = 1 if its
-// rows lie in one batch entry, each is ascending over its valid entries (in
-// [0, L)) followed only by -1, the union holds at most UA_UCAP positions and
-// the rows share its positions enough (UA_SHARE).
+// One workgroup (256 threads, 16 per row) per block of UA_R rows.  The rows
+// must lie in one batch entry, each ascending over its valid entries (in
+// [0, L)) followed only by -1.  Their union is built window by window
+// (UA_WIN positions: per-row membership bitmaps, then the window's union in
+// ascending order with a 16-bit row mask per position) into the block's list
+// of UA_UCAP slots (lpos, lmask).  flag[block] = the union's size if the
+// block takes the union path -- at most UA_UCAP positions, each selected
+// UA_SHARE x G / 8 times on average (sum of n_r >= that x |U|) -- else 0.
 __global__ __launch_bounds__(256) void k_union_plan(const int32_t* __restrict__ idx, int64_t rows, int Lq,
-                                                    int kk, int64_t L, int G, int32_t* __restrict__ flag) {
-  __shared__ uint32_t bm[1024];  // one 32768-position window
-  __shared__ int32_t s_n[UA_R];
-  __shared__ uint32_t s_bad, s_u;
+                                                    int kk, int64_t L, int G, int32_t* __restrict__ flag,
+                                                    int32_t* __restrict__ lpos, uint16_t* __restrict__ lmask) {
+  constexpr int NT = 256, RT = NT / UA_R;                 // 16 threads per row
+  constexpr int BPT = 32, NPASS = UA_WIN / (NT * BPT);    // union bits per thread and pass
+  __shared__ __attribute__((aligned(16))) uint32_t mem[UA_R][UA_WIN / 32];
+  __shared__ int32_t s_n[UA_R], s_cur[UA_R];
+  __shared__ uint32_t s_bad;
+  __shared__ int32_t s_pmax;
+  __shared__ uint32_t scan[NT / 64 + 2];
   const int64_t blk = blockIdx.x;
   const int64_t r0 = blk * UA_R;
-  const int rr = threadIdx.x >> 4, t = threadIdx.x & 15;
+  const int rr = threadIdx.x / RT, t = threadIdx.x % RT;
+  const int gsh = (threadIdx.x & 63) / RT * RT;  // the row's first lane in its wave
+  const uint64_t gm = ((1ull << RT) - 1ull) << gsh;
   if (threadIdx.x == 0) {
     s_bad = (r0 + UA_R > rows || r0 / Lq != (r0 + UA_R - 1) / Lq) ? 1u : 0u;
-    s_u = 0u;
+    s_pmax = -1;
   }
   __syncthreads();
   if (s_bad) {
@@ -734,58 +755,122 @@ __global__ __launch_bounds__(256) void k_union_plan(const int32_t* __restrict__ 
     return;
   }
   const int32_t* ix = idx + (r0 + rr) * kk;
+  // shape and length of each row, UA_LD entries per thread and round
   bool bad = false;
   int n = 0, pmax = -1;
-  for (int e = t; e < kk; e += 16) {
-    const int p = ix[e];
-    const int prv = e > 0 ? ix[e - 1] : -2;
-    bool ok;
-    if (prv == -2) ok = p == -1 || (p >= 0 && (int64_t)p < L);
-    else if (prv == -1) ok = p == -1;
-    else ok = p == -1 || (p > prv && (int64_t)p < L);
-    bad = bad || !ok;
-    n += p >= 0 ? 1 : 0;
-    pmax = max(pmax, p);
+  for (int e0 = 0; e0 < kk; e0 += RT * UA_LD) {
+    int pv[UA_LD], pr[UA_LD];
+#pragma unroll
+    for (int j = 0; j < UA_LD; ++j) {
+      const int e = e0 + t + RT * j;
+      pv[j] = e < kk ? ix[e] : -1;
+      pr[j] = e == 0 ? -2 : (e < kk ? ix[e - 1] : -1);
+    }
+#pragma unroll
+    for (int j = 0; j < UA_LD; ++j) {
+      const int p = pv[j], prv = pr[j];
+      bool ok;
+      if (prv == -2) ok = p == -1 || (p >= 0 && (int64_t)p < L);
+      else if (prv == -1) ok = p == -1;
+      else ok = p == -1 || (p > prv && (int64_t)p < L);
+      bad = bad || !ok;
+      n += p >= 0 ? 1 : 0;
+      pmax = max(pmax, p);
+    }
   }
 #pragma unroll
-  for (int d = 1; d < 16; d <<= 1) {
+  for (int d = 1; d < RT; d <<= 1) {
     n += __shfl_xor(n, d, 64);
     pmax = max(pmax, __shfl_xor(pmax, d, 64));
     bad = bad || __shfl_xor((int)bad, d, 64);
   }
   if (t == 0) {
     s_n[rr] = n;
+    s_cur[rr] = 0;
     if (bad) atomicOr(&s_bad, 1u);
+    atomicMax(&s_pmax, pmax);
   }
-  __shared__ int32_t s_pmax;
-  if (threadIdx.x == 0) s_pmax = -1;
   __syncthreads();
-  if (t == 0) atomicMax(&s_pmax, pmax);
-  __syncthreads();
-  if (s_bad) {
+  int64_t sum_n = 0;
+#pragma unroll
+  for (int r = 0; r < UA_R; ++r) sum_n += s_n[r];
+  // the largest union the block may take the path with
+  const int64_t lim = min((int64_t)UA_UCAP, sum_n * 8 / ((int64_t)UA_SHARE * G));
+  if (s_bad || lim <= 0) {
     if (threadIdx.x == 0) flag[blk] = 0;
     return;
   }
-  const int nr = s_n[rr];
-  for (int w0 = 0; w0 <= s_pmax; w0 += 32768) {
-    for (int i = threadIdx.x; i < 1024; i += 256) bm[i] = 0u;
+  const int plast = s_pmax;
+  int32_t* lp = lpos + blk * UA_UCAP;
+  uint16_t* lm = lmask + blk * UA_UCAP;
+  uint32_t ucount = 0;  // union entries so far (block-uniform)
+  for (int p0 = 0; p0 <= plast; p0 += UA_WIN) {
+    for (int i = threadIdx.x; i < UA_R * (UA_WIN / 128); i += NT)
+      reinterpret_cast<uint4*>(&mem[0][0])[i] = uint4{0u, 0u, 0u, 0u};
     __syncthreads();
-    for (int e = t; e < nr; e += 16) {
-      const int p = ix[e] - w0;
-      if (p >= 0 && p < 32768) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    {
+      const int nr = s_n[rr];
+      int c0 = s_cur[rr];
+      int taken = 0;
+      bool more = true;
+      while (more) {
+        // UA_LD entries per thread per round, all loads issued before any is used
+        int pv[UA_LD];
+#pragma unroll
+        for (int j = 0; j < UA_LD; ++j) {
+          const int e = c0 + t + j * RT;
+          pv[j] = e < nr ? ix[e] : INT32_MAX;
+        }
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < UA_LD; ++j) {
+          const int p = pv[j];
+          const bool in = p < p0 + UA_WIN;
+          if (in) atomicOr(&mem[rr][(p - p0) >> 5], 1u << ((p - p0) & 31));
+          // entries are ascending: the run in the window is a prefix
+          cnt += (uint32_t)__popcll(__ballot(in) & gm);
+        }
+        taken += (int)cnt;
+        more = cnt == (uint32_t)(RT * UA_LD);
+        c0 += RT * UA_LD;
+      }
+      __syncthreads();
+      if (t == 0) s_cur[rr] += taken;
     }
     __syncthreads();
-    uint32_t c = 0;
-    for (int i = threadIdx.x; i < 1024; i += 256) c += __popc(bm[i]);
-    c = wave_sum(c);
-    if ((threadIdx.x & 63) == 0) atomicAdd(&s_u, c);
-    __syncthreads();
+    // the window's union appended in ascending order, BPT bits per thread
+    // and pass
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+      const int wd = pass * NT + (int)threadIdx.x;
+      uint32_t rw[UA_R], ubits = 0;
+#pragma unroll
+      for (int r = 0; r < UA_R; ++r) {
+        rw[r] = mem[r][wd];
+        ubits |= rw[r];
+      }
+      uint32_t nu;
+      uint32_t o2 = ucount + block_excl_scan<NT>(__popc(ubits), scan, nu);
+      if (ucount + nu > (uint64_t)lim) {  // uniform: too large a union
+        if (threadIdx.x == 0) flag[blk] = 0;
+        return;
+      }
+      uint32_t x = ubits;
+      while (x) {
+        const int bbit = __ffs(x) - 1;
+        x &= x - 1;
+        uint32_t msk = 0;
+#pragma unroll
+        for (int r = 0; r < UA_R; ++r) msk |= ((rw[r] >> bbit) & 1u) << r;
+        lp[o2] = p0 + wd * 32 + bbit;
+        lm[o2] = (uint16_t)msk;
+        ++o2;
+      }
+      ucount += nu;
+    }
+    __syncthreads();  // the bitmaps are read before the next window clears them
   }
-  if (threadIdx.x == 0) {
-    int64_t sum_n = 0;
-    for (int r = 0; r < UA_R; ++r) sum_n += s_n[r];
-    flag[blk] = (sum_n > 0 && s_u <= (uint32_t)UA_UCAP && (int64_t)s_u * UA_SHARE * G <= sum_n * 8) ? 1 : 0;
-  }
+  if (threadIdx.x == 0) flag[blk] = (int32_t)ucount;
 }
 
 // P^T V^T product of one half (two 16-token blocks) of a landed V tile.
@@ -843,12 +928,13 @@ LCT_DEV void ua_pv_half(const char (&vh)[2][4][1024], const AttnLanes& a, const 
 
 // Online-softmax attention of one wave's 16 columns over one landed chunk of
 // 64 union positions (base: the chunk's first union slot): S^T = K Q^T from
-// the swizzled K tile, the membership mask of each column's row, weights,
-// O^T += V^T P^T.
+// the swizzled K tile, the membership mask of each column's row (wrm: the
+// wave's row bits in both 16-bit halves), weights, O^T += V^T P^T.
+constexpr float UA_MSLACK = 8.f;  // log2 of the largest weight before a rescale
 LCT_DEV void ua_chunk(int base, const char (&kt)[UA_CH * 256], const char (&va)[2][4][1024],
                       const char (&vb)[2][4][1024], const uint16_t* umask, const AttnLanes& a,
-                      const bf16x8 (&qf)[4], int rbit, float scale_log2, float& m, floatx4& lacc,
-                      floatx4 (&o)[ATT_D / 16]) {
+                      const bf16x8 (&qf)[4], int rbit, uint32_t wrm, float scale_log2, float& m,
+                      floatx4& lacc, floatx4 (&o)[ATT_D / 16]) {
   constexpr int D = ATT_D;
   const int hl = a.hl, kg = a.kg;
   // K: lane (hl, kg) reads 16-byte chunk st*4 + kg of token 16j + hl, stored
@@ -905,42 +991,57 @@ LCT_DEV void ua_chunk(int base, const char (&kt)[UA_CH * 256], const char (&va)[
                                                           sacc[j], 0, 0, 0);
     }
   }
-  // membership of this lane's tokens 16j + 4kg + e for its column's row
-  uint32_t mk[4];
+  // membership of this lane's tokens 16j + 4kg + e (masks of tokens e = 0..3
+  // in the halves of w2[j]) for its column's row; scores of other tokens
+  // drop to -inf.  A chunk that every row of the wave takes whole skips the
+  // per-token test (wave-uniform).
+  uint2 w2[4];
+  bool whole = true;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int t0 = base + 16 * j + 4 * kg;
-    const uint2 w2 = *reinterpret_cast<const uint2*>(&umask[t0]);  // 4 masks (padding: 0)
-    const uint32_t ms[4] = {w2.x & 0xFFFFu, w2.x >> 16, w2.y & 0xFFFFu, w2.y >> 16};
-    uint32_t bits = 0;
+    w2[j] = *reinterpret_cast<const uint2*>(&umask[base + 16 * j + 4 * kg]);  // padding: 0
+    whole = whole && (w2[j].x & wrm) == wrm && (w2[j].y & wrm) == wrm;
+  }
+  float sm[4][4];
+  if (__ballot(!whole) == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bits |= ((ms[e] >> rbit) & 1u) << (4 * e);
-    mk[j] = bits;
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm[j][e] = sacc[j][e];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = e < 2 ? w2[j].x : w2[j].y;
+        sm[j][e] = ((w >> (rbit + 16 * (e & 1))) & 1u) ? sacc[j][e] : -INFINITY;
+      }
   }
   float tmax = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, ((mk[j] >> (4 * e)) & 1) ? sacc[j][e] : -INFINITY);
+    for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sm[j][e]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-  const float mnew = fmaxf(m, tmax * scale_log2);
-  const float mref = mnew == -INFINITY ? 0.f : mnew;
-  const float alpha = __builtin_amdgcn_exp2f(m - mref);
-  m = mnew;
+  const float tm = tmax * scale_log2;
+  // The reference max m moves (and O, l are rescaled) only when a column's
+  // scores pass it by more than UA_MSLACK: the weights stay below
+  // 2^UA_MSLACK, and numerator and denominator share the reference.
+  if (__ballot(tm > m + UA_MSLACK) != 0) {
+    const float mnew = fmaxf(m, tm);
+    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
+    lacc = lacc * alpha;
+    m = mnew;
+  }
+  const float mref = m == -INFINITY ? 0.f : m;
   __bf16 pw[4][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float w = __builtin_amdgcn_exp2f(fmaf(sacc[j][e], scale_log2, -mref));
-      pw[j][e] = (__bf16)(((mk[j] >> (4 * e)) & 1) ? w : 0.f);
-    }
-  if (__ballot(alpha != 1.f) != 0) {
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] = o[dt] * alpha;
-    lacc = lacc * alpha;
-  }
+    for (int e = 0; e < 4; ++e) pw[j][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sm[j][e], scale_log2, -mref));
   ua_pv_half(va, a, pw, 0, o, lacc);
   ua_pv_half(vb, a, pw, 1, o, lacc);
 }
@@ -962,23 +1063,20 @@ LCT_DEV void ua_chunk(int base, const char (&kt)[UA_CH * 256], const char (&va)[
 template <int G>
 __global__ __launch_bounds__(G * 64) void k_union_attn(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ flag, float* __restrict__ out, int Lq,
-    int Hq, int Hkv, int64_t L, int kk, float scale_log2) {
+    const int32_t* __restrict__ flag, const int32_t* __restrict__ lpos, const uint16_t* __restrict__ lmask,
+    float* __restrict__ out, int Lq, int Hq, int Hkv, int64_t L, float scale_log2) {
   constexpr int D = ATT_D;
   constexpr int NT = G * 64;
   constexpr int RW = UA_R / G;  // rows per wave
   static_assert(G >= 4 && G <= 16 && UA_R % G == 0, "union path for 4 to 16 heads per KV head");
-  static_assert(UA_R * (UA_WIN / 32) * 4 <= UA_SET, "membership bitmaps fit one staging buffer");
   static_assert(UA_UCAP % UA_CH == 0, "the last chunk's padding stays in the list");
   __shared__ int32_t upos[UA_UCAP];
   __shared__ __attribute__((aligned(8))) uint16_t umask[UA_UCAP];
   __shared__ __attribute__((aligned(16))) char stage[UA_NBUF][UA_SET];
-  __shared__ int32_t cur[UA_R], nrow[UA_R], plst[UA_R];
-  __shared__ uint32_t scan[NT / 64 + 2];
-  uint32_t (*mem)[UA_WIN / 32] = reinterpret_cast<uint32_t (*)[UA_WIN / 32]>(&stage[0][0]);
   const int64_t blk = blockIdx.x / Hkv;
   const int kvh = (int)(blockIdx.x % Hkv);
-  if (flag[blk] == 0) return;  // uniform: the segment path takes this block
+  const int nu = min(flag[blk], UA_UCAP);
+  if (nu <= 0) return;  // uniform: the segment path takes this block
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int64_t r0 = blk * UA_R;
   const int64_t b = r0 / Lq;
@@ -986,6 +1084,7 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
   const AttnLanes a = attn_lanes(lane);
   // this wave's columns: row r0 + wid*RW + hl / G, head kvh*G + hl % G
   const int rbit = wid * RW + hl / G;
+  const uint32_t wrm = (((1u << RW) - 1u) << (wid * RW)) * 0x10001u;
   bf16x8 qf[4];
   {
     const int64_t row = r0 + rbit;
@@ -993,118 +1092,17 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
 #pragma unroll
     for (int st = 0; st < 4; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qp + st * 32);
   }
-  // row lengths (valid entries: ascending, then -1), cursors and last
-  // positions: RT threads per row narrow the first -1 down together, RT
-  // probes per round
-  constexpr int RT = NT / UA_R;  // threads per row (a power of two, 16 to 64)
-  const int rr = threadIdx.x / RT, t = threadIdx.x % RT;
-  const int gsh = (threadIdx.x & 63) / RT * RT;  // the row's first lane in its wave
-  const uint64_t gm = RT >= 64 ? ~0ull : (((1ull << RT) - 1ull) << gsh);
-  {
-    const int32_t* ix = idx + (r0 + rr) * kk;
-    int lo = 0, hi = kk;  // the first -1 (kk: none) lies in [lo, hi]
-    while (lo < hi) {
-      const int step = (hi - lo + RT - 1) / RT;
-      const int pr = lo + t * step;
-      const bool neg = pr >= hi || ix[pr] < 0;
-      const uint64_t bl = (__ballot(neg) & gm) >> gsh;
-      if (bl == 0) {
-        lo += (RT - 1) * step + 1;  // past the last probe, which is < hi
-      } else {
-        const int f = __ffsll((unsigned long long)bl) - 1;
-        if (f == 0) {
-          hi = lo;
-        } else {
-          hi = min(hi, lo + f * step);
-          lo += (f - 1) * step + 1;
-        }
-      }
-    }
-    if (t == 0) {
-      nrow[rr] = lo;
-      cur[rr] = 0;
-      plst[rr] = lo > 0 ? ix[lo - 1] : -1;
-    }
-  }
-  __syncthreads();
-  int plast = -1;
-#pragma unroll
-  for (int r = 0; r < UA_R; ++r) plast = max(plast, plst[r]);
-
-  // ---- phase 1: the union, window by window
-  constexpr int BPT = UA_WIN / NT < 32 ? UA_WIN / NT : 32;  // union bits per thread and pass
-  constexpr int NPASS = UA_WIN / (NT * BPT);           // passes over the window's bitmap
-  uint32_t ucount = 0;                                 // union entries so far (block-uniform)
-  for (int p0 = 0; p0 <= plast; p0 += UA_WIN) {
-    for (int i = threadIdx.x; i < UA_R * (UA_WIN / 32); i += NT) (&mem[0][0])[i] = 0u;
-    __syncthreads();
-    {
-      const int32_t* ix = idx + (r0 + rr) * kk;
-      const int n = nrow[rr];
-      int c0 = cur[rr];
-      int taken = 0;
-      bool more = true;
-      while (more) {
-        // UA_LD entries per thread per round, all loads issued before any is used
-        int pv[UA_LD];
-#pragma unroll
-        for (int j = 0; j < UA_LD; ++j) {
-          const int e = c0 + t + j * RT;
-          pv[j] = e < n ? ix[e] : INT32_MAX;
-        }
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int j = 0; j < UA_LD; ++j) {
-          const int p = pv[j];
-          const bool in = p < p0 + UA_WIN;
-          if (in) atomicOr(&mem[rr][(p - p0) >> 5], 1u << ((p - p0) & 31));
-          // entries are ascending: the run in the window is a prefix
-          cnt += (uint32_t)__popcll(__ballot(in) & gm);
-        }
-        taken += (int)cnt;
-        more = cnt == (uint32_t)(RT * UA_LD);
-        c0 += RT * UA_LD;
-      }
-      __syncthreads();
-      if (t == 0) cur[rr] += taken;
-    }
-    __syncthreads();
-    // the window's union appended in ascending order, BPT bits per thread
-    // and pass
-#pragma unroll
-    for (int pass = 0; pass < NPASS; ++pass) {
-      const int bit0 = (pass * NT + (int)threadIdx.x) * BPT;
-      const int wd = bit0 >> 5, sh = bit0 & 31;
-      uint32_t rw[UA_R], ubits = 0;
-#pragma unroll
-      for (int r = 0; r < UA_R; ++r) {
-        rw[r] = mem[r][wd] >> sh;
-        ubits |= rw[r];
-      }
-      if (BPT < 32) ubits &= (1u << BPT) - 1u;
-      uint32_t nu;
-      uint32_t o2 = ucount + block_excl_scan<NT>(__popc(ubits), scan, nu);
-      uint32_t x = ubits;
-      while (x) {
-        const int bbit = __ffs(x) - 1;
-        x &= x - 1;
-        uint32_t msk = 0;
-#pragma unroll
-        for (int r = 0; r < UA_R; ++r) msk |= ((rw[r] >> bbit) & 1u) << r;
-        if (o2 < (uint32_t)UA_UCAP) {  // the plan admits no larger union
-          upos[o2] = p0 + bit0 + bbit;
-          umask[o2] = (uint16_t)msk;
-        }
-        ++o2;
-      }
-      ucount += nu;
-    }
-    __syncthreads();  // the bitmaps are read before the next window clears them
-  }
-  const int nu = (int)min(ucount, (uint32_t)UA_UCAP);
-  // padding of the last chunk: no row takes it
+  // ---- the block's union list (k_union_plan), padded to whole chunks with
+  // masks no row takes
   const int nch = (nu + UA_CH - 1) / UA_CH;
-  for (int i = nu + (int)threadIdx.x; i < nch * UA_CH; i += NT) umask[i] = 0;
+  {
+    const int32_t* lp = lpos + blk * UA_UCAP;
+    const uint16_t* lm = lmask + blk * UA_UCAP;
+    for (int i = threadIdx.x; i < nch * UA_CH; i += NT) {
+      upos[i] = i < nu ? lp[i] : 0;
+      umask[i] = i < nu ? lm[i] : (uint16_t)0;
+    }
+  }
   __syncthreads();
 
   // ---- phase 2: the chunks, UA_NBUF - 1 in flight
@@ -1172,7 +1170,7 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
     ua_barrier();
     if (c + UA_NBUF - 1 < nch) issue(c + UA_NBUF - 1);
     const int sb = c % UA_NBUF;
-    ua_chunk(c * UA_CH, kt_of(sb), va_of(sb), vb_of(sb), umask, a, qf, rbit, scale_log2, m, lacc, o);
+    ua_chunk(c * UA_CH, kt_of(sb), va_of(sb), vb_of(sb), umask, a, qf, rbit, wrm, scale_log2, m, lacc, o);
   }
   // o[dt][e] = O^T[d = 16dt + 4kg + e][column hl]; every row of lacc holds
   // the column's denominator
@@ -1195,15 +1193,20 @@ static hipError_t launch_sparse_attn_seg(const uint16_t* q, const uint16_t* k, c
   int32_t* uflag = plan.ua_blocks > 0 ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + attn_ua_offset(plan))
                                       : nullptr;
   const int64_t nblk = plan.ua_blocks;
+  int32_t* lpos = plan.ua_blocks > 0 ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + attn_ul_offset(plan))
+                                      : nullptr;
+  uint16_t* lmask = plan.ua_blocks > 0 ? reinterpret_cast<uint16_t*>(lpos + plan.ua_blocks * UA_UCAP) : nullptr;
+  if (nblk > 0) k_union_plan<<<dim3((unsigned)nblk), 256, 0, st>>>(idx, rows, Lq, kk, L, G, uflag, lpos, lmask);
   k_seg_bounds<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(idx, bnd, rows, kk, L, plan.seg_shift,
-                                                                  plan.nseg);
+                                                                  plan.nseg, uflag, nblk);
   if (nblk > 0) {
-    k_union_plan<<<dim3((unsigned)nblk), 256, 0, st>>>(idx, rows, Lq, kk, L, G, uflag);
     const dim3 ug((unsigned)(nblk * Hkv));
     switch (G) {
-      case 4: k_union_attn<4><<<ug, 4 * 64, 0, st>>>(q, k, v, idx, uflag, out, Lq, Hq, Hkv, L, kk, sl2); break;
-      case 8: k_union_attn<8><<<ug, 8 * 64, 0, st>>>(q, k, v, idx, uflag, out, Lq, Hq, Hkv, L, kk, sl2); break;
-      case 16: k_union_attn<16><<<ug, 16 * 64, 0, st>>>(q, k, v, idx, uflag, out, Lq, Hq, Hkv, L, kk, sl2); break;
+      case 4: k_union_attn<4><<<ug, 4 * 64, 0, st>>>(q, k, v, uflag, lpos, lmask, out, Lq, Hq, Hkv, L, sl2); break;
+      case 8: k_union_attn<8><<<ug, 8 * 64, 0, st>>>(q, k, v, uflag, lpos, lmask, out, Lq, Hq, Hkv, L, sl2); break;
+      case 16:
+        k_union_attn<16><<<ug, 16 * 64, 0, st>>>(q, k, v, uflag, lpos, lmask, out, Lq, Hq, Hkv, L, sl2);
+        break;
       default: return hipErrorInvalidValue;
     }
   }

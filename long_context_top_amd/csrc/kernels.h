@@ -86,14 +86,20 @@ struct AttnPlan {
   int seg_shift;
   size_t bnd_bytes;  // segmented path: per-row segment bounds after the partials
   int64_t ua_blocks;  // segmented path: row blocks that may take the block-union path
-                      // (an int32 flag each, after the bounds)
+                      // (an int32 flag each after the bounds, then each block's
+                      // union list: UA_UCAP int32 positions, then UA_UCAP uint16
+                      // row masks per block)
 };
+constexpr int UA_UCAP = 4096;  // largest union (positions) of a block on the block-union path
 AttnPlan attn_plan(int B, int Lq, int Hq, int Hkv, int kk, int64_t L);
 inline size_t attn_bnd_offset(const AttnPlan& p) { return (p.part_bytes + 255) / 256 * 256; }
 inline size_t attn_ua_offset(const AttnPlan& p) { return (attn_bnd_offset(p) + p.bnd_bytes + 255) / 256 * 256; }
+inline size_t attn_ul_offset(const AttnPlan& p) {
+  return (attn_ua_offset(p) + (size_t)p.ua_blocks * sizeof(int32_t) + 255) / 256 * 256;
+}
 inline size_t attn_ws_bytes(const AttnPlan& p) {
   if (p.nseg == 0) return p.part_bytes;
-  return p.ua_blocks > 0 ? attn_ua_offset(p) + (size_t)p.ua_blocks * sizeof(int32_t)
+  return p.ua_blocks > 0 ? attn_ul_offset(p) + (size_t)p.ua_blocks * UA_UCAP * (sizeof(int32_t) + sizeof(uint16_t))
                          : attn_bnd_offset(p) + p.bnd_bytes;
 }
 // With plan.splits > 1 the kernel writes (O, m, l) partials and a merge

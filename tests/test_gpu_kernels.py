@@ -311,9 +311,16 @@ def _gsa_inputs(cfg, gist_vals=None):
                 rv=C.make(cfg, cfg.rv_spec()))
 
 
+def _union_sizes(idx):
+    """Size of the union of the valid positions of each block of 16 rows."""
+    rows = idx.reshape(-1, idx.shape[-1])
+    return np.array([np.unique(rows[b:b + 16][rows[b:b + 16] >= 0]).size for b in range(0, rows.shape[0], 16)])
+
+
 def _union_flags(ws, B, Lq, Hq, Hkv, L, kk):
     """The block-union decisions the last call left in its workspace (int32
-    per block of 16 rows, after the segment partials and bounds)."""
+    per block of 16 rows, after the segment partials and bounds): the union's
+    size for a block on the union path, else 0."""
     G = Hq // Hkv
     shift = 14
     while ((L - 1) >> shift) + 1 > 64:
@@ -372,7 +379,9 @@ def test_sparse_attn_block_union_path(Hq, Hkv):
     got = host(lct.sparse_attn_gather(q, k, v, dev_i32(idx), scale, ws=ws))
     flags = _union_flags(ws, B, Lq, Hq, Hkv, L, kk)
     kinds = np.array(kinds)
-    assert np.all(flags[kinds == 0] == 1) and np.all(flags[kinds == 1] == 1) and np.all(flags[kinds == 5] == 1)
+    usz = _union_sizes(idx)
+    for kd in (0, 1, 5):
+        assert np.array_equal(flags[kinds == kd], usz[kinds == kd]), kd
     assert np.all(flags[kinds == 4] == 0)          # a row that is not ascending
     if Hq // Hkv == 8:  # independent sets: twice the per-row MFMA columns at least
         assert np.all(flags[kinds == 3] == 0)
@@ -421,7 +430,8 @@ def test_sparse_attn_block_union_large_unions(Hq, Hkv):
     ws = lct.Workspace()
     got = host(lct.sparse_attn_gather(q, k, v, dev_i32(idx), scale, ws=ws))
     flags = _union_flags(ws, B, Lq, Hq, Hkv, L, kk)
-    assert np.all(flags[kinds == 0] == 1) and np.all(flags[kinds == 1] == 1)
+    usz = _union_sizes(idx)
+    assert np.array_equal(flags[kinds == 0], usz[kinds == 0]) and np.all(flags[kinds == 1] == 4096)
     assert np.all(flags[kinds == 2] == 0) and np.all(flags[kinds == 3] == 0)
     rows = [j for j in range(Lq) if j // 16 < 64 or j % 37 == 0]
     worst = 0.0
