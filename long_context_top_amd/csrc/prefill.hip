@@ -32,7 +32,7 @@
 // Rows the lists cannot settle (a ring or list overflow, a crowded bin,
 // fewer than k candidates) are listed and recomputed by the plain path.
 //
-// k_pf_filter waves: 0..7 compute (rows 64*(w&1).., keys 16*(w>>1).. of
+// k_pf_filter waves: 0..7 compute (rows 32*(w%4).., keys 32*(w/4).. of
 // each 64-key tile); wave 8 keeps three key tiles in flight by LDS DMA;
 // wave 9 flushes the candidate rings.  The compute waves issue no global
 // memory operation inside a sweep.  Scores start from -t_r in the MFMA
@@ -55,11 +55,16 @@ constexpr int PF_HD = 256;                 // indexer features per row (int8)
 constexpr int PF_KS = PF_HD / 64;          // 64-byte MFMA k-steps per row
 constexpr int PF_RB = 128;                 // query rows per block
 constexpr int PF_TK = 64;                  // keys per tile
-constexpr int PF_KL = PF_TK / 64;          // 16-key blocks per compute wave and tile
 constexpr int PF_NBUF = 4;                 // key-tile buffers: 3 tiles in flight
 constexpr int PF_SS = 16;                  // sample stride (positions)
 constexpr int PF_NBIN = 128;               // histogram bins
 constexpr int PF_CW = 8;                   // compute waves
+constexpr int PF_QB = 2;                   // 16-row blocks per compute wave
+constexpr int PF_WROWS = 16 * PF_QB;       // rows per compute wave
+constexpr int PF_WR = PF_RB / PF_WROWS;    // row groups
+constexpr int PF_KL = PF_TK * PF_WR / (16 * PF_CW);  // 16-key blocks per compute wave and tile
+static_assert(PF_WR * PF_WROWS == PF_RB && PF_CW % PF_WR == 0 && PF_KL * 16 * (PF_CW / PF_WR) == PF_TK,
+              "compute waves tile the block's rows x the tile's keys");
 constexpr int PF_DMA_W = PF_CW;            // the DMA wave
 constexpr int PF_FL_W = PF_CW + 1;         // the flush wave
 constexpr int PF_NT = (PF_CW + 2) * 64;
@@ -165,10 +170,10 @@ LCT_DEV void pf_sweep(PfShared& sh, __amdgpu_buffer_rsrc_t krs, int n_tiles, int
 
 // acc[qb][kl] = ini[qb] + scores of query rows 16qb + n (of the wave's 64)
 // against keys PF_KL*16 wk + 16kl + 4g + e of the tile, e = vector element.
-LCT_DEV void pf_tile_mfma(const char (&buf)[PF_CHUNKS][1024], const intx4 (&qf)[4][PF_KS], int wk,
-                          int lane, const int32_t (&ini)[4], intx4 (&acc)[4][PF_KL]) {
+LCT_DEV void pf_tile_mfma(const char (&buf)[PF_CHUNKS][1024], const intx4 (&qf)[PF_QB][PF_KS], int wk,
+                          int lane, const int32_t (&ini)[PF_QB], intx4 (&acc)[PF_QB][PF_KL]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < PF_QB; ++i)
 #pragma unroll
     for (int j = 0; j < PF_KL; ++j) acc[i][j] = intx4{ini[i], ini[i], ini[i], ini[i]};
 #pragma unroll
@@ -177,7 +182,7 @@ LCT_DEV void pf_tile_mfma(const char (&buf)[PF_CHUNKS][1024], const intx4 (&qf)[
     for (int ks = 0; ks < PF_KS; ++ks) {
       const intx4 a = *reinterpret_cast<const intx4*>(&buf[(wk * PF_KL + kl) * PF_KS + ks][lane * 16]);
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+      for (int qb = 0; qb < PF_QB; ++qb)
         acc[qb][kl] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qf[qb][ks], acc[qb][kl], 0, 0, 0);
     }
   }
@@ -242,11 +247,11 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
   PfShared sh{kt0, kt1, kt2, kt3, hist, smax, smin, basev, thdv, scnt};
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int n = lane & 15, g = lane >> 4;
-  const int wq = wid & 1, wk = wid >> 1;  // compute waves: row half, key quarter
+  const int wq = wid % PF_WR, wk = wid / PF_WR;  // compute waves: row group, key part
   const int NB = (L + PF_RB - 1) / PF_RB;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k, (int64_t)L * PF_HD);
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(list, (int64_t)L * PF_CROW * 4);
-  const int32_t zero[4] = {0, 0, 0, 0};
+  const int32_t zero[PF_QB] = {};
   auto no_aux = [](int) {};
 
   // The long block first, its sweeps ascending; then the short one, its
@@ -262,12 +267,12 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
     const int r_last = (r0 + PF_RB < L ? r0 + PF_RB : L) - 1;
     if (r_last < r_all) continue;  // shorter rows: every earlier position, or the plain path
 
-    // ---- query fragments (compute waves): rows r0 + 64wq + 16qb + n
-    intx4 qf[4][PF_KS];
+    // ---- query fragments (compute waves): rows r0 + PF_WROWS wq + 16qb + n
+    intx4 qf[PF_QB][PF_KS];
     if (wid < PF_CW) {
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const int row = r0 + wq * 64 + qb * 16 + n;
+      for (int qb = 0; qb < PF_QB; ++qb) {
+        const int row = r0 + wq * PF_WROWS + qb * 16 + n;
 #pragma unroll
         for (int ks = 0; ks < PF_KS; ++ks)
           qf[qb][ks] = row <= r_last ? *reinterpret_cast<const intx4*>(
@@ -288,19 +293,19 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
     const int n_samp = r_last / PF_SS + 1;  // sampled keys j: position 16 j <= r_last
     const int st_tiles = (n_samp + PF_TK - 1) / PF_TK;
     {
-      int32_t mx[4], mn[4];
+      int32_t mx[PF_QB], mn[PF_QB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < PF_QB; ++i) {
         mx[i] = INT32_MIN;
         mn[i] = INT32_MAX;
       }
       pf_sweep(sh, krs, st_tiles, PF_SS, desc, wid, lane, [&](int t, int, auto& buf) {
-        intx4 acc[4][PF_KL];
+        intx4 acc[PF_QB][PF_KL];
         pf_tile_mfma(buf, qf, wk, lane, zero, acc);
         const bool diag = (t * PF_TK + PF_TK - 1) * PF_SS > r0;  // a sample past some row
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const int row = r0 + wq * 64 + qb * 16 + n;
+        for (int qb = 0; qb < PF_QB; ++qb) {
+          const int row = r0 + wq * PF_WROWS + qb * 16 + n;
 #pragma unroll
           for (int kl = 0; kl < PF_KL; ++kl)
 #pragma unroll
@@ -315,14 +320,14 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
       }, no_aux);
       if (wid < PF_CW) {
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
+        for (int qb = 0; qb < PF_QB; ++qb) {
           int32_t a = mx[qb], b = mn[qb];
           a = max(a, __shfl_xor(a, 16, 64));
           a = max(a, __shfl_xor(a, 32, 64));
           b = min(b, __shfl_xor(b, 16, 64));
           b = min(b, __shfl_xor(b, 32, 64));
           if (g == 0) {
-            const int rl = wq * 64 + qb * 16 + n;
+            const int rl = wq * PF_WROWS + qb * 16 + n;
             atomicMax(&sh.smax[rl], a);
             atomicMin(&sh.smin[rl], b);
           }
@@ -332,22 +337,22 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
     }
     // ---- S2: 128-bin histogram of the sampled scores over [min, max]
     {
-      int32_t lo[4];
-      uint32_t M[4];
+      int32_t lo[PF_QB];
+      uint32_t M[PF_QB];
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const int rl = wq * 64 + qb * 16 + n;
+      for (int qb = 0; qb < PF_QB; ++qb) {
+        const int rl = wq * PF_WROWS + qb * 16 + n;
         lo[qb] = sh.smin[rl];
         const uint32_t span = (uint32_t)(sh.smax[rl] - lo[qb]) + 1u;
         M[qb] = span == 0u ? 1u : ((1u << 23) - 1u) / span;
       }
       pf_sweep(sh, krs, st_tiles, PF_SS, desc, wid, lane, [&](int t, int, auto& buf) {
-        intx4 acc[4][PF_KL];
+        intx4 acc[PF_QB][PF_KL];
         pf_tile_mfma(buf, qf, wk, lane, zero, acc);
         const bool diag = (t * PF_TK + PF_TK - 1) * PF_SS > r0;
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const int rl = wq * 64 + qb * 16 + n;
+        for (int qb = 0; qb < PF_QB; ++qb) {
+          const int rl = wq * PF_WROWS + qb * 16 + n;
           const int row = r0 + rl;
 #pragma unroll
           for (int kl = 0; kl < PF_KL; ++kl)
@@ -448,25 +453,25 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
     };
     int m_tiles;
     {
-      int32_t ini[4], thd[4];
-      uint32_t base[4];  // candidates of the row before the current step
+      int32_t ini[PF_QB], thd[PF_QB];
+      uint32_t base[PF_QB];  // candidates of the row before the current step
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const int rl = wq * 64 + qb * 16 + n;
+      for (int qb = 0; qb < PF_QB; ++qb) {
+        const int rl = wq * PF_WROWS + qb * 16 + n;
         ini[qb] = -sh.base[rl];
         thd[qb] = sh.thd[rl];
         base[qb] = 0u;
       }
-      auto emit = [&](auto diag_c, int t, int ts, const intx4 (&acc)[4][PF_KL]) {
+      auto emit = [&](auto diag_c, int t, int ts, const intx4 (&acc)[PF_QB][PF_KL]) {
         constexpr bool DIAG = decltype(diag_c)::value;
         const int cs = ts % 3;
         // candidates of this lane per row: a bit per element, then one slot
         // reservation per row for all of them (the four reservations are
         // unconditional, so their LDS round trips overlap), then the writes
-        uint32_t bits[4], first[4];
+        uint32_t bits[PF_QB], first[PF_QB];
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const int rl = wq * 64 + qb * 16 + n;
+        for (int qb = 0; qb < PF_QB; ++qb) {
+          const int rl = wq * PF_WROWS + qb * 16 + n;
           uint32_t b = 0;
 #pragma unroll
           for (int kl = 0; kl < PF_KL; ++kl)
@@ -479,12 +484,12 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
           bits[qb] = b;
         }
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
-          first[qb] = base[qb] + atomicAdd(&sh.scnt[cs][wq * 64 + qb * 16 + n], (uint32_t)__popc(bits[qb]));
+        for (int qb = 0; qb < PF_QB; ++qb)
+          first[qb] = base[qb] + atomicAdd(&sh.scnt[cs][wq * PF_WROWS + qb * 16 + n], (uint32_t)__popc(bits[qb]));
         const uint32_t pos0 = (uint32_t)(t * PF_TK + wk * PF_KL * 16 + g * 4);
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const int rl = wq * 64 + qb * 16 + n;
+        for (int qb = 0; qb < PF_QB; ++qb) {
+          const int rl = wq * PF_WROWS + qb * 16 + n;
           uint32_t slot = first[qb];
 #pragma unroll
           for (int kl = 0; kl < PF_KL; ++kl)
@@ -499,10 +504,10 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
       };
       m_tiles = (r_last + 1 + PF_TK - 1) / PF_TK;
       pf_sweep(sh, krs, m_tiles, 1, desc, wid, lane, [&](int t, int ts, auto& buf) {
-        intx4 acc[4][PF_KL];
+        intx4 acc[PF_QB][PF_KL];
         if (ts > 0) {
 #pragma unroll
-          for (int qb = 0; qb < 4; ++qb) base[qb] += sh.scnt[(ts - 1) % 3][wq * 64 + qb * 16 + n];
+          for (int qb = 0; qb < PF_QB; ++qb) base[qb] += sh.scnt[(ts - 1) % 3][wq * PF_WROWS + qb * 16 + n];
         }
         pf_tile_mfma(buf, qf, wk, lane, ini, acc);
         if (t * PF_TK + PF_TK - 1 > r0) emit(std::true_type{}, t, ts, acc);
