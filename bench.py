@@ -603,17 +603,58 @@ def bench_prefill_indexer(cfg, steps, warmup, want_cpu=False, attention=True):
     del g
     if attention:
         attn = bench_prefill_attention(cfg, out, max(5, steps // 5), warmup)
-        # the whole prefill of the 28-layer stack: one index per group of layers,
-        # sparse attention in every layer
-        step_ms = cfg.n_groups * ms + cfg.n_layers * attn["ms_per_layer"]
-        res.update({"attention": attn, "prefill_ms_all_layers": step_ms,
-                    "prefill_tokens_per_s": cfg.L / (step_ms * 1e-3)})
+        res["attention"] = attn
     del qi, ki, out, ws
     torch.cuda.empty_cache()
+    if attention:
+        # the whole prefill of the 28-layer stack: one layer group through the
+        # driver (its index, then its layers' attention), times the groups
+        grp = bench_prefill_group(cfg, max(3, steps // 10), 1)
+        step_ms = cfg.n_groups * grp["ms_per_group"]
+        res.update({"group_run": grp, "prefill_ms_all_layers": step_ms,
+                    "prefill_tokens_per_s": cfg.L / (step_ms * 1e-3)})
     if want_cpu:
         log("timing the CPU oracle on sampled prefill rows ...")
         res["cpu_baseline"] = cpu_baseline_prefill(cfg)
     return res
+
+
+def bench_prefill_group(cfg, steps, warmup):
+    """One layer group of the causal prefill through the layer-group driver
+    (lct_group_run, causal): the group's index, then each of its layers'
+    sparse attention over that index (the Shared layers reuse the segment
+    bounds and block-union lists the first layer derived from it)."""
+    import torch
+
+    import long_context_top_amd as lct
+    import synth.device as sd
+
+    dev = torch.device("cuda", 0)
+    n = cfg.group
+    qi = [sd.make(cfg, cfg.qi_spec(0), dev)]
+    ki = [sd.make(cfg, cfg.ki_spec(0), dev)]
+    q = [sd.make(cfg, cfg.q_spec(l), dev) for l in range(n)]
+    k = [sd.make(cfg, cfg.k_spec(l), dev) for l in range(n)]
+    v = [sd.make(cfg, cfg.v_spec(l), dev) for l in range(n)]
+    out = [torch.empty((1, cfg.L, cfg.Hq, cfg.D), dtype=torch.float32, device=dev) for _ in range(n)]
+    run = lct.GroupRun(qi, ki, q, k, v, out, cfg.topk, cfg.group, cfg.scale, causal=True)
+    for _ in range(max(warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    del run, qi, ki, q, k, v, out
+    torch.cuda.empty_cache()
+    return {"ms_per_group": ms, "layers": n,
+            "timing": f"median of {steps} lct_group_run calls (causal: the index, then {n} layers)"}
 
 
 def bench_prefill_attention(cfg, idx, steps, warmup):

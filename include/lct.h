@@ -258,7 +258,10 @@ int lct_gsa_prefill(const uint16_t* q_raw, const uint16_t* q_gist, const uint16_
  * every layer of the group runs sparse attention with that same buffer.
  * With `causal` set the step is a causal prefill: Lq == L, query row r sits
  * at position r, may choose among positions 0..r and keeps min(topk, r+1) of
- * them; the L x L score matrix is never materialised.
+ * them; the L x L score matrix is never materialised.  What the attention of
+ * many rows derives from the index alone (segment bounds, the block-union
+ * decisions and union lists) is computed by the group's Full layer and kept
+ * in the workspace for its Shared layers.
  */
 typedef struct lct_group_desc {
   int B;                 /* batch                                          */

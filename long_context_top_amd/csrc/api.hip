@@ -304,10 +304,10 @@ static int validate_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v
 
 static int run_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
                     float* out, int B, int Lq, int Hq, int Hkv, int64_t L, int kk, float scale,
-                    char* partials, hipStream_t st) {
+                    char* partials, hipStream_t st, bool reuse_index_work = false) {
   const AttnPlan plan = attn_plan(B, Lq, Hq, Hkv, kk, L);
   LCT_HIP(launch_sparse_attn(q, k, v, idx, out, B, Lq, Hq, Hkv, L, kk, scale, plan,
-                             reinterpret_cast<float*>(partials), st),
+                             reinterpret_cast<float*>(partials), st, reuse_index_work),
           "sparse_attn_gather");
   return LCT_OK;
 }
@@ -635,10 +635,12 @@ int lct_group_run(const lct_group_desc* d, void* ws, size_t ws_bytes, void* stre
         if (rc) return rc;
       }
     }
-    // the Full layer and the Shared layers after it read the same buffer
+    // the Full layer and the Shared layers after it read the same buffer;
+    // a Shared layer also reuses what the attention derived from it in the
+    // layer before (same index, shapes and workspace)
     if (d->layer_idx_seen) d->layer_idx_seen[l] = ib;
     rc = run_attn(d->q[l], d->k[l], d->v[l], ib, d->out[l], d->B, d->Lq, d->Hq, d->Hkv, d->L,
-                  d->topk, d->scale, w + lay.attn, st);
+                  d->topk, d->scale, w + lay.attn, st, !layer_is_full(d, l));
     if (rc) return rc;
   }
   return LCT_OK;

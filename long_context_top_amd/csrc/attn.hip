@@ -1184,7 +1184,7 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
 static hipError_t launch_sparse_attn_seg(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                          const int32_t* idx, float* out, int B, int Lq, int Hq,
                                          int Hkv, int64_t L, int kk, float sl2, const AttnPlan& plan,
-                                         float* ws, hipStream_t st) {
+                                         float* ws, hipStream_t st, bool reuse) {
   const int G = Hq / Hkv;
   const int64_t rows = (int64_t)B * Lq;
   const int64_t groups = (rows + ATT_NW - 1) / ATT_NW;
@@ -1196,9 +1196,13 @@ static hipError_t launch_sparse_attn_seg(const uint16_t* q, const uint16_t* k, c
   int32_t* lpos = plan.ua_blocks > 0 ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + attn_ul_offset(plan))
                                       : nullptr;
   uint16_t* lmask = plan.ua_blocks > 0 ? reinterpret_cast<uint16_t*>(lpos + plan.ua_blocks * UA_UCAP) : nullptr;
-  if (nblk > 0) k_union_plan<<<dim3((unsigned)nblk), 256, 0, st>>>(idx, rows, Lq, kk, L, G, uflag, lpos, lmask);
-  k_seg_bounds<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(idx, bnd, rows, kk, L, plan.seg_shift,
-                                                                  plan.nseg, uflag, nblk);
+  // what depends only on the index (block decisions, union lists, segment
+  // bounds) is kept from the previous call on the same index when `reuse`
+  if (!reuse) {
+    if (nblk > 0) k_union_plan<<<dim3((unsigned)nblk), 256, 0, st>>>(idx, rows, Lq, kk, L, G, uflag, lpos, lmask);
+    k_seg_bounds<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(idx, bnd, rows, kk, L, plan.seg_shift,
+                                                                    plan.nseg, uflag, nblk);
+  }
   if (nblk > 0) {
     const dim3 ug((unsigned)(nblk * Hkv));
     switch (G) {
@@ -1232,11 +1236,11 @@ static hipError_t launch_sparse_attn_seg(const uint16_t* q, const uint16_t* k, c
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* idx, float* out, int B, int Lq, int Hq, int Hkv,
                               int64_t L, int kk, float scale, const AttnPlan& plan,
-                              float* partials, hipStream_t st) {
+                              float* partials, hipStream_t st, bool reuse_index_work) {
   const int G = Hq / Hkv;
   const float sl2 = scale * LOG2E;
   if (plan.nseg > 0) return launch_sparse_attn_seg(q, k, v, idx, out, B, Lq, Hq, Hkv, L, kk, sl2, plan,
-                                                   partials, st);
+                                                   partials, st, reuse_index_work);
   const int64_t units = (int64_t)B * Lq * Hkv;
   const int64_t waves = units * plan.splits;
   const dim3 grid((unsigned)((waves + ATT_NW - 1) / ATT_NW));

@@ -104,10 +104,13 @@ inline size_t attn_ws_bytes(const AttnPlan& p) {
 }
 // With plan.splits > 1 the kernel writes (O, m, l) partials and a merge
 // kernel combines them (log-sum-exp merge).
+// reuse_index_work: the workspace already holds what the segmented path
+// derives from this index (block-union decisions and lists, segment bounds),
+// left by the previous call on the same index, shapes and workspace.
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* idx, float* out, int B, int Lq, int Hq, int Hkv,
                               int64_t L, int kk, float scale, const AttnPlan& plan,
-                              float* partials, hipStream_t st);
+                              float* partials, hipStream_t st, bool reuse_index_work = false);
 // Merge of split partials: part[unit][split][hs][rs] (O[D], m, l, pad) ->
 // out[(unit * G + h) * D + d] for h < G.
 hipError_t launch_split_merge(const float* part, float* out, int64_t units, int splits, int hs,

@@ -201,6 +201,30 @@ def test_causal_prefill_segmented_attention():
     assert np.abs(out[0][0, sample] - ref).max() < ATOL
 
 
+def test_causal_prefill_segmented_groups_reuse_index_work():
+    """Causal prefill over 33000 positions with Full layers 0 and 3 of five:
+    the Shared layers (1, 2, 4) reuse the segment bounds and block-union
+    lists their group's Full layer derived from the index, the second Full
+    layer derives them anew from its own index; every layer is checked
+    against the oracle on rows of the union blocks and of the per-row path."""
+    pattern = [1, 0, 0, 1, 0]
+    cfg = C.DecodeConfig("prefill_seg_groups", 8282, B=1, Lq=33000, L=33000, n_layers=len(pattern), group=1,
+                         Hq=16, Hkv=4, D=128, H_idx=4, d_idx=64, topk=512, causal=True)
+    announce(f"{cfg.name} {pattern}")
+    _, idx, out, _ = _run_pattern(cfg, pattern)
+    sample = np.array([0, 1, 15, 16, 300, 511, 512, 513, 1000, 2047, 2048, 4095, 4096, 16383, 16384,
+                       16385, 25000, 32767, 32768, 32999])
+    kh_rows = lambda g: C.rows(cfg, cfg.ki_spec(g), (np.array([0]),))[0]
+    for g in range(2):
+        qh = C.rows(cfg, cfg.qi_spec(g), (np.zeros_like(sample), sample))
+        want = oracle.select_topk_threshold(oracle.index_scores_f32(qh, kh_rows(g)), cfg.topk, sample + 1)
+        assert np.array_equal(idx[g][0][sample], want), g
+    owner = oracle.layer_owner(pattern)
+    for l in range(cfg.n_layers):
+        ref = oracle.prefill_attention_rows(cfg, l, sample, idx[owner[l]][0][sample])
+        assert np.abs(out[l][0, sample] - ref).max() < ATOL, l
+
+
 def test_decode_shared_kv_cache():
     """One KV cache for every layer (YOCO / CLSA): the same K/V tensors are
     handed to all layers; each layer still has its own queries."""
