@@ -175,7 +175,8 @@ int lct_sparse_attn_workspace_bytes(int B, int Lq, int Hq, int Hkv, int D, int64
  *   gscores  fp32 [BH, Nc]          q . gist_key (unscaled), as produced by
  *                                   lct_gist_score_bf16; the gist logit is
  *                                   gscores * scale
- *   chunk_idx int32 [BH, kc]        chosen chunks (-1 = skip)
+ *   chunk_idx int32 [BH, kc]        chosen chunks (-1, or any id outside
+ *                                   [0, Nc): skipped)
  *   out      fp32 [BH, D]
  * Requires chunk == 16, D == 128, 0 <= tail_len <= chunk,
  * raw_cap >= Nc*chunk + tail_len.

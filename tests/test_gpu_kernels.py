@@ -476,6 +476,47 @@ def test_gist_score_and_gsa_decode(tail):
     assert np.abs(host(out) - ref_out).max() < ATOL
 
 
+def test_gsa_attn_long_and_ragged_chunk_lists():
+    """lct_gsa_attn straight from a chunk list: 512 (batch, head) rows of 300
+    chunks each (one split per row, so a wave takes 76 items, more than its
+    preloaded 64), with -1 entries and ids past Nc that are skipped, and a
+    row with no valid chunk (the tail alone).  Rows are compared with the
+    oracle over exactly the listed valid chunks' raw rows, their gists and the
+    tail."""
+    BH, Nc, kc, tail, D = 512, 320, 300, 5, 128
+    announce(f"gsa attn BH={BH} Nc={Nc} kc={kc} tail={tail}")
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    dev = "cuda"
+    raw_cap = Nc * 16 + tail
+    rk = torch.randn((BH, raw_cap, D), generator=gen, device=dev).to(torch.bfloat16)
+    rv = torch.randn((BH, raw_cap, D), generator=gen, device=dev).to(torch.bfloat16)
+    gk = torch.randn((BH, Nc, D), generator=gen, device=dev).to(torch.bfloat16)
+    gv = torch.randn((BH, Nc, D), generator=gen, device=dev).to(torch.bfloat16)
+    q = torch.randn((BH, D), generator=gen, device=dev).to(torch.bfloat16)
+    r = _rng(99)
+    cid = np.stack([r.permutation(Nc)[:kc] for _ in range(BH)]).astype(np.int32)
+    cid[r.random(cid.shape) < 0.05] = -1
+    cid[r.random(cid.shape) < 0.03] = Nc + 7          # past Nc: skipped
+    cid[7, :] = -1                                     # only the tail
+    qh = q.float().cpu().numpy().astype(np.float64)
+    gkh = gk.float().cpu().numpy().astype(np.float64)
+    gs = np.einsum("bd,bnd->bn", qh, gkh).astype(np.float32)
+    scale = 1.0 / math.sqrt(D)
+    got = host(lct.gsa_attn(q, rk, rv, gv, dev_f32(gs), dev_i32(cid), tail, scale))
+    worst = 0.0
+    for b in (0, 7, 100, 257, 511):
+        ch = cid[b][(cid[b] >= 0) & (cid[b] < Nc)]
+        pos = np.concatenate([(ch[:, None] * 16 + np.arange(16)[None, :]).reshape(-1),
+                              Nc * 16 + np.arange(tail)])
+        rkb, rvb = rk[b].float().cpu().numpy(), rv[b].float().cpu().numpy()
+        gvb = gv[b].float().cpu().numpy()
+        want = oracle.gsa_attention(qh[b], rkb[pos], rvb[pos], gkh[b, ch], gvb[ch], scale)
+        err = np.abs(got[b] - want).max()
+        worst = max(worst, err)
+        assert err < ATOL, (b, err)
+    print(f"  max |out - oracle| = {worst:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("Nc,group,km,kc,tail", [(300, 16, 3, 8, 1), (300, 4, 2, 16, 0),
                                                   (1000, 64, 4, 64, 16), (2049, 1, 64, 64, 5),
                                                   (513, 512, 2, 100, 1)])
