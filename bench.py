@@ -527,7 +527,51 @@ def gsa_prefill_pairs(cfg) -> int:
     return raw + gist
 
 
-def bench_gsa_prefill(cfg, steps, warmup):
+def cpu_baseline_gsa_prefill(cfg, n_raw=512, n_gist=128):
+    """The oracle's GSA prefill on sampled rows of one (batch, head): raw and
+    gist queries spread over the sequence, each attending over its visible
+    keys (oracle.gsa_prefill_rows).  The oracle's cost per query grows with
+    its visible keys, so the whole prefill's time is the sample's scaled by
+    (visible pairs of all rows and heads) / (visible pairs of the sample)."""
+    import concurrent.futures as cf
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+    from synth import configs as C
+
+    model, nthreads = host_info()
+    n_rows = cfg.Nc * cfg.chunk
+    raw_rows = [int(x) for x in np.linspace(0, n_rows - 1, n_raw)]
+    gist_rows = [int(x) for x in np.linspace(0, cfg.Nc - 1, n_gist)]
+    idx = (np.array(0), np.array(0))
+    args = [synth.as_float(spec[0], C.rows(cfg, spec, idx)) for spec in
+            (cfg.qr_spec(), cfg.qg_spec(), cfg.rk_spec(), cfg.rv_spec(), cfg.gk_spec(), cfg.gv_spec())]
+    args[2], args[3] = args[2][:n_rows], args[3][:n_rows]
+    ch = cfg.chunk
+    pairs = sum((t // ch) + (t % ch) + 1 for t in raw_rows) + sum(c + 1 + ch for c in gist_rows)
+    run = lambda rr, gr: oracle.gsa_prefill_rows(*args, ch, cfg.scale, raw_rows=rr, gist_rows=gr)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        run(raw_rows, gist_rows)
+        t1 = time.perf_counter() - t0
+        reps = max(1, nthreads // 4)
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(lambda i: run(raw_rows[i::nthreads], gist_rows[i::nthreads]), list(range(nthreads)) * reps))
+        tn = (time.perf_counter() - t0) / reps
+    scale = gsa_prefill_pairs(cfg) * cfg.B * cfg.H / pairs
+    tokens = cfg.B * cfg.Nc * (cfg.chunk + 1)
+    return {"value": tokens / (tn * scale), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": model, "one_thread": {"value": tokens / (t1 * scale), "unit": "tokens/s", "cores": 1},
+            "sample": (f"{n_raw} raw and {n_gist} gist queries of one (batch, head) spread over the sequence, "
+                       f"each over its visible keys: {t1:.1f} s on 1 thread; {reps} x the sample on {nthreads} "
+                       f"threads in {tn * reps:.1f} s; extrapolated by visible pairs (x{scale:.0f})")}
+
+
+def bench_gsa_prefill(cfg, steps, warmup, want_cpu=False):
     """Every raw and gist token of the sequence attends under the gist mask
     (lct_gsa_prefill).  Throughput: bf16 flops of the visible pairs (QK and
     PV: 4 per pair and feature) against the dense bf16 MFMA peak."""
@@ -557,10 +601,16 @@ def bench_gsa_prefill(cfg, steps, warmup):
     flops = 4.0 * cfg.D * gsa_prefill_pairs(cfg) * BH
     tf = flops / (ms * 1e-3) / 1e12
     tokens = cfg.B * cfg.Nc * (cfg.chunk + 1)
-    return {"workload": cfg.name, "ms_per_prefill": ms, "tokens_per_s": tokens / (ms * 1e-3),
-            "roofline": {"bound": "mfma", "kernel": "k_gsa_prefill (raw and gist queries)", "achieved": tf,
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
-                         "flops_per_launch": flops, "us_per_launch": ms * 1e3}}
+    res = {"workload": cfg.name, "ms_per_prefill": ms, "tokens_per_s": tokens / (ms * 1e-3),
+           "roofline": {"bound": "mfma", "kernel": "k_gsa_prefill (raw and gist queries)", "achieved": tf,
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                        "flops_per_launch": flops, "us_per_launch": ms * 1e3}}
+    if want_cpu:
+        del qr, qg, rk, rv, gk, gv, out_r, out_g
+        torch.cuda.empty_cache()
+        log("timing the CPU oracle on sampled GSA prefill rows ...")
+        res["cpu_baseline"] = cpu_baseline_gsa_prefill(cfg)
+    return res
 
 
 # --------------------------------------------------------------- prefill ----
@@ -871,7 +921,7 @@ def main():
     if args.config in ("gsa_128k", "hgsa_128k"):
         res = bench_gsa(cfg, args.steps, args.warmup, want_cpu=not args.no_cpu_baseline)
     elif args.config == "gsa_prefill_128k":
-        res = bench_gsa_prefill(cfg, args.steps, args.warmup)
+        res = bench_gsa_prefill(cfg, args.steps, args.warmup, want_cpu=not args.no_cpu_baseline)
     elif args.config == "prefill_64k":
         res = bench_prefill_indexer(cfg, args.steps, args.warmup, want_cpu=not args.no_cpu_baseline)
     else:
@@ -898,8 +948,9 @@ def main():
             log("GSA workloads ...")
             gsteps = max(10, args.steps // 2)
             res["gsa_decode"] = bench_gsa(C.GSA_128K, gsteps, 2, want_cpu=not args.no_cpu_baseline)
-            res["hgsa_decode"] = bench_gsa(C.HGSA_128K, gsteps, 2)
-            res["gsa_prefill"] = bench_gsa_prefill(C.GSA_PREFILL_128K, max(5, args.steps // 10), 1)
+            res["hgsa_decode"] = bench_gsa(C.HGSA_128K, gsteps, 2, want_cpu=not args.no_cpu_baseline)
+            res["gsa_prefill"] = bench_gsa_prefill(C.GSA_PREFILL_128K, max(5, args.steps // 10), 1,
+                                                   want_cpu=not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
 
