@@ -782,7 +782,8 @@ __global__ __launch_bounds__(256) void k_union_plan(const int32_t* __restrict__ 
   for (int d = 1; d < RT; d <<= 1) {
     n += __shfl_xor(n, d, 64);
     pmax = max(pmax, __shfl_xor(pmax, d, 64));
-    bad = bad || __shfl_xor((int)bad, d, 64);
+    const int ob = __shfl_xor((int)bad, d, 64);  // every lane takes part in the shuffle
+    bad = bad || ob != 0;
   }
   if (t == 0) {
     s_n[rr] = n;

@@ -411,6 +411,52 @@ def test_sparse_attn_block_union_path(Hq, Hkv):
     print(f"  max |out - oracle| = {worst:.2e}", flush=True)
 
 
+def test_sparse_attn_block_union_two_batch_entries():
+    """Two batch entries of 2056 rows (not a multiple of 16): every block of
+    16 rows shares one set, so every block takes the block-union path except
+    the one that straddles the two entries (rows 2048..2063); the second
+    entry's union blocks gather from its own K/V.  A block whose shared set
+    holds a position past the cache (its last entry, seen by one lane of the
+    check) and a block with one row holding one pair out of order are
+    decided per row, which skips the former entry and takes the latter row
+    in any order.  Every row is compared with the oracle."""
+    B, Lq, L, kk, Hq, Hkv = 2, 2056, 40000, 256, 32, 4
+    announce(f"attn block union B={B} Lq={Lq} L={L} kk={kk}")
+    r = _rng(77)
+    q, qh = dev_bf16(r.standard_normal((B, Lq, Hq, 128)))
+    k, kh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    v, vh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    rows = B * Lq
+    idx = np.full((rows, kk), -1, dtype=np.int32)
+    for blk in range(rows // 16 + 1):
+        common = np.sort(r.choice(L, size=kk, replace=False)).astype(np.int32)
+        if blk == 5:
+            common[-1] = L + 3                          # past the cache
+        idx[blk * 16:(blk + 1) * 16] = common
+        if blk == 9:                                    # one row with one pair out of order
+            idx[blk * 16 + 3, 100], idx[blk * 16 + 3, 101] = common[101], common[100]
+    idx = idx.reshape(B, Lq, kk)
+    scale = 1.0 / math.sqrt(128)
+    ws = lct.Workspace()
+    got = host(lct.sparse_attn_gather(q, k, v, dev_i32(idx), scale, ws=ws))
+    flags = _union_flags(ws, B, Lq, Hq, Hkv, L, kk)
+    bad = np.zeros(rows // 16, bool)
+    bad[2048 // 16] = True                              # straddles the two entries
+    bad[5] = bad[9] = True
+    assert np.array_equal(flags, _union_rule(idx, Hq // Hkv, bad))
+    assert np.all(flags[~bad] > 0)
+    worst = 0.0
+    for b in range(B):
+        for j in range(Lq):
+            sel = idx[b, j]
+            sel = sel[(sel >= 0) & (sel < L)]
+            want = oracle.sparse_attention_gqa(qh[b, j], kh[b, sel], vh[b, sel], scale)
+            err = np.abs(got[b, j] - want).max()
+            worst = max(worst, err)
+            assert err < ATOL, (b, j, err)
+    print(f"  max |out - oracle| = {worst:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(32, 4), (16, 4)])
 def test_sparse_attn_block_union_large_unions(Hq, Hkv):
     """Blocks of 16 rows of 2048 positions drawn from a common pool: a pool of
