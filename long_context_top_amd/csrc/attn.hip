@@ -701,7 +701,8 @@ __global__ __launch_bounds__(256) void k_seg_merge(const float* __restrict__ par
 constexpr int UA_WIN = 16384;  // positions per membership window (16 rows x 2 KiB of bits)
 constexpr int UA_CH = 64;      // union positions per chunk
 constexpr int UA_LD = 16;      // index entries per thread and round of the membership pass
-constexpr int UA_NBUF = 4;     // staging buffers of the chunk ring
+constexpr int UA_NBUF = 4;     // staging buffers of the chunk ring (unions over UA_SMALL positions)
+constexpr int UA_SMALL = 2048; // unions up to this size: two staging buffers, two workgroups per CU
 constexpr int UA_SET = UA_CH * 256 * 2;  // one staging buffer: the chunk's K and V tiles
 // Union mode when the block's rows select each union position UA_SHARE x G / 8
 // times on average (sum of n_r >= that x |U|).  A union chunk costs its
@@ -1055,29 +1056,35 @@ LCT_DEV void ua_chunk(int base, const char (&kt)[UA_CH * 256], const char (&va)[
 // cursor) set its membership bits; the window's union is appended to a list of
 // positions + 16-bit row masks (at most UA_UCAP entries: the plan flags no
 // larger union).  The bitmaps live in the first staging buffer, free then.
-// Phase 2 gathers chunks of 64 union positions into a ring of UA_NBUF staging
-// buffers (UA_NBUF - 1 chunks in flight while one is attended) and every wave
+// Phase 2 gathers chunks of 64 union positions into a ring of NBUF staging
+// buffers (NBUF - 1 chunks in flight while one is attended) and every wave
 // attends each chunk with its rows' masks.  K is stored 16-byte-chunk swizzled
 // (chunk s of token t at s ^ (t % 16)), so the A-operand reads (16 tokens of
 // one chunk) fall on distinct banks; V uses the layout of the per-row path
 // for the transposed reads.
-template <int G>
-__global__ __launch_bounds__(G * 64) void k_union_attn(
+template <int G, bool SMALL>
+__global__ __launch_bounds__(G * 64) __attribute__((amdgpu_waves_per_eu(SMALL && G == 8 ? 4 : 1))) void k_union_attn(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ flag, const int32_t* __restrict__ lpos, const uint16_t* __restrict__ lmask,
     float* __restrict__ out, int Lq, int Hq, int Hkv, int64_t L, float scale_log2) {
   constexpr int D = ATT_D;
   constexpr int NT = G * 64;
   constexpr int RW = UA_R / G;  // rows per wave
+  // SMALL: unions of up to UA_SMALL positions with two staging buffers (one
+  // chunk in flight; 76 KiB of LDS, so two workgroups share a CU and run out
+  // of step); else the larger unions with the deeper ring (152 KiB, one per CU)
+  constexpr int NBUF = SMALL ? 2 : UA_NBUF;
+  constexpr int CAP = SMALL ? UA_SMALL : UA_UCAP;
   static_assert(G >= 4 && G <= 16 && UA_R % G == 0, "union path for 4 to 16 heads per KV head");
-  static_assert(UA_UCAP % UA_CH == 0, "the last chunk's padding stays in the list");
-  __shared__ int32_t upos[UA_UCAP];
-  __shared__ __attribute__((aligned(8))) uint16_t umask[UA_UCAP];
-  __shared__ __attribute__((aligned(16))) char stage[UA_NBUF][UA_SET];
+  static_assert(CAP % UA_CH == 0 && UA_SMALL <= UA_UCAP, "the last chunk's padding stays in the list");
+  __shared__ int32_t upos[CAP];
+  __shared__ __attribute__((aligned(8))) uint16_t umask[CAP];
+  __shared__ __attribute__((aligned(16))) char stage[NBUF][UA_SET];
   const int64_t blk = blockIdx.x / Hkv;
   const int kvh = (int)(blockIdx.x % Hkv);
   const int nu = min(flag[blk], UA_UCAP);
-  if (nu <= 0) return;  // uniform: the segment path takes this block
+  // uniform: the segment path takes blocks with no union, each instance its sizes
+  if (nu <= 0 || (SMALL ? nu > UA_SMALL : nu <= UA_SMALL)) return;
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int64_t r0 = blk * UA_R;
   const int64_t b = r0 / Lq;
@@ -1106,7 +1113,7 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
   }
   __syncthreads();
 
-  // ---- phase 2: the chunks, UA_NBUF - 1 in flight
+  // ---- phase 2: the chunks, NBUF - 1 in flight
   const int row_bytes = Hkv * D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (size_t)b * L * Hkv * D + kvh * D, L * (int64_t)row_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (size_t)b * L * Hkv * D + kvh * D, L * (int64_t)row_bytes);
@@ -1125,10 +1132,10 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
   auto vb_of = [&](int sb) -> char (&)[2][4][1024] {
     return *reinterpret_cast<char (*)[2][4][1024]>(&stage[sb][UA_CH * 256 + 8192]);
   };
-  // DMA of chunk c (union positions c*64 ..) into staging buffer c % UA_NBUF:
+  // DMA of chunk c (union positions c*64 ..) into staging buffer c % NBUF:
   // 16 K and 16 V instructions per chunk, 32 / G per wave (i = wid + ii * G)
   auto issue = [&](int c) {
-    const int sb = c % UA_NBUF;
+    const int sb = c % NBUF;
     char* kt = &kt_of(sb)[0];
     char (*va)[4][1024] = va_of(sb);
     char (*vb)[4][1024] = vb_of(sb);
@@ -1152,25 +1159,25 @@ __global__ __launch_bounds__(G * 64) void k_union_attn(
     }
   };
   constexpr int NDMA = 32 / G;  // DMA instructions per wave and chunk
-  static_assert((UA_NBUF - 2) * NDMA <= 63, "vector memory counter range");
+  static_assert(NBUF >= 2 && (NBUF - 2) * NDMA <= 63, "vector memory counter range");
   // Plain barriers (ua_barrier): each wave waits for its own DMA with an
   // explicit count, so the barrier need not drain the DMA in flight.
   __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
 #pragma unroll
-  for (int c = 0; c < UA_NBUF - 1; ++c)
+  for (int c = 0; c < NBUF - 1; ++c)
     if (c < nch) issue(c);
   for (int c = 0; c < nch; ++c) {
-    // this wave's DMA of chunk c has landed once at most min(UA_NBUF - 2,
+    // this wave's DMA of chunk c has landed once at most min(NBUF - 2,
     // nch - 1 - c) later chunks are outstanding
-    const int later = min(UA_NBUF - 2, nch - 1 - c);
+    const int later = min(NBUF - 2, nch - 1 - c);
     if (later >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));
     else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NDMA));
     else __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
     // every wave's DMA of chunk c has landed, and every wave is done with
-    // chunk c - 1, whose buffer takes chunk c + UA_NBUF - 1
+    // chunk c - 1, whose buffer takes chunk c + NBUF - 1
     ua_barrier();
-    if (c + UA_NBUF - 1 < nch) issue(c + UA_NBUF - 1);
-    const int sb = c % UA_NBUF;
+    if (c + NBUF - 1 < nch) issue(c + NBUF - 1);
+    const int sb = c % NBUF;
     ua_chunk(c * UA_CH, kt_of(sb), va_of(sb), vb_of(sb), umask, a, qf, rbit, wrm, scale_log2, m, lacc, o);
   }
   // o[dt][e] = O^T[d = 16dt + 4kg + e][column hl]; every row of lacc holds
@@ -1205,15 +1212,17 @@ static hipError_t launch_sparse_attn_seg(const uint16_t* q, const uint16_t* k, c
                                                                     plan.nseg, uflag, nblk);
   }
   if (nblk > 0) {
+    // unions up to UA_SMALL positions, then the larger ones
     const dim3 ug((unsigned)(nblk * Hkv));
+#define LCT_UA(GG, SM) \
+  k_union_attn<GG, SM><<<ug, GG * 64, 0, st>>>(q, k, v, uflag, lpos, lmask, out, Lq, Hq, Hkv, L, sl2)
     switch (G) {
-      case 4: k_union_attn<4><<<ug, 4 * 64, 0, st>>>(q, k, v, uflag, lpos, lmask, out, Lq, Hq, Hkv, L, sl2); break;
-      case 8: k_union_attn<8><<<ug, 8 * 64, 0, st>>>(q, k, v, uflag, lpos, lmask, out, Lq, Hq, Hkv, L, sl2); break;
-      case 16:
-        k_union_attn<16><<<ug, 16 * 64, 0, st>>>(q, k, v, uflag, lpos, lmask, out, Lq, Hq, Hkv, L, sl2);
-        break;
+      case 4: LCT_UA(4, true); LCT_UA(4, false); break;
+      case 8: LCT_UA(8, true); LCT_UA(8, false); break;
+      case 16: LCT_UA(16, true); LCT_UA(16, false); break;
       default: return hipErrorInvalidValue;
     }
+#undef LCT_UA
   }
   const int64_t wgs = (int64_t)plan.nseg * groups * Hkv;
   if (wgs >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
