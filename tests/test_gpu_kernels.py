@@ -503,6 +503,49 @@ def test_sparse_attn_block_union_large_unions(Hq, Hkv):
     print(f"  {len(rows)} rows, max |out - oracle| = {worst:.2e}", flush=True)
 
 
+def test_sparse_attn_block_union_sixteen_heads_per_kv_head():
+    """16 query heads per KV head: the plan's limit is then 16 x 2048 x 8 /
+    (6 x 16) = 2730 union positions, so pools of 2400 and 2100 positions take
+    the instance for unions above 2048 and a set shared by the whole block the
+    one for unions up to 2048; independent sets go per row.  The decisions
+    match the rule and the rows match the oracle."""
+    B, Lq, L, kk, Hq, Hkv = 1, 4096, 40000, 2048, 64, 4
+    announce(f"attn block union G=16 Lq={Lq} L={L} kk={kk}")
+    r = _rng(1601)
+    q, qh = dev_bf16(r.standard_normal((B, Lq, Hq, 128)))
+    k, kh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    v, vh = dev_bf16(r.standard_normal((B, L, Hkv, 128)))
+    idx = np.full((B, Lq, kk), -1, dtype=np.int32)
+    kinds = np.arange(Lq // 16) % 4
+    for blk, kind in enumerate(kinds):
+        if kind == 3:
+            shared = np.sort(r.choice(L, size=kk, replace=False))
+        pool = np.sort(r.choice(L, size={0: 2400, 1: 2100}[kind], replace=False)) if kind < 2 else None
+        for i in range(16):
+            if pool is not None:
+                sel = np.sort(r.choice(pool, size=kk, replace=False))
+            elif kind == 3:
+                sel = shared
+            else:
+                sel = np.sort(r.choice(L, size=kk, replace=False))
+            idx[0, blk * 16 + i] = sel
+    scale = 1.0 / math.sqrt(128)
+    ws = lct.Workspace()
+    got = host(lct.sparse_attn_gather(q, k, v, dev_i32(idx), scale, ws=ws))
+    flags = _union_flags(ws, B, Lq, Hq, Hkv, L, kk)
+    assert np.array_equal(flags, _union_rule(idx, Hq // Hkv, np.zeros(kinds.size, bool)))
+    assert np.all(flags[kinds < 2] > 2048) and np.all(flags[kinds == 3] == 2048) and np.all(flags[kinds == 2] == 0)
+    rows = [j for j in range(Lq) if j // 16 < 24 or j % 61 == 0]
+    worst = 0.0
+    for j in rows:
+        sel = idx[0, j]
+        want = oracle.sparse_attention_gqa(qh[0, j], kh[0, sel], vh[0, sel], scale)
+        err = np.abs(got[0, j] - want).max()
+        worst = max(worst, err)
+        assert err < ATOL, (j, int(kinds[j // 16]), err)
+    print(f"  {len(rows)} rows, max |out - oracle| = {worst:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("tail", [0, 1, 7, 15, 16])
 def test_gist_score_and_gsa_decode(tail):
     from synth import configs as C
