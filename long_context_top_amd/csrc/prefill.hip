@@ -611,8 +611,9 @@ LCT_DEV bool pf_find_bin(uint32_t c_hi, uint32_t c_lo, int top, uint32_t need, i
 // a top bin or clamped offsets, every entry ranked); the bitmap is expanded
 // into the ascending row (a block-wide prefix sum of popcounts, eight words
 // per thread).  Rows the list cannot settle are listed for the whole-row
-// select.
-__global__ __launch_bounds__(PF_SEL_NT) void k_pf_select(
+// select.  The kernel is latency bound, so it is held to 64 VGPRs: eight
+// waves per SIMD (eight rows per CU) instead of seven.
+__global__ __launch_bounds__(PF_SEL_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_pf_select(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, int L, int kk, int r_all,
     const uint32_t* __restrict__ list, const uint32_t* __restrict__ meta,
     int32_t* __restrict__ idx, int32_t* __restrict__ fails) {
