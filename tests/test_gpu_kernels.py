@@ -247,12 +247,14 @@ def test_sparse_attn_empty_rows_are_zero():
     assert np.all(got == 0.0)
 
 
-def test_sparse_attn_segmented_path_row_shapes():
+@pytest.mark.parametrize("Hq", [8, 4])
+def test_sparse_attn_segmented_path_row_shapes(Hq):
     """Many rows over a long cache take the position-segment path (16800
-    (row, KV head) pairs, 40000 positions: several segments).  Rows of every
-    shape: ascending with -1 padding, inside one segment, skipping a segment,
-    shuffled, with duplicates, with -1 in the middle, empty, full."""
-    B, Lq, Hq, Hkv, L, kk = 2, 2100, 8, 4, 40000, 200
+    (row, KV head) pairs, 40000 positions: several segments), at 2 and 1
+    query heads per KV head.  Rows of every shape: ascending with -1
+    padding, inside one segment, skipping a segment, shuffled, with
+    duplicates, with -1 in the middle, empty, full."""
+    B, Lq, Hkv, L, kk = 2, 2100, 4, 40000, 200
     announce(f"attn segmented B={B} Lq={Lq} Hkv={Hkv} L={L} kk={kk}")
     r = _rng(77)
     q, qh = dev_bf16(r.standard_normal((B, Lq, Hq, 128)))
@@ -677,6 +679,20 @@ def test_gsa_prefill_large_logits(scale):
     assert np.isfinite(out_r).all() and np.isfinite(out_g).all()
     assert np.abs(out_r[0] - want_r).max() < ATOL
     assert np.abs(out_g[0] - want_g).max() < ATOL
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_gist_score_other_head_dims(D):
+    """The gist scorer's 64- and 256-feature instances (the decode workload
+    uses 128): integer-valued bf16 inputs, so every score is exact in fp32;
+    Nc ragged against the 512-gist tiles."""
+    announce(f"gist score D={D}")
+    r = _rng(40 + D)
+    BH, Nc = 3, 1500
+    q, qh = dev_bf16(r.integers(-8, 8, size=(BH, D)).astype(np.float32))
+    gk, gkh = dev_bf16(r.integers(-8, 8, size=(BH, Nc, D)).astype(np.float32))
+    got = host(lct.gist_score(q, gk))
+    assert np.array_equal(got, oracle.gist_scores(qh, gkh))
 
 
 def test_gsa_raw_path_sensitivity():
