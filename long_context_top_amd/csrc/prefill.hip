@@ -486,20 +486,24 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
 #pragma unroll
         for (int qb = 0; qb < PF_QB; ++qb)
           first[qb] = base[qb] + atomicAdd(&sh.scnt[cs][wq * PF_WROWS + qb * 16 + n], (uint32_t)__popc(bits[qb]));
-        const uint32_t pos0 = (uint32_t)(t * PF_TK + wk * PF_KL * 16 + g * 4);
+        // entry = (position << 16) + min(offset, 65535): one three-input add
+        // per candidate over the tile's shifted base; the slot advances by the
+        // candidate bit outside the masked write
+        const uint32_t pos16 = (uint32_t)(t * PF_TK + wk * PF_KL * 16 + g * 4) << 16;
 #pragma unroll
         for (int qb = 0; qb < PF_QB; ++qb) {
-          const int rl = wq * PF_WROWS + qb * 16 + n;
+          uint32_t* const rrow = ring + (wq * PF_WROWS + qb * 16 + n) * PF_RING;
           uint32_t slot = first[qb];
 #pragma unroll
           for (int kl = 0; kl < PF_KL; ++kl)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (bits[qb] & (1u << (kl * 4 + e))) {
-                const uint32_t d = min((uint32_t)acc[qb][kl][e], 65535u);
-                ring[rl * PF_RING + (slot & (PF_RING - 1))] = ((pos0 + kl * 16 + e) << 16) | d;
-                ++slot;
-              }
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t c = (bits[qb] >> (kl * 4 + e)) & 1u;
+              if (c)
+                rrow[slot & (PF_RING - 1)] =
+                    pos16 + ((uint32_t)(kl * 16 + e) << 16) + min((uint32_t)acc[qb][kl][e], 65535u);
+              slot += c;
+            }
         }
       };
       m_tiles = (r_last + 1 + PF_TK - 1) / PF_TK;
