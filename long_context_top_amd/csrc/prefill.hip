@@ -240,7 +240,8 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
   __shared__ __attribute__((aligned(16))) char kt1[PF_CHUNKS][1024];
   __shared__ __attribute__((aligned(16))) char kt2[PF_CHUNKS][1024];
   __shared__ __attribute__((aligned(16))) char kt3[PF_CHUNKS][1024];
-  __shared__ __attribute__((aligned(16))) uint32_t hist[PF_RB][PF_NBIN];
+  // (512-byte rows: a ring row's slot address is one and-or)
+  __shared__ __attribute__((aligned(512))) uint32_t hist[PF_RB][PF_NBIN];
   __shared__ int32_t smax[PF_RB], smin[PF_RB], basev[PF_RB], thdv[PF_RB];
   __shared__ uint32_t scnt[3][PF_RB];
   __shared__ __attribute__((aligned(16))) uint32_t fst[PF_RB][4];  // flush state per row
@@ -486,23 +487,29 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
 #pragma unroll
         for (int qb = 0; qb < PF_QB; ++qb)
           first[qb] = base[qb] + atomicAdd(&sh.scnt[cs][wq * PF_WROWS + qb * 16 + n], (uint32_t)__popc(bits[qb]));
-        // entry = (position << 16) + min(offset, 65535): one three-input add
-        // per candidate over the tile's shifted base; the slot advances by the
-        // candidate bit outside the masked write
-        const uint32_t pos16 = (uint32_t)(t * PF_TK + wk * PF_KL * 16 + g * 4) << 16;
+        // entry = position << 16 | min(offset, 65535): one saturating pack
+        // of the offset and the element's position (positions < 65536); the
+        // slot (in bytes) advances by the candidate bit outside the masked
+        // write, and the row's 512-byte alignment makes its address one and-or
+        static_assert(PF_RING * 4 == 512, "ring rows of 512 bytes");
+        const uint32_t pos0 = (uint32_t)(t * PF_TK + wk * PF_KL * 16 + g * 4);
+        uint32_t pj[PF_KL * 4];
+#pragma unroll
+        for (int j = 0; j < PF_KL * 4; ++j) pj[j] = pos0 + (uint32_t)((j >> 2) * 16 + (j & 3));
 #pragma unroll
         for (int qb = 0; qb < PF_QB; ++qb) {
-          uint32_t* const rrow = ring + (wq * PF_WROWS + qb * 16 + n) * PF_RING;
-          uint32_t slot = first[qb];
+          const uint32_t rrow = ring_lds + 4u * (uint32_t)((wq * PF_WROWS + qb * 16 + n) * PF_RING);
+          uint32_t s4 = first[qb] << 2;
 #pragma unroll
           for (int kl = 0; kl < PF_KL; ++kl)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t c = (bits[qb] >> (kl * 4 + e)) & 1u;
               if (c)
-                rrow[slot & (PF_RING - 1)] =
-                    pos16 + ((uint32_t)(kl * 16 + e) << 16) + min((uint32_t)acc[qb][kl][e], 65535u);
-              slot += c;
+                *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>((uintptr_t)((s4 & 508u) | rrow)) =
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_u16((uint32_t)acc[qb][kl][e],
+                                                                             pj[kl * 4 + e]));
+              s4 += c << 2;
             }
         }
       };
