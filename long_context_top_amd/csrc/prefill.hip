@@ -20,12 +20,13 @@
 //          1.56 k keys expected above it at k = 2048);
 //   M      one sweep over all keys <= the row: every score >= t_r is a
 //          candidate (position << 16 | min(score - t_r, 65535)).  Candidates
-//          go to a per-row ring in LDS; a flush wave copies whole 128-byte
-//          lines of it to the row's list in memory, so that memory sees full
-//          lines, few store instructions and no partially written lines.
+//          go to a per-row ring in LDS; two flush waves (64 rows each) copy
+//          whole 128-byte lines of it to the row's list in memory, so that
+//          memory sees full lines, few store instructions and no partially
+//          written lines.
 // Rows with fewer than 32 m_s earlier positions (a dense candidate stream)
 // are left to the plain path: one block of scores and a row select.
-// k_pf_select (one wave per row): the entries sit in registers; a histogram
+// k_pf_select (one workgroup per row): the entries sit in registers; a histogram
 // of score - t_r names the bin holding the k-th largest; higher bins are all
 // in; that bin is settled exactly (an exact-score histogram, then the ties
 // by position).  Output through a position bitmap, ascending.
@@ -66,8 +67,11 @@ constexpr int PF_KL = PF_TK * PF_WR / (16 * PF_CW);  // 16-key blocks per comput
 static_assert(PF_WR * PF_WROWS == PF_RB && PF_CW % PF_WR == 0 && PF_KL * 16 * (PF_CW / PF_WR) == PF_TK,
               "compute waves tile the block's rows x the tile's keys");
 constexpr int PF_DMA_W = PF_CW;            // the DMA wave
-constexpr int PF_FL_W = PF_CW + 1;         // the flush wave
-constexpr int PF_NT = (PF_CW + 2) * 64;
+constexpr int PF_FL_W = PF_CW + 1;         // the first flush wave
+constexpr int PF_NFL = 2;                  // flush waves
+constexpr int PF_FH = PF_RB / (64 * PF_NFL);  // rows per flush lane
+static_assert(PF_FH * 64 * PF_NFL == PF_RB && PF_FH <= 2, "one or two rows per flush lane");
+constexpr int PF_NT = (PF_CW + 1 + PF_NFL) * 64;
 constexpr int PF_CHUNKS = (PF_TK / 16) * PF_KS;  // 1 KiB fragments per key tile
 constexpr int PF_RING = 128;               // candidate ring entries per row (LDS)
 constexpr int PF_LCAP = 512;               // select: entries of the k-th bin a wave can hold
@@ -109,7 +113,7 @@ struct PfShared {
 // (j = tile * PF_TK + ..), in ascending or (desc) descending tile order.
 // The helper wave keeps PF_NBUF - 1 tiles in flight by LDS DMA while the
 // compute waves run `body(tile, buf)` on the current one.  Every wave calls
-// this; the flush wave runs `aux(step)` once per tile.  Key rows past the cache
+// this; the flush waves run `aux(step)` once per tile.  Key rows past the cache
 // read as zeros (range-checked buffer loads; the whole offset is in the
 // per-lane register).
 #define PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n)&15) | (((n) >> 4) << 14)) | 0x0F70)
@@ -153,7 +157,7 @@ LCT_DEV void pf_sweep(PfShared& sh, __amdgpu_buffer_rsrc_t krs, int n_tiles, int
     pf_barrier();
     if (wid == PF_DMA_W) {
       if (ts + 3 < n_tiles) issue(ahead3, ts + 3);
-    } else if (wid == PF_FL_W) {
+    } else if (wid >= PF_FL_W) {
       aux(ts);
     } else {
       body(desc ? n_tiles - 1 - ts : ts, ts, cur);
@@ -222,6 +226,14 @@ LCT_DEV void pf_lds_ld_state(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
       : "=&v"(s0), "=&v"(s1), "=&v"(c0), "=&v"(c1)
       : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
       : "memory");
+}
+
+// one 16-byte and one 4-byte LDS load, one wait
+LCT_DEV void pf_lds_ld_state1(uint32_t a0, uint32_t b0, uintx4& s0, uint32_t& c0) {
+  __asm__ volatile("ds_read_b128 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(s0), "=&v"(c0)
+                   : "v"(a0), "v"(b0)
+                   : "memory");
 }
 
 // Sample-histogram bin of d = score - min over a span of `span` values:
@@ -404,16 +416,18 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)ring;
     const uint32_t scnt_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&sh.scnt[0][0];
     const uint32_t fst_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&fst[0][0];
-    if (wid == PF_FL_W) {
-      pf_lds_st4(fst_lds + 16 * lane, uintx4{0u, 0u, 0u, 0u});
-      pf_lds_st4(fst_lds + 16 * (lane + 64), uintx4{0u, 0u, 0u, 0u});
-    }
-    // whole lines [ff, lim) of both rows: each lane copies its own rows'
-    // lines, 128 bytes per line (one LDS round trip, eight 16-byte stores)
-    auto flush_lines = [&](uintx4 (&st)[2], const uint32_t (&lim)[2]) {
+    // flush wave f takes rows lane + 64 (PF_FH f + h), h < PF_FH
+    const int frow = lane + 64 * PF_FH * (wid - PF_FL_W);
+    if (wid >= PF_FL_W) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t rl = (uint32_t)(lane + 64 * h);
+      for (int h = 0; h < PF_FH; ++h) pf_lds_st4(fst_lds + 16 * (frow + 64 * h), uintx4{0u, 0u, 0u, 0u});
+    }
+    // whole lines [ff, lim) of the lane's rows: each lane copies its own rows'
+    // lines, 128 bytes per line (one LDS round trip, eight 16-byte stores)
+    auto flush_lines = [&](uintx4 (&st)[PF_FH], const uint32_t (&lim)[PF_FH]) {
+#pragma unroll
+      for (int h = 0; h < PF_FH; ++h) {
+        const uint32_t rl = (uint32_t)(frow + 64 * h);
         while (st[h].y + 32u <= lim[h]) {
           uintx4 v[8];
           pf_lds_ld_line(ring_lds + 4 * (rl * PF_RING + (st[h].y & (PF_RING - 1))), v);
@@ -424,21 +438,24 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
         }
       }
     };
-    // state and the last finished step's counts of rows lane, lane + 64
-    auto load_state = [&](int step, uintx4 (&st)[2], uint32_t (&c)[2]) {
-      pf_lds_ld_state(fst_lds + 16 * lane, fst_lds + 16 * (lane + 64),
-                      scnt_lds + 4 * ((step % 3) * PF_RB + lane),
-                      scnt_lds + 4 * ((step % 3) * PF_RB + lane + 64), st[0], st[1], c[0], c[1]);
+    // state and the last finished step's counts of the lane's rows
+    auto load_state = [&](int step, uintx4 (&st)[PF_FH], uint32_t (&c)[PF_FH]) {
+      if constexpr (PF_FH == 2)
+        pf_lds_ld_state(fst_lds + 16 * frow, fst_lds + 16 * (frow + 64),
+                        scnt_lds + 4 * ((step % 3) * PF_RB + frow),
+                        scnt_lds + 4 * ((step % 3) * PF_RB + frow + 64), st[0], st[1], c[0], c[1]);
+      else
+        pf_lds_ld_state1(fst_lds + 16 * frow, scnt_lds + 4 * ((step % 3) * PF_RB + frow), st[0], c[0]);
     };
     // step ts: the counts of step ts - 1 are final; the counters of step
     // ts + 1 (last read in step ts - 1) are cleared for it
     auto flush_step = [&](int ts) {
-      uintx4 st[2];
-      uint32_t c[2], lim[2] = {0u, 0u};
+      uintx4 st[PF_FH];
+      uint32_t c[PF_FH], lim[PF_FH] = {};
       load_state(ts > 0 ? ts - 1 : 0, st, c);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rl = lane + 64 * h;
+      for (int h = 0; h < PF_FH; ++h) {
+        const int rl = frow + 64 * h;
         const int row = r0 + rl;
         pf_lds_st(scnt_lds + 4 * (((ts + 1) % 3) * PF_RB + rl), 0u);
         if (row > r_last || row < r_all) continue;
@@ -450,8 +467,8 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
         lim[h] = min(st[h].x, (uint32_t)PF_CROW);
       }
       flush_lines(st, lim);
-      pf_lds_st4(fst_lds + 16 * lane, st[0]);
-      pf_lds_st4(fst_lds + 16 * (lane + 64), st[1]);
+#pragma unroll
+      for (int h = 0; h < PF_FH; ++h) pf_lds_st4(fst_lds + 16 * (frow + 64 * h), st[h]);
     };
     int m_tiles;
     {
@@ -529,13 +546,13 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
 
     }
     // ---- the rest of every ring, the counts and the flags
-    if (wid == PF_FL_W) {
-      uintx4 st[2];
-      uint32_t c[2], lim[2] = {0u, 0u};
+    if (wid >= PF_FL_W) {
+      uintx4 st[PF_FH];
+      uint32_t c[PF_FH], lim[PF_FH] = {};
       load_state(m_tiles - 1, st, c);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rl = lane + 64 * h;
+      for (int h = 0; h < PF_FH; ++h) {
+        const int rl = frow + 64 * h;
         const int row = r0 + rl;
         if (row > r_last || row < r_all) continue;
         st[h].x += c[h];
@@ -544,8 +561,8 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
       }
       flush_lines(st, lim);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rl = lane + 64 * h;
+      for (int h = 0; h < PF_FH; ++h) {
+        const int rl = frow + 64 * h;
         const int row = r0 + rl;
         if (row > r_last || row < r_all) continue;
         for (uint32_t i = st[h].y; i < lim[h]; ++i)
