@@ -257,7 +257,8 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
   __shared__ int32_t smax[PF_RB], smin[PF_RB], basev[PF_RB], thdv[PF_RB];
   __shared__ uint32_t scnt[3][PF_RB];
   __shared__ __attribute__((aligned(16))) uint32_t fst[PF_RB][4];  // flush state per row
-  __shared__ uint32_t trash[PF_CW][64];  // the writes of non-candidates land here
+  __shared__ uint32_t trash[PF_CW];  // a wave's non-candidate writes land here (one word: same-address
+                                     // writes cost fewer LDS bank cycles than a word per lane)
   PfShared sh{kt0, kt1, kt2, kt3, hist, smax, smin, basev, thdv, scnt};
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int n = lane & 15, g = lane >> 4;
@@ -517,7 +518,7 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
 #pragma unroll
         for (int qb = 0; qb < PF_QB; ++qb) {
           const uint32_t rrow = ring_lds + 4u * (uint32_t)((wq * PF_WROWS + qb * 16 + n) * PF_RING);
-          const uint32_t tr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&trash[wid][lane];
+          const uint32_t tr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)&trash[wid];
           uint32_t s4 = first[qb] << 2;
 #pragma unroll
           for (int kl = 0; kl < PF_KL; ++kl)
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
             for (int e = 0; e < 4; ++e) {
               const uint32_t c = (bits[qb] >> (kl * 4 + e)) & 1u;
               // every lane stores: a candidate to its slot, the others to the
-              // lane's trash word (no exec-mask branch per element)
+              // wave's trash word (no exec-mask branch per element)
               *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>((uintptr_t)(c ? (s4 & 508u) | rrow : tr)) =
                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_u16((uint32_t)acc[qb][kl][e], pj[kl * 4 + e]));
               s4 += c << 2;
