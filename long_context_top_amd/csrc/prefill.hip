@@ -257,8 +257,9 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
   __shared__ int32_t smax[PF_RB], smin[PF_RB], basev[PF_RB], thdv[PF_RB];
   __shared__ uint32_t scnt[3][PF_RB];
   __shared__ __attribute__((aligned(16))) uint32_t fst[PF_RB][4];  // flush state per row
-  __shared__ uint32_t trash[PF_CW];  // a wave's non-candidate writes land here (one word: same-address
-                                     // writes cost fewer LDS bank cycles than a word per lane)
+  // a compute wave's non-candidate stores land on its one trash word (stores
+  // to one address cost fewer LDS bank cycles than a word per lane)
+  __shared__ uint32_t trash[PF_CW];
   PfShared sh{kt0, kt1, kt2, kt3, hist, smax, smin, basev, thdv, scnt};
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int n = lane & 15, g = lane >> 4;
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
         constexpr bool DIAG = decltype(diag_c)::value;
         const int cs = ts % 3;
         // candidates of this lane per row: a bit per element, then one slot
-        // reservation per row for all of them (the four reservations are
+        // reservation per row for all of them (the reservations are
         // unconditional, so their LDS round trips overlap), then the writes
         uint32_t bits[PF_QB], first[PF_QB];
 #pragma unroll
@@ -508,8 +509,8 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
           first[qb] = base[qb] + atomicAdd(&sh.scnt[cs][wq * PF_WROWS + qb * 16 + n], (uint32_t)__popc(bits[qb]));
         // entry = position << 16 | min(offset, 65535): one saturating pack
         // of the offset and the element's position (positions < 65536); the
-        // slot (in bytes) advances by the candidate bit outside the masked
-        // write, and the row's 512-byte alignment makes its address one and-or
+        // slot (in bytes) advances by the candidate bit after each store, and
+        // the row's 512-byte alignment makes its address one and-or
         static_assert(PF_RING * 4 == 512, "ring rows of 512 bytes");
         const uint32_t pos0 = (uint32_t)(t * PF_TK + wk * PF_KL * 16 + g * 4);
         uint32_t pj[PF_KL * 4];
