@@ -57,7 +57,8 @@ constexpr int PF_KS = PF_HD / 64;          // 64-byte MFMA k-steps per row
 constexpr int PF_RB = 128;                 // query rows per block
 constexpr int PF_TK = 64;                  // keys per tile
 constexpr int PF_NBUF = 4;                 // key-tile buffers: 3 tiles in flight
-constexpr int PF_SS = 16;                  // sample stride (positions)
+constexpr int PF_SS = 16;                  // sample stride (positions) of the histogram sweep
+constexpr int PF_SS1 = 4 * PF_SS;          // sample stride of the min / max sweep
 constexpr int PF_NBIN = 128;               // histogram bins
 constexpr int PF_CW = 8;                   // compute waves
 constexpr int PF_QB = 2;                   // 16-row blocks per compute wave
@@ -304,10 +305,12 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
     for (int i = threadIdx.x; i < PF_RB * PF_NBIN; i += PF_NT) (&sh.hist[0][0])[i] = 0u;
     __syncthreads();
 
-    // ---- S1: per-row min / max of the sampled scores (rows past the
-    // block's end collect garbage that nothing reads)
+    // ---- S1: per-row min / max of every 64th key's score, the range of
+    // the histogram below (rows past the block's end collect garbage that
+    // nothing reads)
     const int n_samp = r_last / PF_SS + 1;  // sampled keys j: position 16 j <= r_last
     const int st_tiles = (n_samp + PF_TK - 1) / PF_TK;
+    const int st_tiles1 = (r_last / PF_SS1 + 1 + PF_TK - 1) / PF_TK;
     {
       int32_t mx[PF_QB], mn[PF_QB];
 #pragma unroll
@@ -315,10 +318,10 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
         mx[i] = INT32_MIN;
         mn[i] = INT32_MAX;
       }
-      pf_sweep(sh, krs, st_tiles, PF_SS, desc, wid, lane, [&](int t, int, auto& buf) {
+      pf_sweep(sh, krs, st_tiles1, PF_SS1, desc, wid, lane, [&](int t, int, auto& buf) {
         intx4 acc[PF_QB][PF_KL];
         pf_tile_mfma(buf, qf, wk, lane, zero, acc);
-        const bool diag = (t * PF_TK + PF_TK - 1) * PF_SS > r0;  // a sample past some row
+        const bool diag = (t * PF_TK + PF_TK - 1) * PF_SS1 > r0;  // a sample past some row
 #pragma unroll
         for (int qb = 0; qb < PF_QB; ++qb) {
           const int row = r0 + wq * PF_WROWS + qb * 16 + n;
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
           for (int kl = 0; kl < PF_KL; ++kl)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int pos = (t * PF_TK + wk * PF_KL * 16 + kl * 16 + g * 4 + e) * PF_SS;
+              const int pos = (t * PF_TK + wk * PF_KL * 16 + kl * 16 + g * 4 + e) * PF_SS1;
               if (!diag || pos <= row) {
                 mx[qb] = max(mx[qb], acc[qb][kl][e]);
                 mn[qb] = min(mn[qb], acc[qb][kl][e]);
@@ -351,15 +354,17 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
       }
       __syncthreads();
     }
-    // ---- S2: 128-bin histogram of the sampled scores over [min, max]
+    // ---- S2: 128-bin histogram of every 16th key's score over S1's
+    // [min, max] (scores outside it are clamped into the end bins)
     {
-      int32_t lo[PF_QB];
+      int32_t lo[PF_QB], hi[PF_QB];
       uint32_t M[PF_QB];
 #pragma unroll
       for (int qb = 0; qb < PF_QB; ++qb) {
         const int rl = wq * PF_WROWS + qb * 16 + n;
         lo[qb] = sh.smin[rl];
-        const uint32_t span = (uint32_t)(sh.smax[rl] - lo[qb]) + 1u;
+        hi[qb] = sh.smax[rl] - lo[qb];
+        const uint32_t span = (uint32_t)hi[qb] + 1u;
         M[qb] = span == 0u ? 1u : ((1u << 23) - 1u) / span;
       }
       pf_sweep(sh, krs, st_tiles, PF_SS, desc, wid, lane, [&](int t, int, auto& buf) {
@@ -376,7 +381,8 @@ __global__ __launch_bounds__(PF_NT) void k_pf_filter(const int8_t* __restrict__ 
             for (int e = 0; e < 4; ++e) {
               const int pos = (t * PF_TK + wk * PF_KL * 16 + kl * 16 + g * 4 + e) * PF_SS;
               if (!diag || pos <= row)
-                atomicAdd(&sh.hist[rl][pf_sample_bin((uint32_t)(acc[qb][kl][e] - lo[qb]), M[qb])], 1u);
+                atomicAdd(&sh.hist[rl][pf_sample_bin((uint32_t)min(max(acc[qb][kl][e] - lo[qb], 0), hi[qb]), M[qb])],
+                          1u);
             }
         }
       }, no_aux);
