@@ -14,9 +14,9 @@
 // k_pf_filter: every workgroup owns whole query-row blocks of 128 rows
 // (block i paired with block NB-1-i so that all workgroups do the same
 // causal work) and runs, per block,
-//   S1/S2  two sweeps over every 16th key: per-row min/max of the sampled
-//          scores, then a 128-bin histogram of them -> a threshold t_r with
-//          m_s samples at or above it, m_s = k/16 + 6 sqrt(k/16) + 4 (about
+//   S1/S2  per-row min/max over every 64th key's score, then a 128-bin
+//          histogram over that range of every 16th key's score -> a threshold
+//          t_r with m_s samples at or above it, m_s = k/16 + 6 sqrt(k/16) + 4 (about
 //          1.56 k keys expected above it at k = 2048);
 //   M      one sweep over all keys <= the row: every score >= t_r is a
 //          candidate (position << 16 | min(score - t_r, 65535)).  Candidates
