@@ -642,7 +642,7 @@ LCT_DEV bool pf_find_bin(uint32_t c_hi, uint32_t c_lo, int top, uint32_t need, i
 
 // Exact top-k of one row from its candidate list: one workgroup of
 // PF_SEL_NT threads per row.  The list is read once into registers (entry
-// 1024 m + 4 t + u in element u of e[m] of thread t); a histogram of
+// 4 NT m + 4 t + u in element u of e[m] of thread t); a histogram of
 // score - t_r names the bin holding the k-th largest; higher bins go to the
 // position bitmap, that bin to an LDS list, which is settled exactly (an
 // exact-score histogram and the ties at the cut ranked by position, or, for
@@ -681,7 +681,7 @@ __global__ __launch_bounds__(PF_SEL_NT) __attribute__((amdgpu_waves_per_eu(8))) 
   uintx4 e[EM];
 #pragma unroll
   for (int m = 0; m < EM; ++m) {
-    const uint32_t i = 1024u * m + 4u * tid;
+    const uint32_t i = 4u * NT * m + 4u * tid;
     e[m] = i < c ? *reinterpret_cast<const uintx4*>(lp + i) : uintx4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
 #pragma unroll
     for (int u = 0; u < 4; ++u)
