@@ -861,7 +861,22 @@ __global__ __launch_bounds__(PF_SEL_NT) __attribute__((amdgpu_waves_per_eu(8))) 
     }
   }
   __syncthreads();
-  for (uint32_t j = tid; j < (uint32_t)kk; j += NT) out[j] = j < tot ? (int32_t)stage[j] : -1;
+  if ((kk & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
+    // eight entries per thread: one 16-byte LDS read, 16-byte stores
+    for (uint32_t j0 = 8u * tid; j0 < (uint32_t)kk; j0 += 8u * NT) {
+      const uintx4 sv = *reinterpret_cast<const uintx4*>(&stage[j0]);  // j0 + 8 <= PF_MAX_K
+      intx4 v[2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t p = (sv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
+        v[u >> 2][u & 3] = j0 + u < tot ? (int32_t)p : -1;
+      }
+      *reinterpret_cast<intx4*>(out + j0) = v[0];
+      if (j0 + 8 <= (uint32_t)kk) *reinterpret_cast<intx4*>(out + j0 + 4) = v[1];  // else j0 + 4 == kk
+    }
+  } else {
+    for (uint32_t j = tid; j < (uint32_t)kk; j += NT) out[j] = j < tot ? (int32_t)stage[j] : -1;
+  }
 }
 
 // ---- whole-row select for the rows the lists could not settle ----------
