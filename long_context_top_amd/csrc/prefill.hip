@@ -193,7 +193,7 @@ LCT_DEV void pf_tile_mfma(const char (&buf)[PF_CHUNKS][1024], const intx4 (&qf)[
   }
 }
 
-// LDS accesses of the flush wave, written as inline assembly with the wait
+// LDS accesses of the flush waves, written as inline assembly with the wait
 // inside: the compiler would otherwise drain the vector memory counter before
 // every LDS access (it cannot tell them from the key DMA), which for the flush
 // wave means waiting for all of its earlier stores.
