@@ -35,10 +35,10 @@
 //
 // k_pf_filter waves: 0..7 compute (rows 32*(w%4).., keys 32*(w/4).. of
 // each 64-key tile); wave 8 keeps three key tiles in flight by LDS DMA;
-// wave 9 flushes the candidate rings.  The compute waves issue no global
-// memory operation inside a sweep.  Scores start from -t_r in the MFMA
-// accumulator, so the threshold test and the entry come straight from the
-// accumulated value.
+// waves 9 and 10 flush the candidate rings (64 rows each).  The compute
+// waves issue no global memory operation inside a sweep.  Scores start from
+// -t_r in the MFMA accumulator, so the threshold test and the entry come
+// straight from the accumulated value.
 
 #include <math.h>
 #include <stddef.h>
