@@ -178,11 +178,17 @@ LCT_DEV void attn_gather_k(__amdgpu_buffer_rsrc_t krs, int row_bytes, int ck, co
 }
 
 // V chunks of blocks 2h, 2h+1 of one iteration into half h of the wave's
-// LDS tile by DMA (no registers).  The halves are separate LDS objects, so
-// the compiler can tell that reads of one do not wait for DMA into the other.
-// (Buffer loads rather than global ones: the compiler counts a global load
-// that writes LDS as touching both memories and then waits for every
-// outstanding load whenever any register load result is needed.)
+// LDS tile, lane l's 16 bytes of each 1 KiB piece at byte 16 l.  VREG = false:
+// by DMA (no registers, the wave does not wait); the halves are separate LDS
+// objects, so the compiler can tell that reads of one do not wait for DMA
+// into the other.  (Buffer loads rather than global ones: the compiler counts
+// a global load that writes LDS as touching both memories and then waits for
+// every outstanding load whenever any register load result is needed.)
+// VREG = true: loaded into registers and written to LDS by the wave, which
+// waits for the data there; measured faster for the many-row kernel, whose
+// gathers keep the address unit busy (16.29 -> 15.69 ms per 64K layer), and
+// slower for the decode kernel, whose gathers are latency bound.
+template <bool VREG>
 LCT_DEV void attn_gather_v_half(__amdgpu_buffer_rsrc_t vrs, int row_bytes, int cv,
                                 const int (&pp)[4], int h, char (*vh)[4][1024]) {
 #pragma unroll
@@ -191,8 +197,14 @@ LCT_DEV void attn_gather_v_half(__amdgpu_buffer_rsrc_t vrs, int row_bytes, int c
     // byte offset of the chunk inside the batch entry's V (< 2 GiB)
     const int roff = (pp[j] >= 0 ? pp[j] : 0) * row_bytes + cv * 16;  // < 2 GiB
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vh[jj][st][0], 16, roff + st * 64, 0, 0, 0);
+    for (int st = 0; st < 4; ++st) {
+      if (VREG) {
+        const uintx4 t = __builtin_amdgcn_raw_buffer_load_b128(vrs, roff + st * 64, 0, 0);
+        *reinterpret_cast<uintx4*>(&vh[jj][st][(threadIdx.x & 63) * 16]) = t;
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vh[jj][st][0], 16, roff + st * 64, 0, 0, 0);
+      }
+    }
   }
 }
 
@@ -234,7 +246,7 @@ LCT_DEV AttnLanes attn_lanes(int lane) {
 // the matching half of this iteration's V tile has been read, so both
 // overlap this iteration's MFMA and softmax work; on exit kr, pp, msk and
 // pos describe the next iteration.
-template <int G, bool NEXT>
+template <int G, bool NEXT, bool VREG>
 LCT_DEV void attn_iter(const int32_t* ix, int e0, int e_end, int64_t L, const AttnLanes& a,
                        int (&pos)[4], int (&pp)[4], uint64_t (&msk)[4], bf16x8 (&kr)[4][4],
                        const bf16x8 (&qf)[4], __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
@@ -340,7 +352,7 @@ LCT_DEV void attn_iter(const int32_t* ix, int e0, int e_end, int64_t L, const At
       // blocks 2h, 2h+1 go there
       __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
       compiler_fence();
-      attn_gather_v_half(vrs, row_bytes, a.cv, ppn, h, vh);
+      attn_gather_v_half<VREG>(vrs, row_bytes, a.cv, ppn, h, vh);
     }
     bf16x8 pf;
 #pragma unroll
@@ -365,7 +377,7 @@ LCT_DEV void attn_iter(const int32_t* ix, int e0, int e_end, int64_t L, const At
 // return m is the running maximum (exp2 domain), lsum the denominator of the
 // lane's head and o = O^T (unnormalised); called with m = -inf, o = 0.  `pos` holds the first iteration's entries
 // (attn_entries).  Entries that are -1 or outside [0, L) are skipped.
-template <int G>
+template <int G, bool VREG>
 LCT_DEV void attn_span(const int32_t* ix, int e_begin, int e_end, int (&pos)[4],
                        const bf16x8 (&qf)[4], const uint16_t* kbase, const uint16_t* vbase,
                        size_t row_stride, int64_t L, float scale_log2, char (*vta)[4][1024],
@@ -384,16 +396,16 @@ LCT_DEV void attn_span(const int32_t* ix, int e_begin, int e_end, int (&pos)[4],
   bf16x8 kr[4][4];
   attn_gather_k(krs, row_bytes, a.ck, pp, kr);
   attn_entries(ix, e_begin + ATT_STEP, e_end, a.tk, pos);  // the next iteration's entries
-  attn_gather_v_half(vrs, row_bytes, a.cv, pp, 0, vta);
-  attn_gather_v_half(vrs, row_bytes, a.cv, pp, 1, vtb);
+  attn_gather_v_half<VREG>(vrs, row_bytes, a.cv, pp, 0, vta);
+  attn_gather_v_half<VREG>(vrs, row_bytes, a.cv, pp, 1, vtb);
   // the softmax denominator accumulates on the MFMA (every row of lacc holds
   // the sum of this lane's head)
   floatx4 lacc = floatx4{0.f, 0.f, 0.f, 0.f};
   int e0 = e_begin;
   for (; e0 + ATT_STEP < e_end; e0 += ATT_STEP)
-    attn_iter<G, true>(ix, e0, e_end, L, a, pos, pp, msk, kr, qf, krs, vrs, row_bytes, scale_log2, vta,
+    attn_iter<G, true, VREG>(ix, e0, e_end, L, a, pos, pp, msk, kr, qf, krs, vrs, row_bytes, scale_log2, vta,
                        vtb, m, lacc, o);
-  attn_iter<G, false>(ix, e0, e_end, L, a, pos, pp, msk, kr, qf, krs, vrs, row_bytes, scale_log2, vta,
+  attn_iter<G, false, VREG>(ix, e0, e_end, L, a, pos, pp, msk, kr, qf, krs, vrs, row_bytes, scale_log2, vta,
                       vtb, m, lacc, o);
   lsum = lacc[0];
 }
@@ -437,7 +449,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn(
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   const size_t row_stride = (size_t)Hkv * D;  // elements between positions
-  attn_span<G>(ix, e_begin, e_end, pos, qf, k + ((size_t)b * L * Hkv + kvh) * D,
+  attn_span<G, false>(ix, e_begin, e_end, pos, qf, k + ((size_t)b * L * Hkv + kvh) * D,
                v + ((size_t)b * L * Hkv + kvh) * D, row_stride, L, scale_log2, vta[wid], vtb[wid], lane, m,
                lsum, o);
 
@@ -626,7 +638,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void k_sparse_attn_seg(
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   const size_t row_stride = (size_t)Hkv * D;
-  attn_span<G>(ix, e_begin, e_end, pos, qf, k + ((size_t)b * L * Hkv + kvh) * D,
+  attn_span<G, true>(ix, e_begin, e_end, pos, qf, k + ((size_t)b * L * Hkv + kvh) * D,
                v + ((size_t)b * L * Hkv + kvh) * D, row_stride, L, scale_log2, vta[wid], vtb[wid], lane, m,
                lsum, o);
 
