@@ -652,14 +652,14 @@ def bench_prefill_indexer(cfg, steps, warmup, want_cpu=False, attention=True):
                         "us_per_launch": ms * 1e3}}
     del g
     if attention:
-        attn = bench_prefill_attention(cfg, out, max(5, steps // 5), warmup)
+        attn = bench_prefill_attention(cfg, out, max(5, steps), warmup)
         res["attention"] = attn
     del qi, ki, out, ws
     torch.cuda.empty_cache()
     if attention:
         # the whole prefill of the 28-layer stack: one layer group through the
         # driver (its index, then its layers' attention), times the groups
-        grp = bench_prefill_group(cfg, max(3, steps // 10), 1)
+        grp = bench_prefill_group(cfg, max(3, steps // 5), 1)
         step_ms = cfg.n_groups * grp["ms_per_group"]
         res.update({"group_run": grp, "prefill_ms_all_layers": step_ms,
                     "prefill_tokens_per_s": cfg.L / (step_ms * 1e-3)})
@@ -946,10 +946,10 @@ def main():
             gc.collect()
             torch.cuda.empty_cache()
             log("GSA workloads ...")
-            gsteps = max(10, args.steps // 2)
+            gsteps = max(10, args.steps)
             res["gsa_decode"] = bench_gsa(C.GSA_128K, gsteps, 2, want_cpu=not args.no_cpu_baseline)
             res["hgsa_decode"] = bench_gsa(C.HGSA_128K, gsteps, 2, want_cpu=not args.no_cpu_baseline)
-            res["gsa_prefill"] = bench_gsa_prefill(C.GSA_PREFILL_128K, max(5, args.steps // 10), 1,
+            res["gsa_prefill"] = bench_gsa_prefill(C.GSA_PREFILL_128K, max(5, args.steps), 1,
                                                    want_cpu=not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
