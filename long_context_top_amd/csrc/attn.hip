@@ -18,9 +18,10 @@
 //   * fp32 online softmax per head (running max and sum, exp2 domain);
 //   * O^T += V^T P^T on the same MFMA: P^T from the C fragments is already in
 //     B-operand layout (the k order inside the MFMA is a fixed permutation of
-//     32 tokens); the V pieces go from memory straight into LDS (buffer loads
-//     to LDS, no registers) and are read back transposed with
-//     ds_read_b64_tr_b16 (4 tokens x 4 features per lane);
+//     32 tokens); the V pieces go into the wave's LDS tile (decode: buffer
+//     loads to LDS, no registers; many rows: through registers and LDS
+//     stores) and are read back transposed with ds_read_b64_tr_b16 (4 tokens
+//     x 4 features per lane);
 //   * software pipelined: the next 64 positions' gathers are in flight while
 //     this iteration's MFMA and softmax run.
 // Few rows (decode): the index row is split over several waves, each writes
@@ -186,7 +187,7 @@ LCT_DEV void attn_gather_k(__amdgpu_buffer_rsrc_t krs, int row_bytes, int ck, co
 // every outstanding load whenever any register load result is needed.)
 // VREG = true: loaded into registers and written to LDS by the wave, which
 // waits for the data there; measured faster for the many-row kernel, whose
-// gathers keep the address unit busy (16.29 -> 15.69 ms per 64K layer), and
+// gathers keep the address unit busy (16.3 -> 15.7-15.9 ms per 64K layer), and
 // slower for the decode kernel, whose gathers are latency bound.
 template <bool VREG>
 LCT_DEV void attn_gather_v_half(__amdgpu_buffer_rsrc_t vrs, int row_bytes, int cv,
