@@ -194,8 +194,9 @@ def test_causal_prefill_64k_full_size():
     for j, r in enumerate(rows):
         assert np.array_equal(idx[r], want[j]), r
     # every row below 2048 (nested prefixes and fast-growing overlaps: the
-    # block-union path) and a spread of long rows
-    sample = list(range(0, 2048)) + [2048, 4097, 33333, 65535]
+    # block-union path) and a spread of long rows (one to four 16384-position
+    # segments, merged)
+    sample = list(range(0, 2048)) + [2048, 4097, 16383, 16384, 33333, 65535] + list(range(2559, cfg.L, 1021))
     ref = oracle.prefill_attention_rows(cfg, 2, sample, idx[sample])
     assert np.abs(host(out[2])[0, sample] - ref).max() < ATOL
     del qi, ki, q, k, v, out, idx_out, run
