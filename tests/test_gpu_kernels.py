@@ -569,9 +569,9 @@ def test_gist_score_and_gsa_decode(tail):
 
 def test_gsa_attn_long_and_ragged_chunk_lists():
     """lct_gsa_attn straight from a chunk list: 512 (batch, head) rows of 300
-    chunks each (one split per row, so a wave takes 76 items, more than its
-    preloaded 64), with -1 entries and ids past Nc that are skipped, and a
-    row with no valid chunk (the tail alone).  Rows are compared with the
+    chunks each (one split per row, so a wave takes 76 items in turn), with
+    -1 entries and ids past Nc that are skipped, and a row with no valid
+    chunk (the tail alone).  Rows are compared with the
     oracle over exactly the listed valid chunks' raw rows, their gists and the
     tail."""
     BH, Nc, kc, tail, D = 512, 320, 300, 5, 128
