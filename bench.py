@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, vendor figure
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
+ADDR_PEAK_GBS = 256 * 64 * 2.4  # vector-memory address rate: 256 CUs x 64 B/clk x 2.4 GHz (GB/s)
 MIB = 1 << 20
 
 
@@ -767,6 +768,10 @@ def bench_prefill_attention(cfg, idx, steps, warmup):
             "shared_sets_note": "every row of a 16-row block attends over its first row's set: the block-union path",
             "bf16_tflops": flops / (ms * 1e-3) / 1e12, "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "gathered_gb_per_s": gathered / (ms * 1e-3) / 1e9,
+            # the vector address unit takes 64 bytes (a quad of 16-byte lanes) per
+            # cycle per CU: 256 CUs x 64 B x 2.4 GHz
+            "address_rate_peak_gb_per_s": ADDR_PEAK_GBS,
+            "frac_of_address_rate": gathered / (ms * 1e-3) / 1e9 / ADDR_PEAK_GBS,
             "note": "selected K/V rows are re-read by many rows: the gathers run from L2/MALL, "
                     "bounded by the per-CU address rate (64 B/clk), not HBM"}
 
